@@ -1,0 +1,532 @@
+// Matrix-core products of the LC-VQ layer on gfx950 (bf16 MFMA, float32 accumulate).
+//
+// The decode c = A z + B (LC-QAT summary, Methodology 1) is linear, so A and B are moved
+// off the weight operand and the products run directly on the 2-bit codes, as the
+// summary's training pipeline says ("restructured to use INT2-FP16 matmul kernels",
+// Methodology 3):
+//   forward  Y  = X What^T            = X' Z^T + (X (1 kron B)) 1^T,   X' = X (I kron A)
+//   dX          = dY What             = (dY Z)(I kron A^T) + (dY 1)(1 kron B)^T
+//   dWp, dA, dB from G = dY^T X       (straight-through epilogue on the accumulators)
+// A code c enters a product as v(c) = 2 + c/2, exact in bf16 (see r16_to_vbf16); the
+// constant part is removed through the row terms prepared by the prologue kernels.
+//
+// One kernel template covers the three products. C (P x Q) = sum_r L[p, r] R[q, r] is
+// computed in 256 x 256 tiles by 4 waves (2 x 2, 128 x 128 each, 32x32x16 MFMA), with
+// the contraction staged through LDS in steps of 64 and double-buffered:
+//   FWD: L = X' (bf16 rows m, loaded straight into LDS), R = codes (rows n, expanded)
+//   DX : L = codes transposed (rows k, expanded),        R = dY (bf16 rows m)
+//   DW : L = X^T (rows k, transposed on the way in),     R = dY^T (rows n, transposed)
+#include "lcvq_device.h"
+#include "lcvq_internal.h"
+
+namespace lcvq {
+
+constexpr int BT = 256;        // C tile edge
+constexpr int BK = 64;         // contraction per stage
+constexpr int ROWB = 128;      // bytes per LDS tile row (64 bf16)
+constexpr int TILEB = BT * ROWB;
+
+enum { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
+
+struct GemmArgs {
+  int P, Q, R;                 // C is P x Q; contraction length R
+  int tilesP, tilesQ, ntiles;
+  // Operand matrices per pass. bf16 activations need one pass; float32 activations are
+  // split into bf16 hi + lo and the products add hi*hi + lo*hi (+ hi*lo) over 2-3 passes.
+  const uint16_t* Lmat[3];     // FWD: X' [M][K]; DW: X [M][K]
+  const uint16_t* Rmat[3];     // DX, DW: dY [M][N]
+  int npass;
+  const uint32_t* codes;       // FWD: R16 of Z along k; DX: R16 of Z^T along n (blocked)
+  int M, N, K;
+  const float* rowvec;         // FWD: beta [M]; DX: r [M]
+  const float* A;              // [d][d]
+  const float* B;              // [d]
+  void* out;                   // FWD: Y [M][N]; DX: dX [M][K]
+  int out_f32;
+  float* dwp;                  // DW: [N][K]
+  const uint8_t* packed;       // DW: canonical codes [N][K/4]
+  const uint8_t* mask;         // DW: mask bits [N][K/8]
+  float* partials;             // DW: [ntiles][d*d + d]
+};
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * ROWB + ((chunk ^ swz(row)) << 4); }
+
+// Tiles are spread so that consecutive workgroup ids land on different XCDs (the
+// dispatcher deals workgroups round-robin over the 8 XCDs) while each XCD works on a
+// compact group of 4 tile-rows, which keeps its operand panels in its own L2.
+__device__ __forceinline__ bool map_tile(int b, int tilesP, int tilesQ, int ntiles, int& tp, int& tq, int& t) {
+  const int per = (ntiles + 7) >> 3;
+  t = (b & 7) * per + (b >> 3);
+  if (t >= ntiles) return false;
+  const int GR = 4;
+  const int group = t / (GR * tilesQ);
+  const int within = t - group * GR * tilesQ;
+  int rows = tilesP - group * GR;
+  if (rows > GR) rows = GR;
+  tp = group * GR + within % rows;
+  tq = within / rows;
+  return true;
+}
+
+// ---- loaders -------------------------------------------------------------------------
+// bf16 rows straight into LDS: wave w fills tile rows [64w, 64w+64), 8 rows per
+// instruction; lane l lands at byte 16*l of the instruction's 1 KiB, i.e. row l/8,
+// physical chunk l%8, so it fetches the logical chunk that the swizzle puts there.
+// Rows past the end are clamped to the last row (they only feed C entries that are
+// never stored).
+__device__ __forceinline__ void load_rows_direct(uint8_t* tile, const uint16_t* mat, int64_t ld,
+                                                 int row0, int rows_total, int k0, int wave,
+                                                 int lane) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = wave * 64 + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int g = row0 + r;
+    g = g < rows_total ? g : rows_total - 1;
+    const uint16_t* src = mat + (int64_t)g * ld + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(tile + (wave * 64 + i * 8) * ROWB), 16, 0, 0);
+  }
+}
+
+// R16 codes: thread t owns tile row t; one 16-byte load holds the row's 64 codes.
+__device__ __forceinline__ uint4 load_codes(const uint32_t* codes, int rowblock, int nk, int kt, int tid) {
+  const uint4* src = reinterpret_cast<const uint4*>(codes + ((int64_t)rowblock * nk + kt) * 1024) + tid;
+  return *src;
+}
+__device__ __forceinline__ void store_codes(uint8_t* tile, uint4 w, int tid) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t o[8];
+    r16_to_vbf16(ws[q], o);
+    *reinterpret_cast<uint4*>(tile + lds_off(tid, 2 * q)) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(tile + lds_off(tid, 2 * q + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// Transposing loader: tile row = a column c of the bf16 matrix (c in [c0, c0+256)),
+// tile column = contraction m in [m0, m0+64). Thread t reads an 8 x 8 block (8 rows m,
+// 8 columns) and writes it transposed. Out-of-range rows or columns read as zero.
+__device__ __forceinline__ void load_trans(uint4 v[8], const uint16_t* mat, int64_t ld, int m0,
+                                           int M, int c0, int cols, int tid) {
+  const int cc = tid & 31, mg = tid >> 5;
+  const int col = c0 + cc * 8;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int m = m0 + mg * 8 + r;
+    if (m < M && col < cols)
+      v[r] = *reinterpret_cast<const uint4*>(mat + (int64_t)m * ld + col);
+    else
+      v[r] = make_uint4(0, 0, 0, 0);
+  }
+}
+__device__ __forceinline__ void store_trans(uint8_t* tile, const uint4 v[8], int tid) {
+  const int cc = tid & 31, mg = tid >> 5;
+  uint32_t in[8][4];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) { in[r][0] = v[r].x; in[r][1] = v[r].y; in[r][2] = v[r].z; in[r][3] = v[r].w; }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lo[q] = __builtin_amdgcn_perm(in[2 * q + 1][s], in[2 * q][s], 0x05040100u);
+      hi[q] = __builtin_amdgcn_perm(in[2 * q + 1][s], in[2 * q][s], 0x07060302u);
+    }
+    const int row = cc * 8 + 2 * s;
+    *reinterpret_cast<uint4*>(tile + lds_off(row, mg)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint4*>(tile + lds_off(row + 1, mg)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  }
+}
+
+// ---- one contraction stage of 64 on the current LDS buffers --------------------------
+__device__ __forceinline__ void mma_stage(const uint8_t* Ls, const uint8_t* Rs, f32x16 acc[4][4],
+                                          int wp, int wq, int lane) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int chunk = 2 * s + (lane >> 5);
+    bf16x8 af[4], bf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wp * 128 + i * 32 + (lane & 31);
+      af[i] = *reinterpret_cast<const bf16x8*>(Ls + lds_off(row, chunk));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wq * 128 + j * 32 + (lane & 31);
+      bf[j] = *reinterpret_cast<const bf16x8*>(Rs + lds_off(row, chunk));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, float a, float b, float c, float d) {
+  if (f32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(a, b, c, d);
+  } else {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+  }
+}
+
+// ---- epilogues -----------------------------------------------------------------------
+// Accumulator layout (32x32 block): lane l holds column l%32 and, in register r, row
+// 8*(r/4) + 4*(l/32) + r%4. For DX and DW the rows run along the d-vectors, so each
+// block is first staged through a per-wave LDS area (32 x 33 floats); then every lane
+// takes whole d-vectors of one column, and finally the block is written back to HBM
+// with each group of 8 lanes covering 32 consecutive elements of one output row.
+
+constexpr int SROW = 33;                  // padded row of the staging area (floats)
+constexpr int WAVE_LDS = 32768;           // LDS bytes per wave in the epilogue
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void stage_block(float* S, const f32x16& acc, int lane) {
+  const int col = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S[(8 * (r >> 2) + 4 * h + (r & 3)) * SROW + col] = acc[r];
+}
+
+// Writes a staged 32 x 32 block (rows = contraction-side index k, columns = output row)
+// transposed to out[row][k] (row stride ld elements), float32 or bf16.
+__device__ __forceinline__ void store_block_rows(const float* S, void* out, int f32, int64_t ld,
+                                                 int row0, int rows, int k0, int K, int lane) {
+  const int kq = (lane & 7) * 4;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int rr = it * 8 + (lane >> 3);
+    const int row = row0 + rr;
+    if (row < rows && k0 + kq < K) {
+      const float v0 = S[(kq + 0) * SROW + rr], v1 = S[(kq + 1) * SROW + rr];
+      const float v2 = S[(kq + 2) * SROW + rr], v3 = S[(kq + 3) * SROW + rr];
+      store_out4(out, f32, (int64_t)row * ld + k0 + kq, v0, v1, v2, v3);
+    }
+  }
+}
+
+// dX[m, g*d+i] = 2 sum_j A[i][j] C[g*d+j, m] + (B[i] - 4 sum_j A[i][j]) r[m]
+// where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m).
+template <int D>
+__device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0, int wp, int wq,
+                            int lane, float* S, const float* Alds) {
+  float bp[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < D; ++j) s += a.A[i * D + j];
+    bp[i] = a.B[i] - 4.f * s;
+  }
+  const int q = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kb = p0 + wp * 128 + i * 32;
+      const int mb = q0 + wq * 128 + j * 32;
+      wave_sync();
+      stage_block(S, acc[i][j], lane);
+      wave_sync();
+      const int m = mb + q;
+      const float rm = m < a.M ? a.rowvec[m] : 0.f;
+      // Re-read A from the scalar cache for every block instead of keeping d*d values
+      // live across the unrolled block sequence.
+      const float* Ab = D == 16 ? Alds : a.A;
+      if (D == 16) asm volatile("" : "+v"(Ab));
+      else asm volatile("" : "+s"(Ab));
+      for (int sl = lane >> 5; sl < 32 / D; sl += 2) {
+        float T[D];
+#pragma unroll
+        for (int e = 0; e < D; ++e) T[e] = S[(sl * D + e) * SROW + q];
+#pragma unroll
+        for (int ii = 0; ii < D; ++ii) {
+          float s = 0.f;
+#pragma unroll
+          for (int e = 0; e < D; ++e) s = __builtin_fmaf(Ab[ii * D + e], T[e], s);
+          S[(sl * D + ii) * SROW + q] = __builtin_fmaf(2.f, s, bp[ii] * rm);
+        }
+      }
+      wave_sync();
+      store_block_rows(S, a.out, a.out_f32, a.K, mb, a.M, kb, a.K, lane);
+    }
+}
+
+// Straight-through epilogue on G (rows k, columns n):
+//   dWp[n, g*d+j] = mask * sum_i A[i][j] G[g*d+i, n]
+//   dA[i][j] += G[g*d+i, n] z[n, g*d+j],   dB[i] += G[g*d+i, n]
+// Per-lane partial sums are reduced over the wave through LDS, then over the 4 waves,
+// in a fixed order, into this tile's slot of `partials`.
+template <int D>
+__device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0, int wp, int wq,
+                            int lane, int wave, int tile, uint8_t* smem, const float* Alds) {
+  constexpr int NP = D == 16 ? 4 : 1;          // passes over the columns j of dA
+  constexpr int JW = D / NP;
+  constexpr int NA = D * JW;                   // dA partials per lane and pass
+  constexpr int NR = NA + D;                   // + dB partials (first pass)
+  constexpr int RROW = NR + 1;
+  float* S = reinterpret_cast<float*>(smem + wave * WAVE_LDS);
+  float* red = S;                              // reused after the blocks of a pass
+  float* wsum = reinterpret_cast<float*>(smem + 4 * WAVE_LDS - 4 * NP * NR * 4);
+  const int q = lane & 31;
+  float dB[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) dB[e] = 0.f;
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+    float dA[NA];
+#pragma unroll
+    for (int x = 0; x < NA; ++x) dA[x] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = p0 + wp * 128 + i * 32;
+        const int nb = q0 + wq * 128 + j * 32;
+        wave_sync();
+        stage_block(S, acc[i][j], lane);
+        wave_sync();
+        const int n = nb + q;
+        const float* Ab = D == 16 ? Alds : a.A;
+        if (D == 16) asm volatile("" : "+v"(Ab));
+        else asm volatile("" : "+s"(Ab));
+        for (int sl = lane >> 5; sl < 32 / D; sl += 2) {
+          const int kv = kb + sl * D;
+          float T[D];
+#pragma unroll
+          for (int e = 0; e < D; ++e) T[e] = S[(sl * D + e) * SROW + q];
+          uint32_t zw = 0, mw = 0;
+          if (n < a.N && kv < a.K) {
+            const uint8_t* zp = a.packed + (int64_t)n * (a.K >> 2) + (kv >> 2);
+            const uint8_t* mp = a.mask + (int64_t)n * (a.K >> 3) + (kv >> 3);
+            if (D == 4) { zw = zp[0]; mw = (mp[0] >> (kv & 4)) & 0xFu; }
+            if (D == 8) { zw = *reinterpret_cast<const uint16_t*>(zp); mw = mp[0]; }
+            if (D == 16) { zw = *reinterpret_cast<const uint32_t*>(zp); mw = *reinterpret_cast<const uint16_t*>(mp); }
+          }
+          if (pass == 0) {
+#pragma unroll
+            for (int jj = 0; jj < D; ++jj) {
+              float s = 0.f;
+#pragma unroll
+              for (int e = 0; e < D; ++e) s = __builtin_fmaf(Ab[e * D + jj], T[e], s);
+              S[(sl * D + jj) * SROW + q] = ((mw >> jj) & 1u) ? s : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < D; ++e) dB[e] += T[e];
+          }
+#pragma unroll
+          for (int jj = 0; jj < JW; ++jj) {
+            const float zj = (float)((zw >> (2 * (pass * JW + jj))) & 3u);
+#pragma unroll
+            for (int e = 0; e < D; ++e) dA[e * JW + jj] = __builtin_fmaf(T[e], zj, dA[e * JW + jj]);
+          }
+        }
+        if (pass == 0) {
+          wave_sync();
+          store_block_rows(S, a.dwp, 1, a.K, nb, a.N, kb, a.K, lane);
+        }
+      }
+    // wave reduction through LDS: lane l writes its row, then lane l sums column(s)
+    wave_sync();
+#pragma unroll
+    for (int x = 0; x < NA; ++x) red[lane * RROW + x] = dA[x];
+#pragma unroll
+    for (int x = 0; x < D; ++x) red[lane * RROW + NA + x] = pass == 0 ? dB[x] : 0.f;
+    wave_sync();
+    for (int x = lane; x < NR; x += 64) {
+      float s = 0.f;
+      for (int l = 0; l < 64; ++l) s += red[l * RROW + x];
+      wsum[(pass * 4 + wave) * NR + x] = s;
+    }
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < D * D + D; o += blockDim.x) {
+    float s = 0.f;
+    if (o < D * D) {
+      const int e = o / D, jj = o % D;
+      const int pass = jj / JW, x = e * JW + (jj % JW);
+      for (int w = 0; w < 4; ++w) s += wsum[(pass * 4 + w) * NR + x];
+    } else {
+      const int x = NA + (o - D * D);
+      for (int w = 0; w < 4; ++w) s += wsum[(0 * 4 + w) * NR + x];
+    }
+    a.partials[(int64_t)tile * (D * D + D) + o] = s;
+  }
+}
+
+// ---- the kernel ----------------------------------------------------------------------
+template <int OP, int D>
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];
+  int tp, tq, tile;
+  if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
+  const int p0 = tp * BT, q0 = tq * BT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wp = wave >> 1, wq = wave & 1;
+  const int nk = (a.R + BK - 1) / BK;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  uint4 creg = make_uint4(0, 0, 0, 0);
+  uint4 lreg[8], rreg[8];
+
+  auto issue = [&](int st, int buf) {
+    uint8_t* Ls = smem + buf * 2 * TILEB;
+    uint8_t* Rs = Ls + TILEB;
+    const int pass = st / nk, kt = st - pass * nk;
+    const int k0 = kt * BK;
+    if (OP == OP_FWD) {
+      load_rows_direct(Ls, a.Lmat[pass], a.K, p0, a.M, k0, wave, lane);
+      creg = load_codes(a.codes, tq, nk, kt, tid);
+    } else if (OP == OP_DX) {
+      creg = load_codes(a.codes, tp, nk, kt, tid);
+      load_rows_direct(Rs, a.Rmat[pass], a.N, q0, a.M, k0, wave, lane);
+    } else {
+      load_trans(lreg, a.Lmat[pass], a.K, k0, a.M, p0, a.K, tid);
+      load_trans(rreg, a.Rmat[pass], a.N, k0, a.M, q0, a.N, tid);
+    }
+  };
+  auto commit = [&](int buf) {
+    uint8_t* Ls = smem + buf * 2 * TILEB;
+    uint8_t* Rs = Ls + TILEB;
+    if (OP == OP_FWD) store_codes(Rs, creg, tid);
+    else if (OP == OP_DX) store_codes(Ls, creg, tid);
+    else { store_trans(Ls, lreg, tid); store_trans(Rs, rreg, tid); }
+  };
+
+  const int nst = nk * a.npass;
+  issue(0, 0);
+  commit(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    if (st + 1 < nst) issue(st + 1, cur ^ 1);
+    mma_stage(smem + cur * 2 * TILEB, smem + cur * 2 * TILEB + TILEB, acc, wp, wq, lane);
+    if (st + 1 < nst) commit(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (OP == OP_FWD) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = q0 + wq * 128 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = p0 + wp * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (p < a.M && q < a.N) {
+            const float v = acc[i][j][r] + a.rowvec[p];
+            if (a.out_f32) static_cast<float*>(a.out)[(int64_t)p * a.N + q] = v;
+            else static_cast<__bf16*>(a.out)[(int64_t)p * a.N + q] = (__bf16)v;
+          }
+        }
+      }
+  } else {
+    // Main-loop buffers are free after the last barrier. For d = 16 a copy of A sits
+    // in LDS (bytes [120 KiB, 121 KiB), clear of the staging and reduction areas).
+    float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
+    if (D == 16) {
+      if (tid < D * D) Alds[tid] = a.A[tid];
+      __syncthreads();
+    }
+    if (OP == OP_DX) epilogue_dx<D>(a, acc, p0, q0, wp, wq, lane, reinterpret_cast<float*>(smem + wave * WAVE_LDS), Alds);
+    else epilogue_dw<D>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
+  }
+}
+
+// Fixed-order sum of the per-tile dA / dB partials.
+__global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ partials,
+                                                         int ntiles, int nout,
+                                                         float* __restrict__ dA,
+                                                         float* __restrict__ dB, int d) {
+  for (int o = threadIdx.x; o < nout; o += blockDim.x) {
+    float s = 0.f;
+    for (int t = 0; t < ntiles; ++t) s += partials[(int64_t)t * nout + o];
+    if (o < d * d) dA[o] = s;
+    else dB[o - d * d] = s;
+  }
+}
+
+// ---- launchers -----------------------------------------------------------------------
+template <int OP>
+static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
+  a.tilesP = (a.P + BT - 1) / BT;
+  a.tilesQ = (a.Q + BT - 1) / BT;
+  a.ntiles = a.tilesP * a.tilesQ;
+  const int grid = ((a.ntiles + 7) / 8) * 8;
+  switch (d) {
+    case 4: hipLaunchKernelGGL((k_gemm<OP, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_gemm<OP, 8>), dim3(grid), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm<OP, 16>), dim3(grid), dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+int gemm_tiles(int64_t P, int64_t Q) { return (int)(((P + BT - 1) / BT) * ((Q + BT - 1) / BT)); }
+
+hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint32_t* r16,
+                           const float* beta, int M, int N, int K, int d, void* Y, bool y_f32,
+                           hipStream_t s) {
+  GemmArgs a = {};
+  a.P = M; a.Q = N; a.R = K;
+  a.Lmat[0] = xs; a.Lmat[1] = xs_lo;
+  a.npass = xs_lo ? 2 : 1;
+  a.codes = r16; a.rowvec = beta;
+  a.M = M; a.N = N; a.K = K;
+  a.out = Y; a.out_f32 = y_f32;
+  return launch_op<OP_FWD>(a, d, s);
+}
+
+hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16_t* dy_lo,
+                          const float* r, const float* A, const float* B, int M, int N, int K,
+                          int d, void* dX, bool f32, hipStream_t s) {
+  GemmArgs a = {};
+  a.P = K; a.Q = M; a.R = N;
+  a.codes = r16t;
+  a.Rmat[0] = dy; a.Rmat[1] = dy_lo;
+  a.npass = dy_lo ? 2 : 1;
+  a.rowvec = r; a.A = A; a.B = B;
+  a.M = M; a.N = N; a.K = K;
+  a.out = dX; a.out_f32 = f32;
+  return launch_op<OP_DX>(a, d, s);
+}
+
+hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_t* dy,
+                          const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
+                          const float* A, int M, int N, int K, int d, float* dWp,
+                          float* partials, float* dA, float* dB, hipStream_t s) {
+  GemmArgs a = {};
+  a.P = K; a.Q = N; a.R = M;
+  a.Lmat[0] = x; a.Rmat[0] = dy;
+  a.npass = 1;
+  if (x_lo && dy_lo) {        // hi*hi + lo*hi + hi*lo
+    a.Lmat[1] = x_lo; a.Rmat[1] = dy;
+    a.Lmat[2] = x; a.Rmat[2] = dy_lo;
+    a.npass = 3;
+  }
+  a.A = A;
+  a.M = M; a.N = N; a.K = K;
+  a.dwp = dWp; a.packed = packed; a.mask = mask; a.partials = partials;
+  hipError_t e = launch_op<OP_DW>(a, d, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_reduce_partials, dim3(1), dim3(256), 0, s, partials, a.ntiles,
+                     d * d + d, dA, dB, d);
+  return hipGetLastError();
+}
+
+}  // namespace lcvq

@@ -1,0 +1,234 @@
+// C ABI of the LC-VQ library: argument checks, workspace carving and kernel launch order.
+// Declarations and the contract of every call are in include/lcvq.h.
+#include "lcvq.h"
+#include "lcvq_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+using namespace lcvq;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool d_ok(int d) { return d == 4 || d == 8 || d == 16; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+inline lcvq_status_t from_hip(hipError_t e) { return e == hipSuccess ? LCVQ_OK : LCVQ_ERR_HIP; }
+
+// Linear-layer shapes: M rows of activations, weight [N, K].
+inline bool layer_shape_ok(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > INT32_MAX) return false;
+  if (N < 64 || K < 64 || (N % 64) || (K % 64)) return false;
+  if (N > INT32_MAX || K > INT32_MAX) return false;
+  if (N * K >= (int64_t(1) << 40)) return false;
+  return true;
+}
+
+// Blocked R16 code words for `rows` operand rows and a contraction of length `kc`.
+inline size_t r16_bytes(int64_t rows, int64_t kc) {
+  return (size_t)((rows + 255) / 256) * 256 * (size_t)(kc / 16) * 4;
+}
+
+struct FwdWs {
+  size_t xs, beta, r16, xs_lo, total;
+};
+inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, bool f32) {
+  FwdWs w;
+  w.xs = 0;
+  w.beta = w.xs + up((size_t)M * K * 2);
+  w.r16 = w.beta + up((size_t)M * 4);
+  w.xs_lo = w.r16 + up(r16_bytes(N, K));
+  w.total = w.xs_lo + (f32 ? up((size_t)M * K * 2) : 0);
+  return w;
+}
+
+struct BwdWs {
+  size_t r, r16t, partials, dy_hi, dy_lo, x_hi, x_lo, total;
+};
+inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int d, bool f32) {
+  BwdWs w;
+  w.r = 0;
+  w.r16t = w.r + up((size_t)M * 4);
+  w.partials = w.r16t + up(r16_bytes(K, N));
+  const size_t ntiles = (size_t)gemm_tiles(K, N);
+  w.dy_hi = w.partials + up(ntiles * (size_t)(d * d + d) * 4);
+  const size_t dyb = f32 ? up((size_t)M * N * 2) : 0, xb = f32 ? up((size_t)M * K * 2) : 0;
+  w.dy_lo = w.dy_hi + dyb;
+  w.x_hi = w.dy_lo + dyb;
+  w.x_lo = w.x_hi + xb;
+  w.total = w.x_lo + xb;
+  return w;
+}
+
+struct GemvWs {
+  size_t xq, rowinfo, total;
+};
+inline GemvWs gemv_ws(int64_t K) {
+  GemvWs w;
+  const size_t nkb = (size_t)(K / 256);
+  w.xq = 0;
+  w.rowinfo = up(nkb * 4 * 2 * 1024);
+  w.total = w.rowinfo + up(nkb * 16 * 8);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lcvq_status_string(lcvq_status_t s) {
+  switch (s) {
+    case LCVQ_OK: return "ok";
+    case LCVQ_ERR_NULL: return "a required pointer is NULL";
+    case LCVQ_ERR_SHAPE: return "shape outside the supported limits";
+    case LCVQ_ERR_D: return "d must be 4, 8 or 16";
+    case LCVQ_ERR_DTYPE: return "unknown dtype";
+    case LCVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case LCVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case LCVQ_ERR_HIP: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+lcvq_status_t lcvq_quantize(const float* Wp, int64_t N, int64_t K, uint8_t* z_u8,
+                            uint8_t* packed, uint8_t* mask, void* stream) {
+  if (!Wp) return LCVQ_ERR_NULL;
+  if (N < 1 || K < 16 || (K % 16) || N * K >= (int64_t(1) << 40)) return LCVQ_ERR_SHAPE;
+  if (!aligned16(Wp) || !aligned16(z_u8) || !aligned16(packed) || !aligned16(mask))
+    return LCVQ_ERR_ALIGN;
+  if (!z_u8 && !packed && !mask) return LCVQ_OK;
+  return from_hip(launch_quantize(Wp, N, K, z_u8, packed, mask, nullptr, nullptr, nullptr,
+                                  nullptr, 4, as_stream(stream)));
+}
+
+lcvq_status_t lcvq_pack2b(const uint8_t* z_u8, int64_t N, int64_t K, uint8_t* packed,
+                          void* stream) {
+  if (!z_u8 || !packed) return LCVQ_ERR_NULL;
+  if (N < 1 || K < 16 || (K % 16) || N * K >= (int64_t(1) << 40)) return LCVQ_ERR_SHAPE;
+  if (!aligned16(z_u8) || !aligned16(packed)) return LCVQ_ERR_ALIGN;
+  return from_hip(launch_pack2b(z_u8, N, K, packed, as_stream(stream)));
+}
+
+lcvq_status_t lcvq_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t* z_u8,
+                            void* stream) {
+  if (!z_u8 || !packed) return LCVQ_ERR_NULL;
+  if (N < 1 || K < 16 || (K % 16) || N * K >= (int64_t(1) << 40)) return LCVQ_ERR_SHAPE;
+  if (!aligned16(z_u8) || !aligned16(packed)) return LCVQ_ERR_ALIGN;
+  return from_hip(launch_unpack2b(packed, N, K, z_u8, as_stream(stream)));
+}
+
+size_t lcvq_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int d) {
+  (void)d;
+  if (!layer_shape_ok(M, N, K)) return 0;
+  return fwd_ws(M, N, K, true).total;   // sized for float32 activations (the larger case)
+}
+
+lcvq_status_t lcvq_linear_fwd(const void* X, lcvq_dtype_t xdt, int64_t M, int64_t N,
+                              int64_t K, int d, const float* Wp, const float* A,
+                              const float* B, void* Y, uint8_t* packed_out,
+                              uint8_t* mask_out, float* What_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!X || !Wp || !A || !B || !Y || !packed_out || !mask_out) return LCVQ_ERR_NULL;
+  if (xdt != LCVQ_F32 && xdt != LCVQ_BF16) return LCVQ_ERR_DTYPE;
+  if (!d_ok(d)) return LCVQ_ERR_D;
+  if (!layer_shape_ok(M, N, K)) return LCVQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(Wp) || !aligned16(A) || !aligned16(B) || !aligned16(Y) ||
+      !aligned16(packed_out) || !aligned16(mask_out) || !aligned16(What_out) ||
+      !aligned16(workspace))
+    return LCVQ_ERR_ALIGN;
+  const bool f32 = xdt == LCVQ_F32;
+  const FwdWs w = fwd_ws(M, N, K, f32);
+  if (!workspace || workspace_bytes < w.total) return LCVQ_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(ws + w.xs);
+  uint16_t* xs_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.xs_lo) : nullptr;
+  float* beta = reinterpret_cast<float*>(ws + w.beta);
+  uint32_t* r16 = reinterpret_cast<uint32_t*>(ws + w.r16);
+  hipError_t e = launch_quantize(Wp, N, K, nullptr, packed_out, mask_out, r16, What_out, A, B,
+                                 d, s);
+  if (e != hipSuccess) return LCVQ_ERR_HIP;
+  e = launch_fwd_prologue(X, f32, M, K, A, B, d, xs, xs_lo, beta, s);
+  if (e != hipSuccess) return LCVQ_ERR_HIP;
+  return from_hip(launch_gemm_fwd(xs, xs_lo, r16, beta, (int)M, (int)N, (int)K, d, Y, f32, s));
+}
+
+size_t lcvq_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int d) {
+  if (!layer_shape_ok(M, N, K) || !d_ok(d)) return 0;
+  // sized for float32 activations (the larger case)
+  return bwd_ws(M, N, K, d, true).total;
+}
+
+lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, int64_t M,
+                              int64_t N, int64_t K, int d, const uint8_t* packed,
+                              const uint8_t* mask, const float* A, const float* B,
+                              void* dX, float* dWp, float* dA, float* dB, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!dY || !X || !packed || !mask || !A || !B || !dWp || !dA || !dB) return LCVQ_ERR_NULL;
+  if (dt != LCVQ_F32 && dt != LCVQ_BF16) return LCVQ_ERR_DTYPE;
+  if (!d_ok(d)) return LCVQ_ERR_D;
+  if (!layer_shape_ok(M, N, K)) return LCVQ_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(X) || !aligned16(packed) || !aligned16(mask) ||
+      !aligned16(A) || !aligned16(B) || !aligned16(dX) || !aligned16(dWp) || !aligned16(dA) ||
+      !aligned16(dB) || !aligned16(workspace))
+    return LCVQ_ERR_ALIGN;
+  const bool f32 = dt == LCVQ_F32;
+  const BwdWs w = bwd_ws(M, N, K, d, f32);
+  if (!workspace || workspace_bytes < w.total) return LCVQ_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* r = reinterpret_cast<float*>(ws + w.r);
+  uint32_t* r16t = reinterpret_cast<uint32_t*>(ws + w.r16t);
+  float* partials = reinterpret_cast<float*>(ws + w.partials);
+  uint16_t* dy_hi = f32 ? reinterpret_cast<uint16_t*>(ws + w.dy_hi) : nullptr;
+  uint16_t* dy_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.dy_lo) : nullptr;
+  uint16_t* x_hi = f32 ? reinterpret_cast<uint16_t*>(ws + w.x_hi) : nullptr;
+  uint16_t* x_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.x_lo) : nullptr;
+  hipError_t e = launch_bwd_prologue(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi, x_lo, s);
+  if (e != hipSuccess) return LCVQ_ERR_HIP;
+  const uint16_t* dyb = f32 ? dy_hi : static_cast<const uint16_t*>(dY);
+  const uint16_t* xb = f32 ? x_hi : static_cast<const uint16_t*>(X);
+  if (dX) {
+    e = launch_codes_to_r16t(packed, N, K, r16t, s);
+    if (e != hipSuccess) return LCVQ_ERR_HIP;
+    e = launch_gemm_dx(r16t, dyb, dy_lo, r, A, B, (int)M, (int)N, (int)K, d, dX, f32, s);
+    if (e != hipSuccess) return LCVQ_ERR_HIP;
+  }
+  return from_hip(launch_gemm_dw(xb, x_lo, dyb, dy_lo, packed, mask, A, (int)M, (int)N,
+                                 (int)K, d, dWp, partials, dA, dB, s));
+}
+
+size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t K, int d) {
+  (void)d;
+  if (M < 1 || M > 16 || K < 256 || (K % 256) || K > INT32_MAX) return 0;
+  return gemv_ws(K).total;
+}
+
+lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                          const uint8_t* packed, const void* A16, const void* B16, void* Y,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!X || !packed || !A16 || !B16 || !Y) return LCVQ_ERR_NULL;
+  if (!d_ok(d)) return LCVQ_ERR_D;
+  if (M < 1 || M > 16 || N < 16 || (N % 16) || K < 256 || (K % 256) || N > INT32_MAX ||
+      K > INT32_MAX || N * K >= (int64_t(1) << 40))
+    return LCVQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(packed) || !aligned16(A16) || !aligned16(B16) ||
+      !aligned16(Y) || !aligned16(workspace))
+    return LCVQ_ERR_ALIGN;
+  const GemvWs w = gemv_ws(K);
+  if (!workspace || workspace_bytes < w.total) return LCVQ_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  int8_t* xq = reinterpret_cast<int8_t*>(ws + w.xq);
+  float* rowinfo = reinterpret_cast<float*>(ws + w.rowinfo);
+  hipError_t e = launch_gemv_prologue(static_cast<const uint16_t*>(X), (int)M, (int)K,
+                                      static_cast<const uint16_t*>(A16),
+                                      static_cast<const uint16_t*>(B16), d, xq, rowinfo, s);
+  if (e != hipSuccess) return LCVQ_ERR_HIP;
+  return from_hip(launch_gemv(xq, rowinfo, packed, (int)M, (int)N, (int)K,
+                              static_cast<uint16_t*>(Y), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal launchers of the LC-VQ kernels (not part of the public ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lcvq {
+
+hipError_t launch_quantize(const float* wp, int64_t N, int64_t K, uint8_t* z, uint8_t* packed,
+                           uint8_t* mask, uint32_t* r16, float* what, const float* A,
+                           const float* B, int d, hipStream_t s);
+hipError_t launch_pack2b(const uint8_t* z, int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
+hipError_t launch_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t* z, hipStream_t s);
+hipError_t launch_codes_to_r16t(const uint8_t* packed, int64_t N, int64_t K, uint32_t* r16t,
+                                hipStream_t s);
+hipError_t launch_fwd_prologue(const void* X, bool x_f32, int64_t M, int64_t K, const float* A,
+                               const float* B, int d, uint16_t* xs, uint16_t* xs_lo,
+                               float* beta, hipStream_t s);
+hipError_t launch_bwd_prologue(const void* dY, const void* X, bool f32, int64_t M, int64_t N,
+                               int64_t K, float* r, uint16_t* dy_hi, uint16_t* dy_lo,
+                               uint16_t* x_hi, uint16_t* x_lo, hipStream_t s);
+
+int gemm_tiles(int64_t P, int64_t Q);
+// Products. `*_lo` operands are NULL for bf16 activations; for float32 activations
+// they hold the low bf16 half of each value and add the cross terms in extra passes.
+hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint32_t* r16,
+                           const float* beta, int M, int N, int K, int d, void* Y, bool y_f32,
+                           hipStream_t s);
+hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16_t* dy_lo,
+                          const float* r, const float* A, const float* B, int M, int N, int K,
+                          int d, void* dX, bool f32, hipStream_t s);
+hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_t* dy,
+                          const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
+                          const float* A, int M, int N, int K, int d, float* dWp,
+                          float* partials, float* dA, float* dB, hipStream_t s);
+
+hipError_t launch_gemv_prologue(const uint16_t* X, int M, int K, const uint16_t* A16,
+                                const uint16_t* B16, int d, int8_t* xq, float* rowinfo,
+                                hipStream_t s);
+hipError_t launch_gemv(const int8_t* xq, const float* rowinfo, const uint8_t* packed, int M,
+                       int N, int K, uint16_t* Y, hipStream_t s);
+
+}  // namespace lcvq

@@ -1,0 +1,338 @@
+// Elementwise and layout kernels of the LC-VQ path (gfx950):
+//  * the quantizer z = clamp(round(Wp), 0, 3) with mask, packing and an optional
+//    float32 decode (LC-QAT summary, Methodology 1 and 3);
+//  * 2-bit pack / unpack;
+//  * the transposed code layout the dX product reads;
+//  * the forward prologue X' = X (I kron A) and the backward prologue r = dY 1.
+// All are HBM-bound: each thread owns 16 consecutive elements so that its codes form
+// exactly one 32-bit packed word, and every d-vector (d <= 16) lies inside one thread.
+#include "lcvq_device.h"
+#include "lcvq_internal.h"
+
+namespace lcvq {
+
+// Index of the R16 word holding codes (row, 16*w .. 16*w+15) in the blocked layout
+// the GEMM loaders read: rows in blocks of 256, contraction in steps of 64, and each
+// (row block, step) slab of 256 rows x 4 words contiguous (4 KiB).
+__device__ __forceinline__ int64_t r16_blocked_index(int64_t row, int64_t w, int64_t ksteps) {
+  return ((row >> 8) * ksteps + (w >> 2)) * 1024 + (row & 255) * 4 + (w & 3);
+}
+
+// ------------------------------------------------------------------ quantizer
+__global__ __launch_bounds__(256) void k_quantize(
+    const float* __restrict__ wp, int64_t groups /* N*K/16 */, int64_t K,
+    uint8_t* __restrict__ z_out, uint32_t* __restrict__ packed_out,
+    uint16_t* __restrict__ mask_out, uint32_t* __restrict__ r16_out,
+    float* __restrict__ what_out, const float* __restrict__ A,
+    const float* __restrict__ B, int d) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4* src = reinterpret_cast<const f4*>(wp) + gi * 4;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f4 f = __builtin_nontemporal_load(src + q);
+      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    }
+    uint32_t c[16];
+    uint32_t packed = 0, mbits = 0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float r = __builtin_rintf(v[t]);                // round half to even
+      // Comparisons are false for NaN, so NaN -> code 0; +inf -> 3; -inf -> 0.
+      c[t] = (uint32_t)(r >= 1.0f) + (uint32_t)(r >= 2.0f) + (uint32_t)(r >= 3.0f);
+      mbits |= (uint32_t)((r >= 0.0f) & (r <= 3.0f)) << t;
+      packed |= c[t] << (2 * t);
+    }
+    if (packed_out) packed_out[gi] = packed;
+    if (mask_out) mask_out[gi] = (uint16_t)mbits;
+    if (z_out) {
+      uint4 zz;
+      zz.x = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
+      zz.y = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
+      zz.z = c[8] | c[9] << 8 | c[10] << 16 | c[11] << 24;
+      zz.w = c[12] | c[13] << 8 | c[14] << 16 | c[15] << 24;
+      reinterpret_cast<uint4*>(z_out)[gi] = zz;
+    }
+    if (r16_out) {
+      const int64_t e = gi * 16;
+      const int64_t row = e / K;
+      const int64_t w = (e - row * K) >> 4;
+      r16_out[r16_blocked_index(row, w, K >> 6)] = r16_encode(c);
+    }
+    if (what_out) {
+      // What[n, g*d+i] = B[i] + sum_j A[i][j] z[n, g*d+j], in float32.
+      float o[16];
+      for (int v0 = 0; v0 < 16; v0 += d) {
+        for (int i = 0; i < d; ++i) {
+          float s = B[i];
+          for (int j = 0; j < d; ++j) s = __builtin_fmaf(A[i * d + j], (float)c[v0 + j], s);
+          o[v0 + i] = s;
+        }
+      }
+      float4* dst = reinterpret_cast<float4*>(what_out) + gi * 4;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ pack / unpack
+__global__ __launch_bounds__(256) void k_pack2b(const uint8_t* __restrict__ z, int64_t groups,
+                                                uint32_t* __restrict__ packed) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
+    const uint4 q = reinterpret_cast<const uint4*>(z)[gi];
+    const uint32_t in[4] = {q.x, q.y, q.z, q.w};
+    uint32_t p = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) p |= ((in[b] >> (8 * t)) & 3u) << (2 * (4 * b + t));
+    packed[gi] = p;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_unpack2b(const uint32_t* __restrict__ packed,
+                                                  int64_t groups, uint8_t* __restrict__ z) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
+    const uint32_t p = packed[gi];
+    uint32_t o[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      o[b] = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[b] |= ((p >> (2 * (4 * b + t))) & 3u) << (8 * t);
+    }
+    reinterpret_cast<uint4*>(z)[gi] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// ------------------------------------------------------------------ transposed codes
+// Canonical packed [N][K/4] -> R16 words along n, blocked for the dX product whose
+// operand rows are k: word (k, n/16) of the blocked layout with contraction length N.
+// One block transposes a 64 (n) x 64 (k) tile through LDS.
+__global__ __launch_bounds__(256) void k_codes_to_r16t(const uint8_t* __restrict__ packed,
+                                                       int64_t N, int64_t K,
+                                                       uint32_t* __restrict__ r16t) {
+  __shared__ uint8_t tile[64][68];
+  const int tid = threadIdx.x;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  {
+    const int nr = tid >> 2, kq = tid & 3;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(packed + (n0 + nr) * (K >> 2) + (k0 >> 2) + kq * 4);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) tile[nr][kq * 16 + t] = (w >> (2 * t)) & 3u;
+  }
+  __syncthreads();
+  {
+    const int kr = tid >> 2, wq = tid & 3;
+    uint32_t c[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) c[t] = tile[wq * 16 + t][kr];
+    r16t[r16_blocked_index(k0 + kr, (n0 >> 4) + wq, N >> 6)] = r16_encode(c);
+  }
+}
+
+// ------------------------------------------------------------------ block reduction
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+template <typename T> __device__ __forceinline__ void load16(const T* p, float out[16]);
+template <> __device__ __forceinline__ void load16<uint16_t>(const uint16_t* p, float out[16]) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  const uint4 a = q[0], b = q[1];
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { out[2 * i] = bf16lo_to_f32(w[i]); out[2 * i + 1] = bf16hi_to_f32(w[i]); }
+}
+template <> __device__ __forceinline__ void load16<float>(const float* p, float out[16]) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { float4 f = q[i]; out[4*i] = f.x; out[4*i+1] = f.y; out[4*i+2] = f.z; out[4*i+3] = f.w; }
+}
+
+// ------------------------------------------------------------------ forward prologue
+// Folds A into the activations (exact algebra, see the GEMM):
+//   X'[m, g*d+j] = sum_i X[m, g*d+i] A[i][j]          rounded to bf16 -> X'b
+//   xs[m, k]     = 2 * X'b[m, k]                        (bf16, exact)
+//   beta[m]      = sum_k X[m, k] B[k % d] - 4 sum_k X'b[m, k]
+// so that Y[m, n] = sum_k xs[m, k] v(z[n, k]) + beta[m], with v(c) = 2 + c/2.
+// With float32 activations X' is kept to about 16 bits: xs_lo = 2 bf16(X' - X'b) is a
+// second operand added by a second pass of the product, and beta uses X'b + X'lo.
+template <typename T>
+__global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, int64_t K,
+                                                      const float* __restrict__ A,
+                                                      const float* __restrict__ B, int d,
+                                                      uint16_t* __restrict__ xs,
+                                                      uint16_t* __restrict__ xs_lo,
+                                                      float* __restrict__ beta) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  const T* xrow = X + m * K;
+  uint16_t* orow = xs + m * K;
+  float acc = 0.f;
+  for (int64_t c = threadIdx.x; c < (K >> 4); c += blockDim.x) {
+    float x[16];
+    load16<T>(xrow + c * 16, x);
+    float xp[16];
+    for (int v0 = 0; v0 < 16; v0 += d) {
+      for (int j = 0; j < d; ++j) {
+        float s = 0.f;
+        for (int i = 0; i < d; ++i) s = __builtin_fmaf(x[v0 + i], A[i * d + j], s);
+        xp[v0 + j] = s;
+      }
+      for (int i = 0; i < d; ++i) acc = __builtin_fmaf(x[v0 + i], B[i], acc);
+    }
+    uint32_t o[8], ol[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t pb = pack_bf16x2(xp[2 * i], xp[2 * i + 1]);
+      const float e0 = bf16lo_to_f32(pb), e1 = bf16hi_to_f32(pb);
+      o[i] = pack_bf16x2(2.f * e0, 2.f * e1);
+      if (xs_lo) {
+        const uint32_t pl = pack_bf16x2(xp[2 * i] - e0, xp[2 * i + 1] - e1);
+        const float l0 = bf16lo_to_f32(pl), l1 = bf16hi_to_f32(pl);
+        ol[i] = pack_bf16x2(2.f * l0, 2.f * l1);
+        acc -= 4.f * ((e0 + l0) + (e1 + l1));
+      } else {
+        acc -= 4.f * (e0 + e1);
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(orow + c * 16);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    if (xs_lo) {
+      uint4* dl = reinterpret_cast<uint4*>(xs_lo + m * K + c * 16);
+      dl[0] = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+      dl[1] = make_uint4(ol[4], ol[5], ol[6], ol[7]);
+    }
+  }
+  const float s = block_sum_256(acc, red);
+  if (threadIdx.x == 0) beta[m] = s;
+}
+
+// ------------------------------------------------------------------ backward prologue
+// r[m] = sum_n dY[m, n] (float32). With float32 activations, also splits dY and X into
+// bf16 pairs hi + lo (hi = bf16(x), lo = bf16(x - hi)) for the matrix-core products,
+// which then add the cross terms in extra passes.
+__device__ __forceinline__ void split16(const float x[16], uint16_t* hi, uint16_t* lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    l[i] = pack_bf16x2(x[2 * i] - bf16lo_to_f32(h[i]), x[2 * i + 1] - bf16hi_to_f32(h[i]));
+  }
+  uint4* dh = reinterpret_cast<uint4*>(hi);
+  uint4* dl = reinterpret_cast<uint4*>(lo);
+  dh[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  dh[1] = make_uint4(h[4], h[5], h[6], h[7]);
+  dl[0] = make_uint4(l[0], l[1], l[2], l[3]);
+  dl[1] = make_uint4(l[4], l[5], l[6], l[7]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_prologue(const T* __restrict__ dY,
+                                                      const T* __restrict__ X, int64_t N,
+                                                      int64_t K, float* __restrict__ r,
+                                                      uint16_t* __restrict__ dy_hi,
+                                                      uint16_t* __restrict__ dy_lo,
+                                                      uint16_t* __restrict__ x_hi,
+                                                      uint16_t* __restrict__ x_lo) {
+  __shared__ float red[4];
+  const int64_t m = blockIdx.x;
+  float acc = 0.f;
+  for (int64_t c = threadIdx.x; c < (N >> 4); c += blockDim.x) {
+    float y[16];
+    load16<T>(dY + m * N + c * 16, y);
+    if (dy_hi) split16(y, dy_hi + m * N + c * 16, dy_lo + m * N + c * 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += y[i];
+  }
+  if (x_hi) {
+    for (int64_t c = threadIdx.x; c < (K >> 4); c += blockDim.x) {
+      float x[16];
+      load16<T>(X + m * K + c * 16, x);
+      split16(x, x_hi + m * K + c * 16, x_lo + m * K + c * 16);
+    }
+  }
+  const float s = block_sum_256(acc, red);
+  if (threadIdx.x == 0) r[m] = s;
+}
+
+// ------------------------------------------------------------------ launchers
+static int grid_for(int64_t groups) {
+  int64_t g = (groups + 255) / 256;
+  if (g > 65536) g = 65536;
+  return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_quantize(const float* wp, int64_t N, int64_t K, uint8_t* z, uint8_t* packed,
+                           uint8_t* mask, uint32_t* r16, float* what, const float* A,
+                           const float* B, int d, hipStream_t s) {
+  const int64_t groups = N * K / 16;
+  hipLaunchKernelGGL(k_quantize, dim3(grid_for(groups)), dim3(256), 0, s, wp, groups, K, z,
+                     reinterpret_cast<uint32_t*>(packed), reinterpret_cast<uint16_t*>(mask),
+                     r16, what, A, B, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack2b(const uint8_t* z, int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
+  const int64_t groups = N * K / 16;
+  hipLaunchKernelGGL(k_pack2b, dim3(grid_for(groups)), dim3(256), 0, s, z, groups,
+                     reinterpret_cast<uint32_t*>(packed));
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t* z, hipStream_t s) {
+  const int64_t groups = N * K / 16;
+  hipLaunchKernelGGL(k_unpack2b, dim3(grid_for(groups)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t*>(packed), groups, z);
+  return hipGetLastError();
+}
+
+hipError_t launch_codes_to_r16t(const uint8_t* packed, int64_t N, int64_t K, uint32_t* r16t,
+                                hipStream_t s) {
+  hipLaunchKernelGGL(k_codes_to_r16t, dim3((unsigned)(K / 64), (unsigned)(N / 64)), dim3(256), 0,
+                     s, packed, N, K, r16t);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_prologue(const void* X, bool x_f32, int64_t M, int64_t K, const float* A,
+                               const float* B, int d, uint16_t* xs, uint16_t* xs_lo,
+                               float* beta, hipStream_t s) {
+  if (x_f32)
+    hipLaunchKernelGGL(k_fwd_prologue<float>, dim3((unsigned)M), dim3(256), 0, s,
+                       static_cast<const float*>(X), K, A, B, d, xs, xs_lo, beta);
+  else
+    hipLaunchKernelGGL(k_fwd_prologue<uint16_t>, dim3((unsigned)M), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(X), K, A, B, d, xs, (uint16_t*)nullptr,
+                       beta);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prologue(const void* dY, const void* X, bool f32, int64_t M, int64_t N,
+                               int64_t K, float* r, uint16_t* dy_hi, uint16_t* dy_lo,
+                               uint16_t* x_hi, uint16_t* x_lo, hipStream_t s) {
+  if (f32)
+    hipLaunchKernelGGL(k_bwd_prologue<float>, dim3((unsigned)M), dim3(256), 0, s,
+                       static_cast<const float*>(dY), static_cast<const float*>(X), N, K, r,
+                       dy_hi, dy_lo, x_hi, x_lo);
+  else
+    hipLaunchKernelGGL(k_bwd_prologue<uint16_t>, dim3((unsigned)M), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(X), N,
+                       K, r, (uint16_t*)nullptr, (uint16_t*)nullptr, (uint16_t*)nullptr,
+                       (uint16_t*)nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace lcvq

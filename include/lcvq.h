@@ -1,0 +1,140 @@
+/*
+ * lcvq.h -- C ABI of the LC-VQ hot path on AMD Instinct MI355X (gfx950).
+ *
+ * LC-VQ reconstructs every d-vector of a weight matrix as c = A z + B, where the code
+ * z = clamp(round(Wp), 0, 3) comes from float proxy weights Wp, and one d x d matrix A
+ * and one d-vector B are shared by the whole matrix ("LC-QAT: Data-Efficient 2-Bit QAT
+ * for LLMs via Linear-Constrained Vector Quantization", technical summary, Methodology 1
+ * and 3). This library runs the quantizer, the forward product with the decoded weights,
+ * the straight-through backward, 2-bit packing and the packed-weight decode product.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller. The library
+ *    never allocates, frees or synchronizes; it validates arguments on the host, enqueues
+ *    kernels on `stream` (a hipStream_t; NULL means the default stream) and returns.
+ *  - Tensors are dense and row-major. A weight matrix is W[N, K] (N outputs, K inputs, as
+ *    torch.nn.Linear stores it) and the layer computes Y = X W^T. The d-vectors run along
+ *    K: vector (n, g) is W[n, g*d : (g+1)*d]. Decoding: What[n, g*d+i] = B[i] +
+ *    sum_j A[i*d + j] * z[n, g*d+j] (A row-major, multiplying z as a column vector).
+ *  - Rounding is round-half-to-even. The straight-through mask is 1 exactly where
+ *    0 <= round(Wp) <= 3 (the clamp did nothing). NaN gives code 0, +inf code 3, -inf
+ *    code 0, all with mask 0.
+ *  - Packed codes: 4 per byte, code k = 4b + t in bits [2t, 2t+1] of byte b of its row.
+ *    Mask: 8 per byte, bit k = 8c + t in bit t of byte c of its row.
+ *  - All pointers must be 16-byte aligned. Outputs must not overlap inputs or each other.
+ *  - Shape limits: d in {4, 8, 16}; 1 <= M <= 2^31 - 1; N, K >= 64 and multiples of 64;
+ *    N * K < 2^40. (lcvq_quantize / pack / unpack need only K a multiple of 16.)
+ *  - Errors are returned synchronously from host-side checks, before anything is
+ *    enqueued. LCVQ_ERR_HIP reports a failed launch; faults inside kernels surface at the
+ *    caller's next synchronization, as with any HIP work.
+ *  - Calls are re-entrant; the library keeps no state between calls.
+ */
+#ifndef LCVQ_H
+#define LCVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LCVQ_OK = 0,
+  LCVQ_ERR_NULL = 1,       /* a required pointer is NULL */
+  LCVQ_ERR_SHAPE = 2,      /* M, N or K outside the limits above */
+  LCVQ_ERR_D = 3,          /* d not in {4, 8, 16} */
+  LCVQ_ERR_DTYPE = 4,      /* unknown dtype code */
+  LCVQ_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
+  LCVQ_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than the *_workspace_size() */
+  LCVQ_ERR_HIP = 7         /* a kernel launch failed */
+} lcvq_status_t;
+
+typedef enum { LCVQ_F32 = 0, LCVQ_BF16 = 1 } lcvq_dtype_t;
+
+/* Text for a status code (static storage). */
+const char* lcvq_status_string(lcvq_status_t s);
+
+/*
+ * Quantizer: z = clamp(round(Wp), 0, 3) and the straight-through mask
+ * (LC-QAT summary, Methodology 1 "rounding and clamping", Methodology 3 forward).
+ *   Wp      float [N, K]            in
+ *   z_u8    uint8 [N, K]   or NULL  out: one code per byte
+ *   packed  uint8 [N, K/4] or NULL  out: 4 codes per byte
+ *   mask    uint8 [N, K/8] or NULL  out: 8 mask bits per byte
+ * Requires K % 16 == 0, N >= 1.
+ */
+lcvq_status_t lcvq_quantize(const float* Wp, int64_t N, int64_t K, uint8_t* z_u8,
+                            uint8_t* packed, uint8_t* mask, void* stream);
+
+/*
+ * 2-bit packing of codes (values 0..3; higher bits are ignored) and its inverse.
+ * The integer part is what a deployment keeps (decoupleQ, section 3.2).
+ *   z_u8 uint8 [N, K] <-> packed uint8 [N, K/4]. Requires K % 16 == 0.
+ */
+lcvq_status_t lcvq_pack2b(const uint8_t* z_u8, int64_t N, int64_t K, uint8_t* packed,
+                          void* stream);
+lcvq_status_t lcvq_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t* z_u8,
+                            void* stream);
+
+/*
+ * Forward of one LC-VQ linear layer: quantize Wp, decode with A z + B, Y = X What^T
+ * (LC-QAT summary, Methodology 3 forward; the product runs on 2-bit codes).
+ *   X          [M, K] in xdt (LCVQ_BF16 or LCVQ_F32; F32 is rounded to bf16 on load)
+ *   Wp         float [N, K];  A float [d, d];  B float [d]
+ *   Y          [M, N] in xdt                         out
+ *   packed_out uint8 [N, K/4]                        out (required: the backward needs it)
+ *   mask_out   uint8 [N, K/8]                        out (required)
+ *   What_out   float [N, K] or NULL                  out: decoded weights in float32
+ *   workspace  >= lcvq_linear_fwd_workspace_size(M, N, K, d) bytes, device memory
+ * Numerics: the product runs on bf16 matrix cores with float32 accumulation; the
+ * decoding matrix A is applied to X (X' = X (I kron A), rounded to bf16), the codes
+ * enter exactly, and X B is added in float32.
+ */
+size_t lcvq_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int d);
+lcvq_status_t lcvq_linear_fwd(const void* X, lcvq_dtype_t xdt, int64_t M, int64_t N,
+                              int64_t K, int d, const float* Wp, const float* A,
+                              const float* B, void* Y, uint8_t* packed_out,
+                              uint8_t* mask_out, float* What_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Straight-through backward of the same layer (gradients flow through the linear decode,
+ * LC-QAT summary, Methodology 1; the rounding is passed straight through, masked where
+ * the clamp was active):
+ *   dX  = dY What                                              [M, K] in dt, or NULL
+ *   G   = dY^T X  (never stored)
+ *   dWp[n, g*d+j] = mask * sum_i A[i, j] G[n, g*d+i]           float [N, K]
+ *   dA[i, j] = sum over vectors of G[n, g*d+i] z[n, g*d+j]     float [d, d]
+ *   dB[i]    = sum over vectors of G[n, g*d+i]                 float [d]
+ * Inputs: dY [M, N] and X [M, K] in dt; packed and mask as written by lcvq_linear_fwd.
+ * All outputs are overwritten. dA and dB are reduced in a fixed order, so repeated
+ * calls give identical bytes.
+ */
+size_t lcvq_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int d);
+lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, int64_t M,
+                              int64_t N, int64_t K, int d, const uint8_t* packed,
+                              const uint8_t* mask, const float* A, const float* B,
+                              void* dX, float* dWp, float* dA, float* dB, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Decode product from the deployed artefact (packed codes plus half-precision A, B):
+ * Y = X What^T for a few tokens (decoupleQ, section 3.2: one linear transform turns the
+ * integer part back into weights; LC-QAT summary, Methodology 3).
+ *   X   bfloat16 [M, K], 1 <= M <= 16;  packed uint8 [N, K/4]
+ *   A16 float16 [d, d];  B16 float16 [d]
+ *   Y   bfloat16 [M, N]                                          out
+ *   workspace >= lcvq_gemv2b_workspace_size(M, K, d) bytes
+ * Numerics: X (I kron A) is formed in float32 and held as 16-bit fixed point per row;
+ * the product with the codes is exact integer arithmetic.
+ */
+size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t K, int d);
+lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                          const uint8_t* packed, const void* A16, const void* B16, void* Y,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LCVQ_H */

@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and
+every argument error is reported before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lcvq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import bit_weight_only_lc_amd as P
+    if not os.path.exists(P.LIB_PATH):
+        from bit_weight_only_lc_amd import build
+        build.build()
+    return P.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lcvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["lcvq_quantize", "lcvq_linear_fwd", "lcvq_linear_bwd", "lcvq_pack2b",
+              "lcvq_gemv2b", "lcvq_unpack2b", "lcvq_status_string",
+              "lcvq_linear_fwd_workspace_size", "lcvq_linear_bwd_workspace_size",
+              "lcvq_gemv2b_workspace_size"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.lcvq_status_string(s)
+    assert L.lcvq_status_string(99) == b"unknown status"
+
+
+# Fake but well-aligned "device" addresses: every check below fails before any launch.
+P = 1 << 20          # 16-byte aligned
+MIS = P + 4          # misaligned
+
+
+def test_quantize_errors(L):
+    assert L.lcvq_quantize(None, 4, 64, P, P, P, None) == 1           # NULL
+    assert L.lcvq_quantize(P, 4, 60, P, P, P, None) == 2              # K % 16
+    assert L.lcvq_quantize(P, 0, 64, P, P, P, None) == 2              # N < 1
+    assert L.lcvq_quantize(MIS, 4, 64, P, P, P, None) == 5            # alignment
+    assert L.lcvq_quantize(P, 4, 64, None, None, None, None) == 0     # nothing to do
+
+
+def test_pack_errors(L):
+    assert L.lcvq_pack2b(None, 4, 64, P, None) == 1
+    assert L.lcvq_pack2b(P, 4, 8, P, None) == 2
+    assert L.lcvq_unpack2b(P, 4, 64, MIS, None) == 5
+
+
+def _fwd(L, **kw):
+    a = dict(X=P, xdt=1, M=16, N=256, K=256, d=8, Wp=P, A=P, B=P, Y=P, packed=P, mask=P,
+             What=None, ws=P, wsb=1 << 30, s=None)
+    a.update(kw)
+    return L.lcvq_linear_fwd(a["X"], a["xdt"], a["M"], a["N"], a["K"], a["d"], a["Wp"],
+                             a["A"], a["B"], a["Y"], a["packed"], a["mask"], a["What"],
+                             a["ws"], a["wsb"], a["s"])
+
+
+def test_linear_fwd_errors(L):
+    assert _fwd(L, X=None) == 1
+    assert _fwd(L, packed=None) == 1
+    assert _fwd(L, xdt=7) == 4
+    assert _fwd(L, d=6) == 3
+    assert _fwd(L, M=0) == 2
+    assert _fwd(L, N=100) == 2
+    assert _fwd(L, K=96) == 2
+    assert _fwd(L, Y=MIS) == 5
+    need = L.lcvq_linear_fwd_workspace_size(16, 256, 256, 8)
+    assert need > 0
+    assert _fwd(L, xdt=0, wsb=need - 1) == 6   # sized for float32
+    assert _fwd(L, ws=None) == 6
+
+
+def _bwd(L, **kw):
+    a = dict(dY=P, X=P, dt=1, M=16, N=256, K=256, d=8, packed=P, mask=P, A=P, B=P, dX=P,
+             dWp=P, dA=P, dB=P, ws=P, wsb=1 << 30, s=None)
+    a.update(kw)
+    return L.lcvq_linear_bwd(a["dY"], a["X"], a["dt"], a["M"], a["N"], a["K"], a["d"],
+                             a["packed"], a["mask"], a["A"], a["B"], a["dX"], a["dWp"],
+                             a["dA"], a["dB"], a["ws"], a["wsb"], a["s"])
+
+
+def test_linear_bwd_errors(L):
+    assert _bwd(L, dY=None) == 1
+    assert _bwd(L, dA=None) == 1
+    assert _bwd(L, dt=3) == 4
+    assert _bwd(L, d=2) == 3
+    assert _bwd(L, K=128 + 32) == 2
+    assert _bwd(L, dWp=MIS) == 5
+    need = L.lcvq_linear_bwd_workspace_size(16, 256, 256, 8)   # sized for float32
+    assert need > 0
+    assert _bwd(L, dt=0, wsb=need - 1) == 6
+    assert _bwd(L, ws=None) == 6
+
+
+def test_gemv_errors(L):
+    def g(**kw):
+        a = dict(X=P, M=1, N=256, K=256, d=8, packed=P, A=P, B=P, Y=P, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return L.lcvq_gemv2b(a["X"], a["M"], a["N"], a["K"], a["d"], a["packed"], a["A"],
+                             a["B"], a["Y"], a["ws"], a["wsb"], None)
+    assert g(X=None) == 1
+    assert g(M=17) == 2
+    assert g(M=0) == 2
+    assert g(K=320) == 2
+    assert g(N=40) == 2
+    assert g(d=5) == 3
+    assert g(Y=MIS) == 5
+    assert g(wsb=L.lcvq_gemv2b_workspace_size(1, 256, 8) - 1) == 6
+
+
+def test_workspace_sizes_grow_with_shape(L):
+    a = L.lcvq_linear_fwd_workspace_size(64, 256, 256, 8)
+    b = L.lcvq_linear_fwd_workspace_size(4096, 4096, 4096, 8)
+    assert 0 < a < b
+    assert L.lcvq_linear_fwd_workspace_size(0, 256, 256, 8) == 0
+    assert L.lcvq_linear_bwd_workspace_size(64, 256, 256, 16) > \
+        L.lcvq_linear_bwd_workspace_size(64, 256, 256, 4)

@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Codes, packed bytes and mask bytes must match bit for bit. Floating-point outputs must
+match within max relative Frobenius error 1e-5 (float32 decode) and 1e-2 (bf16-input,
+float32-accumulate products and gradients), computed per tensor as
+||gpu - oracle||_F / ||oracle||_F.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as SI
+from oracle import lcvq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL_W = 1e-5
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import bit_weight_only_lc_amd as P
+    P.lib()
+    return P
+
+
+def rel(gpu, ref):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(r)
+    return float(np.linalg.norm(g - r) / (den if den > 0 else 1.0))
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.is_floating_point() \
+        else t.detach().cpu().numpy()
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------------ quantizer / packing
+SPECIAL = [-0.6, -0.5, -0.4, 0.0, 0.49, 0.5, 0.50000006, 1.5, 2.5, 2.5000002, 3.49, 3.5,
+           3.51, 4.0, -1.0, 1e30, -1e30, float("nan"), float("inf"), float("-inf")]
+
+
+@pytest.mark.parametrize("N,K", [(64, 256), (3, 48), (1, 16), (129, 1024)])
+def test_quantize_bitexact(P, N, K):
+    note(f"quantize N={N} K={K}")
+    wp = SI.make_wp(N, K, seed=N * 7 + K, lo=-2.0, hi=5.0)
+    flat = wp.view(-1)
+    sp = torch.tensor(SPECIAL, dtype=torch.float32)
+    flat[: min(len(SPECIAL), flat.numel())] = sp[: min(len(SPECIAL), flat.numel())]
+    d_wp = wp.cuda()
+    z = torch.empty((N, K), dtype=torch.uint8, device="cuda")
+    pk = torch.empty((N, K // 4), dtype=torch.uint8, device="cuda")
+    mk = torch.empty((N, K // 8), dtype=torch.uint8, device="cuda")
+    P.lcvq_quantize(d_wp, z, pk, mk)
+    torch.cuda.synchronize()
+    zr, mr = O.quantize(wp.numpy())
+    assert np.array_equal(host(z), zr)
+    assert np.array_equal(host(pk), O.pack2b(zr))
+    assert np.array_equal(host(mk), O.pack_mask(mr))
+
+
+def test_pack_unpack(P):
+    note("pack/unpack")
+    g = torch.Generator().manual_seed(9)
+    z = torch.randint(0, 4, (37, 512), generator=g, dtype=torch.uint8)
+    dz = z.cuda()
+    pk = torch.empty((37, 128), dtype=torch.uint8, device="cuda")
+    P.lcvq_pack2b(dz, pk)
+    back = torch.empty_like(dz)
+    P.lcvq_unpack2b(pk, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(pk), O.pack2b(z.numpy()))
+    assert np.array_equal(host(back), z.numpy())
+    allb = torch.arange(256, dtype=torch.uint8).view(1, 256).repeat(2, 1)
+    out = torch.empty((2, 1024), dtype=torch.uint8, device="cuda")
+    P.lcvq_unpack2b(allb.cuda(), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), O.unpack2b(allb.numpy(), 1024))
+
+
+# ------------------------------------------------------------------ linear layer
+def run_layer(P, inp, d, want_what=True):
+    X, Wp, A, B, dY = (inp[k].cuda() for k in ("X", "Wp", "A", "B", "dY"))
+    f = P.linear_fwd(X, Wp, A, B, d, want_what=want_what)
+    b = P.linear_bwd(dY, X, f["packed"], f["mask"], A, B, d)
+    torch.cuda.synchronize()
+    return f, b
+
+
+def check_layer(P, inp, d, label):
+    f, b = run_layer(P, inp, d)
+    X = host(inp["X"])
+    dY = host(inp["dY"])
+    wp = inp["Wp"].numpy()
+    A = inp["A"].double().numpy()
+    B = inp["B"].double().numpy()
+    of = O.linear_fwd(X, wp, A, B, d)
+    ob = O.linear_bwd(dY, X, of["z"], of["m"], A, B, d)
+    assert np.array_equal(host(f["packed"]), of["packed"]), label
+    assert np.array_equal(host(f["mask"]), of["maskbits"]), label
+    errs = {
+        "What": rel(host(f["What"]), of["What"]),
+        "Y": rel(host(f["Y"]), of["Y"]),
+        "dX": rel(host(b["dX"]), ob["dX"]),
+        "dWp": rel(host(b["dWp"]), ob["dWp"]),
+        "dA": rel(host(b["dA"]), ob["dA"]),
+        "dB": rel(host(b["dB"]), ob["dB"]),
+    }
+    note(f"{label}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert errs["What"] <= TOL_W, (label, errs)
+    for k in ("Y", "dX", "dWp", "dA", "dB"):
+        assert errs[k] <= TOL, (label, k, errs)
+    return errs
+
+
+def test_config0_single_layer(P):
+    """256 x 256 layer, 16 float32 tokens, d = 8, seed 0."""
+    c = SI.CONFIGS["c0_single_256"]
+    (N, K), M, d = c["mats"][0], c["M"], c["d"]
+    inp = SI.make_layer(N, K, M, d, seed=0, x_dtype="f32")
+    check_layer(P, inp, d, "c0")
+
+
+@pytest.mark.parametrize("d", [4, 8, 16])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(16, 256, 256), (1, 64, 64), (300, 320, 192),
+                                   (513, 576, 320)])
+def test_layer_shapes(P, d, xdt, M, N, K):
+    """Several tiles, ragged tails in every dimension, and the clamp mask exercised."""
+    inp = SI.make_layer(N, K, M, d, seed=M + N + K + d, x_dtype=xdt, lo=-2.0, hi=5.0)
+    check_layer(P, inp, d, f"M={M} N={N} K={K} d={d} {xdt}")
+
+
+def test_degenerate_A(P):
+    """A = 0, negative and singular A are valid decodes (decoupleQ section 3.2 allows a
+    zero or negative scale)."""
+    M, N, K, d = 64, 128, 128, 8
+    for name, A in [("zero", torch.zeros(d, d)), ("neg", -0.03 * torch.eye(d)),
+                    ("rank1", torch.outer(torch.arange(d, dtype=torch.float32),
+                                          torch.ones(d)) * 0.01)]:
+        inp = SI.make_layer(N, K, M, d, seed=5, lo=-2.0, hi=5.0)
+        inp["A"] = A.contiguous()
+        check_layer(P, inp, d, f"A={name}")
+
+
+def test_backward_is_deterministic(P):
+    M, N, K, d = 512, 512, 512, 8
+    inp = SI.make_layer(N, K, M, d, seed=77)
+    X, Wp, A, B, dY = (inp[k].cuda() for k in ("X", "Wp", "A", "B", "dY"))
+    f = P.linear_fwd(X, Wp, A, B, d)
+    r1 = P.linear_bwd(dY, X, f["packed"], f["mask"], A, B, d)
+    r2 = P.linear_bwd(dY, X, f["packed"], f["mask"], A, B, d)
+    f2 = P.linear_fwd(X, Wp, A, B, d)
+    torch.cuda.synchronize()
+    for k in ("dX", "dWp", "dA", "dB"):
+        assert torch.equal(r1[k], r2[k]), k
+    assert torch.equal(f["Y"], f2["Y"])
+
+
+def test_config1_full(P):
+    """4096 x 4096 weight, 4096 bf16 tokens, d = 8: every output against the full oracle."""
+    c = SI.CONFIGS["c1_square_4096"]
+    (N, K), M, d = c["mats"][0], c["M"], c["d"]
+    note("c1: generating")
+    inp = {k: v.cpu() for k, v in SI.make_layer(N, K, M, d, seed=1000, device="cuda").items()}
+    check_layer(P, inp, d, "c1")
+
+
+# ------------------------------------------------------------------ decode product
+@pytest.mark.parametrize("N,K", [(256, 256), (4096, 4096), (14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("M", [1, 4, 16, 3])
+def test_gemv(P, N, K, M):
+    d = 8
+    note(f"gemv N={N} K={K} M={M}")
+    wp = SI.make_wp(N, K, seed=3000 + N + K, device="cuda")
+    A, B = SI.make_ab(d, seed=3000 + M)
+    X = SI.make_act(M, K, seed=3100 + M, device="cuda")
+    pk = torch.empty((N, K // 4), dtype=torch.uint8, device="cuda")
+    P.lcvq_quantize(wp, None, pk, None)
+    A16, B16 = A.half().cuda(), B.half().cuda()
+    Y = P.gemv2b(X, pk, A16, B16, d)
+    torch.cuda.synchronize()
+    ref = O.gemv2b(host(X), host(pk), A.half().double().numpy(), B.half().double().numpy(), d)
+    e = rel(host(Y), ref)
+    note(f"  rel={e:.2e}")
+    assert e <= TOL
