@@ -62,6 +62,8 @@ def lib():
             f.argtypes = [i64, i64, i64, i32]
         L.lcvq_gemv2b_workspace_size.restype = sz
         L.lcvq_gemv2b_workspace_size.argtypes = [i64, i64, i32]
+        L.lcvq_profile_next.restype = i32
+        L.lcvq_profile_next.argtypes = [i32, vp, vp]
         _lib = L
     return _lib
 

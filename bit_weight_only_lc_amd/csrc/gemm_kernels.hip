@@ -469,10 +469,11 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   a.tilesQ = (a.Q + BT - 1) / BT;
   a.ntiles = a.tilesP * a.tilesQ;
   const int grid = ((a.ntiles + 7) / 8) * 8;
+  constexpr int id = OP == OP_FWD ? PROF_FWD : (OP == OP_DX ? PROF_DX : PROF_DW);
   switch (d) {
-    case 4: hipLaunchKernelGGL((k_gemm<OP, 4>), dim3(grid), dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_gemm<OP, 8>), dim3(grid), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm<OP, 16>), dim3(grid), dim3(256), 0, s, a); break;
+    case 4: LCVQ_LAUNCH(id, (k_gemm<OP, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    case 8: LCVQ_LAUNCH(id, (k_gemm<OP, 8>), dim3(grid), dim3(256), 0, s, a); break;
+    default: LCVQ_LAUNCH(id, (k_gemm<OP, 16>), dim3(grid), dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }

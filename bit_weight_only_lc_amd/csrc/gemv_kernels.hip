@@ -156,7 +156,7 @@ hipError_t launch_gemv_prologue(const uint16_t* X, int M, int K, const uint16_t*
 
 hipError_t launch_gemv(const int8_t* xq, const float* rowinfo, const uint8_t* packed, int M,
                        int N, int K, uint16_t* Y, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemv, dim3(N / 16), dim3(256), 0, s, xq,
+  LCVQ_LAUNCH(PROF_GEMV, k_gemv, dim3(N / 16), dim3(256), 0, s, xq,
                      reinterpret_cast<const float2*>(rowinfo), packed, M, N, K, Y);
   return hipGetLastError();
 }

@@ -74,9 +74,31 @@ inline GemvWs gemv_ws(int64_t K) {
   return w;
 }
 
+struct ProfSlot {
+  int id = 0;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local ProfSlot g_prof;
+
 }  // namespace
 
+bool lcvq::take_profile(int id, hipEvent_t* start, hipEvent_t* stop) {
+  if (g_prof.id != id || !g_prof.start || !g_prof.stop) return false;
+  *start = g_prof.start;
+  *stop = g_prof.stop;
+  g_prof = ProfSlot();
+  return true;
+}
+
 extern "C" {
+
+lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event) {
+  if (kernel_id < PROF_QUANTIZE || kernel_id > PROF_GEMV) return LCVQ_ERR_SHAPE;
+  g_prof.id = (start_event && stop_event) ? kernel_id : 0;
+  g_prof.start = static_cast<hipEvent_t>(start_event);
+  g_prof.stop = static_cast<hipEvent_t>(stop_event);
+  return LCVQ_OK;
+}
 
 const char* lcvq_status_string(lcvq_status_t s) {
   switch (s) {

@@ -5,6 +5,27 @@
 
 namespace lcvq {
 
+// Kernel ids of the profiling hook (lcvq_profile_next).
+enum { PROF_QUANTIZE = 1, PROF_FWD = 2, PROF_DX = 3, PROF_DW = 4, PROF_GEMV = 5 };
+// True (once) if the calling thread armed timing for kernel `id`; returns the events.
+bool take_profile(int id, hipEvent_t* start, hipEvent_t* stop);
+
+}  // namespace lcvq
+
+#include <hip/hip_ext.h>
+// Launch through hipExtLaunchKernelGGL when timing is armed for this kernel id.
+#define LCVQ_LAUNCH(ID, KERNEL, GRID, BLOCK, SHM, STREAM, ...)                            \
+  do {                                                                                  \
+    hipEvent_t lcvq_ev0_, lcvq_ev1_;                                                    \
+    if (::lcvq::take_profile((ID), &lcvq_ev0_, &lcvq_ev1_))                             \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, lcvq_ev0_, lcvq_ev1_, 0,    \
+                            __VA_ARGS__);                                               \
+    else                                                                                \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, __VA_ARGS__);                \
+  } while (0)
+
+namespace lcvq {
+
 hipError_t launch_quantize(const float* wp, int64_t N, int64_t K, uint8_t* z, uint8_t* packed,
                            uint8_t* mask, uint32_t* r16, float* what, const float* A,
                            const float* B, int d, hipStream_t s);

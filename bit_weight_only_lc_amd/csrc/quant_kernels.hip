@@ -280,7 +280,7 @@ hipError_t launch_quantize(const float* wp, int64_t N, int64_t K, uint8_t* z, ui
                            uint8_t* mask, uint32_t* r16, float* what, const float* A,
                            const float* B, int d, hipStream_t s) {
   const int64_t groups = N * K / 16;
-  hipLaunchKernelGGL(k_quantize, dim3(grid_for(groups)), dim3(256), 0, s, wp, groups, K, z,
+  LCVQ_LAUNCH(PROF_QUANTIZE, k_quantize, dim3(grid_for(groups)), dim3(256), 0, s, wp, groups, K, z,
                      reinterpret_cast<uint32_t*>(packed), reinterpret_cast<uint16_t*>(mask),
                      r16, what, A, B, d);
   return hipGetLastError();

@@ -27,7 +27,8 @@
  *  - Errors are returned synchronously from host-side checks, before anything is
  *    enqueued. LCVQ_ERR_HIP reports a failed launch; faults inside kernels surface at the
  *    caller's next synchronization, as with any HIP work.
- *  - Calls are re-entrant; the library keeps no state between calls.
+ *  - Calls are re-entrant; the library keeps no state between calls (apart from the
+ *    per-thread profiling hook at the end of this file).
  */
 #ifndef LCVQ_H
 #define LCVQ_H
@@ -80,7 +81,7 @@ lcvq_status_t lcvq_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t
 /*
  * Forward of one LC-VQ linear layer: quantize Wp, decode with A z + B, Y = X What^T
  * (LC-QAT summary, Methodology 3 forward; the product runs on 2-bit codes).
- *   X          [M, K] in xdt (LCVQ_BF16 or LCVQ_F32; F32 is rounded to bf16 on load)
+ *   X          [M, K] in xdt (LCVQ_BF16 or LCVQ_F32)
  *   Wp         float [N, K];  A float [d, d];  B float [d]
  *   Y          [M, N] in xdt                         out
  *   packed_out uint8 [N, K/4]                        out (required: the backward needs it)
@@ -89,7 +90,9 @@ lcvq_status_t lcvq_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t
  *   workspace  >= lcvq_linear_fwd_workspace_size(M, N, K, d) bytes, device memory
  * Numerics: the product runs on bf16 matrix cores with float32 accumulation; the
  * decoding matrix A is applied to X (X' = X (I kron A), rounded to bf16), the codes
- * enter exactly, and X B is added in float32.
+ * enter exactly, and X B is added in float32. With LCVQ_F32 activations every bf16
+ * operand is carried as a hi + lo pair (about 16 significant bits) over extra passes.
+ * The workspace size covers both activation types.
  */
 size_t lcvq_linear_fwd_workspace_size(int64_t M, int64_t N, int64_t K, int d);
 lcvq_status_t lcvq_linear_fwd(const void* X, lcvq_dtype_t xdt, int64_t M, int64_t N,
@@ -123,6 +126,7 @@ lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, in
  * Y = X What^T for a few tokens (decoupleQ, section 3.2: one linear transform turns the
  * integer part back into weights; LC-QAT summary, Methodology 3).
  *   X   bfloat16 [M, K], 1 <= M <= 16;  packed uint8 [N, K/4]
+ *   N a multiple of 16, K a multiple of 256
  *   A16 float16 [d, d];  B16 float16 [d]
  *   Y   bfloat16 [M, N]                                          out
  *   workspace >= lcvq_gemv2b_workspace_size(M, K, d) bytes
@@ -133,6 +137,16 @@ size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t K, int d);
 lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
                           const uint8_t* packed, const void* A16, const void* B16, void* Y,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling hook (changes no result). Arms a one-shot timing of the next launch of one
+ * kernel by calls made from this host thread: the kernel is launched with
+ * hipExtLaunchKernel between `start_event` and `stop_event` (hipEvent_t handles created
+ * by the caller with timing enabled). kernel_id: 1 quantizer, 2 forward product,
+ * 3 dX product, 4 dW product (with the straight-through epilogue), 5 decode product.
+ * Passing NULL events disarms. Returns LCVQ_ERR_SHAPE for an unknown kernel_id.
+ */
+lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }
