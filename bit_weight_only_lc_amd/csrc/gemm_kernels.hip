@@ -11,11 +11,14 @@
 // constant part is removed through the row terms prepared by the prologue kernels.
 //
 // One kernel template covers the three products. C (P x Q) = sum_r L[p, r] R[q, r] is
-// computed in 256 x 256 tiles by 4 waves (2 x 2, 128 x 128 each, 32x32x16 MFMA), with
-// the contraction staged through LDS in steps of 64 and double-buffered:
-//   FWD: L = X' (bf16 rows m, loaded straight into LDS), R = codes (rows n, expanded)
-//   DX : L = codes transposed (rows k, expanded),        R = dY (bf16 rows m)
-//   DW : L = X^T (rows k, transposed on the way in),     R = dY^T (rows n, transposed)
+// computed in 256 x 256 tiles (32x32x16 bf16 MFMA, contraction staged through LDS in
+// steps of 64):
+//   FWD: L = X' (bf16 rows m),        R = codes (rows n)       8 waves, 4-slot LDS ring
+//   DX : L = codes transposed (rows k), R = dY (bf16 rows m)   8 waves, 4-slot LDS ring
+//   DW : L = X^T (rows k), R = dY^T (rows n), both transposed on the way into LDS;
+//        4 waves, double buffer.
+// With 8 waves two waves share each SIMD, so one wave's LDS waits and code expansion
+// overlap the other wave's MFMAs.
 #include "lcvq_device.h"
 #include "lcvq_internal.h"
 
@@ -27,6 +30,14 @@ constexpr int ROWB = 128;      // bytes per LDS tile row (64 bf16)
 constexpr int TILEB = BT * ROWB;
 
 enum { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
+
+// Wave layout per workgroup: 2 wave rows x (NW/2) wave columns; a wave owns 128 rows and
+// 32*WJ columns of the C tile.
+template <int OP> struct Tiling {
+  static constexpr int NW = OP == OP_DW ? 4 : 8;
+  static constexpr int WGQ = NW / 2;
+  static constexpr int WJ = 8 / WGQ;
+};
 
 struct GemmArgs {
   int P, Q, R;                 // C is P x Q; contraction length R
@@ -141,27 +152,55 @@ __device__ __forceinline__ void store_trans(uint8_t* tile, const uint4 v[8], int
 }
 
 // ---- one contraction stage of 64 on the current LDS buffers --------------------------
-__device__ __forceinline__ void mma_stage(const uint8_t* Ls, const uint8_t* Rs, f32x16 acc[4][4],
-                                          int wp, int wq, int lane) {
+// Fragments are double-buffered in registers: the LDS reads of sub-step s+1 are issued
+// between the MFMAs of sub-step s (two MFMAs per read), so the matrix cores never wait
+// for LDS once the stage has started.
+template <int WJ>
+__device__ __forceinline__ void load_frags(const uint8_t* Ls, const uint8_t* Rs, int s, int wp,
+                                           int wq, int lane, bf16x8 af[4], bf16x8 bf[WJ]) {
+  const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wp * 128 + i * 32 + (lane & 31);
+    af[i] = *reinterpret_cast<const bf16x8*>(Ls + lds_off(row, chunk));
+  }
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int row = wq * 32 * WJ + j * 32 + (lane & 31);
+    bf[j] = *reinterpret_cast<const bf16x8*>(Rs + lds_off(row, chunk));
+  }
+}
+
+// Single-buffered variant for the dW product, whose transposing loaders already hold
+// 64 registers of prefetched data.
+__device__ __forceinline__ void mma_stage_single(const uint8_t* Ls, const uint8_t* Rs,
+                                                 f32x16 acc[4][4], int wp, int wq, int lane) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const int chunk = 2 * s + (lane >> 5);
     bf16x8 af[4], bf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wp * 128 + i * 32 + (lane & 31);
-      af[i] = *reinterpret_cast<const bf16x8*>(Ls + lds_off(row, chunk));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wq * 128 + j * 32 + (lane & 31);
-      bf[j] = *reinterpret_cast<const bf16x8*>(Rs + lds_off(row, chunk));
-    }
+    load_frags<4>(Ls, Rs, s, wp, wq, lane, af, bf);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+template <int WJ>
+__device__ __forceinline__ void mma_stage(const uint8_t* Ls, const uint8_t* Rs, f32x16 acc[4][WJ],
+                                          int wp, int wq, int lane) {
+  bf16x8 af[2][4], bf[2][WJ];
+  load_frags<WJ>(Ls, Rs, 0, wp, wq, lane, af[0], bf[0]);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = s & 1;
+    if (s < 3) load_frags<WJ>(Ls, Rs, s + 1, wp, wq, lane, af[c ^ 1], bf[c ^ 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
   }
 }
 
@@ -213,8 +252,8 @@ __device__ __forceinline__ void store_block_rows(const float* S, void* out, int 
 
 // dX[m, g*d+i] = 2 sum_j A[i][j] C[g*d+j, m] + (B[i] - 4 sum_j A[i][j]) r[m]
 // where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m).
-template <int D>
-__device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0, int wp, int wq,
+template <int D, int WJ>
+__device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
                             int lane, float* S, const float* Alds) {
   float bp[D];
 #pragma unroll
@@ -228,9 +267,9 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0,
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < WJ; ++j) {
       const int kb = p0 + wp * 128 + i * 32;
-      const int mb = q0 + wq * 128 + j * 32;
+      const int mb = q0 + wq * 32 * WJ + j * 32;
       wave_sync();
       stage_block(S, acc[i][j], lane);
       wave_sync();
@@ -360,10 +399,184 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0,
   }
 }
 
+// ---- ring pipeline for the products with one 2-bit operand (FWD, DX) -----------------
+// Each stage of 64 contraction steps occupies one LDS slot: the bf16 operand tile
+// (256 rows x 128 bytes, swizzled) and the raw R16 code words of the other operand
+// (256 rows x 16 bytes). Both arrive by direct global->LDS loads, four slots deep, so
+// three stages are in flight while one is consumed. Codes are expanded to bf16 only
+// when a wave reads its MFMA fragment, which halves the LDS traffic per stage.
+// Within a row, word w of the R16 slab sits at position (w + row/8) mod 4 (the global
+// blocked layout is written that way), which keeps the fragment reads conflict-free.
+constexpr int RING = 4;
+constexpr int CODEB = 256 * 16;
+constexpr int SLOTB = TILEB + CODEB;
+constexpr int RING_LOADS = 6;           // per lane and stage: 4 bf16-tile + 2 code loads
+
+// 8 waves: wave w fills tile rows [32w, 32w+32) (4 x 1 KiB) and code rows
+// [32w, 32w+32) (2 x 256 B of 4-byte words).
+__device__ __forceinline__ void issue_ring_stage(uint8_t* slot, const uint16_t* mat, int64_t ld,
+                                                 int row0, int rows_total, int k0,
+                                                 const uint32_t* codes, int rowblock, int nk,
+                                                 int kt, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 32 + i * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(r);
+    int g = row0 + r;
+    g = g < rows_total ? g : rows_total - 1;
+    const uint16_t* src = mat + (int64_t)g * ld + k0 + c * 8;
+    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(slot + (wave * 32 + i * 8) * ROWB), 16, 0, 0);
+  }
+  const uint32_t* slab = codes + ((int64_t)rowblock * nk + kt) * 1024;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int w0 = (wave * 32 + h * 16) * 4;           // first word of these 16 rows
+    __builtin_amdgcn_global_load_lds(slab + w0 + lane, (LCVQ_LDS void*)(slot + TILEB + w0 * 4), 4, 0, 0);
+  }
+}
+
+// The MFMA fragment (8 consecutive codes as v(c) bf16) of tile row `row`, sub-step s,
+// half h of the 16-code word.
+__device__ __forceinline__ bf16x8 codes_frag(const uint8_t* ctile, int row, int s, int h) {
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(ctile + row * 16 + (((s + (row >> 3)) & 3) << 2));
+  const uint32_t src = h ? __builtin_amdgcn_alignbit(w, w, 8) : w;
+  u32x4 o;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) o[p] = ((src >> (2 * p)) & 0x00600060u) | 0x40004000u;
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+template <bool CODES_ARE_L, int WJ>
+__device__ __forceinline__ void load_frags_ring(const uint8_t* slot, int s, int wp, int wq, int lane,
+                                                bf16x8 af[4], bf16x8 bf[WJ]) {
+  const uint8_t* tile = slot;
+  const uint8_t* ctile = slot + TILEB;
+  const int chunk = 2 * s + (lane >> 5), h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wp * 128 + i * 32 + (lane & 31);
+    af[i] = CODES_ARE_L ? codes_frag(ctile, row, s, h)
+                        : *reinterpret_cast<const bf16x8*>(tile + lds_off(row, chunk));
+  }
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int row = wq * 32 * WJ + j * 32 + (lane & 31);
+    bf[j] = CODES_ARE_L ? *reinterpret_cast<const bf16x8*>(tile + lds_off(row, chunk))
+                        : codes_frag(ctile, row, s, h);
+  }
+}
+
+template <bool CODES_ARE_L, int WJ>
+__device__ __forceinline__ void mma_ring_stage(const uint8_t* slot, f32x16 acc[4][WJ], int wp,
+                                               int wq, int lane) {
+  bf16x8 af[2][4], bf[2][WJ];
+  load_frags_ring<CODES_ARE_L, WJ>(slot, 0, wp, wq, lane, af[0], bf[0]);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = s & 1;
+    if (s < 3) load_frags_ring<CODES_ARE_L, WJ>(slot, s + 1, wp, wq, lane, af[c ^ 1], bf[c ^ 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Wait until at most `stages_after` (0..2) stages of this wave's ring loads are still
+// outstanding; the other counters are not waited on.
+__device__ __forceinline__ void wait_vm_stages(int stages_after) {
+  static_assert(RING_LOADS == 6, "immediates below assume 6 loads per stage");
+  if (stages_after >= 2) __builtin_amdgcn_s_waitcnt(0x0F7C);        // vmcnt(12)
+  else if (stages_after == 1) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
+  else __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+}
+
 // ---- the kernel ----------------------------------------------------------------------
+// FWD and dX: 8 waves (512 threads), 4-slot ring of direct global->LDS loads.
 template <int OP, int D>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_gemm_ring(GemmArgs a) {
+  using T = Tiling<OP>;
+  constexpr int WJ = T::WJ;
+  constexpr bool CL = OP == OP_DX;               // codes are the L operand for dX
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOTB];   // 144 KiB
+  int tp, tq, tile;
+  if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
+  const int p0 = tp * BT, q0 = tq * BT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wp = wave / T::WGQ, wq = wave % T::WGQ;
+  const int nk = (a.R + BK - 1) / BK;
+
+  f32x16 acc[4][WJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // One pipelined pass over the contraction per bf16 operand (bf16 activations: one
+  // pass; float32 activations: hi and lo halves in two passes).
+  for (int pass = 0; pass < a.npass; ++pass) {
+    const uint16_t* mat = CL ? (pass == 0 ? a.Rmat[0] : a.Rmat[1])
+                             : (pass == 0 ? a.Lmat[0] : a.Lmat[1]);
+    const int64_t ld = CL ? a.N : a.K;
+    const int row0 = CL ? q0 : p0;
+    const int rowblock = CL ? tp : tq;
+#pragma unroll
+    for (int st = 0; st < RING - 1; ++st)
+      if (st < nk)
+        issue_ring_stage(smem + st * SLOTB, mat, ld, row0, a.M, st * BK, a.codes, rowblock, nk,
+                         st, wave, lane);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int after = nk - 1 - kt;
+      wait_vm_stages(after < 2 ? after : 2);
+      // Plain s_barrier: __syncthreads() would also wait for every outstanding load
+      // (a workgroup release fence), which would drain the ring. The memory clobber
+      // keeps the compiler from moving LDS reads across it.
+      asm volatile("s_barrier" ::: "memory");
+      if (kt + RING - 1 < nk)
+        issue_ring_stage(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
+                         (kt + RING - 1) * BK, a.codes, rowblock, nk, kt + RING - 1, wave, lane);
+      mma_ring_stage<CL, WJ>(smem + (kt % RING) * SLOTB, acc, wp, wq, lane);
+    }
+    __syncthreads();
+  }
+
+  if (OP == OP_FWD) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j) {
+        const int q = q0 + wq * 32 * WJ + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int p = p0 + wp * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (p < a.M && q < a.N) {
+            const float v = acc[i][j][r] + a.rowvec[p];
+            if (a.out_f32) static_cast<float*>(a.out)[(int64_t)p * a.N + q] = v;
+            else static_cast<__bf16*>(a.out)[(int64_t)p * a.N + q] = (__bf16)v;
+          }
+        }
+      }
+  } else {
+    // The ring is free after the last barrier: per-wave staging areas of 4.5 KiB, and
+    // for d = 16 a copy of A at 120 KiB.
+    float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
+    if (D == 16) {
+      if (tid < D * D) Alds[tid] = a.A[tid];
+      __syncthreads();
+    }
+    epilogue_dx<D, WJ>(a, acc, p0, q0, wp, wq, lane, reinterpret_cast<float*>(smem + wave * 4608), Alds);
+  }
+}
+
+// dW: 4 waves (256 threads), operands transposed through registers, double buffer.
+template <int D>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_dw(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];   // 128 KiB
   int tp, tq, tile;
   if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
   const int p0 = tp * BT, q0 = tq * BT;
@@ -379,86 +592,61 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 creg = make_uint4(0, 0, 0, 0);
   uint4 lreg[8], rreg[8];
-
-  auto issue = [&](int st, int buf) {
-    uint8_t* Ls = smem + buf * 2 * TILEB;
-    uint8_t* Rs = Ls + TILEB;
-    const int pass = st / nk, kt = st - pass * nk;
-    const int k0 = kt * BK;
-    if (OP == OP_FWD) {
-      load_rows_direct(Ls, a.Lmat[pass], a.K, p0, a.M, k0, wave, lane);
-      creg = load_codes(a.codes, tq, nk, kt, tid);
-    } else if (OP == OP_DX) {
-      creg = load_codes(a.codes, tp, nk, kt, tid);
-      load_rows_direct(Rs, a.Rmat[pass], a.N, q0, a.M, k0, wave, lane);
-    } else {
-      load_trans(lreg, a.Lmat[pass], a.K, k0, a.M, p0, a.K, tid);
-      load_trans(rreg, a.Rmat[pass], a.N, k0, a.M, q0, a.N, tid);
-    }
-  };
-  auto commit = [&](int buf) {
-    uint8_t* Ls = smem + buf * 2 * TILEB;
-    uint8_t* Rs = Ls + TILEB;
-    if (OP == OP_FWD) store_codes(Rs, creg, tid);
-    else if (OP == OP_DX) store_codes(Ls, creg, tid);
-    else { store_trans(Ls, lreg, tid); store_trans(Rs, rreg, tid); }
-  };
-
-  const int nst = nk * a.npass;
-  issue(0, 0);
-  commit(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int cur = st & 1;
-    if (st + 1 < nst) issue(st + 1, cur ^ 1);
-    mma_stage(smem + cur * 2 * TILEB, smem + cur * 2 * TILEB + TILEB, acc, wp, wq, lane);
-    if (st + 1 < nst) commit(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);
+  for (int pass = 0; pass < a.npass; ++pass) {
+    const uint16_t* Lp = pass == 0 ? a.Lmat[0] : (pass == 1 ? a.Lmat[1] : a.Lmat[2]);
+    const uint16_t* Rp = pass == 0 ? a.Rmat[0] : (pass == 1 ? a.Rmat[1] : a.Rmat[2]);
+    auto issue = [&](int kt) {
+      const int k0 = kt * BK;
+      load_trans(lreg, Lp, a.K, k0, a.M, p0, a.K, tid);
+      load_trans(rreg, Rp, a.N, k0, a.M, q0, a.N, tid);
+    };
+    auto commit = [&](int buf) {
+      uint8_t* Ls = smem + buf * 2 * TILEB;
+      store_trans(Ls, lreg, tid);
+      store_trans(Ls + TILEB, rreg, tid);
+    };
+    issue(0);
+    commit(0);
     __syncthreads();
-  }
-
-  if (OP == OP_FWD) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = q0 + wq * 128 + j * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = p0 + wp * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (p < a.M && q < a.N) {
-            const float v = acc[i][j][r] + a.rowvec[p];
-            if (a.out_f32) static_cast<float*>(a.out)[(int64_t)p * a.N + q] = v;
-            else static_cast<__bf16*>(a.out)[(int64_t)p * a.N + q] = (__bf16)v;
-          }
-        }
-      }
-  } else {
-    // Main-loop buffers are free after the last barrier. For d = 16 a copy of A sits
-    // in LDS (bytes [120 KiB, 121 KiB), clear of the staging and reduction areas).
-    float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
-    if (D == 16) {
-      if (tid < D * D) Alds[tid] = a.A[tid];
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) issue(kt + 1);
+      mma_stage_single(smem + cur * 2 * TILEB, smem + cur * 2 * TILEB + TILEB, acc, wp, wq, lane);
+      if (kt + 1 < nk) commit(cur ^ 1);
       __syncthreads();
     }
-    if (OP == OP_DX) epilogue_dx<D>(a, acc, p0, q0, wp, wq, lane, reinterpret_cast<float*>(smem + wave * WAVE_LDS), Alds);
-    else epilogue_dw<D>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
   }
+  // Main-loop buffers are free after the last barrier. For d = 16 a copy of A sits in
+  // LDS (bytes [120 KiB, 121 KiB), clear of the staging and reduction areas).
+  float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
+  if (D == 16) {
+    if (tid < D * D) Alds[tid] = a.A[tid];
+    __syncthreads();
+  }
+  epilogue_dw<D>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
 }
 
-// Fixed-order sum of the per-tile dA / dB partials.
+// One block per output: thread t adds tiles t, t+256, ... in order, then a fixed
+// binary tree in LDS combines the 256 thread sums.
 __global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ partials,
                                                          int ntiles, int nout,
                                                          float* __restrict__ dA,
                                                          float* __restrict__ dB, int d) {
-  for (int o = threadIdx.x; o < nout; o += blockDim.x) {
-    float s = 0.f;
-    for (int t = 0; t < ntiles; ++t) s += partials[(int64_t)t * nout + o];
-    if (o < d * d) dA[o] = s;
-    else dB[o - d * d] = s;
+  __shared__ float red[256];
+  const int o = blockIdx.x, t = threadIdx.x;
+  float s = 0.f;
+  for (int i = t; i < ntiles; i += 256) s += partials[(int64_t)i * nout + o];
+  red[t] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  if (t == 0) {
+    if (o < d * d) dA[o] = red[0];
+    else dB[o - d * d] = red[0];
   }
 }
 
@@ -469,11 +657,19 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   a.tilesQ = (a.Q + BT - 1) / BT;
   a.ntiles = a.tilesP * a.tilesQ;
   const int grid = ((a.ntiles + 7) / 8) * 8;
-  constexpr int id = OP == OP_FWD ? PROF_FWD : (OP == OP_DX ? PROF_DX : PROF_DW);
-  switch (d) {
-    case 4: LCVQ_LAUNCH(id, (k_gemm<OP, 4>), dim3(grid), dim3(256), 0, s, a); break;
-    case 8: LCVQ_LAUNCH(id, (k_gemm<OP, 8>), dim3(grid), dim3(256), 0, s, a); break;
-    default: LCVQ_LAUNCH(id, (k_gemm<OP, 16>), dim3(grid), dim3(256), 0, s, a); break;
+  if constexpr (OP == OP_DW) {
+    switch (d) {
+      case 4: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<4>, dim3(grid), dim3(256), 0, s, a); break;
+      case 8: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<8>, dim3(grid), dim3(256), 0, s, a); break;
+      default: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<16>, dim3(grid), dim3(256), 0, s, a); break;
+    }
+  } else {
+    constexpr int id = OP == OP_FWD ? PROF_FWD : PROF_DX;
+    switch (d) {
+      case 4: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 4>), dim3(grid), dim3(512), 0, s, a); break;
+      case 8: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 8>), dim3(grid), dim3(512), 0, s, a); break;
+      default: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 16>), dim3(grid), dim3(512), 0, s, a); break;
+    }
   }
   return hipGetLastError();
 }
@@ -525,7 +721,7 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
   a.dwp = dWp; a.packed = packed; a.mask = mask; a.partials = partials;
   hipError_t e = launch_op<OP_DW>(a, d, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_reduce_partials, dim3(1), dim3(256), 0, s, partials, a.ntiles,
+  hipLaunchKernelGGL(k_reduce_partials, dim3(d * d + d), dim3(256), 0, s, partials, a.ntiles,
                      d * d + d, dA, dB, d);
   return hipGetLastError();
 }

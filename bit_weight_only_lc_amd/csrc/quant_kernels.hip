@@ -13,67 +13,86 @@ namespace lcvq {
 
 // Index of the R16 word holding codes (row, 16*w .. 16*w+15) in the blocked layout
 // the GEMM loaders read: rows in blocks of 256, contraction in steps of 64, and each
-// (row block, step) slab of 256 rows x 4 words contiguous (4 KiB).
+// (row block, step) slab of 256 rows x 4 words contiguous (4 KiB). Inside a row the
+// word w sits at position (w + row/8) mod 4, which spreads the MFMA fragment reads of
+// 32 consecutive rows over all LDS banks.
 __device__ __forceinline__ int64_t r16_blocked_index(int64_t row, int64_t w, int64_t ksteps) {
-  return ((row >> 8) * ksteps + (w >> 2)) * 1024 + (row & 255) * 4 + (w & 3);
+  return ((row >> 8) * ksteps + (w >> 2)) * 1024 + (row & 255) * 4 + (((w & 3) + ((row >> 3) & 3)) & 3);
 }
 
 // ------------------------------------------------------------------ quantizer
+// Each wave streams a contiguous chunk of 1024 proxies with four fully coalesced
+// 16-byte loads per lane (lane l holds elements 256 j + 4 l .. +3 of load j). A group of
+// 16 consecutive codes (one packed word, one R16 word, one d-vector for d <= 16) is
+// spread over 4 neighbouring lanes and gathered with lane shuffles.
+template <int D>   // D = 0: no float32 decode requested
 __global__ __launch_bounds__(256) void k_quantize(
-    const float* __restrict__ wp, int64_t groups /* N*K/16 */, int64_t K,
-    uint8_t* __restrict__ z_out, uint32_t* __restrict__ packed_out,
-    uint16_t* __restrict__ mask_out, uint32_t* __restrict__ r16_out,
+    const float* __restrict__ wp, int64_t total /* N*K */, int64_t K,
+    uint8_t* __restrict__ z_out, uint8_t* __restrict__ packed_out,
+    uint8_t* __restrict__ mask_out, uint32_t* __restrict__ r16_out,
     float* __restrict__ what_out, const float* __restrict__ A,
-    const float* __restrict__ B, int d) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    const f4* src = reinterpret_cast<const f4*>(wp) + gi * 4;
-    float v[16];
+    const float* __restrict__ B) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int DD = D > 0 ? D : 1;
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 3;
+  const int64_t nchunks = (total + 1023) >> 10;
+  const int64_t wstride = (int64_t)gridDim.x * 4;
+  for (int64_t ch = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); ch < nchunks; ch += wstride) {
+    const int64_t base = ch << 10;
+    f4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f4 f = __builtin_nontemporal_load(src + q);
-      v[4 * q] = f.x; v[4 * q + 1] = f.y; v[4 * q + 2] = f.z; v[4 * q + 3] = f.w;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e = base + 256 * j + 4 * lane;
+      v[j] = e < total ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(wp + e))
+                       : f4{0.f, 0.f, 0.f, 0.f};
     }
-    uint32_t c[16];
-    uint32_t packed = 0, mbits = 0;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const float r = __builtin_rintf(v[t]);                // round half to even
-      // Comparisons are false for NaN, so NaN -> code 0; +inf -> 3; -inf -> 0.
-      c[t] = (uint32_t)(r >= 1.0f) + (uint32_t)(r >= 2.0f) + (uint32_t)(r >= 3.0f);
-      mbits |= (uint32_t)((r >= 0.0f) & (r <= 3.0f)) << t;
-      packed |= c[t] << (2 * t);
-    }
-    if (packed_out) packed_out[gi] = packed;
-    if (mask_out) mask_out[gi] = (uint16_t)mbits;
-    if (z_out) {
-      uint4 zz;
-      zz.x = c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24;
-      zz.y = c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24;
-      zz.z = c[8] | c[9] << 8 | c[10] << 16 | c[11] << 24;
-      zz.w = c[12] | c[13] << 8 | c[14] << 16 | c[15] << 24;
-      reinterpret_cast<uint4*>(z_out)[gi] = zz;
-    }
-    if (r16_out) {
-      const int64_t e = gi * 16;
-      const int64_t row = e / K;
-      const int64_t w = (e - row * K) >> 4;
-      r16_out[r16_blocked_index(row, w, K >> 6)] = r16_encode(c);
-    }
-    if (what_out) {
-      // What[n, g*d+i] = B[i] + sum_j A[i][j] z[n, g*d+j], in float32.
-      float o[16];
-      for (int v0 = 0; v0 < 16; v0 += d) {
-        for (int i = 0; i < d; ++i) {
-          float s = B[i];
-          for (int j = 0; j < d; ++j) s = __builtin_fmaf(A[i * d + j], (float)c[v0 + j], s);
-          o[v0 + i] = s;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e = base + 256 * j + 4 * lane;
+      uint32_t byte = 0, m4 = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float r = __builtin_rintf(v[j][t]);            // round half to even
+        // Comparisons are false for NaN, so NaN -> code 0; +inf -> 3; -inf -> 0.
+        const uint32_t c = (uint32_t)(r >= 1.0f) + (uint32_t)(r >= 2.0f) + (uint32_t)(r >= 3.0f);
+        byte |= c << (2 * t);
+        m4 |= (uint32_t)((r >= 0.0f) & (r <= 3.0f)) << t;
+      }
+      // the packed word of this lane's 16-code group (lanes 4a .. 4a+3)
+      const int g0 = lane & ~3;
+      const uint32_t w = (uint32_t)__shfl((int)byte, g0) | (uint32_t)__shfl((int)byte, g0 + 1) << 8 |
+                         (uint32_t)__shfl((int)byte, g0 + 2) << 16 | (uint32_t)__shfl((int)byte, g0 + 3) << 24;
+      const uint32_t mpair = m4 | ((uint32_t)__shfl_xor((int)m4, 1) << 4);
+      if (e < total) {
+        if (packed_out) packed_out[e >> 2] = (uint8_t)byte;
+        if (mask_out && !(lane & 1)) mask_out[e >> 3] = (uint8_t)mpair;
+        if (z_out)
+          *reinterpret_cast<uint32_t*>(z_out + e) =
+              (byte & 3u) | ((byte >> 2) & 3u) << 8 | ((byte >> 4) & 3u) << 16 | (byte >> 6) << 24;
+        if (r16_out && q == 0) {
+          uint32_t c[16];
+#pragma unroll
+          for (int t = 0; t < 16; ++t) c[t] = (w >> (2 * t)) & 3u;
+          const int64_t row = e / K;
+          r16_out[r16_blocked_index(row, (e - row * K) >> 4, K >> 6)] = r16_encode(c);
+        }
+        if (D > 0 && what_out) {
+          // What[n, g*d+i] = B[i] + sum_j A[i][j] z[n, g*d+j], in float32.
+          float o[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int p = 4 * q + t;             // position in the 16-group
+            const int v0 = (p / DD) * DD, i = p % DD;
+            float sacc = B[i];
+#pragma unroll
+            for (int jj = 0; jj < DD; ++jj)
+              sacc = __builtin_fmaf(A[i * DD + jj], (float)((w >> (2 * (v0 + jj))) & 3u), sacc);
+            o[t] = sacc;
+          }
+          *reinterpret_cast<float4*>(what_out + e) = make_float4(o[0], o[1], o[2], o[3]);
         }
       }
-      float4* dst = reinterpret_cast<float4*>(what_out) + gi * 4;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dst[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
     }
   }
 }
@@ -113,26 +132,35 @@ __global__ __launch_bounds__(256) void k_unpack2b(const uint32_t* __restrict__ p
 // ------------------------------------------------------------------ transposed codes
 // Canonical packed [N][K/4] -> R16 words along n, blocked for the dX product whose
 // operand rows are k: word (k, n/16) of the blocked layout with contraction length N.
-// One block transposes a 64 (n) x 64 (k) tile through LDS.
+// One block handles 64 rows n x 256 columns k: the 64 x 16 packed words go through LDS
+// and each thread then assembles the words of one column k for the 4 groups of 16 n.
 __global__ __launch_bounds__(256) void k_codes_to_r16t(const uint8_t* __restrict__ packed,
                                                        int64_t N, int64_t K,
                                                        uint32_t* __restrict__ r16t) {
-  __shared__ uint8_t tile[64][68];
+  __shared__ uint32_t tile[64][17];
   const int tid = threadIdx.x;
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
+  const int kcols = K - k0 < 256 ? (int)(K - k0) : 256;   // a multiple of 64
   {
     const int nr = tid >> 2, kq = tid & 3;
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(packed + (n0 + nr) * (K >> 2) + (k0 >> 2) + kq * 4);
-#pragma unroll
-    for (int t = 0; t < 16; ++t) tile[nr][kq * 16 + t] = (w >> (2 * t)) & 3u;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (kq * 64 < kcols)
+      w = *reinterpret_cast<const uint4*>(packed + (n0 + nr) * (K >> 2) + (k0 >> 2) + kq * 16);
+    tile[nr][kq * 4 + 0] = w.x;
+    tile[nr][kq * 4 + 1] = w.y;
+    tile[nr][kq * 4 + 2] = w.z;
+    tile[nr][kq * 4 + 3] = w.w;
   }
   __syncthreads();
-  {
-    const int kr = tid >> 2, wq = tid & 3;
+  const int kr = tid;                       // column k0 + kr
+  if (kr >= kcols) return;
+  const int sh = 2 * (kr & 15), wc = kr >> 4;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
     uint32_t c[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) c[t] = tile[wq * 16 + t][kr];
-    r16t[r16_blocked_index(k0 + kr, (n0 >> 4) + wq, N >> 6)] = r16_encode(c);
+    for (int t = 0; t < 16; ++t) c[t] = (tile[16 * g + t][wc] >> sh) & 3u;
+    r16t[r16_blocked_index(k0 + kr, (n0 >> 4) + g, N >> 6)] = r16_encode(c);
   }
 }
 
@@ -169,14 +197,19 @@ template <> __device__ __forceinline__ void load16<float>(const float* p, float 
 // so that Y[m, n] = sum_k xs[m, k] v(z[n, k]) + beta[m], with v(c) = 2 + c/2.
 // With float32 activations X' is kept to about 16 bits: xs_lo = 2 bf16(X' - X'b) is a
 // second operand added by a second pass of the product, and beta uses X'b + X'lo.
-template <typename T>
+// One block per row m; each thread takes 16 consecutive columns per step.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, int64_t K,
                                                       const float* __restrict__ A,
-                                                      const float* __restrict__ B, int d,
+                                                      const float* __restrict__ B,
                                                       uint16_t* __restrict__ xs,
                                                       uint16_t* __restrict__ xs_lo,
                                                       float* __restrict__ beta) {
   __shared__ float red[4];
+  __shared__ float As[D * D], Bs[D];
+  if (threadIdx.x < D * D) As[threadIdx.x] = A[threadIdx.x];
+  if (threadIdx.x < D) Bs[threadIdx.x] = B[threadIdx.x];
+  __syncthreads();
   const int64_t m = blockIdx.x;
   const T* xrow = X + m * K;
   uint16_t* orow = xs + m * K;
@@ -185,13 +218,17 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, i
     float x[16];
     load16<T>(xrow + c * 16, x);
     float xp[16];
-    for (int v0 = 0; v0 < 16; v0 += d) {
-      for (int j = 0; j < d; ++j) {
-        float s = 0.f;
-        for (int i = 0; i < d; ++i) s = __builtin_fmaf(x[v0 + i], A[i * d + j], s);
-        xp[v0 + j] = s;
+#pragma unroll
+    for (int v0 = 0; v0 < 16; v0 += D) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) sum = __builtin_fmaf(x[v0 + i], As[i * D + j], sum);
+        xp[v0 + j] = sum;
       }
-      for (int i = 0; i < d; ++i) acc = __builtin_fmaf(x[v0 + i], B[i], acc);
+#pragma unroll
+      for (int i = 0; i < D; ++i) acc = __builtin_fmaf(x[v0 + i], Bs[i], acc);
     }
     uint32_t o[8], ol[8];
 #pragma unroll
@@ -217,8 +254,8 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, i
       dl[1] = make_uint4(ol[4], ol[5], ol[6], ol[7]);
     }
   }
-  const float s = block_sum_256(acc, red);
-  if (threadIdx.x == 0) beta[m] = s;
+  const float sum = block_sum_256(acc, red);
+  if (threadIdx.x == 0) beta[m] = sum;
 }
 
 // ------------------------------------------------------------------ backward prologue
@@ -279,10 +316,24 @@ static int grid_for(int64_t groups) {
 hipError_t launch_quantize(const float* wp, int64_t N, int64_t K, uint8_t* z, uint8_t* packed,
                            uint8_t* mask, uint32_t* r16, float* what, const float* A,
                            const float* B, int d, hipStream_t s) {
-  const int64_t groups = N * K / 16;
-  LCVQ_LAUNCH(PROF_QUANTIZE, k_quantize, dim3(grid_for(groups)), dim3(256), 0, s, wp, groups, K, z,
-                     reinterpret_cast<uint32_t*>(packed), reinterpret_cast<uint16_t*>(mask),
-                     r16, what, A, B, d);
+  const int64_t total = N * K;
+  int64_t blocks = ((total + 1023) / 1024 + 3) / 4;
+  if (blocks > 65535) blocks = 65535;
+  if (blocks < 1) blocks = 1;
+  const dim3 g((unsigned)blocks);
+  if (!what) {
+    LCVQ_LAUNCH(PROF_QUANTIZE, k_quantize<0>, g, dim3(256), 0, s, wp, total, K, z, packed, mask,
+                r16, what, A, B);
+  } else if (d == 4) {
+    LCVQ_LAUNCH(PROF_QUANTIZE, k_quantize<4>, g, dim3(256), 0, s, wp, total, K, z, packed, mask,
+                r16, what, A, B);
+  } else if (d == 8) {
+    LCVQ_LAUNCH(PROF_QUANTIZE, k_quantize<8>, g, dim3(256), 0, s, wp, total, K, z, packed, mask,
+                r16, what, A, B);
+  } else {
+    LCVQ_LAUNCH(PROF_QUANTIZE, k_quantize<16>, g, dim3(256), 0, s, wp, total, K, z, packed, mask,
+                r16, what, A, B);
+  }
   return hipGetLastError();
 }
 
@@ -302,21 +353,29 @@ hipError_t launch_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t*
 
 hipError_t launch_codes_to_r16t(const uint8_t* packed, int64_t N, int64_t K, uint32_t* r16t,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(k_codes_to_r16t, dim3((unsigned)(K / 64), (unsigned)(N / 64)), dim3(256), 0,
+  hipLaunchKernelGGL(k_codes_to_r16t, dim3((unsigned)((K + 255) / 256), (unsigned)(N / 64)), dim3(256), 0,
                      s, packed, N, K, r16t);
   return hipGetLastError();
+}
+
+template <int D>
+static void fwd_prologue_d(const void* X, bool x_f32, int64_t M, int64_t K, const float* A,
+                           const float* B, uint16_t* xs, uint16_t* xs_lo, float* beta,
+                           hipStream_t s) {
+  if (x_f32)
+    hipLaunchKernelGGL((k_fwd_prologue<float, D>), dim3((unsigned)M), dim3(256), 0, s,
+                       static_cast<const float*>(X), K, A, B, xs, xs_lo, beta);
+  else
+    hipLaunchKernelGGL((k_fwd_prologue<uint16_t, D>), dim3((unsigned)M), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(X), K, A, B, xs, (uint16_t*)nullptr, beta);
 }
 
 hipError_t launch_fwd_prologue(const void* X, bool x_f32, int64_t M, int64_t K, const float* A,
                                const float* B, int d, uint16_t* xs, uint16_t* xs_lo,
                                float* beta, hipStream_t s) {
-  if (x_f32)
-    hipLaunchKernelGGL(k_fwd_prologue<float>, dim3((unsigned)M), dim3(256), 0, s,
-                       static_cast<const float*>(X), K, A, B, d, xs, xs_lo, beta);
-  else
-    hipLaunchKernelGGL(k_fwd_prologue<uint16_t>, dim3((unsigned)M), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(X), K, A, B, d, xs, (uint16_t*)nullptr,
-                       beta);
+  if (d == 4) fwd_prologue_d<4>(X, x_f32, M, K, A, B, xs, xs_lo, beta, s);
+  else if (d == 8) fwd_prologue_d<8>(X, x_f32, M, K, A, B, xs, xs_lo, beta, s);
+  else fwd_prologue_d<16>(X, x_f32, M, K, A, B, xs, xs_lo, beta, s);
   return hipGetLastError();
 }
 
