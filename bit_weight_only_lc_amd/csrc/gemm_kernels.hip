@@ -302,17 +302,19 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
 //   dA[i][j] += G[g*d+i, n] z[n, g*d+j],   dB[i] += G[g*d+i, n]
 // Per-lane partial sums are reduced over the wave through LDS, then over the 4 waves,
 // in a fixed order, into this tile's slot of `partials`.
-template <int D>
-__device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0, int wp, int wq,
+template <int D, int NW, int WJ>
+__device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
                             int lane, int wave, int tile, uint8_t* smem, const float* Alds) {
   constexpr int NP = D == 16 ? 4 : 1;          // passes over the columns j of dA
   constexpr int JW = D / NP;
   constexpr int NA = D * JW;                   // dA partials per lane and pass
   constexpr int NR = NA + D;                   // + dB partials (first pass)
   constexpr int RROW = NR + 1;
-  float* S = reinterpret_cast<float*>(smem + wave * WAVE_LDS);
+  constexpr int WREG = 12 * 1024;              // per-wave LDS area: staging, then reduction
+  static_assert(32 * RROW * 4 <= WREG && 32 * SROW * 4 <= WREG, "per-wave LDS area");
+  float* S = reinterpret_cast<float*>(smem + wave * WREG);
   float* red = S;                              // reused after the blocks of a pass
-  float* wsum = reinterpret_cast<float*>(smem + 4 * WAVE_LDS - 4 * NP * NR * 4);
+  float* wsum = reinterpret_cast<float*>(smem + NW * WREG);      // [NP][NW][NR]
   const int q = lane & 31;
   float dB[D];
 #pragma unroll
@@ -325,9 +327,9 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < WJ; ++j) {
         const int kb = p0 + wp * 128 + i * 32;
-        const int nb = q0 + wq * 128 + j * 32;
+        const int nb = q0 + wq * 32 * WJ + j * 32;
         wave_sync();
         stage_block(S, acc[i][j], lane);
         wave_sync();
@@ -341,7 +343,10 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0,
 #pragma unroll
           for (int e = 0; e < D; ++e) T[e] = S[(sl * D + e) * SROW + q];
           uint32_t zw = 0, mw = 0;
-          if (n < a.N && kv < a.K) {
+          // Rows and columns past the end of G hold clamped-operand values, not zeros:
+          // they must not reach dA or dB.
+          const bool valid = n < a.N && kv < a.K;
+          if (valid) {
             const uint8_t* zp = a.packed + (int64_t)n * (a.K >> 2) + (kv >> 2);
             const uint8_t* mp = a.mask + (int64_t)n * (a.K >> 3) + (kv >> 3);
             if (D == 4) { zw = zp[0]; mw = (mp[0] >> (kv & 4)) & 0xFu; }
@@ -351,13 +356,13 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0,
           if (pass == 0) {
 #pragma unroll
             for (int jj = 0; jj < D; ++jj) {
-              float s = 0.f;
+              float sum = 0.f;
 #pragma unroll
-              for (int e = 0; e < D; ++e) s = __builtin_fmaf(Ab[e * D + jj], T[e], s);
-              S[(sl * D + jj) * SROW + q] = ((mw >> jj) & 1u) ? s : 0.f;
+              for (int e = 0; e < D; ++e) sum = __builtin_fmaf(Ab[e * D + jj], T[e], sum);
+              S[(sl * D + jj) * SROW + q] = ((mw >> jj) & 1u) ? sum : 0.f;
             }
 #pragma unroll
-            for (int e = 0; e < D; ++e) dB[e] += T[e];
+            for (int e = 0; e < D; ++e) dB[e] += valid ? T[e] : 0.f;
           }
 #pragma unroll
           for (int jj = 0; jj < JW; ++jj) {
@@ -371,31 +376,39 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][4], int p0, int q0,
           store_block_rows(S, a.dwp, 1, a.K, nb, a.N, kb, a.K, lane);
         }
       }
-    // wave reduction through LDS: lane l writes its row, then lane l sums column(s)
+    // Wave reduction: lanes l and l+32 hold the same entries for different vectors; add
+    // them with one exchange, then lane l < 32 writes its row and lanes sum columns.
+#pragma unroll
+    for (int x = 0; x < NA; ++x) dA[x] += __shfl_xor(dA[x], 32);
+    float dBp[D];
+#pragma unroll
+    for (int x = 0; x < D; ++x) dBp[x] = pass == 0 ? dB[x] + __shfl_xor(dB[x], 32) : 0.f;
     wave_sync();
+    if (lane < 32) {
 #pragma unroll
-    for (int x = 0; x < NA; ++x) red[lane * RROW + x] = dA[x];
+      for (int x = 0; x < NA; ++x) red[lane * RROW + x] = dA[x];
 #pragma unroll
-    for (int x = 0; x < D; ++x) red[lane * RROW + NA + x] = pass == 0 ? dB[x] : 0.f;
+      for (int x = 0; x < D; ++x) red[lane * RROW + NA + x] = dBp[x];
+    }
     wave_sync();
     for (int x = lane; x < NR; x += 64) {
-      float s = 0.f;
-      for (int l = 0; l < 64; ++l) s += red[l * RROW + x];
-      wsum[(pass * 4 + wave) * NR + x] = s;
+      float sum = 0.f;
+      for (int l = 0; l < 32; ++l) sum += red[l * RROW + x];
+      wsum[(pass * NW + wave) * NR + x] = sum;
     }
   }
   __syncthreads();
   for (int o = threadIdx.x; o < D * D + D; o += blockDim.x) {
-    float s = 0.f;
+    float sum = 0.f;
     if (o < D * D) {
       const int e = o / D, jj = o % D;
       const int pass = jj / JW, x = e * JW + (jj % JW);
-      for (int w = 0; w < 4; ++w) s += wsum[(pass * 4 + w) * NR + x];
+      for (int w = 0; w < NW; ++w) sum += wsum[(pass * NW + w) * NR + x];
     } else {
       const int x = NA + (o - D * D);
-      for (int w = 0; w < 4; ++w) s += wsum[(0 * 4 + w) * NR + x];
+      for (int w = 0; w < NW; ++w) sum += wsum[w * NR + x];
     }
-    a.partials[(int64_t)tile * (D * D + D) + o] = s;
+    a.partials[(int64_t)tile * (D * D + D) + o] = sum;
   }
 }
 
@@ -572,59 +585,137 @@ void k_gemm_ring(GemmArgs a) {
   }
 }
 
-// dW: 4 waves (256 threads), operands transposed through registers, double buffer.
+// ---- dW product: both operands arrive in their natural [m][column] layout ------------
+// G^T[k, n] = sum_m X[m, k] dY[m, n] contracts over the rows of both matrices. Their
+// tiles (64 rows m x 256 columns, 512 bytes per row) go straight from HBM into LDS, and
+// the MFMA fragments (8 consecutive m for one column) are read with gfx950's
+// transposing LDS read ds_read_b64_tr_b16: within each group of 16 lanes, lane t
+// receives element t%4 of the 64-bit pieces supplied by lanes 4e + t/4, e = 0..3.
+// Source lane t of a group therefore points at row m0 + t/4, columns c0 + 4(t%4); the
+// group gets columns c0 .. c0+15 with 4 consecutive m each. Two reads (m, m+4) fill an
+// 8-element operand. 16-byte chunks are XOR-swizzled by 4*(m mod 4), which spreads the
+// 8 rows x 4 chunks of one read evenly over the banks.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+constexpr int TROWB = 512;                     // bytes per LDS row of a transposed tile
+constexpr int TTILEB = 64 * TROWB;             // 32 KiB
+__device__ __forceinline__ int tswz(int m) { return (m & 3) << 2; }
+
+__device__ __forceinline__ bf16x8 trans_frag(const uint8_t* tile, int colbase, int s, int lane) {
+  const int g = lane >> 4, t = lane & 15;
+  const int col = colbase + 16 * (g & 1) + 4 * (t & 3);
+  const int m = 16 * s + 8 * (g >> 1) + (t >> 2);
+  const int m2 = m + 4;
+  const LCVQ_LDS uint8_t* base = (const LCVQ_LDS uint8_t*)tile;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LCVQ_LDS v4i16*)(base + m * TROWB + (((col >> 3) ^ tswz(m)) << 4) + ((col & 4) << 1)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LCVQ_LDS v4i16*)(base + m2 * TROWB + (((col >> 3) ^ tswz(m2)) << 4) + ((col & 4) << 1)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// One stage: 64 rows m of X (columns p0..p0+255) and of dY (columns q0..q0+255). Wave w
+// fills rows [8w, 8w+8) of each tile, 2 rows per instruction (lane l: row l/32, physical
+// chunk l%32). Rows past M are written as zeros (they are contraction terms); columns
+// past the end are clamped (they only feed C entries that are never stored).
+__device__ __forceinline__ void issue_dw_stage(uint8_t* slot, const uint16_t* X, const uint16_t* dY,
+                                               int M, int N, int K, int m0, int p0, int q0,
+                                               int wave, int lane) {
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const uint16_t* mat = op == 0 ? X : dY;
+    const int ld = op == 0 ? K : N;
+    const int c0 = op == 0 ? p0 : q0;
+    uint8_t* tile = slot + op * TTILEB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 8 + i * 2 + (lane >> 5);
+      const int phys = lane & 31;
+      const int c = phys ^ tswz(r);
+      int col = c0 + c * 8;
+      col = col < ld ? col : ld - 8;
+      const int m = m0 + r;
+      if (m < M) {
+        const uint16_t* src = mat + (int64_t)m * ld + col;
+        __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(tile + (wave * 8 + i * 2) * TROWB), 16, 0, 0);
+      } else {
+        *reinterpret_cast<uint4*>(tile + r * TROWB + phys * 16) = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int WJ>
+__device__ __forceinline__ void mma_dw_stage(const uint8_t* slot, f32x16 acc[4][WJ], int wp, int wq,
+                                             int lane) {
+  const uint8_t* Xt = slot;
+  const uint8_t* Yt = slot + TTILEB;
+  bf16x8 af[2][4], bf[2][WJ];
+  auto load = [&](int s, bf16x8* fa, bf16x8* fb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = trans_frag(Xt, wp * 128 + i * 32, s, lane);
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) fb[j] = trans_frag(Yt, wq * 32 * WJ + j * 32, s, lane);
+  };
+  load(0, af[0], bf[0]);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int c = s & 1;
+    if (s < 3) load(s + 1, af[c ^ 1], bf[c ^ 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// dW: 8 waves (512 threads), double-buffered direct loads into LDS (2 x 64 KiB).
 template <int D>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_dw(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TILEB];   // 128 KiB
+  constexpr int NW = 8, WGQ = 4, WJ = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TTILEB];   // 128 KiB
   int tp, tq, tile;
   if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wp = wave >> 1, wq = wave & 1;
+  const int wp = wave / WGQ, wq = wave % WGQ;
   const int nk = (a.R + BK - 1) / BK;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][WJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 lreg[8], rreg[8];
   for (int pass = 0; pass < a.npass; ++pass) {
     const uint16_t* Lp = pass == 0 ? a.Lmat[0] : (pass == 1 ? a.Lmat[1] : a.Lmat[2]);
     const uint16_t* Rp = pass == 0 ? a.Rmat[0] : (pass == 1 ? a.Rmat[1] : a.Rmat[2]);
-    auto issue = [&](int kt) {
-      const int k0 = kt * BK;
-      load_trans(lreg, Lp, a.K, k0, a.M, p0, a.K, tid);
-      load_trans(rreg, Rp, a.N, k0, a.M, q0, a.N, tid);
-    };
-    auto commit = [&](int buf) {
-      uint8_t* Ls = smem + buf * 2 * TILEB;
-      store_trans(Ls, lreg, tid);
-      store_trans(Ls + TILEB, rreg, tid);
-    };
-    issue(0);
-    commit(0);
+    issue_dw_stage(smem, Lp, Rp, a.M, a.N, a.K, 0, p0, q0, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) issue(kt + 1);
-      mma_stage_single(smem + cur * 2 * TILEB, smem + cur * 2 * TILEB + TILEB, acc, wp, wq, lane);
-      if (kt + 1 < nk) commit(cur ^ 1);
+      if (kt + 1 < nk)
+        issue_dw_stage(smem + (cur ^ 1) * 2 * TTILEB, Lp, Rp, a.M, a.N, a.K, (kt + 1) * BK, p0,
+                       q0, wave, lane);
+      mma_dw_stage<WJ>(smem + cur * 2 * TTILEB, acc, wp, wq, lane);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
-  // Main-loop buffers are free after the last barrier. For d = 16 a copy of A sits in
-  // LDS (bytes [120 KiB, 121 KiB), clear of the staging and reduction areas).
+  // The buffers are free after the last barrier: per-wave areas of 12 KiB from 0, the
+  // per-wave sums after them, and for d = 16 a copy of A at 120 KiB.
   float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
   if (D == 16) {
     if (tid < D * D) Alds[tid] = a.A[tid];
     __syncthreads();
   }
-  epilogue_dw<D>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
+  epilogue_dw<D, NW, WJ>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
 }
 
 // One block per output: thread t adds tiles t, t+256, ... in order, then a fixed
@@ -659,9 +750,9 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   const int grid = ((a.ntiles + 7) / 8) * 8;
   if constexpr (OP == OP_DW) {
     switch (d) {
-      case 4: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<4>, dim3(grid), dim3(256), 0, s, a); break;
-      case 8: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<8>, dim3(grid), dim3(256), 0, s, a); break;
-      default: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<16>, dim3(grid), dim3(256), 0, s, a); break;
+      case 4: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<4>, dim3(grid), dim3(512), 0, s, a); break;
+      case 8: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<8>, dim3(grid), dim3(512), 0, s, a); break;
+      default: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<16>, dim3(grid), dim3(512), 0, s, a); break;
     }
   } else {
     constexpr int id = OP == OP_FWD ? PROF_FWD : PROF_DX;
