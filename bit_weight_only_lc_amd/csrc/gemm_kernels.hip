@@ -31,11 +31,15 @@ constexpr int TILEB = BT * ROWB;
 
 enum { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
 
-// Wave layout per workgroup: 2 wave rows x (NW/2) wave columns; a wave owns 128 rows and
-// 32*WJ columns of the C tile.
+// Wave layout of the 8-wave products: WGP wave rows x WGQ wave columns; a wave owns
+// 32*WI rows and 32*WJ columns of the C tile. The operand made of codes is spread over
+// the wave dimension with fewer waves, so that each wave expands as few code fragments
+// as possible (forward: codes are columns; dX: codes are rows).
 template <int OP> struct Tiling {
-  static constexpr int NW = OP == OP_DW ? 4 : 8;
-  static constexpr int WGQ = NW / 2;
+  static constexpr int NW = 8;
+  static constexpr int WGP = OP == OP_DX ? 4 : 2;
+  static constexpr int WGQ = NW / WGP;
+  static constexpr int WI = 8 / WGP;
   static constexpr int WJ = 8 / WGQ;
 };
 
@@ -252,8 +256,8 @@ __device__ __forceinline__ void store_block_rows(const float* S, void* out, int 
 
 // dX[m, g*d+i] = 2 sum_j A[i][j] C[g*d+j, m] + (B[i] - 4 sum_j A[i][j]) r[m]
 // where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m).
-template <int D, int WJ>
-__device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
+template <int D, int WI, int WJ>
+__device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp, int wq,
                             int lane, float* S, const float* Alds) {
   float bp[D];
 #pragma unroll
@@ -265,10 +269,10 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
   }
   const int q = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
     for (int j = 0; j < WJ; ++j) {
-      const int kb = p0 + wp * 128 + i * 32;
+      const int kb = p0 + wp * 32 * WI + i * 32;
       const int mb = q0 + wq * 32 * WJ + j * 32;
       wave_sync();
       stage_block(S, acc[i][j], lane);
@@ -448,10 +452,12 @@ __device__ __forceinline__ void issue_ring_stage(uint8_t* slot, const uint16_t* 
   }
 }
 
-// The MFMA fragment (8 consecutive codes as v(c) bf16) of tile row `row`, sub-step s,
-// half h of the 16-code word.
-__device__ __forceinline__ bf16x8 codes_frag(const uint8_t* ctile, int row, int s, int h) {
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(ctile + row * 16 + (((s + (row >> 3)) & 3) << 2));
+// The R16 word of tile row `row` for sub-step s, and its expansion into the MFMA
+// fragment (8 consecutive codes as v(c) bf16) for half h of the 16-code word.
+__device__ __forceinline__ uint32_t codes_word(const uint8_t* ctile, int row, int s) {
+  return *reinterpret_cast<const uint32_t*>(ctile + row * 16 + (((s + (row >> 3)) & 3) << 2));
+}
+__device__ __forceinline__ bf16x8 codes_expand(uint32_t w, int h) {
   const uint32_t src = h ? __builtin_amdgcn_alignbit(w, w, 8) : w;
   u32x4 o;
 #pragma unroll
@@ -459,40 +465,71 @@ __device__ __forceinline__ bf16x8 codes_frag(const uint8_t* ctile, int row, int 
   return __builtin_bit_cast(bf16x8, o);
 }
 
-template <bool CODES_ARE_L, int WJ>
-__device__ __forceinline__ void load_frags_ring(const uint8_t* slot, int s, int wp, int wq, int lane,
-                                                bf16x8 af[4], bf16x8 bf[WJ]) {
-  const uint8_t* tile = slot;
-  const uint8_t* ctile = slot + TILEB;
-  const int chunk = 2 * s + (lane >> 5), h = lane >> 5;
+// Sub-step fragments: NB bf16 fragments read from the swizzled tile and NC code words.
+template <bool CODES_ARE_L, int WI, int WJ>
+struct RingFrags {
+  static constexpr int NB = CODES_ARE_L ? WJ : WI;   // bf16-tile fragments
+  static constexpr int NC = CODES_ARE_L ? WI : WJ;   // code fragments
+  bf16x8 b[NB];
+  uint32_t w[NC];
+  bf16x8 c[NC];
+};
+
+template <bool CODES_ARE_L, int WI, int WJ>
+__device__ __forceinline__ void ring_read(const uint8_t* slot, int s, int wp, int wq, int lane,
+                                          RingFrags<CODES_ARE_L, WI, WJ>& f) {
+  using F = RingFrags<CODES_ARE_L, WI, WJ>;
+  const int chunk = 2 * s + (lane >> 5);
+  const int tb = CODES_ARE_L ? wq * 32 * WJ : wp * 32 * WI;  // bf16-tile rows
+  const int cb = CODES_ARE_L ? wp * 32 * WI : wq * 32 * WJ;  // code rows
+  // code words first: their expansion is the first consumer
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wp * 128 + i * 32 + (lane & 31);
-    af[i] = CODES_ARE_L ? codes_frag(ctile, row, s, h)
-                        : *reinterpret_cast<const bf16x8*>(tile + lds_off(row, chunk));
-  }
+  for (int i = 0; i < F::NC; ++i) f.w[i] = codes_word(slot + TILEB, cb + i * 32 + (lane & 31), s);
 #pragma unroll
-  for (int j = 0; j < WJ; ++j) {
-    const int row = wq * 32 * WJ + j * 32 + (lane & 31);
-    bf[j] = CODES_ARE_L ? *reinterpret_cast<const bf16x8*>(tile + lds_off(row, chunk))
-                        : codes_frag(ctile, row, s, h);
+  for (int i = 0; i < F::NB; ++i) {
+    const int row = tb + i * 32 + (lane & 31);
+    f.b[i] = *reinterpret_cast<const bf16x8*>(slot + lds_off(row, chunk));
   }
 }
 
-template <bool CODES_ARE_L, int WJ>
-__device__ __forceinline__ void mma_ring_stage(const uint8_t* slot, f32x16 acc[4][WJ], int wp,
+template <bool CODES_ARE_L, int WI, int WJ>
+__device__ __forceinline__ void ring_expand(RingFrags<CODES_ARE_L, WI, WJ>& f, int lane) {
+#pragma unroll
+  for (int i = 0; i < RingFrags<CODES_ARE_L, WI, WJ>::NC; ++i) f.c[i] = codes_expand(f.w[i], lane >> 5);
+}
+
+template <bool CODES_ARE_L, int WI, int WJ>
+__device__ __forceinline__ void mma_ring_stage(const uint8_t* slot, f32x16 acc[WI][WJ], int wp,
                                                int wq, int lane) {
-  bf16x8 af[2][4], bf[2][WJ];
-  load_frags_ring<CODES_ARE_L, WJ>(slot, 0, wp, wq, lane, af[0], bf[0]);
+  using F = RingFrags<CODES_ARE_L, WI, WJ>;
+  F f[2];
+  ring_read<CODES_ARE_L, WI, WJ>(slot, 0, wp, wq, lane, f[0]);
+  ring_expand<CODES_ARE_L, WI, WJ>(f[0], lane);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int c = s & 1;
-    if (s < 3) load_frags_ring<CODES_ARE_L, WJ>(slot, s + 1, wp, wq, lane, af[c ^ 1], bf[c ^ 1]);
+    // LDS reads of the next sub-step go out before this sub-step's MFMAs; the code
+    // expansion of the next sub-step is interleaved with those MFMAs.
+    if (s < 3) ring_read<CODES_ARE_L, WI, WJ>(slot, s + 1, wp, wq, lane, f[c ^ 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
-      for (int j = 0; j < WJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < WJ; ++j) {
+        const bf16x8 av = CODES_ARE_L ? f[c].c[i] : f[c].b[i];
+        const bf16x8 bv = CODES_ARE_L ? f[c].b[j] : f[c].c[j];
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
+      }
+    if (s < 3) {
+      ring_expand<CODES_ARE_L, WI, WJ>(f[c ^ 1], lane);
+      constexpr int NV = (F::NC * 10 + WI * WJ - 1) / (WI * WJ);  // VALU per MFMA slot
+#pragma unroll
+      for (int g = 0; g < WI * WJ; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -511,7 +548,7 @@ template <int OP, int D>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_ring(GemmArgs a) {
   using T = Tiling<OP>;
-  constexpr int WJ = T::WJ;
+  constexpr int WI = T::WI, WJ = T::WJ;
   constexpr bool CL = OP == OP_DX;               // codes are the L operand for dX
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOTB];   // 144 KiB
   int tp, tq, tile;
@@ -521,9 +558,9 @@ void k_gemm_ring(GemmArgs a) {
   const int wp = wave / T::WGQ, wq = wave % T::WGQ;
   const int nk = (a.R + BK - 1) / BK;
 
-  f32x16 acc[4][WJ];
+  f32x16 acc[WI][WJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
     for (int j = 0; j < WJ; ++j)
 #pragma unroll
@@ -552,20 +589,20 @@ void k_gemm_ring(GemmArgs a) {
       if (kt + RING - 1 < nk)
         issue_ring_stage(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
                          (kt + RING - 1) * BK, a.codes, rowblock, nk, kt + RING - 1, wave, lane);
-      mma_ring_stage<CL, WJ>(smem + (kt % RING) * SLOTB, acc, wp, wq, lane);
+      mma_ring_stage<CL, WI, WJ>(smem + (kt % RING) * SLOTB, acc, wp, wq, lane);
     }
     __syncthreads();
   }
 
   if (OP == OP_FWD) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WI; ++i)
 #pragma unroll
       for (int j = 0; j < WJ; ++j) {
         const int q = q0 + wq * 32 * WJ + j * 32 + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int p = p0 + wp * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int p = p0 + wp * 32 * WI + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (p < a.M && q < a.N) {
             const float v = acc[i][j][r] + a.rowvec[p];
             if (a.out_f32) static_cast<float*>(a.out)[(int64_t)p * a.N + q] = v;
@@ -581,7 +618,7 @@ void k_gemm_ring(GemmArgs a) {
       if (tid < D * D) Alds[tid] = a.A[tid];
       __syncthreads();
     }
-    epilogue_dx<D, WJ>(a, acc, p0, q0, wp, wq, lane, reinterpret_cast<float*>(smem + wave * 4608), Alds);
+    epilogue_dx<D, WI, WJ>(a, acc, p0, q0, wp, wq, lane, reinterpret_cast<float*>(smem + wave * 4608), Alds);
   }
 }
 
@@ -663,11 +700,13 @@ __device__ __forceinline__ void mma_dw_stage(const uint8_t* slot, f32x16 acc[4][
   for (int s = 0; s < 4; ++s) {
     const int c = s & 1;
     if (s < 3) load(s + 1, af[c ^ 1], bf[c ^ 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < WJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
