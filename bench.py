@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=10)
+    ap.add_argument("--no-copy-probe", action="store_true")
     return ap.parse_args()
 
 
@@ -165,6 +166,29 @@ def main():
             del pool
             torch.cuda.empty_cache()
 
+    # ---------------------------------------------------------------- HBM copy ceiling
+    # A plain device-to-device copy of 1 GiB: the streaming ceiling measured beside the
+    # decode product, and the kernel of known size that scales the HBM byte counters.
+    copy_probe = None
+    if not args.no_copy_probe:
+        nb = 1 << 30
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).random_(0, 256)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        reps = 10
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        c1.record()
+        torch.cuda.synchronize()
+        t_c = c0.elapsed_time(c1) / reps * 1e-3
+        copy_probe = {"bytes_read": nb, "bytes_written": nb, "us": round(t_c * 1e6, 1),
+                      "gbs": round(2 * nb / t_c / 1e9, 1)}
+        del src, dst
+        torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -211,6 +235,7 @@ def main():
                    "M": M, "N": N, "K": K, "d": d},
         "roofline": roofline,
         "decode": decode,
+        "hbm_copy_probe": copy_probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
