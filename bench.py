@@ -30,6 +30,41 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
 KERNELS = {1: "quantize", 2: "fwd_product", 3: "dx_product", 4: "dw_product"}
 
+# HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE, each
+# scaled by what it reads for a copy of known size). They are valid only for the kernel
+# sources they were taken on; the summary records those sources' SHA-256.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "train_step_4096x4096_m4096_d8_hbm_counters.md")
+CSRC = os.path.join(ROOT, "bit_weight_only_lc_amd", "csrc")
+KERNEL_SOURCES = {
+    "products": ["gemm_kernels.hip", "lcvq_device.h", "lcvq_internal.h"],
+    "quantize": ["quant_kernels.hip", "lcvq_device.h", "lcvq_internal.h"],
+}
+SOURCE_GROUP = {"quantize": "quantize", "fwd_product": "products", "dx_product": "products",
+                "dw_product": "products"}
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    the summary is missing or the kernel's sources changed since it was taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    group = SOURCE_GROUP[kernel]
+    if rec.get("sources_sha256", {}).get(group) != source_digest(KERNEL_SOURCES[group]):
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -116,7 +151,8 @@ def main():
     achieved = gemm_flops / (prods[dom] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic(dom),
                 "per_kernel_ms": {k: round(v, 4) for k, v in kern.items()},
                 "per_product_tflops": {k: round(gemm_flops / (v * 1e-3) / 1e12, 1)
                                        for k, v in prods.items()}}

@@ -15,8 +15,8 @@
 // steps of 64):
 //   FWD: L = X' (bf16 rows m),        R = codes (rows n)       8 waves, 4-slot LDS ring
 //   DX : L = codes transposed (rows k), R = dY (bf16 rows m)   8 waves, 4-slot LDS ring
-//   DW : L = X^T (rows k), R = dY^T (rows n), both transposed on the way into LDS;
-//        4 waves, double buffer.
+//   DW : L = X^T (rows k), R = dY^T (rows n); both tiles arrive in their natural layout
+//        and are transposed by the LDS reads; 8 waves, double buffer.
 // With 8 waves two waves share each SIMD, so one wave's LDS waits and code expansion
 // overlap the other wave's MFMAs.
 #include "lcvq_device.h"
@@ -304,7 +304,7 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
 // Straight-through epilogue on G (rows k, columns n):
 //   dWp[n, g*d+j] = mask * sum_i A[i][j] G[g*d+i, n]
 //   dA[i][j] += G[g*d+i, n] z[n, g*d+j],   dB[i] += G[g*d+i, n]
-// Per-lane partial sums are reduced over the wave through LDS, then over the 4 waves,
+// Per-lane partial sums are reduced over the wave through LDS, then over the waves,
 // in a fixed order, into this tile's slot of `partials`.
 template <int D, int NW, int WJ>
 __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
