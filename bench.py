@@ -174,7 +174,7 @@ def main():
             for m in SI.CONFIGS["c3_decode"]["Ms"]:
                 Xd = SI.make_act(m, k, seed=3100 + m, device=dev)
                 Yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-                ws = torch.empty(P.lcvq_gemv2b_workspace_size(m, k, 8), dtype=torch.uint8,
+                ws = torch.empty(P.lcvq_gemv2b_workspace_size(m, n, k, 8), dtype=torch.uint8,
                                  device=dev)
                 calls = 2 * copies
                 for i in range(copies):

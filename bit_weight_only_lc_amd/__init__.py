@@ -61,7 +61,7 @@ def lib():
             f.restype = sz
             f.argtypes = [i64, i64, i64, i32]
         L.lcvq_gemv2b_workspace_size.restype = sz
-        L.lcvq_gemv2b_workspace_size.argtypes = [i64, i64, i32]
+        L.lcvq_gemv2b_workspace_size.argtypes = [i64, i64, i64, i32]
         L.lcvq_profile_next.restype = i32
         L.lcvq_profile_next.argtypes = [i32, vp, vp]
         _lib = L
@@ -113,8 +113,8 @@ def lcvq_linear_bwd_workspace_size(M, N, K, d):
     return int(lib().lcvq_linear_bwd_workspace_size(M, N, K, d))
 
 
-def lcvq_gemv2b_workspace_size(M, K, d):
-    return int(lib().lcvq_gemv2b_workspace_size(M, K, d))
+def lcvq_gemv2b_workspace_size(M, N, K, d):
+    return int(lib().lcvq_gemv2b_workspace_size(M, N, K, d))
 
 
 # ------------------------------------------------------------------ entry points
@@ -197,7 +197,7 @@ def lcvq_gemv2b(X, packed, A16, B16, d, Y, workspace=None):
     M, K = X.shape
     N = packed.shape[0]
     if workspace is None:
-        workspace = torch.empty(max(lcvq_gemv2b_workspace_size(M, K, d), 1),
+        workspace = torch.empty(max(lcvq_gemv2b_workspace_size(M, N, K, d), 1),
                                 dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", torch.uint8, dev)
     _ok(lib().lcvq_gemv2b(_p(X), M, N, K, d, _p(packed), _p(A16), _p(B16), _p(Y),

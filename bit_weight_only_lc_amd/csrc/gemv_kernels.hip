@@ -12,19 +12,82 @@
 //     limbs, so each block is two exact int32 MFMA sums, scaled once per block.
 // The order in which a lane's 16 codes reach the MFMA differs from their order in k;
 // the prologue writes X' limbs in that same order.
+#include <algorithm>
+
 #include "lcvq_device.h"
 #include "lcvq_internal.h"
 
 namespace lcvq {
 
 constexpr int GK = 256;   // k per block (4 MFMA of k = 64)
+constexpr int GEMV_FUSED_M = 2;     // up to this many tokens one fused kernel does it all
 
-// X' limbs layout: for block kb, MFMA step s (0..3), limb (0 = high, 1 = low):
-//   1 KiB at ((kb*4 + s)*2 + limb) * 1024, lane l = 16*kq + m at byte 16*l; the lane's
-//   dword t, byte b holds column 64*kq + 16*s + 4*b + t of the block.
+// The fused path (X' formed in LDS by every workgroup) serves few tokens and K up to 64
+// blocks; otherwise a prologue kernel writes X' once and the product reads it.
+inline bool gemv_fused(int M, int K) { return M <= GEMV_FUSED_M && K / 256 <= 64; }
+
+// X' limbs: each (block kb, MFMA step s, limb 0 = high / 1 = low, quarter kq, row m) is
+// a 16-byte chunk whose dword t, byte b holds column 64*kq + 16*s + 4*b + t of the block.
+// The two-kernel path keeps them in global memory in MFMA lane order, 1 KiB per
+// (kb, s, limb) with lane l = 16*kq + m at byte 16*l; the fused path keeps only rows
+// m < M, dense in LDS, chunk index ((kb*8 + 2s + limb)*4 + kq)*M + m.
 // rowinfo[kb][m] = (2^-e, partial beta) with e the block's fixed-point exponent; rows
 // m >= M hold zeros.
-// Thread t = 16*m + kc of block kb forms the 16 columns of (kq, s) = (kc >> 2, kc & 3).
+
+// X' for one (row m, 256-column block): 16 consecutive lanes (kc = 0..15) each take the
+// 16 columns of (kq, s) = (kc >> 2, kc & 3), given as 32 bytes of bf16 X. The lanes form
+// X' = X (I kron A) and X (1 kron B) in float32, agree on the block's exponent
+// (|X' 2^e| < 2^14) and return the two int8 limbs in MFMA byte order (column 4b + t in
+// dword t, byte b), the scale 2^-e and the block's partial beta.
+template <int D>
+__device__ __forceinline__ void xprime_chunk(uint4 a, uint4 b, const float* As, const float* Bs,
+                                             uint32_t (&hi)[4], uint32_t (&lo)[4],
+                                             float& scale, float& bsum) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float x[16], xp[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { x[2 * i] = bf16lo_to_f32(w[i]); x[2 * i + 1] = bf16hi_to_f32(w[i]); }
+  float amax = 0.f;
+  bsum = 0.f;
+#pragma unroll
+  for (int v0 = 0; v0 < 16; v0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) s = __builtin_fmaf(x[v0 + i], As[i * D + j], s);
+      xp[v0 + j] = s;
+      amax = fmaxf(amax, fabsf(s));
+    }
+#pragma unroll
+    for (int i = 0; i < D; ++i) bsum = __builtin_fmaf(x[v0 + i], Bs[i], bsum);
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    amax = fmaxf(amax, __shfl_xor(amax, o));
+    bsum += __shfl_xor(bsum, o);
+  }
+  int ex = 0;
+  if (amax > 0.f) {
+    int E;
+    frexpf(amax, &E);          // amax = f * 2^E, f in [0.5, 1)
+    ex = 14 - E;               // |X' * 2^ex| < 2^14
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) hi[t] = lo[t] = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int q = (int)__builtin_rintf(ldexpf(xp[u], ex));
+    const int l = ((q + 128) & 255) - 128;
+    const int h = (q - l) >> 8;
+    const int tt = u & 3, bb = u >> 2;          // column 4*bb + tt -> dword tt, byte bb
+    hi[tt] |= (uint32_t)(h & 255) << (8 * bb);
+    lo[tt] |= (uint32_t)(l & 255) << (8 * bb);
+  }
+  scale = ldexpf(1.f, -ex);
+}
+
+// Prologue of the two-kernel path: thread t = 16*m + kc of block kb.
 template <int D>
 __global__ __launch_bounds__(256) void k_gemv_prologue(const uint16_t* __restrict__ X, int M,
                                                        int K, const uint16_t* __restrict__ A16,
@@ -45,63 +108,27 @@ __global__ __launch_bounds__(256) void k_gemv_prologue(const uint16_t* __restric
   if (t < D * D) As[t] = (float)__builtin_bit_cast(_Float16, A16[t]);
   if (t < D) Bs[t] = (float)__builtin_bit_cast(_Float16, B16[t]);
   __syncthreads();
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  float x[16], xp[16];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { x[2 * i] = bf16lo_to_f32(w[i]); x[2 * i + 1] = bf16hi_to_f32(w[i]); }
-  float bsum = 0.f, amax = 0.f;
-#pragma unroll
-  for (int v0 = 0; v0 < 16; v0 += D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < D; ++i) s = __builtin_fmaf(x[v0 + i], As[i * D + j], s);
-      xp[v0 + j] = s;
-      amax = fmaxf(amax, fabsf(s));
-    }
-#pragma unroll
-    for (int i = 0; i < D; ++i) bsum = __builtin_fmaf(x[v0 + i], Bs[i], bsum);
-  }
-  // reduce over the 16 threads of row m (consecutive lanes)
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    amax = fmaxf(amax, __shfl_xor(amax, o));
-    bsum += __shfl_xor(bsum, o);
-  }
-  int ex = 0;
-  if (amax > 0.f) {
-    int E;
-    frexpf(amax, &E);          // amax = f * 2^E, f in [0.5, 1)
-    ex = 14 - E;               // |X' * 2^ex| < 2^14
-  }
-  uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int q = (int)__builtin_rintf(ldexpf(xp[u], ex));
-    const int l = ((q + 128) & 255) - 128;
-    const int h = (q - l) >> 8;
-    const int tt = u & 3, bb = u >> 2;          // column 4*bb + tt -> dword tt, byte bb
-    hi[tt] |= (uint32_t)(h & 255) << (8 * bb);
-    lo[tt] |= (uint32_t)(l & 255) << (8 * bb);
-  }
+  uint32_t hi[4], lo[4];
+  float scale, bsum;
+  xprime_chunk<D>(a, b, As, Bs, hi, lo, scale, bsum);
   if (m < M) {
     const int kq = kc >> 2, s = kc & 3;
-    const int lane = 16 * kq + m;
-    uint4* dh = reinterpret_cast<uint4*>(xq + ((int64_t)(kb * 4 + s) * 2 + 0) * 1024 + lane * 16);
-    uint4* dl = reinterpret_cast<uint4*>(xq + ((int64_t)(kb * 4 + s) * 2 + 1) * 1024 + lane * 16);
-    *dh = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *dl = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    const int64_t oh = ((int64_t)(kb * 4 + s) * 2 + 0) * 1024 + (16 * kq + m) * 16;
+    const int64_t ol = ((int64_t)(kb * 4 + s) * 2 + 1) * 1024 + (16 * kq + m) * 16;
+    *reinterpret_cast<uint4*>(xq + oh) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(xq + ol) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
-  if (kc == 0) rowinfo[kb * 16 + m] = m < M ? make_float2(ldexpf(1.f, -ex), bsum) : make_float2(0.f, 0.f);
+  if (kc == 0) rowinfo[kb * 16 + m] = m < M ? make_float2(scale, bsum) : make_float2(0.f, 0.f);
 }
 
-// One workgroup = GW waves on 16 output rows n; wave w takes the PF blocks
-// kb = w + GW*u (u < PF). It issues the code loads of all of them first (one round trip
-// to HBM for the whole share), then walks them with the X' limbs and block scales of the
-// next block in flight while the current one runs on the matrix cores. The GW partial
-// sums of a row are added in LDS in a fixed order.
-constexpr int GW = 8;
+// One workgroup = GW waves on RG groups of 16 output rows n, over the whole of K. Wave w
+// takes the blocks kb = w + GW*u; it issues the code loads of all of them (for every row
+// group) first, then walks them with the X' limbs and block scales of the next block in
+// flight while the current one runs on the matrix cores. One X' fragment serves the RG
+// row groups. The GW partial sums of a row are added in LDS in a fixed order. The grid
+// is shaped so that every workgroup of a launch is resident at once (one round), which
+// keeps each workgroup's chain to one HBM round trip plus the X' walk.
+constexpr int GW = 16;
 
 struct GemvA {
   i32x4 hi[4], lo[4];
@@ -143,82 +170,274 @@ __device__ __forceinline__ void gemv_block(f32x4& acc, const GemvA& a, const u32
   acc[3] = __builtin_fmaf((float)(chi[3] * 256 + clo[3]), a.r1[2], acc[3] + a.r1[3]);
 }
 
-template <int PF>
+template <int RG, int KSW>
 __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
                                                   const float2* __restrict__ rowinfo,
                                                   const uint8_t* __restrict__ packed, int M,
                                                   int N, int K, uint16_t* __restrict__ Y) {
-  __shared__ f32x4 red[GW][64];
+  __shared__ f32x4 red[GW][RG][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * RG;
   const int nl = lane & 15, kq = lane >> 4;
   const int nkb = K / GK;
+  const int64_t rowb = K >> 2;                     // also 16 rows, in 16-byte units
   const u32x4* crow =
-      reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 + nl) * (K >> 2) + kq * 16);
+      reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 + nl) * rowb + kq * 16);
   const i32x4* xa = reinterpret_cast<const i32x4*>(xq) + lane;
   const f32x4* ri = reinterpret_cast<const f32x4*>(rowinfo) + 2 * kq;
   const bool has_a = nl < M;                       // A-operand lane row m = lane % 16
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = wave; kb0 < nkb; kb0 += GW * PF) {
-    u32x4 cw[PF];
+  f32x4 acc[RG];
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+  for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb0 = wave; kb0 < nkb; kb0 += GW * KSW) {
+    u32x4 cw[KSW][RG];
+#pragma unroll
+    for (int u = 0; u < KSW; ++u) {
       const int kb = kb0 + GW * u;
-      cw[u] = kb < nkb ? __builtin_nontemporal_load(crow + kb * 4) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        cw[u][g] = (kb < nkb && n0 + 16 * g < N)
+                       ? __builtin_nontemporal_load(crow + g * rowb + kb * 4)
+                       : u32x4{0, 0, 0, 0};
     }
     GemvA a[2];
     gemv_load_a(a[0], xa, ri, kb0, has_a);
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < KSW; ++u) {
       const int kb = kb0 + GW * u;
       if (kb >= nkb) break;
-      if (u + 1 < PF && kb + GW < nkb) gemv_load_a(a[(u + 1) & 1], xa, ri, kb + GW, has_a);
-      gemv_block(acc, a[u & 1], cw[u]);
+      if (u + 1 < KSW && kb + GW < nkb) gemv_load_a(a[(u + 1) & 1], xa, ri, kb + GW, has_a);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) gemv_block(acc[g], a[u & 1], cw[u][g]);
     }
   }
-  red[wave][lane] = acc;
+#pragma unroll
+  for (int g = 0; g < RG; ++g) red[wave][g][lane] = acc[g];
   __syncthreads();
-  if (wave == 0) {
-    f32x4 v = red[0][lane];
+  if (wave < RG) {
+    const int g = wave;
+    f32x4 v = red[0][g][lane];
 #pragma unroll
     for (int w = 1; w < GW; ++w) {
-      const f32x4 o = red[w][lane];
+      const f32x4 o = red[w][g][lane];
       v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
     }
+    const int n = n0 + 16 * g + nl;
+    if (n < N) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 4 * kq + r;
-      if (m < M) reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n0 + nl] = (__bf16)v[r];
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kq + r;
+        if (m < M) reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n] = (__bf16)v[r];
+      }
     }
   }
 }
 
-hipError_t launch_gemv_prologue(const uint16_t* X, int M, int K, const uint16_t* A16,
-                                const uint16_t* B16, int d, int8_t* xq, float* rowinfo,
-                                hipStream_t s) {
-  float2* ri = reinterpret_cast<float2*>(rowinfo);
-  switch (d) {
-    case 4: hipLaunchKernelGGL(k_gemv_prologue<4>, dim3(K / GK), dim3(256), 0, s, X, M, K, A16, B16, xq, ri); break;
-    case 8: hipLaunchKernelGGL(k_gemv_prologue<8>, dim3(K / GK), dim3(256), 0, s, X, M, K, A16, B16, xq, ri); break;
-    default: hipLaunchKernelGGL(k_gemv_prologue<16>, dim3(K / GK), dim3(256), 0, s, X, M, K, A16, B16, xq, ri); break;
+// Fused path for M <= GEMV_FUSED_M tokens: one launch. A workgroup of GWF waves covers
+// RG groups of 16 rows n over the whole of K. It first issues the code loads of all its
+// waves' blocks (they stream from HBM meanwhile), then forms X' of rows m < M for the
+// whole of K in LDS (dense chunk order, M * K * 2 bytes, at most 64 KiB) plus the block
+// scales, and then runs the int8 products with fragments read from LDS one step at a
+// time. Forming X' per workgroup repeats M * K * d multiply-adds that a separate
+// prologue would do once, but it overlaps the code stream and saves a kernel boundary
+// and the X' round trip through memory.
+constexpr int GWF = 8;
+
+template <int D, int RG, int KSW>
+__global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restrict__ X,
+                                                         const uint16_t* __restrict__ A16,
+                                                         const uint16_t* __restrict__ B16,
+                                                         const uint8_t* __restrict__ packed,
+                                                         int M, int N, int K,
+                                                         uint16_t* __restrict__ Y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n0 = blockIdx.x * 16 * RG;
+  const int nl = lane & 15, kq = lane >> 4;
+  const int nkb = K / GK;
+  const int64_t rowb = K >> 2;
+  const int XB = nkb * 32 * M * 16;                // dense X' bytes
+  float2* ris = reinterpret_cast<float2*>(gsm + XB);              // [nkb][16]
+  float* As = reinterpret_cast<float*>(gsm + XB + nkb * 128);     // [D][D], then B [D]
+  float* Bs = As + D * D;
+
+  // 1. the codes of this wave's blocks, for every row group
+  const u32x4* crow =
+      reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 + nl) * rowb + kq * 16);
+  u32x4 cw[KSW][RG];
+#pragma unroll
+  for (int u = 0; u < KSW; ++u) {
+    const int kb = wave + GWF * u;
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+      cw[u][g] = (kb < nkb && n0 + 16 * g < N)
+                     ? __builtin_nontemporal_load(crow + g * rowb + kb * 4)
+                     : u32x4{0, 0, 0, 0};
   }
-  return hipGetLastError();
+  // 2. A, B, and zero block scales for the rows m >= M
+  if (t < D * D) As[t] = (float)__builtin_bit_cast(_Float16, A16[t]);
+  if (t < D) Bs[t] = (float)__builtin_bit_cast(_Float16, B16[t]);
+  for (int i = t; i < nkb * 16; i += GWF * 64)
+    if ((i & 15) >= M) ris[i] = make_float2(0.f, 0.f);
+  __syncthreads();
+  // 3. X' of rows m < M: item i = (kb * M + m) * 16 + kc; the 16 items of a (kb, m)
+  //    are 16 consecutive lanes
+  for (int i = t; i < nkb * M * 16; i += GWF * 64) {
+    const int kc = i & 15, gm = i >> 4;
+    const int m = gm % M, kb = gm / M;
+    const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)m * K + kb * GK + kc * 16);
+    uint32_t hi[4], lo[4];
+    float scale, bsum;
+    xprime_chunk<D>(src[0], src[1], As, Bs, hi, lo, scale, bsum);
+    const int q = kc >> 2, s = kc & 3;
+    *reinterpret_cast<uint4*>(gsm + (((kb * 8 + 2 * s) * 4 + q) * M + m) * 16) =
+        make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *reinterpret_cast<uint4*>(gsm + (((kb * 8 + 2 * s + 1) * 4 + q) * M + m) * 16) =
+        make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    if (kc == 0) ris[kb * 16 + m] = make_float2(scale, bsum);
+  }
+  __syncthreads();
+
+  // 4. the products
+  const bool has_a = nl < M;                       // A-operand lane row m = lane % 16
+  f32x4 acc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* ri = gsm + XB + kq * 32;
+  const uint8_t* xl = gsm + (kq * M + nl) * 16;
+#pragma unroll
+  for (int u = 0; u < KSW; ++u) {
+    const int kb = wave + GWF * u;
+    if (kb >= nkb) break;
+    i32x4 chi[RG], clo[RG];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) chi[g] = clo[g] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {                  // fragments read one step at a time
+      i32x4 h = {0, 0, 0, 0}, l = {0, 0, 0, 0};
+      if (has_a) {
+        h = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s) * 4 * M * 16);
+        l = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s + 1) * 4 * M * 16);
+      }
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        const uint32_t w = cw[u][g][s];
+        i32x4 bz;
+        bz[0] = (int)(w & 0x03030303u);
+        bz[1] = (int)((w >> 2) & 0x03030303u);
+        bz[2] = (int)((w >> 4) & 0x03030303u);
+        bz[3] = (int)((w >> 6) & 0x03030303u);
+        chi[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h, bz, chi[g], 0, 0, 0);
+        clo[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l, bz, clo[g], 0, 0, 0);
+      }
+    }
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(ri + kb * 128);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(ri + kb * 128 + 16);
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      f32x4& a = acc[g];
+      a[0] = __builtin_fmaf((float)(chi[g][0] * 256 + clo[g][0]), r0[0], a[0] + r0[1]);
+      a[1] = __builtin_fmaf((float)(chi[g][1] * 256 + clo[g][1]), r0[2], a[1] + r0[3]);
+      a[2] = __builtin_fmaf((float)(chi[g][2] * 256 + clo[g][2]), r1[0], a[2] + r1[1]);
+      a[3] = __builtin_fmaf((float)(chi[g][3] * 256 + clo[g][3]), r1[2], a[3] + r1[3]);
+    }
+  }
+  // 5. the GWF partial sums of each row, in wave order
+  __syncthreads();                                 // the X' area becomes the reduction area
+  f32x4* red = reinterpret_cast<f32x4*>(gsm);
+#pragma unroll
+  for (int g = 0; g < RG; ++g) red[(wave * RG + g) * 64 + lane] = acc[g];
+  __syncthreads();
+  if (wave < RG) {
+    const int g = wave;
+    f32x4 v = red[g * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < GWF; ++w) {
+      const f32x4 o = red[(w * RG + g) * 64 + lane];
+      v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
+    }
+    const int n = n0 + 16 * g + nl;
+    if (n < N) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kq + r;
+        if (m < M) reinterpret_cast<__bf16*>(Y)[(int64_t)m * N + n] = (__bf16)v[r];
+      }
+    }
+  }
 }
 
-hipError_t launch_gemv(const int8_t* xq, const float* rowinfo, const uint8_t* packed, int M,
-                       int N, int K, uint16_t* Y, hipStream_t s) {
-  const int per_wave = (K / GK + GW - 1) / GW;     // blocks per wave
-  const dim3 grid(N / 16), block(GW * 64);
-  const float2* ri = reinterpret_cast<const float2*>(rowinfo);
-  if (per_wave <= 1)
-    LCVQ_LAUNCH(PROF_GEMV, k_gemv<1>, grid, block, 0, s, xq, ri, packed, M, N, K, Y);
-  else if (per_wave <= 2)
-    LCVQ_LAUNCH(PROF_GEMV, k_gemv<2>, grid, block, 0, s, xq, ri, packed, M, N, K, Y);
-  else if (per_wave <= 4)
-    LCVQ_LAUNCH(PROF_GEMV, k_gemv<4>, grid, block, 0, s, xq, ri, packed, M, N, K, Y);
-  else
-    LCVQ_LAUNCH(PROF_GEMV, k_gemv<8>, grid, block, 0, s, xq, ri, packed, M, N, K, Y);
+template <int D, int RG, int KSW>
+static void launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
+                         const uint16_t* A16, const uint16_t* B16, const uint8_t* packed, int M,
+                         int N, int K, uint16_t* Y) {
+  static bool attr = false;                        // LDS beyond 64 KiB must be requested
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr = true;
+  }
+  LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW>), grid, dim3(GWF * 64), shm, s, X, A16, B16,
+              packed, M, N, K, Y);
+}
+
+template <int D>
+static void launch_fused_d(int M, int N, int K, bool two, size_t shm, hipStream_t s,
+                           const uint16_t* X, const uint16_t* A16, const uint16_t* B16,
+                           const uint8_t* packed, uint16_t* Y) {
+  const int pw = (K / GK + GWF - 1) / GWF;
+  const dim3 grid(two ? (N + 31) / 32 : N / 16);
+  if (two) {
+    if (pw <= 2) launch_fused<D, 2, 2>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+    else if (pw <= 4) launch_fused<D, 2, 4>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+    else launch_fused<D, 2, 8>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+  } else {
+    if (pw <= 2) launch_fused<D, 1, 2>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+    else if (pw <= 4) launch_fused<D, 1, 4>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+    else launch_fused<D, 1, 8>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+  }
+}
+
+hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,
+                       const uint16_t* B16, int d, const uint8_t* packed, uint16_t* Y,
+                       int8_t* xq, float* rowinfo, hipStream_t s) {
+  const int nkb = K / GK;
+  // Two row groups per workgroup when N still gives a workgroup per CU.
+  const bool two = N >= 2 * 16 * 256;
+  if (gemv_fused(M, K)) {
+    const size_t base = (size_t)nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
+    const size_t shm = std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
+    switch (d) {
+      case 4: launch_fused_d<4>(M, N, K, two, shm, s, X, A16, B16, packed, Y); break;
+      case 8: launch_fused_d<8>(M, N, K, two, shm, s, X, A16, B16, packed, Y); break;
+      default: launch_fused_d<16>(M, N, K, two, shm, s, X, A16, B16, packed, Y); break;
+    }
+    return hipGetLastError();
+  }
+  float2* ri = reinterpret_cast<float2*>(rowinfo);
+  const dim3 pgrid(nkb), pblock(256);
+  switch (d) {
+    case 4: hipLaunchKernelGGL(k_gemv_prologue<4>, pgrid, pblock, 0, s, X, M, K, A16, B16, xq, ri); break;
+    case 8: hipLaunchKernelGGL(k_gemv_prologue<8>, pgrid, pblock, 0, s, X, M, K, A16, B16, xq, ri); break;
+    default: hipLaunchKernelGGL(k_gemv_prologue<16>, pgrid, pblock, 0, s, X, M, K, A16, B16, xq, ri); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int per_wave = (nkb + GW - 1) / GW;
+  const dim3 grid(two ? (N + 31) / 32 : N / 16), block(GW * 64);
+#define LCVQ_GEMV(RG, KSW) \
+  LCVQ_LAUNCH(PROF_GEMV, (k_gemv<RG, KSW>), grid, block, 0, s, xq, ri, packed, M, N, K, Y)
+  if (two) {
+    if (per_wave <= 1) LCVQ_GEMV(2, 1);
+    else LCVQ_GEMV(2, 2);
+  } else {
+    if (per_wave <= 1) LCVQ_GEMV(1, 1);
+    else LCVQ_GEMV(1, 2);
+  }
+#undef LCVQ_GEMV
   return hipGetLastError();
 }
 

@@ -222,9 +222,11 @@ lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, in
                                  (int)K, d, dWp, partials, dA, dB, s));
 }
 
-size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t K, int d) {
+size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t N, int64_t K, int d) {
   (void)d;
-  if (M < 1 || M > 16 || K < 256 || (K % 256) || K > INT32_MAX) return 0;
+  if (M < 1 || M > 16 || N < 16 || (N % 16) || N > INT32_MAX || K < 256 || (K % 256) ||
+      K > INT32_MAX)
+    return 0;
   return gemv_ws(K).total;
 }
 
@@ -245,12 +247,10 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   int8_t* xq = reinterpret_cast<int8_t*>(ws + w.xq);
   float* rowinfo = reinterpret_cast<float*>(ws + w.rowinfo);
-  hipError_t e = launch_gemv_prologue(static_cast<const uint16_t*>(X), (int)M, (int)K,
-                                      static_cast<const uint16_t*>(A16),
-                                      static_cast<const uint16_t*>(B16), d, xq, rowinfo, s);
-  if (e != hipSuccess) return LCVQ_ERR_HIP;
-  return from_hip(launch_gemv(xq, rowinfo, packed, (int)M, (int)N, (int)K,
-                              static_cast<uint16_t*>(Y), s));
+  return from_hip(launch_gemv(static_cast<const uint16_t*>(X), (int)M, (int)N, (int)K,
+                              static_cast<const uint16_t*>(A16),
+                              static_cast<const uint16_t*>(B16), d, packed,
+                              static_cast<uint16_t*>(Y), xq, rowinfo, s));
 }
 
 }  // extern "C"

@@ -54,10 +54,10 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, hipStream_t s);
 
-hipError_t launch_gemv_prologue(const uint16_t* X, int M, int K, const uint16_t* A16,
-                                const uint16_t* B16, int d, int8_t* xq, float* rowinfo,
-                                hipStream_t s);
-hipError_t launch_gemv(const int8_t* xq, const float* rowinfo, const uint8_t* packed, int M,
-                       int N, int K, uint16_t* Y, hipStream_t s);
+// Decode product. Few tokens: one fused kernel (xq and rowinfo unused); otherwise a
+// prologue writes X' limbs to xq and block scales to rowinfo, and the product reads them.
+hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,
+                       const uint16_t* B16, int d, const uint8_t* packed, uint16_t* Y,
+                       int8_t* xq, float* rowinfo, hipStream_t s);
 
 }  // namespace lcvq

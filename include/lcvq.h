@@ -129,11 +129,14 @@ lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, in
  *   N a multiple of 16, K a multiple of 256
  *   A16 float16 [d, d];  B16 float16 [d]
  *   Y   bfloat16 [M, N]                                          out
- *   workspace >= lcvq_gemv2b_workspace_size(M, K, d) bytes
+ *   workspace >= lcvq_gemv2b_workspace_size(M, N, K, d) bytes (0 for invalid shapes)
  * Numerics: X (I kron A) is formed in float32 and held as 16-bit fixed point per row;
- * the product with the codes is exact integer arithmetic.
+ * the product with the codes is exact integer arithmetic, and partial sums are added
+ * in a fixed order, so repeated calls give identical bytes. The workspace size depends
+ * on K only today; N is part of the query so that it may grow with N later. Calls that
+ * share one workspace must not run concurrently.
  */
-size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t K, int d);
+size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t N, int64_t K, int d);
 lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
                           const uint8_t* packed, const void* A16, const void* B16, void* Y,
                           void* workspace, size_t workspace_bytes, void* stream);

@@ -124,7 +124,11 @@ def test_gemv_errors(L):
     assert g(N=40) == 2
     assert g(d=5) == 3
     assert g(Y=MIS) == 5
-    assert g(wsb=L.lcvq_gemv2b_workspace_size(1, 256, 8) - 1) == 6
+    assert g(wsb=L.lcvq_gemv2b_workspace_size(1, 256, 256, 8) - 1) == 6
+    need = L.lcvq_gemv2b_workspace_size(16, 4096, 14336, 8)
+    assert need > L.lcvq_gemv2b_workspace_size(1, 4096, 4096, 8) > 0
+    assert g(M=16, N=4096, K=14336, wsb=need - 1) == 6
+    assert L.lcvq_gemv2b_workspace_size(1, 40, 256, 8) == 0
 
 
 def test_workspace_sizes_grow_with_shape(L):

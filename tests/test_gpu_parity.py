@@ -177,7 +177,7 @@ def test_config1_full(P):
 
 # ------------------------------------------------------------------ decode product
 @pytest.mark.parametrize("N,K", [(256, 256), (4096, 4096), (14336, 4096), (4096, 14336)])
-@pytest.mark.parametrize("M", [1, 4, 16, 3])
+@pytest.mark.parametrize("M", [1, 2, 4, 16, 3])
 def test_gemv(P, N, K, M):
     d = 8
     note(f"gemv N={N} K={K} M={M}")
@@ -191,5 +191,32 @@ def test_gemv(P, N, K, M):
     torch.cuda.synchronize()
     ref = O.gemv2b(host(X), host(pk), A.half().double().numpy(), B.half().double().numpy(), d)
     e = rel(host(Y), ref)
+    note(f"  rel={e:.2e}")
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("N,K,M", [(4096, 14336, 16), (14336, 4096, 1), (272, 8192, 5),
+                                   (256, 16640, 2)])
+def test_gemv_repeat_shared_workspace(P, N, K, M):
+    """Calls that reuse one workspace (its row-set counters included) give identical
+    bytes, and the slices of long rows add up to the oracle's product."""
+    d = 8
+    note(f"gemv repeat N={N} K={K} M={M}")
+    wp = SI.make_wp(N, K, seed=5000 + N + K, device="cuda")
+    A, B = SI.make_ab(d, seed=5000 + M)
+    X = SI.make_act(M, K, seed=5100 + M, device="cuda")
+    pk = torch.empty((N, K // 4), dtype=torch.uint8, device="cuda")
+    P.lcvq_quantize(wp, None, pk, None)
+    A16, B16 = A.half().cuda(), B.half().cuda()
+    ws = torch.empty(P.lcvq_gemv2b_workspace_size(M, N, K, d), dtype=torch.uint8, device="cuda")
+    ys = []
+    for _ in range(3):
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        P.lcvq_gemv2b(X, pk, A16, B16, d, Y, ws)
+        ys.append(Y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+    ref = O.gemv2b(host(X), host(pk), A.half().double().numpy(), B.half().double().numpy(), d)
+    e = rel(host(ys[0]), ref)
     note(f"  rel={e:.2e}")
     assert e <= TOL
