@@ -38,44 +38,76 @@ __global__ __launch_bounds__(256) void k_quantize(
   const int q = lane & 3;
   const int64_t nchunks = (total + 1023) >> 10;
   const int64_t wstride = (int64_t)gridDim.x * 4;
-  for (int64_t ch = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); ch < nchunks; ch += wstride) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int64_t ch = (int64_t)blockIdx.x * 4 + wv; ch < nchunks; ch += wstride) {
     const int64_t base = ch << 10;
+    // Row of the chunk's first element (one scalar division per chunk); a lane's element
+    // lies less than 1024 elements further, i.e. in row0 or a few rows later.
+    const int64_t row0 = r16_out ? base / K : 0;
+    const int off0 = (int)(base - row0 * K);
+    // 64-bit chunk bases are uniform (scalar); per-lane offsets stay 32-bit
+    const int rem = (int)(total - base < 1024 ? total - base : 1024);
+    const float* wpc = wp + base;
     f4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t e = base + 256 * j + 4 * lane;
-      v[j] = e < total ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(wp + e))
-                       : f4{0.f, 0.f, 0.f, 0.f};
+      const int le = 256 * j + 4 * lane;
+      v[j] = le < rem ? __builtin_nontemporal_load(reinterpret_cast<const f4*>(wpc + le))
+                      : f4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t e = base + 256 * j + 4 * lane;
+      const int le = 256 * j + 4 * lane;
+      const int64_t e = base + le;
       uint32_t byte = 0, m4 = 0;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const float r = __builtin_rintf(v[j][t]);            // round half to even
-        // Comparisons are false for NaN, so NaN -> code 0; +inf -> 3; -inf -> 0.
-        const uint32_t c = (uint32_t)(r >= 1.0f) + (uint32_t)(r >= 2.0f) + (uint32_t)(r >= 3.0f);
-        byte |= c << (2 * t);
-        m4 |= (uint32_t)((r >= 0.0f) & (r <= 3.0f)) << t;
+        // maxNum/minNum return the number for a NaN operand: NaN -> 0, +inf -> 3,
+        // -inf -> 0. The mask is 1 exactly when the clamp left r unchanged (never for
+        // NaN or infinities).
+        const float cf = fminf(fmaxf(r, 0.f), 3.f);
+        byte |= (uint32_t)(int)cf << (2 * t);
+        m4 |= (uint32_t)(cf == r) << t;
       }
-      // the packed word of this lane's 16-code group (lanes 4a .. 4a+3)
-      const int g0 = lane & ~3;
-      const uint32_t w = (uint32_t)__shfl((int)byte, g0) | (uint32_t)__shfl((int)byte, g0 + 1) << 8 |
-                         (uint32_t)__shfl((int)byte, g0 + 2) << 16 | (uint32_t)__shfl((int)byte, g0 + 3) << 24;
       const uint32_t mpair = m4 | ((uint32_t)__shfl_xor((int)m4, 1) << 4);
-      if (e < total) {
-        if (packed_out) packed_out[e >> 2] = (uint8_t)byte;
-        if (mask_out && !(lane & 1)) mask_out[e >> 3] = (uint8_t)mpair;
+      // R16 word of this lane's 16-code group: lane q of the group holds codes 4q..4q+3;
+      // its even codes go to bits 5 + 2p and its odd codes to bits 21 + 2p of an 8-code
+      // half (p = position in the half), and the second half is rotated left by 8, so
+      // each lane places its two 2-code runs with one rotate and the four lanes OR them.
+      uint32_t rw = 0;
+      if (r16_out) {
+        const uint32_t E = (byte & 3u) | ((byte >> 2) & 0xCu);
+        const uint32_t O = ((byte >> 2) & 3u) | ((byte >> 4) & 0xCu);
+        const uint64_t v = (uint64_t)((E << 5) | (O << 21)) << (4 * (q & 1) + 8 * (q >> 1));
+        rw = (uint32_t)v | (uint32_t)(v >> 32);
+        rw |= (uint32_t)__shfl_xor((int)rw, 1);
+        rw |= (uint32_t)__shfl_xor((int)rw, 2);
+      }
+      // the packed word of the group, for the float32 decode only
+      uint32_t w = 0;
+      if (D > 0 && what_out) {
+        const int g0 = lane & ~3;
+        w = (uint32_t)__shfl((int)byte, g0) | (uint32_t)__shfl((int)byte, g0 + 1) << 8 |
+            (uint32_t)__shfl((int)byte, g0 + 2) << 16 | (uint32_t)__shfl((int)byte, g0 + 3) << 24;
+      }
+      if (le < rem) {
+        if (packed_out) packed_out[(base >> 2) + (le >> 2)] = (uint8_t)byte;
+        if (mask_out && !(lane & 1)) mask_out[(base >> 3) + (le >> 3)] = (uint8_t)mpair;
         if (z_out)
           *reinterpret_cast<uint32_t*>(z_out + e) =
               (byte & 3u) | ((byte >> 2) & 3u) << 8 | ((byte >> 4) & 3u) << 16 | (byte >> 6) << 24;
         if (r16_out && q == 0) {
-          uint32_t c[16];
-#pragma unroll
-          for (int t = 0; t < 16; ++t) c[t] = (w >> (2 * t)) & 3u;
-          const int64_t row = e / K;
-          r16_out[r16_blocked_index(row, (e - row * K) >> 4, K >> 6)] = r16_encode(c);
+          const int off = off0 + 256 * j + 4 * lane;   // < K + 1024
+          int dr, col;
+          if (K >= 1024) {
+            dr = off >= K;
+            col = off - (dr ? (int)K : 0);
+          } else {
+            dr = (int)((uint32_t)off / (uint32_t)K);
+            col = off - dr * (int)K;
+          }
+          r16_out[r16_blocked_index(row0 + dr, col >> 4, K >> 6)] = rw;
         }
         if (D > 0 && what_out) {
           // What[n, g*d+i] = B[i] + sum_j A[i][j] z[n, g*d+j], in float32.
@@ -206,10 +238,19 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, i
                                                       uint16_t* __restrict__ xs_lo,
                                                       float* __restrict__ beta) {
   __shared__ float red[4];
-  __shared__ float As[D * D], Bs[D];
-  if (threadIdx.x < D * D) As[threadIdx.x] = A[threadIdx.x];
-  if (threadIdx.x < D) Bs[threadIdx.x] = B[threadIdx.x];
-  __syncthreads();
+  __shared__ float Asm[D * D], Bsm[D];
+  // A and B are the same for every lane: for d <= 8 they are read with scalar loads into
+  // scalar registers (64 + 8 values), which keeps the vector registers for the data;
+  // for d = 16 they are staged in LDS.
+  const float* As = A;
+  const float* Bs = B;
+  if (D > 8) {
+    if (threadIdx.x < D * D) Asm[threadIdx.x] = A[threadIdx.x];
+    if (threadIdx.x < D) Bsm[threadIdx.x] = B[threadIdx.x];
+    __syncthreads();
+    As = Asm;
+    Bs = Bsm;
+  }
   const int64_t m = blockIdx.x;
   const T* xrow = X + m * K;
   uint16_t* orow = xs + m * K;
@@ -218,15 +259,32 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, i
     float x[16];
     load16<T>(xrow + c * 16, x);
     float xp[16];
+    if (D <= 8) {
+#pragma unroll
+      for (int v0 = 0; v0 < 16; v0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < D; ++i) sum = __builtin_fmaf(x[v0 + i], As[i * D + j], sum);
+          xp[v0 + j] = sum;
+        }
+      }
+    } else {
+      // one row of A at a time from LDS, so that only the 16 outputs stay in registers
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xp[j] = 0.f;
+#pragma unroll 1
+      for (int i = 0; i < D; ++i) {
+        float xi = x[0];
+#pragma unroll
+        for (int q = 1; q < 16; ++q) xi = i == q ? x[q] : xi;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) xp[j] = __builtin_fmaf(xi, As[i * D + j], xp[j]);
+      }
+    }
 #pragma unroll
     for (int v0 = 0; v0 < 16; v0 += D) {
-#pragma unroll
-      for (int j = 0; j < D; ++j) {
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < D; ++i) sum = __builtin_fmaf(x[v0 + i], As[i * D + j], sum);
-        xp[v0 + j] = sum;
-      }
 #pragma unroll
       for (int i = 0; i < D; ++i) acc = __builtin_fmaf(x[v0 + i], Bs[i], acc);
     }

@@ -220,3 +220,50 @@ def test_gemv_repeat_shared_workspace(P, N, K, M):
     e = rel(host(ys[0]), ref)
     note(f"  rel={e:.2e}")
     assert e <= TOL
+
+
+def test_graph_replay_matches_eager(P):
+    """The forward and backward captured in one HIP graph give the eager step's bytes on
+    every replay, with other GPU work and synchronizations between the replays."""
+    M, N, K, d = 300, 320, 192, 8
+    inp = SI.make_layer(N, K, M, d, seed=91, lo=-2.0, hi=5.0)
+    X, Wp, A, B, dY = (inp[k].cuda() for k in ("X", "Wp", "A", "B", "dY"))
+    out = {"Y": torch.empty((M, N), dtype=X.dtype, device="cuda"),
+           "packed": torch.empty((N, K // 4), dtype=torch.uint8, device="cuda"),
+           "mask": torch.empty((N, K // 8), dtype=torch.uint8, device="cuda"),
+           "dX": torch.empty((M, K), dtype=X.dtype, device="cuda"),
+           "dWp": torch.empty((N, K), dtype=torch.float32, device="cuda"),
+           "dA": torch.empty((d, d), dtype=torch.float32, device="cuda"),
+           "dB": torch.empty((d,), dtype=torch.float32, device="cuda")}
+    wsf = torch.empty(P.lcvq_linear_fwd_workspace_size(M, N, K, d), dtype=torch.uint8,
+                      device="cuda")
+    wsb = torch.empty(P.lcvq_linear_bwd_workspace_size(M, N, K, d), dtype=torch.uint8,
+                      device="cuda")
+
+    def step():
+        P.lcvq_linear_fwd(X, Wp, A, B, d, out["Y"], out["packed"], out["mask"], None, wsf)
+        P.lcvq_linear_bwd(dY, X, out["packed"], out["mask"], A, B, d, out["dX"], out["dWp"],
+                          out["dA"], out["dB"], wsb)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in out.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(4):
+        for v in out.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in out:
+            assert torch.equal(out[k], ref[k]), (i, k)
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
