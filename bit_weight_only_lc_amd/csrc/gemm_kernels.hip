@@ -31,13 +31,28 @@ constexpr int TILEB = BT * ROWB;
 
 enum { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
 
+// Waves per workgroup of the forward and dX products (4 or 8).
+#ifndef LCVQ_FWD_WAVES
+#define LCVQ_FWD_WAVES 8
+#endif
+#ifndef LCVQ_DX_WAVES
+#define LCVQ_DX_WAVES 8
+#endif
+// Wave rows of the 8-wave forward product (2: waves own 128 x 64, 4: 64 x 128).
+#ifndef LCVQ_FWD_WGP
+#define LCVQ_FWD_WGP 2
+#endif
+
 // Wave layout of the 8-wave products: WGP wave rows x WGQ wave columns; a wave owns
 // 32*WI rows and 32*WJ columns of the C tile. The operand made of codes is spread over
 // the wave dimension with fewer waves, so that each wave expands as few code fragments
 // as possible (forward: codes are columns; dX: codes are rows).
-template <int OP> struct Tiling {
-  static constexpr int NW = 8;
-  static constexpr int WGP = OP == OP_DX ? 4 : 2;
+// With 4 waves (one per SIMD) each wave owns a 128 x 128 quarter of the tile: 16
+// accumulator blocks of 32 x 32 (256 values, held in the accumulation registers) and 4
+// + 4 operand fragments per contraction sub-step, i.e. fewer LDS bytes per MFMA.
+template <int OP, int NWV = 8> struct Tiling {
+  static constexpr int NW = NWV;
+  static constexpr int WGP = NW == 4 ? 2 : (OP == OP_DX ? 4 : LCVQ_FWD_WGP);
   static constexpr int WGQ = NW / WGP;
   static constexpr int WI = 8 / WGP;
   static constexpr int WJ = 8 / WGQ;
@@ -268,10 +283,12 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
     bp[i] = a.B[i] - 4.f * s;
   }
   const int q = lane & 31;
+  // j outer: the blocks i of one j cover consecutive 64-byte halves of the same output
+  // lines, so each line is completed while it is still in the L2.
 #pragma unroll
-  for (int i = 0; i < WI; ++i)
+  for (int j = 0; j < WJ; ++j)
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) {
+    for (int i = 0; i < WI; ++i) {
       const int kb = p0 + wp * 32 * WI + i * 32;
       const int mb = q0 + wq * 32 * WJ + j * 32;
       wave_sync();
@@ -427,27 +444,30 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
 constexpr int RING = 4;
 constexpr int CODEB = 256 * 16;
 constexpr int SLOTB = TILEB + CODEB;
-constexpr int RING_LOADS = 6;           // per lane and stage: 4 bf16-tile + 2 code loads
+// Loads per lane and stage: RPW/8 bf16-tile loads (8 rows each) + RPW/16 code loads
+// (16 rows of 16 bytes each), RPW = 256 / NW rows per wave.
+template <int NW> constexpr int ring_loads() { return (256 / NW) / 8 + (256 / NW) / 16; }
 
-// 8 waves: wave w fills tile rows [32w, 32w+32) (4 x 1 KiB) and code rows
-// [32w, 32w+32) (2 x 256 B of 4-byte words).
+// Wave w fills tile rows [RPW w, RPW (w+1)) and the code words of the same rows.
+template <int NW>
 __device__ __forceinline__ void issue_ring_stage(uint8_t* slot, const uint16_t* mat, int64_t ld,
                                                  int row0, int rows_total, int k0,
                                                  const uint32_t* codes, int rowblock, int nk,
                                                  int kt, int wave, int lane) {
+  constexpr int RPW = 256 / NW;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = wave * 32 + i * 8 + (lane >> 3);
+  for (int i = 0; i < RPW / 8; ++i) {
+    const int r = wave * RPW + i * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     int g = row0 + r;
     g = g < rows_total ? g : rows_total - 1;
     const uint16_t* src = mat + (int64_t)g * ld + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(slot + (wave * 32 + i * 8) * ROWB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(slot + (wave * RPW + i * 8) * ROWB), 16, 0, 0);
   }
   const uint32_t* slab = codes + ((int64_t)rowblock * nk + kt) * 1024;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int w0 = (wave * 32 + h * 16) * 4;           // first word of these 16 rows
+  for (int h = 0; h < RPW / 16; ++h) {
+    const int w0 = (wave * RPW + h * 16) * 4;           // first word of these 16 rows
     __builtin_amdgcn_global_load_lds(slab + w0 + lane, (LCVQ_LDS void*)(slot + TILEB + w0 * 4), 4, 0, 0);
   }
 }
@@ -535,19 +555,22 @@ __device__ __forceinline__ void mma_ring_stage(const uint8_t* slot, f32x16 acc[W
 
 // Wait until at most `stages_after` (0..2) stages of this wave's ring loads are still
 // outstanding; the other counters are not waited on.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+template <int NW>
 __device__ __forceinline__ void wait_vm_stages(int stages_after) {
-  static_assert(RING_LOADS == 6, "immediates below assume 6 loads per stage");
-  if (stages_after >= 2) __builtin_amdgcn_s_waitcnt(0x0F7C);        // vmcnt(12)
-  else if (stages_after == 1) __builtin_amdgcn_s_waitcnt(0x0F76);   // vmcnt(6)
-  else __builtin_amdgcn_s_waitcnt(0x0F70);                          // vmcnt(0)
+  constexpr int L = ring_loads<NW>();
+  static_assert(2 * L < 64, "vmcnt range");
+  if (stages_after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
+  else if (stages_after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+  else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // ---- the kernel ----------------------------------------------------------------------
-// FWD and dX: 8 waves (512 threads), 4-slot ring of direct global->LDS loads.
-template <int OP, int D>
-__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// FWD and dX: NW waves (4 or 8), 4-slot ring of direct global->LDS loads.
+template <int OP, int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_gemm_ring(GemmArgs a) {
-  using T = Tiling<OP>;
+  using T = Tiling<OP, NW>;
   constexpr int WI = T::WI, WJ = T::WJ;
   constexpr bool CL = OP == OP_DX;               // codes are the L operand for dX
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOTB];   // 144 KiB
@@ -577,18 +600,19 @@ void k_gemm_ring(GemmArgs a) {
 #pragma unroll
     for (int st = 0; st < RING - 1; ++st)
       if (st < nk)
-        issue_ring_stage(smem + st * SLOTB, mat, ld, row0, a.M, st * BK, a.codes, rowblock, nk,
-                         st, wave, lane);
+        issue_ring_stage<NW>(smem + st * SLOTB, mat, ld, row0, a.M, st * BK, a.codes, rowblock,
+                             nk, st, wave, lane);
     for (int kt = 0; kt < nk; ++kt) {
       const int after = nk - 1 - kt;
-      wait_vm_stages(after < 2 ? after : 2);
+      wait_vm_stages<NW>(after < 2 ? after : 2);
       // Plain s_barrier: __syncthreads() would also wait for every outstanding load
       // (a workgroup release fence), which would drain the ring. The memory clobber
       // keeps the compiler from moving LDS reads across it.
       asm volatile("s_barrier" ::: "memory");
       if (kt + RING - 1 < nk)
-        issue_ring_stage(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
-                         (kt + RING - 1) * BK, a.codes, rowblock, nk, kt + RING - 1, wave, lane);
+        issue_ring_stage<NW>(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
+                             (kt + RING - 1) * BK, a.codes, rowblock, nk, kt + RING - 1, wave,
+                             lane);
       mma_ring_stage<CL, WI, WJ>(smem + (kt % RING) * SLOTB, acc, wp, wq, lane);
     }
     __syncthreads();
@@ -795,10 +819,11 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
     }
   } else {
     constexpr int id = OP == OP_FWD ? PROF_FWD : PROF_DX;
+    constexpr int NW = OP == OP_FWD ? LCVQ_FWD_WAVES : LCVQ_DX_WAVES;
     switch (d) {
-      case 4: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 4>), dim3(grid), dim3(512), 0, s, a); break;
-      case 8: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 8>), dim3(grid), dim3(512), 0, s, a); break;
-      default: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 16>), dim3(grid), dim3(512), 0, s, a); break;
+      case 4: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 4, NW>), dim3(grid), dim3(NW * 64), 0, s, a); break;
+      case 8: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 8, NW>), dim3(grid), dim3(NW * 64), 0, s, a); break;
+      default: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 16, NW>), dim3(grid), dim3(NW * 64), 0, s, a); break;
     }
   }
   return hipGetLastError();
