@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
-KERNELS = {1: "quantize", 2: "fwd_product", 3: "dx_product", 4: "dw_product"}
+KERNELS = {1: "quantize_prologue", 2: "fwd_product", 3: "dx_product", 4: "dw_product"}
 
 # HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE, each
 # scaled by what it reads for a copy of known size). They are valid only for the kernel
@@ -39,8 +39,8 @@ KERNEL_SOURCES = {
     "products": ["gemm_kernels.hip", "lcvq_device.h", "lcvq_internal.h"],
     "quantize": ["quant_kernels.hip", "lcvq_device.h", "lcvq_internal.h"],
 }
-SOURCE_GROUP = {"quantize": "quantize", "fwd_product": "products", "dx_product": "products",
-                "dw_product": "products"}
+SOURCE_GROUP = {"quantize_prologue": "quantize", "fwd_product": "products",
+                "dx_product": "products", "dw_product": "products"}
 
 
 def source_digest(files):
@@ -182,8 +182,10 @@ def main():
                 "per_kernel_ms": {k: round(v, 4) for k, v in kern.items()},
                 "per_product_tflops": {k: round(gemm_flops / (v * 1e-3) / 1e12, 1)
                                        for k, v in prods.items()}}
-    q_bytes = N * K * (4 + 0.25 + 0.125 + 0.25)   # Wp read; packed, mask, GEMM codes written
-    roofline["quantize_gbs"] = round(q_bytes / (kern["quantize"] * 1e-3) / 1e9, 1)
+    # one launch: Wp read; packed codes, mask bits, GEMM code words written; X read and
+    # X' written (bf16), one float per row
+    q_bytes = N * K * (4 + 0.25 + 0.125 + 0.25) + M * K * (2 + 2) + M * 4
+    roofline["quantize_prologue_gbs"] = round(q_bytes / (kern["quantize_prologue"] * 1e-3) / 1e9, 1)
 
     # ---------------------------------------------------------------- decode product
     decode = None

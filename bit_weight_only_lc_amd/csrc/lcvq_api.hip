@@ -169,10 +169,14 @@ lcvq_status_t lcvq_linear_fwd(const void* X, lcvq_dtype_t xdt, int64_t M, int64_
   uint16_t* xs_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.xs_lo) : nullptr;
   float* beta = reinterpret_cast<float*>(ws + w.beta);
   uint32_t* r16 = reinterpret_cast<uint32_t*>(ws + w.r16);
-  hipError_t e = launch_quantize(Wp, N, K, nullptr, packed_out, mask_out, r16, What_out, A, B,
-                                 d, s);
-  if (e != hipSuccess) return LCVQ_ERR_HIP;
-  e = launch_fwd_prologue(X, f32, M, K, A, B, d, xs, xs_lo, beta, s);
+  hipError_t e;
+  if (M + 65536 < INT32_MAX) {                     // quantizer and prologue in one launch
+    e = launch_fwd_prep(Wp, N, K, packed_out, mask_out, r16, What_out, X, f32, M, A, B, d, xs,
+                        xs_lo, beta, s);
+  } else {
+    e = launch_quantize(Wp, N, K, nullptr, packed_out, mask_out, r16, What_out, A, B, d, s);
+    if (e == hipSuccess) e = launch_fwd_prologue(X, f32, M, K, A, B, d, xs, xs_lo, beta, s);
+  }
   if (e != hipSuccess) return LCVQ_ERR_HIP;
   return from_hip(launch_gemm_fwd(xs, xs_lo, r16, beta, (int)M, (int)N, (int)K, d, Y, f32, s));
 }
@@ -208,13 +212,21 @@ lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, in
   uint16_t* dy_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.dy_lo) : nullptr;
   uint16_t* x_hi = f32 ? reinterpret_cast<uint16_t*>(ws + w.x_hi) : nullptr;
   uint16_t* x_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.x_lo) : nullptr;
-  hipError_t e = launch_bwd_prologue(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi, x_lo, s);
+  // prologue and (when dX is wanted) the transposed codes in one launch
+  const int64_t rblocks = dX ? ((K + 255) / 256) * (N / 64) : 0;
+  const bool merged = M + rblocks < INT32_MAX;
+  hipError_t e = merged ? launch_bwd_prep(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi, x_lo,
+                                          packed, dX ? r16t : nullptr, s)
+                        : launch_bwd_prologue(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi,
+                                              x_lo, s);
   if (e != hipSuccess) return LCVQ_ERR_HIP;
   const uint16_t* dyb = f32 ? dy_hi : static_cast<const uint16_t*>(dY);
   const uint16_t* xb = f32 ? x_hi : static_cast<const uint16_t*>(X);
   if (dX) {
-    e = launch_codes_to_r16t(packed, N, K, r16t, s);
-    if (e != hipSuccess) return LCVQ_ERR_HIP;
+    if (!merged) {
+      e = launch_codes_to_r16t(packed, N, K, r16t, s);
+      if (e != hipSuccess) return LCVQ_ERR_HIP;
+    }
     e = launch_gemm_dx(r16t, dyb, dy_lo, r, A, B, (int)M, (int)N, (int)K, d, dX, f32, s);
     if (e != hipSuccess) return LCVQ_ERR_HIP;
   }

@@ -40,6 +40,18 @@ hipError_t launch_bwd_prologue(const void* dY, const void* X, bool f32, int64_t 
                                int64_t K, float* r, uint16_t* dy_hi, uint16_t* dy_lo,
                                uint16_t* x_hi, uint16_t* x_lo, hipStream_t s);
 
+// One launch each for the forward's quantizer + prologue and the backward's prologue +
+// transposed codes (r16t may be NULL when dX is not wanted). The grid must fit in
+// 2^31 - 1 blocks (launch_*_prep_fits).
+hipError_t launch_fwd_prep(const float* wp, int64_t N, int64_t K, uint8_t* packed, uint8_t* mask,
+                           uint32_t* r16, float* what, const void* X, bool x_f32, int64_t M,
+                           const float* A, const float* B, int d, uint16_t* xs,
+                           uint16_t* xs_lo, float* beta, hipStream_t s);
+hipError_t launch_bwd_prep(const void* dY, const void* X, bool f32, int64_t M, int64_t N,
+                           int64_t K, float* r, uint16_t* dy_hi, uint16_t* dy_lo,
+                           uint16_t* x_hi, uint16_t* x_lo, const uint8_t* packed,
+                           uint32_t* r16t, hipStream_t s);
+
 int gemm_tiles(int64_t P, int64_t Q);
 // Products. `*_lo` operands are NULL for bf16 activations; for float32 activations
 // they hold the low bf16 half of each value and add the cross terms in extra passes.

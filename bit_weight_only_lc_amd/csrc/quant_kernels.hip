@@ -25,9 +25,9 @@ __device__ __forceinline__ int64_t r16_blocked_index(int64_t row, int64_t w, int
 // 16-byte loads per lane (lane l holds elements 256 j + 4 l .. +3 of load j). A group of
 // 16 consecutive codes (one packed word, one R16 word, one d-vector for d <= 16) is
 // spread over 4 neighbouring lanes and gathered with lane shuffles.
-template <int D>   // D = 0: no float32 decode requested
-__global__ __launch_bounds__(256) void k_quantize(
-    const float* __restrict__ wp, int64_t total /* N*K */, int64_t K,
+template <int D>   // D = 0: no float32 decode requested; (bx, gx) = block, grid size
+__device__ __forceinline__ void quantize_body(
+    int bx, int gx, const float* __restrict__ wp, int64_t total /* N*K */, int64_t K,
     uint8_t* __restrict__ z_out, uint8_t* __restrict__ packed_out,
     uint8_t* __restrict__ mask_out, uint32_t* __restrict__ r16_out,
     float* __restrict__ what_out, const float* __restrict__ A,
@@ -37,9 +37,9 @@ __global__ __launch_bounds__(256) void k_quantize(
   const int lane = threadIdx.x & 63;
   const int q = lane & 3;
   const int64_t nchunks = (total + 1023) >> 10;
-  const int64_t wstride = (int64_t)gridDim.x * 4;
+  const int64_t wstride = (int64_t)gx * 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  for (int64_t ch = (int64_t)blockIdx.x * 4 + wv; ch < nchunks; ch += wstride) {
+  for (int64_t ch = (int64_t)bx * 4 + wv; ch < nchunks; ch += wstride) {
     const int64_t base = ch << 10;
     // Row of the chunk's first element (one scalar division per chunk); a lane's element
     // lies less than 1024 elements further, i.e. in row0 or a few rows later.
@@ -129,6 +129,16 @@ __global__ __launch_bounds__(256) void k_quantize(
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(256) void k_quantize(
+    const float* __restrict__ wp, int64_t total, int64_t K, uint8_t* __restrict__ z_out,
+    uint8_t* __restrict__ packed_out, uint8_t* __restrict__ mask_out,
+    uint32_t* __restrict__ r16_out, float* __restrict__ what_out, const float* __restrict__ A,
+    const float* __restrict__ B) {
+  quantize_body<D>(blockIdx.x, gridDim.x, wp, total, K, z_out, packed_out, mask_out, r16_out,
+                   what_out, A, B);
+}
+
 // ------------------------------------------------------------------ pack / unpack
 __global__ __launch_bounds__(256) void k_pack2b(const uint8_t* __restrict__ z, int64_t groups,
                                                 uint32_t* __restrict__ packed) {
@@ -166,12 +176,11 @@ __global__ __launch_bounds__(256) void k_unpack2b(const uint32_t* __restrict__ p
 // operand rows are k: word (k, n/16) of the blocked layout with contraction length N.
 // One block handles 64 rows n x 256 columns k: the 64 x 16 packed words go through LDS
 // and each thread then assembles the words of one column k for the 4 groups of 16 n.
-__global__ __launch_bounds__(256) void k_codes_to_r16t(const uint8_t* __restrict__ packed,
-                                                       int64_t N, int64_t K,
-                                                       uint32_t* __restrict__ r16t) {
+__device__ __forceinline__ void r16t_body(int bx, int by, const uint8_t* __restrict__ packed,
+                                          int64_t N, int64_t K, uint32_t* __restrict__ r16t) {
   __shared__ uint32_t tile[64][17];
   const int tid = threadIdx.x;
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
+  const int64_t n0 = (int64_t)by * 64, k0 = (int64_t)bx * 256;
   const int kcols = K - k0 < 256 ? (int)(K - k0) : 256;   // a multiple of 64
   {
     const int nr = tid >> 2, kq = tid & 3;
@@ -194,6 +203,12 @@ __global__ __launch_bounds__(256) void k_codes_to_r16t(const uint8_t* __restrict
     for (int t = 0; t < 16; ++t) c[t] = (tile[16 * g + t][wc] >> sh) & 3u;
     r16t[r16_blocked_index(k0 + kr, (n0 >> 4) + g, N >> 6)] = r16_encode(c);
   }
+}
+
+__global__ __launch_bounds__(256) void k_codes_to_r16t(const uint8_t* __restrict__ packed,
+                                                       int64_t N, int64_t K,
+                                                       uint32_t* __restrict__ r16t) {
+  r16t_body(blockIdx.x, blockIdx.y, packed, N, K, r16t);
 }
 
 // ------------------------------------------------------------------ block reduction
@@ -231,7 +246,7 @@ template <> __device__ __forceinline__ void load16<float>(const float* p, float 
 // second operand added by a second pass of the product, and beta uses X'b + X'lo.
 // One block per row m; each thread takes 16 consecutive columns per step.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, int64_t K,
+__device__ __forceinline__ void fwd_prologue_body(int64_t m, const T* __restrict__ X, int64_t K,
                                                       const float* __restrict__ A,
                                                       const float* __restrict__ B,
                                                       uint16_t* __restrict__ xs,
@@ -251,7 +266,6 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, i
     As = Asm;
     Bs = Bsm;
   }
-  const int64_t m = blockIdx.x;
   const T* xrow = X + m * K;
   uint16_t* orow = xs + m * K;
   float acc = 0.f;
@@ -316,6 +330,16 @@ __global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, i
   if (threadIdx.x == 0) beta[m] = sum;
 }
 
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_fwd_prologue(const T* __restrict__ X, int64_t K,
+                                                      const float* __restrict__ A,
+                                                      const float* __restrict__ B,
+                                                      uint16_t* __restrict__ xs,
+                                                      uint16_t* __restrict__ xs_lo,
+                                                      float* __restrict__ beta) {
+  fwd_prologue_body<T, D>(blockIdx.x, X, K, A, B, xs, xs_lo, beta);
+}
+
 // ------------------------------------------------------------------ backward prologue
 // r[m] = sum_n dY[m, n] (float32). With float32 activations, also splits dY and X into
 // bf16 pairs hi + lo (hi = bf16(x), lo = bf16(x - hi)) for the matrix-core products,
@@ -336,15 +360,14 @@ __device__ __forceinline__ void split16(const float x[16], uint16_t* hi, uint16_
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_bwd_prologue(const T* __restrict__ dY,
-                                                      const T* __restrict__ X, int64_t N,
-                                                      int64_t K, float* __restrict__ r,
-                                                      uint16_t* __restrict__ dy_hi,
-                                                      uint16_t* __restrict__ dy_lo,
-                                                      uint16_t* __restrict__ x_hi,
-                                                      uint16_t* __restrict__ x_lo) {
+__device__ __forceinline__ void bwd_prologue_body(int64_t m, const T* __restrict__ dY,
+                                                  const T* __restrict__ X, int64_t N,
+                                                  int64_t K, float* __restrict__ r,
+                                                  uint16_t* __restrict__ dy_hi,
+                                                  uint16_t* __restrict__ dy_lo,
+                                                  uint16_t* __restrict__ x_hi,
+                                                  uint16_t* __restrict__ x_lo) {
   __shared__ float red[4];
-  const int64_t m = blockIdx.x;
   float acc = 0.f;
   for (int64_t c = threadIdx.x; c < (N >> 4); c += blockDim.x) {
     float y[16];
@@ -362,6 +385,59 @@ __global__ __launch_bounds__(256) void k_bwd_prologue(const T* __restrict__ dY,
   }
   const float s = block_sum_256(acc, red);
   if (threadIdx.x == 0) r[m] = s;
+}
+
+// ------------------------------------------------------------------ merged launches
+// Work that does not depend on each other shares one launch: block ranges of one grid
+// run the two parts, which saves a kernel boundary and lets the VALU-bound quantizer
+// overlap the memory-bound prologue.
+//   forward:  blocks [0, qblocks) quantize, then one block per activation row m;
+//   backward: one block per row m (r = dY 1), then the blocks of the transposed codes.
+template <typename T, int DQ, int D>
+__global__ __launch_bounds__(256) void k_fwd_prep(const float* __restrict__ wp, int64_t total,
+                                                  int64_t K, uint8_t* __restrict__ packed,
+                                                  uint8_t* __restrict__ mask,
+                                                  uint32_t* __restrict__ r16,
+                                                  float* __restrict__ what, int qblocks,
+                                                  const T* __restrict__ X, int64_t KX,
+                                                  const float* __restrict__ A,
+                                                  const float* __restrict__ B,
+                                                  uint16_t* __restrict__ xs,
+                                                  uint16_t* __restrict__ xs_lo,
+                                                  float* __restrict__ beta) {
+  if ((int)blockIdx.x < qblocks)
+    quantize_body<DQ>(blockIdx.x, qblocks, wp, total, K, nullptr, packed, mask, r16, what, A, B);
+  else
+    fwd_prologue_body<T, D>((int64_t)blockIdx.x - qblocks, X, KX, A, B, xs, xs_lo, beta);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ dY,
+                                                  const T* __restrict__ X, int64_t M,
+                                                  int64_t N, int64_t K, float* __restrict__ r,
+                                                  uint16_t* __restrict__ dy_hi,
+                                                  uint16_t* __restrict__ dy_lo,
+                                                  uint16_t* __restrict__ x_hi,
+                                                  uint16_t* __restrict__ x_lo,
+                                                  const uint8_t* __restrict__ packed,
+                                                  uint32_t* __restrict__ r16t, int kblocks) {
+  if ((int64_t)blockIdx.x < M) {
+    bwd_prologue_body<T>(blockIdx.x, dY, X, N, K, r, dy_hi, dy_lo, x_hi, x_lo);
+  } else {
+    const int vb = (int)((int64_t)blockIdx.x - M);
+    r16t_body(vb % kblocks, vb / kblocks, packed, N, K, r16t);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_bwd_prologue(const T* __restrict__ dY,
+                                                      const T* __restrict__ X, int64_t N,
+                                                      int64_t K, float* __restrict__ r,
+                                                      uint16_t* __restrict__ dy_hi,
+                                                      uint16_t* __restrict__ dy_lo,
+                                                      uint16_t* __restrict__ x_hi,
+                                                      uint16_t* __restrict__ x_lo) {
+  bwd_prologue_body<T>(blockIdx.x, dY, X, N, K, r, dy_hi, dy_lo, x_hi, x_lo);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -434,6 +510,74 @@ hipError_t launch_fwd_prologue(const void* X, bool x_f32, int64_t M, int64_t K, 
   if (d == 4) fwd_prologue_d<4>(X, x_f32, M, K, A, B, xs, xs_lo, beta, s);
   else if (d == 8) fwd_prologue_d<8>(X, x_f32, M, K, A, B, xs, xs_lo, beta, s);
   else fwd_prologue_d<16>(X, x_f32, M, K, A, B, xs, xs_lo, beta, s);
+  return hipGetLastError();
+}
+
+static int quantize_blocks(int64_t total) {
+  int64_t blocks = ((total + 1023) / 1024 + 3) / 4;
+  if (blocks > 65535) blocks = 65535;
+  return (int)(blocks < 1 ? 1 : blocks);
+}
+
+template <typename T, int DQ, int D>
+static void fwd_prep_launch(const float* wp, int64_t N, int64_t K, uint8_t* packed, uint8_t* mask,
+                            uint32_t* r16, float* what, const T* X, int64_t M, const float* A,
+                            const float* B, uint16_t* xs, uint16_t* xs_lo, float* beta,
+                            hipStream_t s) {
+  const int qb = quantize_blocks(N * K);
+  LCVQ_LAUNCH(PROF_QUANTIZE, (k_fwd_prep<T, DQ, D>), dim3((unsigned)(qb + M)), dim3(256), 0, s,
+              wp, N * K, K, packed, mask, r16, what, qb, X, K, A, B, xs, xs_lo, beta);
+}
+
+template <typename T, int D>
+static void fwd_prep_t(const float* wp, int64_t N, int64_t K, uint8_t* packed, uint8_t* mask,
+                       uint32_t* r16, float* what, const void* X, int64_t M, const float* A,
+                       const float* B, uint16_t* xs, uint16_t* xs_lo, float* beta,
+                       hipStream_t s) {
+  const T* x = static_cast<const T*>(X);
+  if (what)
+    fwd_prep_launch<T, D, D>(wp, N, K, packed, mask, r16, what, x, M, A, B, xs, xs_lo, beta, s);
+  else
+    fwd_prep_launch<T, 0, D>(wp, N, K, packed, mask, r16, what, x, M, A, B, xs, xs_lo, beta, s);
+}
+
+template <int D>
+static void fwd_prep_d(const float* wp, int64_t N, int64_t K, uint8_t* packed, uint8_t* mask,
+                       uint32_t* r16, float* what, const void* X, bool x_f32, int64_t M,
+                       const float* A, const float* B, uint16_t* xs, uint16_t* xs_lo,
+                       float* beta, hipStream_t s) {
+  if (x_f32)
+    fwd_prep_t<float, D>(wp, N, K, packed, mask, r16, what, X, M, A, B, xs, xs_lo, beta, s);
+  else
+    fwd_prep_t<uint16_t, D>(wp, N, K, packed, mask, r16, what, X, M, A, B, xs, nullptr, beta, s);
+}
+
+hipError_t launch_fwd_prep(const float* wp, int64_t N, int64_t K, uint8_t* packed, uint8_t* mask,
+                           uint32_t* r16, float* what, const void* X, bool x_f32, int64_t M,
+                           const float* A, const float* B, int d, uint16_t* xs,
+                           uint16_t* xs_lo, float* beta, hipStream_t s) {
+  if (d == 4) fwd_prep_d<4>(wp, N, K, packed, mask, r16, what, X, x_f32, M, A, B, xs, xs_lo, beta, s);
+  else if (d == 8) fwd_prep_d<8>(wp, N, K, packed, mask, r16, what, X, x_f32, M, A, B, xs, xs_lo, beta, s);
+  else fwd_prep_d<16>(wp, N, K, packed, mask, r16, what, X, x_f32, M, A, B, xs, xs_lo, beta, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const void* dY, const void* X, bool f32, int64_t M, int64_t N,
+                           int64_t K, float* r, uint16_t* dy_hi, uint16_t* dy_lo,
+                           uint16_t* x_hi, uint16_t* x_lo, const uint8_t* packed,
+                           uint32_t* r16t, hipStream_t s) {
+  const int kblocks = (int)((K + 255) / 256);
+  const int64_t rb = r16t ? (int64_t)kblocks * (N / 64) : 0;
+  const dim3 g((unsigned)(M + rb)), b(256);
+  if (f32)
+    hipLaunchKernelGGL(k_bwd_prep<float>, g, b, 0, s, static_cast<const float*>(dY),
+                       static_cast<const float*>(X), M, N, K, r, dy_hi, dy_lo, x_hi, x_lo,
+                       packed, r16t, kblocks);
+  else
+    hipLaunchKernelGGL(k_bwd_prep<uint16_t>, g, b, 0, s, static_cast<const uint16_t*>(dY),
+                       static_cast<const uint16_t*>(X), M, N, K, r, (uint16_t*)nullptr,
+                       (uint16_t*)nullptr, (uint16_t*)nullptr, (uint16_t*)nullptr, packed,
+                       r16t, kblocks);
   return hipGetLastError();
 }
 
