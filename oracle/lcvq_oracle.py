@@ -42,6 +42,7 @@ import numpy as np
 __all__ = [
     "quantize", "pack2b", "unpack2b", "pack_mask", "unpack_mask", "reconstruct",
     "linear_fwd", "linear_bwd", "gemv2b", "nearest_codeword", "decoupleq_quant",
+    "dge_curve", "dge_slope",
 ]
 
 
@@ -132,7 +133,37 @@ def linear_fwd(X, wp, A, B, d):
     return out
 
 
-def linear_bwd(dY, X, z, m, A, B, d):
+def dge_curve(w, alpha):
+    """Smooth stand-in for rounding used by the DGE backward.
+
+    [LCQAT-M3] says only that LC-QAT's differentiable gradient estimator (DGE)
+    approximates the discretization with a smooth, differentiable curve and uses its
+    gradient instead of the straight-through one; the curve itself is not given. The
+    family used here (this implementation's reading, parity unpinned against the pages):
+      s(w) = floor(w) + 1/2 + tanh(alpha (f - 1/2)) / (2 tanh(alpha / 2)),  f = w - floor(w)
+    It passes through every integer, is steepest at the half-integers where rounding
+    jumps, tends to s(w) = w (the straight-through estimator) as alpha -> 0 and to
+    rounding as alpha -> infinity.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    n = np.floor(w)
+    f = w - n
+    return n + 0.5 + np.tanh(alpha * (f - 0.5)) / (2.0 * np.tanh(alpha / 2.0))
+
+
+def dge_slope(w, alpha):
+    """Derivative of dge_curve: alpha (1 - tanh^2(alpha (f - 1/2))) / (2 tanh(alpha / 2)).
+    Zero for non-finite w (those weights are masked by the clamp anyway)."""
+    w = np.asarray(w, dtype=np.float64)
+    out = np.zeros(w.shape)
+    fin = np.isfinite(w)
+    f = w[fin] - np.floor(w[fin])
+    t = np.tanh(alpha * (f - 0.5))
+    out[fin] = alpha * (1.0 - t * t) / (2.0 * np.tanh(alpha / 2.0))
+    return out
+
+
+def linear_bwd(dY, X, z, m, A, B, d, wp=None, dge_alpha=None):
     """Straight-through backward of Y = X What(z, A, B)^T.
 
     Standard backpropagation through the linear decode [LCQAT-M1]; the rounding is
@@ -142,6 +173,8 @@ def linear_bwd(dY, X, z, m, A, B, d):
       dWp[n, g*d + j] = m[n, g*d + j] * sum_i A[i, j] G[n, g*d + i]
       dA[i, j] = sum over vectors (n, g) of G[n, g*d + i] * z[n, g*d + j]
       dB[i]    = sum over vectors (n, g) of G[n, g*d + i]
+    With dge_alpha (and the proxies wp) the rounding's gradient is dge_slope(wp) instead
+    of 1, still masked by the clamp: dWp is multiplied elementwise by dge_slope(wp).
     """
     dY = np.asarray(dY, dtype=np.float64)
     X = np.asarray(X, dtype=np.float64)
@@ -154,6 +187,8 @@ def linear_bwd(dY, X, z, m, A, B, d):
     zv = z.astype(np.float64).reshape(n, k // d, d)
     dW_hat_to_wp = np.einsum("ij,ngi->ngj", A, gv).reshape(n, k)
     dWp = dW_hat_to_wp * np.asarray(m, dtype=np.float64)
+    if dge_alpha is not None:
+        dWp = dWp * dge_slope(np.asarray(wp, dtype=np.float32), dge_alpha)
     dA = np.einsum("ngi,ngj->ij", gv, zv)
     dB = gv.sum(axis=(0, 1))
     return {"dX": dX, "dWp": dWp, "dA": dA, "dB": dB}

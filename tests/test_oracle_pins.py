@@ -268,3 +268,58 @@ def test_mask_zero_outside_clamp_range():
     A, B = np.eye(8), np.zeros(8)
     b = O.linear_bwd(np.ones((1, 1)), np.ones((1, 8)), z, m, A, B, 8)
     assert b["dWp"].tolist() == [[0, 1, 1, 0, 0, 0, 1, 1]]
+
+
+# ---------------------------------------------------------------- DGE curve (own family)
+# The pages fix no DGE curve, so these pins check the oracle's family against its own
+# definition by other routes: derivative by finite differences, its limits, and torch
+# autograd through the literal smooth-rounding formula.
+@pytest.mark.parametrize("alpha", [0.5, 4.0, 12.0])
+def test_dge_slope_is_derivative_of_curve(alpha):
+    w = np.random.default_rng(5).uniform(-1.0, 4.0, 2000)
+    h = 1e-6
+    fd = (O.dge_curve(w + h, alpha) - O.dge_curve(w - h, alpha)) / (2 * h)
+    np.testing.assert_allclose(O.dge_slope(w, alpha), fd, rtol=1e-6, atol=1e-6)
+
+
+def test_dge_curve_limits_and_fixed_points():
+    ints = np.arange(-2.0, 6.0)
+    np.testing.assert_allclose(O.dge_curve(ints, 7.0), ints, atol=1e-14)
+    np.testing.assert_allclose(O.dge_curve(ints + 0.5, 7.0), ints + 0.5, atol=1e-14)
+    w = np.random.default_rng(6).uniform(-1.0, 4.0, 1000)
+    # alpha -> 0: the straight-through estimator (identity curve, slope 1)
+    np.testing.assert_allclose(O.dge_curve(w, 1e-6), w, atol=1e-9)
+    np.testing.assert_allclose(O.dge_slope(w, 1e-6), 1.0, atol=1e-9)
+    # alpha -> infinity: rounding, away from the half-integers
+    far = w[np.abs(w - np.floor(w) - 0.5) > 0.1]
+    np.testing.assert_allclose(O.dge_curve(far, 200.0), np.rint(far), atol=1e-12)
+    # monotone, and the slope integrates to 1 over a cell
+    x = np.linspace(0.0, 1.0, 200001)
+    assert np.all(np.diff(O.dge_curve(x, 9.0)) > 0)
+    assert abs(np.trapezoid(O.dge_slope(x, 9.0), x) - 1.0) < 1e-8
+    assert np.all(O.dge_slope(np.array([np.nan, np.inf, -np.inf]), 3.0) == 0.0)
+
+
+@pytest.mark.parametrize("d", [4, 8])
+def test_dge_backward_matches_torch_autograd(d):
+    """Forward rounds; the backward differentiates the smooth curve (value of round,
+    gradient of s): zs = s(Wp) + (round(Wp) - s(Wp)).detach(), then clamp and decode."""
+    alpha = 6.0
+    wp, A, B, X, dY = _layer(300 + d, M=4, N=8, K=64, d=d)
+    wp = (wp * 1.6 - 1.0).astype(np.float32)                  # some clamped proxies too
+    f = O.linear_fwd(X, wp, A, B, d)
+    b = O.linear_bwd(dY, X, f["z"], f["m"], A, B, d, wp=wp, dge_alpha=alpha)
+    Wt = torch.tensor(wp.astype(np.float64), requires_grad=True)
+    fl = torch.floor(Wt).detach()
+    s = fl + 0.5 + torch.tanh(alpha * (Wt - fl - 0.5)) / (2 * math.tanh(alpha / 2))
+    zs = s + (torch.round(Wt) - s).detach()
+    zc = torch.clamp(zs, 0, 3)
+    n, k = wp.shape
+    At = torch.tensor(A)
+    Bt = torch.tensor(B)
+    w = (zc.view(n, k // d, d) @ At.T + Bt).view(n, k)
+    Y = torch.tensor(X) @ w.T
+    (Y * torch.tensor(dY)).sum().backward()
+    np.testing.assert_allclose(Y.detach().numpy(), f["Y"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Wt.grad.numpy(), b["dWp"], rtol=1e-10, atol=1e-12)
+    assert np.count_nonzero(f["m"] == 0) > 0
