@@ -162,6 +162,20 @@ def main():
     ms = min(ms_eager, ms_graph)
     tflops = flops / (ms * 1e-3) / 1e12
 
+    # the same step with the DGE estimator in the backward (sharpness 8)
+    def step_dge():
+        P.lcvq_linear_fwd(X, Wp, A, B, d, Y, packed, mask, None, wsf)
+        P.lcvq_linear_bwd_dge(dY, X, packed, mask, Wp, 8.0, A, B, d, dX, dWp, dA, dB, wsb)
+
+    for _ in range(args.warmup):
+        step_dge()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_dge()
+    torch.cuda.synchronize()
+    ms_dge = (time.perf_counter() - t0) * 1e3 / args.steps
+
     # per-kernel durations, one kernel id armed per step
     kern = {}
     for kid, name in KERNELS.items():
@@ -290,6 +304,7 @@ def main():
         "ms_per_step": round(ms, 4),
         "ms_per_step_eager": round(ms_eager, 4),
         "ms_per_step_graph": round(ms_graph, 4),
+        "ms_per_step_dge": round(ms_dge, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

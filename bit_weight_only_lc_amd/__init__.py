@@ -6,7 +6,7 @@ declared in include/lcvq.h. All arithmetic runs in the library's HIP kernels; if
 library is missing the import of any entry point raises.
 
 Names follow the C ABI (lcvq_quantize, lcvq_pack2b, lcvq_unpack2b, lcvq_linear_fwd,
-lcvq_linear_bwd, lcvq_gemv2b and the *_workspace_size helpers).
+lcvq_linear_bwd, lcvq_linear_bwd_dge, lcvq_gemv2b and the *_workspace_size helpers).
 """
 
 import ctypes
@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "liblcvq.so")
 
 LCVQ_F32, LCVQ_BF16 = 0, 1
 _STATUS = {0: "LCVQ_OK", 1: "LCVQ_ERR_NULL", 2: "LCVQ_ERR_SHAPE", 3: "LCVQ_ERR_D",
-           4: "LCVQ_ERR_DTYPE", 5: "LCVQ_ERR_ALIGN", 6: "LCVQ_ERR_WORKSPACE", 7: "LCVQ_ERR_HIP"}
+           4: "LCVQ_ERR_DTYPE", 5: "LCVQ_ERR_ALIGN", 6: "LCVQ_ERR_WORKSPACE", 7: "LCVQ_ERR_HIP",
+           8: "LCVQ_ERR_VALUE"}
 
 _lib = None
 
@@ -40,6 +41,7 @@ def lib():
                               "`python -m bit_weight_only_lc_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        f32 = ctypes.c_float
         L.lcvq_status_string.restype = ctypes.c_char_p
         L.lcvq_status_string.argtypes = [i32]
         sigs = {
@@ -50,6 +52,8 @@ def lib():
                                 sz, vp],
             "lcvq_linear_bwd": [vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, vp,
                                 vp, vp, sz, vp],
+            "lcvq_linear_bwd_dge": [vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, f32, vp, vp,
+                                    vp, vp, vp, vp, vp, sz, vp],
             "lcvq_gemv2b": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp],
         }
         for name, args in sigs.items():
@@ -187,6 +191,32 @@ def lcvq_linear_bwd(dY, X, packed, mask, A, B, d, dX, dWp, dA, dB, workspace=Non
                               workspace.numel(), _stream(dev)), "lcvq_linear_bwd")
 
 
+def lcvq_linear_bwd_dge(dY, X, packed, mask, Wp, alpha, A, B, d, dX, dWp, dA, dB,
+                        workspace=None):
+    _check(dY, "dY", (torch.bfloat16, torch.float32))
+    dev = dY.device
+    _check(X, "X", dY.dtype, dev)
+    _check(packed, "packed", torch.uint8, dev)
+    _check(mask, "mask", torch.uint8, dev)
+    _check(Wp, "Wp", torch.float32, dev)
+    _check(A, "A", torch.float32, dev)
+    _check(B, "B", torch.float32, dev)
+    _check(dX, "dX", dY.dtype, dev)
+    _check(dWp, "dWp", torch.float32, dev)
+    _check(dA, "dA", torch.float32, dev)
+    _check(dB, "dB", torch.float32, dev)
+    M, N = dY.shape
+    K = X.shape[1]
+    if workspace is None:
+        workspace = torch.empty(max(lcvq_linear_bwd_workspace_size(M, N, K, d), 1),
+                                dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    _ok(lib().lcvq_linear_bwd_dge(_p(dY), _p(X), _dt(dY), M, N, K, d, _p(packed), _p(mask),
+                                  _p(Wp), float(alpha), _p(A), _p(B), _p(dX), _p(dWp), _p(dA),
+                                  _p(dB), _p(workspace), workspace.numel(), _stream(dev)),
+        "lcvq_linear_bwd_dge")
+
+
 def lcvq_gemv2b(X, packed, A16, B16, d, Y, workspace=None):
     _check(X, "X", torch.bfloat16)
     dev = X.device
@@ -220,8 +250,9 @@ def linear_fwd(X, Wp, A, B, d, want_what=False):
     return out
 
 
-def linear_bwd(dY, X, packed, mask, A, B, d, want_dx=True):
-    """Allocates the outputs of lcvq_linear_bwd and returns them in a dict."""
+def linear_bwd(dY, X, packed, mask, A, B, d, want_dx=True, dge_wp=None, dge_alpha=None):
+    """Allocates the outputs of lcvq_linear_bwd (or, with dge_wp and dge_alpha, of
+    lcvq_linear_bwd_dge) and returns them in a dict."""
     M, N = dY.shape
     K = X.shape[1]
     dev = dY.device
@@ -231,7 +262,12 @@ def linear_bwd(dY, X, packed, mask, A, B, d, want_dx=True):
         "dA": torch.empty((d, d), dtype=torch.float32, device=dev),
         "dB": torch.empty((d,), dtype=torch.float32, device=dev),
     }
-    lcvq_linear_bwd(dY, X, packed, mask, A, B, d, out["dX"], out["dWp"], out["dA"], out["dB"])
+    if dge_alpha is None:
+        lcvq_linear_bwd(dY, X, packed, mask, A, B, d, out["dX"], out["dWp"], out["dA"],
+                        out["dB"])
+    else:
+        lcvq_linear_bwd_dge(dY, X, packed, mask, dge_wp, dge_alpha, A, B, d, out["dX"],
+                            out["dWp"], out["dA"], out["dB"])
     return out
 
 

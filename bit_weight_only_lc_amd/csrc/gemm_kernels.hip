@@ -77,6 +77,8 @@ struct GemmArgs {
   const uint8_t* packed;       // DW: canonical codes [N][K/4]
   const uint8_t* mask;         // DW: mask bits [N][K/8]
   float* partials;             // DW: [ntiles][d*d + d]
+  const float* dge_wp;         // DW with the DGE estimator: proxies [N][K], else NULL
+  float dge_alpha, dge_c;      // sharpness and alpha / (2 tanh(alpha / 2))
 };
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -269,6 +271,37 @@ __device__ __forceinline__ void store_block_rows(const float* S, void* out, int 
   }
 }
 
+// Slope of the DGE curve s(w) = floor(w) + 1/2 + tanh(alpha (f - 1/2)) / (2 tanh(alpha/2)),
+// f = w - floor(w): c (1 - tanh^2(alpha (f - 1/2))) with c = alpha / (2 tanh(alpha / 2)).
+// Zero for non-finite proxies (the clamp masks them).
+__device__ __forceinline__ float dge_slope(float w, float alpha, float c) {
+  if (!__builtin_isfinite(w)) return 0.f;
+  const float t = tanhf(alpha * ((w - floorf(w)) - 0.5f));
+  return c * (1.f - t * t);
+}
+
+// store_block_rows for dWp under the DGE estimator: each value is multiplied by the
+// slope at its proxy, read as the same 4 consecutive floats of Wp [N][K].
+__device__ __forceinline__ void store_block_rows_dge(const float* S, float* out, const float* wp,
+                                                     float alpha, float c, int64_t ld, int row0,
+                                                     int rows, int k0, int K, int lane) {
+  const int kq = (lane & 7) * 4;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int rr = it * 8 + (lane >> 3);
+    const int row = row0 + rr;
+    if (row < rows && k0 + kq < K) {
+      const int64_t idx = (int64_t)row * ld + k0 + kq;
+      const float4 w = *reinterpret_cast<const float4*>(wp + idx);
+      *reinterpret_cast<float4*>(out + idx) =
+          make_float4(S[(kq + 0) * SROW + rr] * dge_slope(w.x, alpha, c),
+                      S[(kq + 1) * SROW + rr] * dge_slope(w.y, alpha, c),
+                      S[(kq + 2) * SROW + rr] * dge_slope(w.z, alpha, c),
+                      S[(kq + 3) * SROW + rr] * dge_slope(w.w, alpha, c));
+    }
+  }
+}
+
 // dX[m, g*d+i] = 2 sum_j A[i][j] C[g*d+j, m] + (B[i] - 4 sum_j A[i][j]) r[m]
 // where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m).
 template <int D, int WI, int WJ>
@@ -394,7 +427,11 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
         }
         if (pass == 0) {
           wave_sync();
-          store_block_rows(S, a.dwp, 1, a.K, nb, a.N, kb, a.K, lane);
+          if (a.dge_wp)
+            store_block_rows_dge(S, a.dwp, a.dge_wp, a.dge_alpha, a.dge_c, a.K, nb, a.N, kb,
+                                 a.K, lane);
+          else
+            store_block_rows(S, a.dwp, 1, a.K, nb, a.N, kb, a.K, lane);
         }
       }
     // Wave reduction: lanes l and l+32 hold the same entries for different vectors; add
@@ -861,7 +898,8 @@ hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16
 hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_t* dy,
                           const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
-                          float* partials, float* dA, float* dB, hipStream_t s) {
+                          float* partials, float* dA, float* dB, const float* dge_wp,
+                          float dge_alpha, hipStream_t s) {
   GemmArgs a = {};
   a.P = K; a.Q = N; a.R = M;
   a.Lmat[0] = x; a.Rmat[0] = dy;
@@ -874,6 +912,9 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
   a.A = A;
   a.M = M; a.N = N; a.K = K;
   a.dwp = dWp; a.packed = packed; a.mask = mask; a.partials = partials;
+  a.dge_wp = dge_wp;
+  a.dge_alpha = dge_alpha;
+  a.dge_c = dge_wp ? (float)((double)dge_alpha / (2.0 * tanh((double)dge_alpha / 2.0))) : 0.f;
   hipError_t e = launch_op<OP_DW>(a, d, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_reduce_partials, dim3(d * d + d), dim3(256), 0, s, partials, a.ntiles,

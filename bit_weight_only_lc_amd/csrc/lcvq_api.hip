@@ -110,6 +110,7 @@ const char* lcvq_status_string(lcvq_status_t s) {
     case LCVQ_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case LCVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case LCVQ_ERR_HIP: return "kernel launch failed";
+    case LCVQ_ERR_VALUE: return "a scalar argument is out of range";
   }
   return "unknown status";
 }
@@ -187,11 +188,15 @@ size_t lcvq_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int d) {
   return bwd_ws(M, N, K, d, true).total;
 }
 
-lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, int64_t M,
+}  // extern "C"
+
+namespace {
+lcvq_status_t linear_bwd_impl(const void* dY, const void* X, lcvq_dtype_t dt, int64_t M,
                               int64_t N, int64_t K, int d, const uint8_t* packed,
-                              const uint8_t* mask, const float* A, const float* B,
-                              void* dX, float* dWp, float* dA, float* dB, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              const uint8_t* mask, const float* Wp, float alpha,
+                              const float* A, const float* B, void* dX, float* dWp, float* dA,
+                              float* dB, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (!dY || !X || !packed || !mask || !A || !B || !dWp || !dA || !dB) return LCVQ_ERR_NULL;
   if (dt != LCVQ_F32 && dt != LCVQ_BF16) return LCVQ_ERR_DTYPE;
   if (!d_ok(d)) return LCVQ_ERR_D;
@@ -231,7 +236,32 @@ lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, in
     if (e != hipSuccess) return LCVQ_ERR_HIP;
   }
   return from_hip(launch_gemm_dw(xb, x_lo, dyb, dy_lo, packed, mask, A, (int)M, (int)N,
-                                 (int)K, d, dWp, partials, dA, dB, s));
+                                 (int)K, d, dWp, partials, dA, dB, Wp, alpha, s));
+}
+}  // namespace
+
+extern "C" {
+
+lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, int64_t M,
+                              int64_t N, int64_t K, int d, const uint8_t* packed,
+                              const uint8_t* mask, const float* A, const float* B,
+                              void* dX, float* dWp, float* dA, float* dB, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return linear_bwd_impl(dY, X, dt, M, N, K, d, packed, mask, nullptr, 0.f, A, B, dX, dWp, dA,
+                         dB, workspace, workspace_bytes, stream);
+}
+
+lcvq_status_t lcvq_linear_bwd_dge(const void* dY, const void* X, lcvq_dtype_t dt, int64_t M,
+                                  int64_t N, int64_t K, int d, const uint8_t* packed,
+                                  const uint8_t* mask, const float* Wp, float alpha,
+                                  const float* A, const float* B, void* dX, float* dWp,
+                                  float* dA, float* dB, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!Wp) return LCVQ_ERR_NULL;
+  if (!aligned16(Wp)) return LCVQ_ERR_ALIGN;
+  if (!(alpha > 0.f) || !(alpha <= 1000.f)) return LCVQ_ERR_VALUE;   // also rejects NaN
+  return linear_bwd_impl(dY, X, dt, M, N, K, d, packed, mask, Wp, alpha, A, B, dX, dWp, dA,
+                         dB, workspace, workspace_bytes, stream);
 }
 
 size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t N, int64_t K, int d) {

@@ -64,7 +64,8 @@ hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16
 hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_t* dy,
                           const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
-                          float* partials, float* dA, float* dB, hipStream_t s);
+                          float* partials, float* dA, float* dB, const float* dge_wp,
+                          float dge_alpha, hipStream_t s);
 
 // Decode product. Few tokens: one fused kernel (xq and rowinfo unused); otherwise a
 // prologue writes X' limbs to xq and block scales to rowinfo, and the product reads them.

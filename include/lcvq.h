@@ -48,7 +48,8 @@ typedef enum {
   LCVQ_ERR_DTYPE = 4,      /* unknown dtype code */
   LCVQ_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
   LCVQ_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than the *_workspace_size() */
-  LCVQ_ERR_HIP = 7         /* a kernel launch failed */
+  LCVQ_ERR_HIP = 7,        /* a kernel launch failed */
+  LCVQ_ERR_VALUE = 8       /* a scalar argument is out of range */
 } lcvq_status_t;
 
 typedef enum { LCVQ_F32 = 0, LCVQ_BF16 = 1 } lcvq_dtype_t;
@@ -120,6 +121,29 @@ lcvq_status_t lcvq_linear_bwd(const void* dY, const void* X, lcvq_dtype_t dt, in
                               const uint8_t* mask, const float* A, const float* B,
                               void* dX, float* dWp, float* dA, float* dB, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/*
+ * The same backward with LC-QAT's differentiable gradient estimator in place of the
+ * straight-through one (LC-QAT summary, Methodology 3 backward: the rounding's gradient
+ * comes from a smooth, differentiable curve that approximates the discretization). The
+ * summary does not give the curve; this library uses tanh-smoothed rounding,
+ *   s(w) = floor(w) + 1/2 + tanh(alpha (f - 1/2)) / (2 tanh(alpha / 2)),  f = w - floor(w),
+ * which passes through every integer, is steepest at the half-integers, tends to the
+ * straight-through estimator as alpha -> 0 and to rounding as alpha grows. The forward
+ * is unchanged (it rounds). Only dWp changes:
+ *   dWp[n, k] = mask * s'(Wp[n, k]) * sum_i A[i, j] G[n, g*d+i]     (k = g*d + j)
+ * with s'(w) = alpha (1 - tanh^2(alpha (f - 1/2))) / (2 tanh(alpha / 2)) (0 for non-finite
+ * w). dX, dA and dB are those of lcvq_linear_bwd.
+ *   Wp     float [N, K], the proxies the forward quantized (read once more, 4 B/weight)
+ *   alpha  sharpness, 0 < alpha <= 1000 (LCVQ_ERR_VALUE otherwise)
+ * Every other argument, the workspace and the errors are as for lcvq_linear_bwd.
+ */
+lcvq_status_t lcvq_linear_bwd_dge(const void* dY, const void* X, lcvq_dtype_t dt, int64_t M,
+                                  int64_t N, int64_t K, int d, const uint8_t* packed,
+                                  const uint8_t* mask, const float* Wp, float alpha,
+                                  const float* A, const float* B, void* dX, float* dWp,
+                                  float* dA, float* dB, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * Decode product from the deployed artefact (packed codes plus half-precision A, B):

@@ -34,7 +34,9 @@ Layout conventions (readings of what the pages leave open):
   bit k = 8c + t sits in bit t of mask byte c.
 
 Parity of every function here is pinned by tests/test_oracle_pins.py (brute force,
-special cases, closed forms, exact finite differences, a hand-worked example).
+special cases, closed forms, exact finite differences, a hand-worked example), except
+dge_curve / dge_slope: parity unpinned against the pages, which give no DGE curve; they
+are pinned only against their own definition (finite differences, limits, autograd).
 """
 
 import numpy as np

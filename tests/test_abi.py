@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["lcvq_quantize", "lcvq_linear_fwd", "lcvq_linear_bwd", "lcvq_pack2b",
-              "lcvq_gemv2b", "lcvq_unpack2b", "lcvq_status_string",
+              "lcvq_gemv2b", "lcvq_unpack2b", "lcvq_status_string", "lcvq_linear_bwd_dge",
               "lcvq_linear_fwd_workspace_size", "lcvq_linear_bwd_workspace_size",
               "lcvq_gemv2b_workspace_size"]:
         assert n in names
@@ -41,8 +41,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for s in range(8):
-        assert L.lcvq_status_string(s)
+    for s in range(9):
+        assert L.lcvq_status_string(s) != b"unknown status"
     assert L.lcvq_status_string(99) == b"unknown status"
 
 
@@ -109,6 +109,28 @@ def test_linear_bwd_errors(L):
     assert need > 0
     assert _bwd(L, dt=0, wsb=need - 1) == 6
     assert _bwd(L, ws=None) == 6
+
+
+def _bwd_dge(L, **kw):
+    a = dict(dY=P, X=P, dt=1, M=16, N=256, K=256, d=8, packed=P, mask=P, Wp=P, alpha=4.0,
+             A=P, B=P, dX=P, dWp=P, dA=P, dB=P, ws=P, wsb=1 << 30, s=None)
+    a.update(kw)
+    return L.lcvq_linear_bwd_dge(a["dY"], a["X"], a["dt"], a["M"], a["N"], a["K"], a["d"],
+                                 a["packed"], a["mask"], a["Wp"], a["alpha"], a["A"], a["B"],
+                                 a["dX"], a["dWp"], a["dA"], a["dB"], a["ws"], a["wsb"],
+                                 a["s"])
+
+
+def test_linear_bwd_dge_errors(L):
+    assert _bwd_dge(L, Wp=None) == 1
+    assert _bwd_dge(L, Wp=MIS) == 5
+    assert _bwd_dge(L, alpha=0.0) == 8
+    assert _bwd_dge(L, alpha=-1.0) == 8
+    assert _bwd_dge(L, alpha=float("nan")) == 8
+    assert _bwd_dge(L, alpha=1e4) == 8
+    assert _bwd_dge(L, dY=None) == 1          # then the checks of lcvq_linear_bwd
+    assert _bwd_dge(L, d=2) == 3
+    assert _bwd_dge(L, ws=None) == 6
 
 
 def test_gemv_errors(L):

@@ -267,3 +267,31 @@ def test_graph_replay_matches_eager(P):
         junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
+
+
+@pytest.mark.parametrize("d,xdt,alpha", [(8, "bf16", 6.0), (4, "f32", 2.0), (16, "bf16", 20.0)])
+@pytest.mark.parametrize("M,N,K", [(300, 320, 192), (513, 576, 320)])
+def test_dge_backward(P, M, N, K, d, xdt, alpha):
+    """The DGE backward: dWp within tolerance of the oracle's DGE backward (including
+    proxies that are NaN, infinite or clamped); dX, dA and dB identical to the
+    straight-through backward's bytes."""
+    note(f"dge M={M} N={N} K={K} d={d} {xdt} alpha={alpha}")
+    inp = SI.make_layer(N, K, M, d, seed=M + N + K + 17, x_dtype=xdt, lo=-2.0, hi=5.0)
+    flat = inp["Wp"].view(-1)
+    flat[: len(SPECIAL)] = torch.tensor(SPECIAL, dtype=torch.float32)
+    X, Wp, A, B, dY = (inp[k].cuda() for k in ("X", "Wp", "A", "B", "dY"))
+    f = P.linear_fwd(X, Wp, A, B, d)
+    b = P.linear_bwd(dY, X, f["packed"], f["mask"], A, B, d, dge_wp=Wp, dge_alpha=alpha)
+    b0 = P.linear_bwd(dY, X, f["packed"], f["mask"], A, B, d)
+    torch.cuda.synchronize()
+    for k in ("dX", "dA", "dB"):
+        assert torch.equal(b[k], b0[k]), k
+    assert torch.isfinite(b["dWp"]).all()
+    wp = inp["Wp"].numpy()
+    Xh, dYh = host(inp["X"]), host(inp["dY"])
+    Ah, Bh = inp["A"].double().numpy(), inp["B"].double().numpy()
+    z, m = O.quantize(wp)
+    ob = O.linear_bwd(dYh, Xh, z, m, Ah, Bh, d, wp=wp, dge_alpha=alpha)
+    e = rel(host(b["dWp"]), ob["dWp"])
+    note(f"  dWp rel={e:.2e}")
+    assert e <= TOL
