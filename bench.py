@@ -244,6 +244,94 @@ def main():
             del pool
             torch.cuda.empty_cache()
 
+    # ------------------------------------------------- decode step of an 8B-shaped stack
+    # One token through all 7 projections of 32 layers (1.63 GiB of codes, far beyond the
+    # last-level cache), as 224 single calls and as 128 calls that group the matrices
+    # sharing an input (q, k, v and gate, up) into one launch each.
+    decode_stack = None
+    if not args.no_decode:
+        shapes = SI.CONFIGS["c4_stack_8b_layer"]["mats"]     # q, k, v, o, gate, up, down
+        layers = SI.CONFIGS["c4_stack_8b_layer"]["layers"]
+        dd = 8
+        gen = torch.Generator(device=dev).manual_seed(7000)
+        xs = {k: SI.make_act(1, k, seed=7100 + k, device=dev) for k in {k for _, k in shapes}}
+        A16, B16 = (t.half().to(dev) for t in SI.make_ab(dd, seed=7200))
+        mats = []
+        for _ in range(layers):
+            mats.append([(torch.randint(0, 256, (n, k // 4), generator=gen, dtype=torch.uint8,
+                                        device=dev),
+                          torch.empty((1, n), dtype=torch.bfloat16, device=dev), k)
+                         for n, k in shapes])
+        ws_s = torch.empty(P.lcvq_gemv2b_workspace_size(1, 14336, 14336, dd), dtype=torch.uint8,
+                           device=dev)
+        groups = [[0, 1, 2], [3], [4, 5], [6]]
+        total_bytes = layers * sum(n * k // 4 for n, k in shapes)
+
+        def run_single():
+            for lay in mats:
+                for pk, y, k in lay:
+                    P.lcvq_gemv2b(xs[k], pk, A16, B16, dd, y, ws_s)
+
+        def run_grouped():
+            for lay in mats:
+                for g in groups:
+                    k = lay[g[0]][2]
+                    if len(g) == 1:
+                        pk, y, _ = lay[g[0]]
+                        P.lcvq_gemv2b(xs[k], pk, A16, B16, dd, y, ws_s)
+                    else:
+                        P.lcvq_gemv2b_batched(xs[k], [(lay[i][0], A16, B16, lay[i][1]) for i in g],
+                                              dd, ws_s)
+
+        decode_stack = {"codes_bytes": total_bytes, "layers": layers, "tokens": 1}
+        for name, fn, calls in (("single", run_single, layers * 7),
+                                ("grouped", run_grouped, layers * len(groups))):
+            fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t_s = e0.elapsed_time(e1) / reps * 1e-3
+            # the same calls captured once in a HIP graph (no host work per call); the
+            # replayed outputs must equal the eager ones
+            ref = [y.clone() for lay in mats for _, y, _ in lay]
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            for lay in mats:
+                for _, y, _ in lay:
+                    y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            got = [y for lay in mats for _, y, _ in lay]
+            if not all(torch.equal(a_, b_) for a_, b_ in zip(ref, got)):
+                raise RuntimeError("decode graph replay differs from the eager calls")
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t_g = e0.elapsed_time(e1) / reps * 1e-3
+            del g
+            decode_stack[name] = {"calls": calls, "ms": round(t_s * 1e3, 3),
+                                  "gbs": round(total_bytes / t_s / 1e9, 1),
+                                  "frac": round(total_bytes / t_s / 1e9 / PEAK_HBM_GBS, 4),
+                                  "graph_ms": round(t_g * 1e3, 3),
+                                  "graph_gbs": round(total_bytes / t_g / 1e9, 1),
+                                  "graph_frac": round(total_bytes / t_g / 1e9 / PEAK_HBM_GBS, 4)}
+        del mats
+        torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- HBM copy ceiling
     # A plain device-to-device copy of 1 GiB: the streaming ceiling measured beside the
     # decode product, and the kernel of known size that scales the HBM byte counters.
@@ -316,6 +404,7 @@ def main():
                    "M": M, "N": N, "K": K, "d": d},
         "roofline": roofline,
         "decode": decode,
+        "decode_stack_8b": decode_stack,
         "hbm_copy_probe": copy_probe,
         "cpu_baseline": cpu,
     }

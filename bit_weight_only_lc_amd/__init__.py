@@ -6,7 +6,8 @@ declared in include/lcvq.h. All arithmetic runs in the library's HIP kernels; if
 library is missing the import of any entry point raises.
 
 Names follow the C ABI (lcvq_quantize, lcvq_pack2b, lcvq_unpack2b, lcvq_linear_fwd,
-lcvq_linear_bwd, lcvq_linear_bwd_dge, lcvq_gemv2b and the *_workspace_size helpers).
+lcvq_linear_bwd, lcvq_linear_bwd_dge, lcvq_gemv2b, lcvq_gemv2b_batched and the
+*_workspace_size helpers).
 """
 
 import ctypes
@@ -23,6 +24,12 @@ _STATUS = {0: "LCVQ_OK", 1: "LCVQ_ERR_NULL", 2: "LCVQ_ERR_SHAPE", 3: "LCVQ_ERR_D
            8: "LCVQ_ERR_VALUE"}
 
 _lib = None
+
+
+class GemvMatrix(ctypes.Structure):
+    """lcvq_gemv2b_matrix: one matrix of a batched decode product."""
+    _fields_ = [("packed", ctypes.c_void_p), ("A16", ctypes.c_void_p), ("B16", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("N", ctypes.c_int64)]
 
 
 class LcvqError(RuntimeError):
@@ -64,6 +71,9 @@ def lib():
             f = getattr(L, name)
             f.restype = sz
             f.argtypes = [i64, i64, i64, i32]
+        L.lcvq_gemv2b_batched.restype = i32
+        L.lcvq_gemv2b_batched.argtypes = [vp, i64, i64, i32, ctypes.POINTER(GemvMatrix), i32,
+                                          vp, sz, vp]
         L.lcvq_gemv2b_workspace_size.restype = sz
         L.lcvq_gemv2b_workspace_size.argtypes = [i64, i64, i64, i32]
         L.lcvq_profile_next.restype = i32
@@ -232,6 +242,29 @@ def lcvq_gemv2b(X, packed, A16, B16, d, Y, workspace=None):
     _check(workspace, "workspace", torch.uint8, dev)
     _ok(lib().lcvq_gemv2b(_p(X), M, N, K, d, _p(packed), _p(A16), _p(B16), _p(Y),
                           _p(workspace), workspace.numel(), _stream(dev)), "lcvq_gemv2b")
+
+
+def lcvq_gemv2b_batched(X, mats, d, workspace=None):
+    """mats: list of (packed, A16, B16, Y) sharing the input X."""
+    _check(X, "X", torch.bfloat16)
+    dev = X.device
+    M, K = X.shape
+    arr = (GemvMatrix * max(len(mats), 1))()
+    nmax = 16
+    for i, (pk, a16, b16, y) in enumerate(mats):
+        _check(pk, "packed", torch.uint8, dev)
+        _check(a16, "A16", torch.float16, dev)
+        _check(b16, "B16", torch.float16, dev)
+        _check(y, "Y", torch.bfloat16, dev)
+        arr[i] = GemvMatrix(pk.data_ptr(), a16.data_ptr(), b16.data_ptr(), y.data_ptr(),
+                            pk.shape[0])
+        nmax = max(nmax, pk.shape[0])
+    if workspace is None:
+        workspace = torch.empty(max(lcvq_gemv2b_workspace_size(M, nmax, K, d), 1),
+                                dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    _ok(lib().lcvq_gemv2b_batched(_p(X), M, K, d, arr, len(mats), _p(workspace),
+                                  workspace.numel(), _stream(dev)), "lcvq_gemv2b_batched")
 
 
 # ------------------------------------------------------------------ allocating helpers

@@ -25,6 +25,7 @@ constexpr int GEMV_FUSED_M = 2;     // up to this many tokens one fused kernel d
 // The fused path (X' formed in LDS by every workgroup) serves few tokens and K up to 64
 // blocks; otherwise a prologue kernel writes X' once and the product reads it.
 inline bool gemv_fused(int M, int K) { return M <= GEMV_FUSED_M && K / 256 <= 64; }
+bool gemv_fused_path(int M, int K) { return gemv_fused(M, K); }
 
 // X' limbs: each (block kb, MFMA step s, limb 0 = high / 1 = low, quarter kq, row m) is
 // a 16-byte chunk whose dword t, byte b holds column 64*kq + 16*s + 4*b + t of the block.
@@ -242,20 +243,27 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
 // time. Forming X' per workgroup repeats M * K * d multiply-adds that a separate
 // prologue would do once, but it overlaps the code stream and saves a kernel boundary
 // and the X' round trip through memory.
+// One launch can serve up to GEMV_MAX_BATCH matrices that share X (and K), each with its
+// own codes, A, B and output: workgroups [wg0[i], wg0[i+1]) belong to matrix i.
 constexpr int GWF = 8;
 
 template <int D, int RG, int KSW>
 __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restrict__ X,
-                                                         const uint16_t* __restrict__ A16,
-                                                         const uint16_t* __restrict__ B16,
-                                                         const uint8_t* __restrict__ packed,
-                                                         int M, int N, int K,
-                                                         uint16_t* __restrict__ Y) {
+                                                         GemvBatch batch, int M, int K) {
   extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int n0 = blockIdx.x * 16 * RG;
+  int mi = 0;
+#pragma unroll
+  for (int i = 1; i < GEMV_MAX_BATCH; ++i)
+    if (i < batch.count && (int)blockIdx.x >= batch.wg0[i]) mi = i;
+  const uint8_t* __restrict__ packed = batch.packed[mi];
+  const uint16_t* __restrict__ A16 = batch.A16[mi];
+  const uint16_t* __restrict__ B16 = batch.B16[mi];
+  uint16_t* __restrict__ Y = batch.Y[mi];
+  const int N = batch.N[mi];
+  const int n0 = ((int)blockIdx.x - batch.wg0[mi]) * 16 * RG;
   const int nl = lane & 15, kq = lane >> 4;
   const int nkb = K / GK;
   const int64_t rowb = K >> 2;
@@ -372,33 +380,53 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
 
 template <int D, int RG, int KSW>
 static void launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
-                         const uint16_t* A16, const uint16_t* B16, const uint8_t* packed, int M,
-                         int N, int K, uint16_t* Y) {
+                         const GemvBatch& b, int M, int K) {
   static bool attr = false;                        // LDS beyond 64 KiB must be requested
   if (!attr) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr = true;
   }
-  LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW>), grid, dim3(GWF * 64), shm, s, X, A16, B16,
-              packed, M, N, K, Y);
+  LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW>), grid, dim3(GWF * 64), shm, s, X, b, M, K);
 }
 
 template <int D>
-static void launch_fused_d(int M, int N, int K, bool two, size_t shm, hipStream_t s,
-                           const uint16_t* X, const uint16_t* A16, const uint16_t* B16,
-                           const uint8_t* packed, uint16_t* Y) {
+static void launch_fused_d(int M, int K, bool two, size_t shm, hipStream_t s, const uint16_t* X,
+                           const GemvBatch& b, int wgs) {
   const int pw = (K / GK + GWF - 1) / GWF;
-  const dim3 grid(two ? (N + 31) / 32 : N / 16);
+  const dim3 grid(wgs);
   if (two) {
-    if (pw <= 2) launch_fused<D, 2, 2>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
-    else if (pw <= 4) launch_fused<D, 2, 4>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
-    else launch_fused<D, 2, 8>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+    if (pw <= 2) launch_fused<D, 2, 2>(grid, shm, s, X, b, M, K);
+    else if (pw <= 4) launch_fused<D, 2, 4>(grid, shm, s, X, b, M, K);
+    else launch_fused<D, 2, 8>(grid, shm, s, X, b, M, K);
   } else {
-    if (pw <= 2) launch_fused<D, 1, 2>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
-    else if (pw <= 4) launch_fused<D, 1, 4>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
-    else launch_fused<D, 1, 8>(grid, shm, s, X, A16, B16, packed, M, N, K, Y);
+    if (pw <= 2) launch_fused<D, 1, 2>(grid, shm, s, X, b, M, K);
+    else if (pw <= 4) launch_fused<D, 1, 4>(grid, shm, s, X, b, M, K);
+    else launch_fused<D, 1, 8>(grid, shm, s, X, b, M, K);
   }
+}
+
+// One fused launch over the matrices of `b` (count, packed, A16, B16, Y, N filled in).
+hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b,
+                             hipStream_t s) {
+  int64_t rows = 0;
+  for (int i = 0; i < b.count; ++i) rows += b.N[i];
+  // Two row groups per workgroup when the rows still give a workgroup per CU.
+  const bool two = rows >= 2 * 16 * 256;
+  int wgs = 0;
+  for (int i = 0; i < b.count; ++i) {
+    b.wg0[i] = wgs;
+    wgs += two ? (b.N[i] + 31) / 32 : b.N[i] / 16;
+  }
+  const int nkb = K / GK;
+  const size_t base = (size_t)nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
+  const size_t shm = std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
+  switch (d) {
+    case 4: launch_fused_d<4>(M, K, two, shm, s, X, b, wgs); break;
+    case 8: launch_fused_d<8>(M, K, two, shm, s, X, b, wgs); break;
+    default: launch_fused_d<16>(M, K, two, shm, s, X, b, wgs); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,
@@ -408,14 +436,10 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
   // Two row groups per workgroup when N still gives a workgroup per CU.
   const bool two = N >= 2 * 16 * 256;
   if (gemv_fused(M, K)) {
-    const size_t base = (size_t)nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
-    const size_t shm = std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
-    switch (d) {
-      case 4: launch_fused_d<4>(M, N, K, two, shm, s, X, A16, B16, packed, Y); break;
-      case 8: launch_fused_d<8>(M, N, K, two, shm, s, X, A16, B16, packed, Y); break;
-      default: launch_fused_d<16>(M, N, K, two, shm, s, X, A16, B16, packed, Y); break;
-    }
-    return hipGetLastError();
+    GemvBatch b = {};
+    b.count = 1;
+    b.packed[0] = packed; b.A16[0] = A16; b.B16[0] = B16; b.Y[0] = Y; b.N[0] = N;
+    return launch_gemv_fused(X, M, K, d, b, s);
   }
   float2* ri = reinterpret_cast<float2*>(rowinfo);
   const dim3 pgrid(nkb), pblock(256);

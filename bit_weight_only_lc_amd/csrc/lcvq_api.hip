@@ -295,4 +295,52 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
                               static_cast<uint16_t*>(Y), xq, rowinfo, s));
 }
 
+lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
+                                  const lcvq_gemv2b_matrix* mats, int count, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!X || !mats) return LCVQ_ERR_NULL;
+  if (!d_ok(d)) return LCVQ_ERR_D;
+  if (count < 1 || count > GEMV_MAX_BATCH) return LCVQ_ERR_SHAPE;
+  if (M < 1 || M > 16 || K < 256 || (K % 256) || K > INT32_MAX) return LCVQ_ERR_SHAPE;
+  int64_t nmax = 0, groups = 0;
+  for (int i = 0; i < count; ++i) {
+    const lcvq_gemv2b_matrix& m = mats[i];
+    if (!m.packed || !m.A16 || !m.B16 || !m.Y) return LCVQ_ERR_NULL;
+    if (m.N < 16 || (m.N % 16) || m.N > INT32_MAX || m.N * K >= (int64_t(1) << 40))
+      return LCVQ_ERR_SHAPE;
+    if (!aligned16(m.packed) || !aligned16(m.A16) || !aligned16(m.B16) || !aligned16(m.Y))
+      return LCVQ_ERR_ALIGN;
+    nmax = m.N > nmax ? m.N : nmax;
+    groups += m.N / 16;
+  }
+  if (groups > INT32_MAX) return LCVQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(workspace)) return LCVQ_ERR_ALIGN;
+  const GemvWs w = gemv_ws(K);
+  if (!workspace || workspace_bytes < w.total) return LCVQ_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  if (gemv_fused_path((int)M, (int)K)) {
+    GemvBatch b = {};
+    b.count = count;
+    for (int i = 0; i < count; ++i) {
+      b.packed[i] = mats[i].packed;
+      b.A16[i] = static_cast<const uint16_t*>(mats[i].A16);
+      b.B16[i] = static_cast<const uint16_t*>(mats[i].B16);
+      b.Y[i] = static_cast<uint16_t*>(mats[i].Y);
+      b.N[i] = (int)mats[i].N;
+    }
+    return from_hip(launch_gemv_fused(static_cast<const uint16_t*>(X), (int)M, (int)K, d, b, s));
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  for (int i = 0; i < count; ++i) {
+    const hipError_t e = launch_gemv(static_cast<const uint16_t*>(X), (int)M, (int)mats[i].N,
+                                     (int)K, static_cast<const uint16_t*>(mats[i].A16),
+                                     static_cast<const uint16_t*>(mats[i].B16), d,
+                                     mats[i].packed, static_cast<uint16_t*>(mats[i].Y),
+                                     reinterpret_cast<int8_t*>(ws + w.xq),
+                                     reinterpret_cast<float*>(ws + w.rowinfo), s);
+    if (e != hipSuccess) return LCVQ_ERR_HIP;
+  }
+  return LCVQ_OK;
+}
+
 }  // extern "C"

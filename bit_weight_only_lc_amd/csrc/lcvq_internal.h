@@ -67,6 +67,22 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
                           float* partials, float* dA, float* dB, const float* dge_wp,
                           float dge_alpha, hipStream_t s);
 
+// Matrices that share X for one fused decode launch (kernel argument, by value).
+constexpr int GEMV_MAX_BATCH = 8;
+struct GemvBatch {
+  const uint8_t* packed[GEMV_MAX_BATCH];
+  const uint16_t* A16[GEMV_MAX_BATCH];
+  const uint16_t* B16[GEMV_MAX_BATCH];
+  uint16_t* Y[GEMV_MAX_BATCH];
+  int N[GEMV_MAX_BATCH];
+  int wg0[GEMV_MAX_BATCH];     // first workgroup of each matrix (set by the launcher)
+  int count;
+};
+// True when the fused single-launch path serves M tokens at this K.
+bool gemv_fused_path(int M, int K);
+hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b,
+                             hipStream_t s);
+
 // Decode product. Few tokens: one fused kernel (xq and rowinfo unused); otherwise a
 // prologue writes X' limbs to xq and block scales to rowinfo, and the product reads them.
 hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,

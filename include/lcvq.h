@@ -166,6 +166,31 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode product of several matrices that share the input X (and K), for instance the
+ * q, k and v projections, or gate and up, of one transformer layer; each matrix has its
+ * own codes and its own A, B (LC-QAT summary, Methodology 1: A and B are shared within
+ * one weight matrix). Every output equals what lcvq_gemv2b gives for that matrix, byte
+ * for byte. With M <= 2 and K <= 16384 all of them run in one launch; otherwise one
+ * matrix after the other, on `stream`.
+ *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 256
+ *   mats    host array of `count` descriptors, 1 <= count <= 8; mats[i].N a multiple of
+ *           16; packed uint8 [N, K/4], A16 float16 [d, d], B16 float16 [d] and the output
+ *           Y bfloat16 [M, N] are device pointers; outputs must not overlap anything
+ *   workspace >= lcvq_gemv2b_workspace_size(M, largest N, K, d) bytes
+ * Errors as for lcvq_gemv2b; LCVQ_ERR_SHAPE also for count outside 1..8.
+ */
+typedef struct {
+  const uint8_t* packed;
+  const void* A16;
+  const void* B16;
+  void* Y;
+  int64_t N;
+} lcvq_gemv2b_matrix;
+lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
+                                  const lcvq_gemv2b_matrix* mats, int count, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Profiling hook (changes no result). Arms a one-shot timing of the next launch of one
  * kernel by calls made from this host thread: the kernel is launched with
  * hipExtLaunchKernel between `start_event` and `stop_event` (hipEvent_t handles created

@@ -153,6 +153,31 @@ def test_gemv_errors(L):
     assert L.lcvq_gemv2b_workspace_size(1, 40, 256, 8) == 0
 
 
+def test_gemv_batched_errors(L):
+    import bit_weight_only_lc_amd as PK
+    mats = (PK.GemvMatrix * 9)(*[PK.GemvMatrix(P, P, P, P, 256) for _ in range(9)])
+    ws = L.lcvq_gemv2b_workspace_size(1, 256, 256, 8)
+
+    def g(X=P, M=1, K=256, d=8, m=mats, count=3, wsp=P, wsb=ws):
+        return L.lcvq_gemv2b_batched(X, M, K, d, m, count, wsp, wsb, None)
+    assert g(X=None) == 1
+    assert g(m=None) == 1
+    assert g(count=0) == 2
+    assert g(count=9) == 2
+    assert g(M=17) == 2
+    assert g(K=320) == 2
+    assert g(d=5) == 3
+    assert g(wsb=ws - 1) == 6
+    mats[1].N = 40
+    assert g() == 2
+    mats[1].N = 256
+    mats[2].Y = MIS
+    assert g() == 5
+    mats[2].Y = P
+    mats[0].packed = None
+    assert g() == 1
+
+
 def test_workspace_sizes_grow_with_shape(L):
     a = L.lcvq_linear_fwd_workspace_size(64, 256, 256, 8)
     b = L.lcvq_linear_fwd_workspace_size(4096, 4096, 4096, 8)

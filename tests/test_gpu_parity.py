@@ -295,3 +295,30 @@ def test_dge_backward(P, M, N, K, d, xdt, alpha):
     e = rel(host(b["dWp"]), ob["dWp"])
     note(f"  dWp rel={e:.2e}")
     assert e <= TOL
+
+
+@pytest.mark.parametrize("shapes,K", [([4096, 1024, 1024], 4096), ([14336, 14336], 4096),
+                                      ([8192, 272], 256), ([4096], 14336)])
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_gemv_batched(P, shapes, K, M):
+    """Several matrices sharing X in one call: every output equals the single-matrix
+    call's bytes and the oracle's product."""
+    d = 8
+    note(f"gemv batched N={shapes} K={K} M={M}")
+    X = SI.make_act(M, K, seed=6100 + M, device="cuda")
+    mats, singles, refs = [], [], []
+    for i, n in enumerate(shapes):
+        g = torch.Generator(device="cuda").manual_seed(6200 + i)
+        pk = torch.randint(0, 256, (n, K // 4), generator=g, dtype=torch.uint8, device="cuda")
+        A, B = SI.make_ab(d, seed=6300 + i)
+        A16, B16 = A.half().cuda(), B.half().cuda()
+        Y = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
+        mats.append((pk, A16, B16, Y))
+        singles.append(P.gemv2b(X, pk, A16, B16, d))
+        refs.append((pk, A.half().double().numpy(), B.half().double().numpy()))
+    P.lcvq_gemv2b_batched(X, mats, d)
+    torch.cuda.synchronize()
+    for (pk, _, _, Y), ys, (pkr, Ah, Bh) in zip(mats, singles, refs):
+        assert torch.equal(Y, ys)
+        e = rel(host(Y), O.gemv2b(host(X), host(pkr), Ah, Bh, d))
+        assert e <= TOL, e
