@@ -514,11 +514,26 @@ __device__ __forceinline__ void issue_ring_stage(uint8_t* slot, const uint16_t* 
 __device__ __forceinline__ uint32_t codes_word(const uint8_t* ctile, int row, int s) {
   return *reinterpret_cast<const uint32_t*>(ctile + row * 16 + (((s + (row >> 3)) & 3) << 2));
 }
-__device__ __forceinline__ bf16x8 codes_expand(uint32_t w, int h) {
-  const uint32_t src = h ? __builtin_amdgcn_alignbit(w, w, 8) : w;
+// Expansion constants held in registers: gfx950's three-operand encodings take no 32-bit
+// literal and at most one scalar operand, so with the mask in a scalar register and the
+// exponent bits in a vector register each dword is one shift and one v_and_or_b32.
+struct ExpandK {
+  uint32_t mask;   // 0x00600060, scalar
+  uint32_t one;    // 0x40004000, vector
+  uint32_t rot;    // 8 for lanes 32..63 (second half of the word), else 0
+};
+__device__ __forceinline__ ExpandK expand_consts(int lane) {
+  ExpandK k;
+  asm volatile("s_mov_b32 %0, 0x600060" : "=s"(k.mask));
+  asm volatile("v_mov_b32 %0, 0x40004000" : "=v"(k.one));
+  k.rot = (uint32_t)(lane >> 5) << 3;
+  return k;
+}
+__device__ __forceinline__ bf16x8 codes_expand(uint32_t w, const ExpandK& k) {
+  const uint32_t src = __builtin_amdgcn_alignbit(w, w, k.rot);
   u32x4 o;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) o[p] = ((src >> (2 * p)) & 0x00600060u) | 0x40004000u;
+  for (int p = 0; p < 4; ++p) o[p] = ((src >> (2 * p)) & k.mask) | k.one;
   return __builtin_bit_cast(bf16x8, o);
 }
 
@@ -550,9 +565,9 @@ __device__ __forceinline__ void ring_read(const uint8_t* slot, int s, int wp, in
 }
 
 template <bool CODES_ARE_L, int WI, int WJ>
-__device__ __forceinline__ void ring_expand(RingFrags<CODES_ARE_L, WI, WJ>& f, int lane) {
+__device__ __forceinline__ void ring_expand(RingFrags<CODES_ARE_L, WI, WJ>& f, const ExpandK& k) {
 #pragma unroll
-  for (int i = 0; i < RingFrags<CODES_ARE_L, WI, WJ>::NC; ++i) f.c[i] = codes_expand(f.w[i], lane >> 5);
+  for (int i = 0; i < RingFrags<CODES_ARE_L, WI, WJ>::NC; ++i) f.c[i] = codes_expand(f.w[i], k);
 }
 
 template <bool CODES_ARE_L, int WI, int WJ>
@@ -560,8 +575,9 @@ __device__ __forceinline__ void mma_ring_stage(const uint8_t* slot, f32x16 acc[W
                                                int wq, int lane) {
   using F = RingFrags<CODES_ARE_L, WI, WJ>;
   F f[2];
+  const ExpandK ek = expand_consts(lane);
   ring_read<CODES_ARE_L, WI, WJ>(slot, 0, wp, wq, lane, f[0]);
-  ring_expand<CODES_ARE_L, WI, WJ>(f[0], lane);
+  ring_expand<CODES_ARE_L, WI, WJ>(f[0], ek);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int c = s & 1;
@@ -578,7 +594,7 @@ __device__ __forceinline__ void mma_ring_stage(const uint8_t* slot, f32x16 acc[W
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
       }
     if (s < 3) {
-      ring_expand<CODES_ARE_L, WI, WJ>(f[c ^ 1], lane);
+      ring_expand<CODES_ARE_L, WI, WJ>(f[c ^ 1], ek);
       constexpr int NV = (F::NC * 10 + WI * WJ - 1) / (WI * WJ);  // VALU per MFMA slot
 #pragma unroll
       for (int g = 0; g < WI * WJ; ++g) {
