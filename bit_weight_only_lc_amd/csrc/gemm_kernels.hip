@@ -356,6 +356,13 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
 //   dA[i][j] += G[g*d+i, n] z[n, g*d+j],   dB[i] += G[g*d+i, n]
 // Per-lane partial sums are reduced over the wave through LDS, then over the waves,
 // in a fixed order, into this tile's slot of `partials`.
+// dW LDS map: the double buffer (2 x 64 KiB) during the main loop, then per-wave
+// epilogue areas below 128 KiB; the tile's codes (256 columns n x 64 bytes) and mask bits
+// (256 x 32 bytes) live above it from kernel start, for the straight-through epilogue.
+constexpr int DW_CODES_OFF = 128 * 1024;
+constexpr int DW_MASK_OFF = DW_CODES_OFF + 256 * 64;    // 144 KiB
+constexpr int DW_SMEM = DW_MASK_OFF + 256 * 32;         // 152 KiB
+
 template <int D, int NW, int WJ>
 __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
                             int lane, int wave, int tile, uint8_t* smem, const float* Alds) {
@@ -401,8 +408,9 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
           // they must not reach dA or dB.
           const bool valid = n < a.N && kv < a.K;
           if (valid) {
-            const uint8_t* zp = a.packed + (int64_t)n * (a.K >> 2) + (kv >> 2);
-            const uint8_t* mp = a.mask + (int64_t)n * (a.K >> 3) + (kv >> 3);
+            // the tile's codes and mask bits were brought into LDS at kernel start
+            const uint8_t* zp = smem + DW_CODES_OFF + (n - q0) * 64 + ((kv - p0) >> 2);
+            const uint8_t* mp = smem + DW_MASK_OFF + (n - q0) * 32 + ((kv - p0) >> 3);
             if (D == 4) { zw = zp[0]; mw = (mp[0] >> (kv & 4)) & 0xFu; }
             if (D == 8) { zw = *reinterpret_cast<const uint16_t*>(zp); mw = mp[0]; }
             if (D == 16) { zw = *reinterpret_cast<const uint32_t*>(zp); mw = *reinterpret_cast<const uint16_t*>(mp); }
@@ -787,18 +795,47 @@ __device__ __forceinline__ void mma_dw_stage(const uint8_t* slot, f32x16 acc[4][
   }
 }
 
+// Codes: 16-byte direct loads, 2 per lane; mask: 4-byte direct loads (mask rows are only
+// 8-byte aligned), 4 per lane. Columns past N and k past K read a valid address; those
+// entries are never used.
+__device__ __forceinline__ void issue_dw_codes(uint8_t* smem, const uint8_t* packed,
+                                               const uint8_t* mask, int N, int K, int p0,
+                                               int q0, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = (wave * 2 + i) * 64 + lane;            // 16-byte chunk of the code tile
+    int n = q0 + (c >> 2);
+    n = n < N ? n : N - 1;
+    int kb = p0 + (c & 3) * 64;
+    kb = kb < K ? kb : 0;
+    const uint8_t* src = packed + (int64_t)n * (K >> 2) + (kb >> 2);
+    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(smem + DW_CODES_OFF + (wave * 2 + i) * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = (wave * 4 + i) * 64 + lane;            // 4-byte word of the mask tile
+    int n = q0 + (c >> 3);
+    n = n < N ? n : N - 1;
+    int kb = p0 + (c & 7) * 32;
+    kb = kb < K ? kb : 0;
+    const uint8_t* src = mask + (int64_t)n * (K >> 3) + (kb >> 3);
+    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(smem + DW_MASK_OFF + (wave * 4 + i) * 256), 4, 0, 0);
+  }
+}
+
 // dW: 8 waves (512 threads), double-buffered direct loads into LDS (2 x 64 KiB).
 template <int D>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_dw(GemmArgs a) {
   constexpr int NW = 8, WGQ = 4, WJ = 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * TTILEB];   // 128 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DW_SMEM];   // 152 KiB
   int tp, tq, tile;
   if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wp = wave / WGQ, wq = wave % WGQ;
   const int nk = (a.R + BK - 1) / BK;
+  issue_dw_codes(smem, a.packed, a.mask, a.N, a.K, p0, q0, wave, lane);
 
   f32x16 acc[4][WJ];
 #pragma unroll
