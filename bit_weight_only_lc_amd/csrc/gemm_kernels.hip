@@ -302,11 +302,90 @@ __device__ __forceinline__ void store_block_rows_dge(const float* S, float* out,
   }
 }
 
+// Forward epilogue: Y[p, q] = C[p, q] + beta[p]. Each 32-row strip of the wave's
+// 32 x 32*WJ sub-tile is staged row-major through the wave's LDS area (the ring is
+// free by now), then written with 16-byte stores, so that every store instruction
+// covers whole 32*WJ-element runs of 16 / WJ output rows.
+template <int NW, int WI, int WJ>
+__device__ void epilogue_fwd(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp,
+                             int wq, int lane, int wave, uint8_t* smem) {
+  constexpr int CW = 32 * WJ, SR = CW + 4;             // strip width, padded LDS row
+  constexpr int LPR = CW / 8, RPI = 64 / LPR;          // lanes per row, rows per store
+  static_assert(NW * 32 * SR * 4 <= 144 * 1024, "forward staging area");
+  float* S = reinterpret_cast<float*>(smem) + wave * 32 * SR;
+  const int col = lane & 31, h = lane >> 5;
+  const int qb = q0 + wq * CW, c8 = (lane % LPR) * 8, q = qb + c8;
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int pb = p0 + wp * 32 * WI + i * 32;
+    wave_sync();
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        S[(8 * (r >> 2) + 4 * h + (r & 3)) * SR + j * 32 + col] = acc[i][j][r];
+    wave_sync();
+#pragma unroll
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int rr = it * RPI + lane / LPR, p = pb + rr;
+      if (p < a.M && q < a.N) {
+        const float b = a.rowvec[p];
+        const f32x4 x = *reinterpret_cast<const f32x4*>(S + rr * SR + c8);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(S + rr * SR + c8 + 4);
+        const int64_t idx = (int64_t)p * a.N + q;
+        if (a.out_f32) {
+          float* o = static_cast<float*>(a.out) + idx;
+          *reinterpret_cast<f32x4*>(o) = x + b;
+          *reinterpret_cast<f32x4*>(o + 4) = y + b;
+        } else {
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + idx) =
+              make_uint4(pack_bf16x2(x[0] + b, x[1] + b), pack_bf16x2(x[2] + b, x[3] + b),
+                         pack_bf16x2(y[0] + b, y[1] + b), pack_bf16x2(y[2] + b, y[3] + b));
+        }
+      }
+    }
+  }
+}
+
+// Writes a staged 64 x 32 area (rows = contraction-side index k, columns = output row)
+// transposed to out[row][k0 .. k0+63] (row stride ld elements), float32 or bf16: each
+// group of 8 lanes covers the 64 consecutive k of one output row, 8 per lane.
+__device__ __forceinline__ void store_block_rows64(const float* S, void* out, int f32,
+                                                   int64_t ld, int row0, int rows, int k0,
+                                                   int K, int lane) {
+  const int kq = (lane & 7) * 8;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int rr = it * 8 + (lane >> 3);
+    const int row = row0 + rr;
+    if (row < rows && k0 + kq < K) {
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = S[(kq + e) * SROW + rr];
+      const int64_t idx = (int64_t)row * ld + k0 + kq;
+      if (f32) {
+        float* o = static_cast<float*>(out) + idx;
+        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + idx) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      }
+    }
+  }
+}
+
 // dX[m, g*d+i] = 2 sum_j A[i][j] C[g*d+j, m] + (B[i] - 4 sum_j A[i][j]) r[m]
 // where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m).
+// Blocks are taken in pairs along k, so that each output row receives 128 contiguous
+// bytes (bf16) per store instruction.
+constexpr int DX_WAVE_LDS = 64 * SROW * 4;   // per-wave staging area: 64 x 33 floats
+
 template <int D, int WI, int WJ>
 __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp, int wq,
                             int lane, float* S, const float* Alds) {
+  static_assert(WI % 2 == 0, "k blocks are staged in pairs");
   float bp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -316,25 +395,24 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
     bp[i] = a.B[i] - 4.f * s;
   }
   const int q = lane & 31;
-  // j outer: the blocks i of one j cover consecutive 64-byte halves of the same output
-  // lines, so each line is completed while it is still in the L2.
 #pragma unroll
   for (int j = 0; j < WJ; ++j)
 #pragma unroll
-    for (int i = 0; i < WI; ++i) {
-      const int kb = p0 + wp * 32 * WI + i * 32;
+    for (int i2 = 0; i2 < WI / 2; ++i2) {
+      const int kb = p0 + wp * 32 * WI + i2 * 64;
       const int mb = q0 + wq * 32 * WJ + j * 32;
       wave_sync();
-      stage_block(S, acc[i][j], lane);
+      stage_block(S, acc[2 * i2][j], lane);
+      stage_block(S + 32 * SROW, acc[2 * i2 + 1][j], lane);
       wave_sync();
       const int m = mb + q;
       const float rm = m < a.M ? a.rowvec[m] : 0.f;
-      // Re-read A from the scalar cache for every block instead of keeping d*d values
-      // live across the unrolled block sequence.
+      // Re-read A from the scalar cache for every block pair instead of keeping d*d
+      // values live across the unrolled sequence.
       const float* Ab = D == 16 ? Alds : a.A;
       if (D == 16) asm volatile("" : "+v"(Ab));
       else asm volatile("" : "+s"(Ab));
-      for (int sl = lane >> 5; sl < 32 / D; sl += 2) {
+      for (int sl = lane >> 5; sl < 64 / D; sl += 2) {
         float T[D];
 #pragma unroll
         for (int e = 0; e < D; ++e) T[e] = S[(sl * D + e) * SROW + q];
@@ -347,7 +425,7 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
         }
       }
       wave_sync();
-      store_block_rows(S, a.out, a.out_f32, a.K, mb, a.M, kb, a.K, lane);
+      store_block_rows64(S, a.out, a.out_f32, a.K, mb, a.M, kb, a.K, lane);
     }
 }
 
@@ -680,30 +758,18 @@ void k_gemm_ring(GemmArgs a) {
   }
 
   if (OP == OP_FWD) {
-#pragma unroll
-    for (int i = 0; i < WI; ++i)
-#pragma unroll
-      for (int j = 0; j < WJ; ++j) {
-        const int q = q0 + wq * 32 * WJ + j * 32 + (lane & 31);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int p = p0 + wp * 32 * WI + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (p < a.M && q < a.N) {
-            const float v = acc[i][j][r] + a.rowvec[p];
-            if (a.out_f32) static_cast<float*>(a.out)[(int64_t)p * a.N + q] = v;
-            else static_cast<__bf16*>(a.out)[(int64_t)p * a.N + q] = (__bf16)v;
-          }
-        }
-      }
+    epilogue_fwd<NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, wave, smem);
   } else {
-    // The ring is free after the last barrier: per-wave staging areas of 4.5 KiB, and
+    // The ring is free after the last barrier: per-wave staging areas of 8.25 KiB, and
     // for d = 16 a copy of A at 120 KiB.
     float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
     if (D == 16) {
       if (tid < D * D) Alds[tid] = a.A[tid];
       __syncthreads();
     }
-    epilogue_dx<D, WI, WJ>(a, acc, p0, q0, wp, wq, lane, reinterpret_cast<float*>(smem + wave * 4608), Alds);
+    static_assert(NW * DX_WAVE_LDS <= 120 * 1024, "dX staging below the copy of A");
+    epilogue_dx<D, WI, WJ>(a, acc, p0, q0, wp, wq, lane,
+                           reinterpret_cast<float*>(smem + wave * DX_WAVE_LDS), Alds);
   }
 }
 
