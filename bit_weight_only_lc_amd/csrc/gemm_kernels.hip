@@ -376,16 +376,51 @@ __device__ __forceinline__ void store_block_rows64(const float* S, void* out, in
   }
 }
 
+// Whole d-vectors per lane. In a 32x32 accumulator block, lane (column l%32, half
+// h = l/32) holds rows 8*(r/4) + 4h + r%4 in register r: for d = 4 these are complete
+// d-vectors already, for d = 8 and 16 each vector is split between lanes l and l^32.
+// Swapping registers 0..7 of the upper half with registers 8..15 of the lower half
+// (v_permlane32_swap: the first operand's lanes 32..63 trade places with the second
+// operand's lanes 0..31) leaves every lane with whole vectors: d = 8, vectors 2h and
+// 2h+1; d = 16, vector h. Element e of local vector v then sits in register
+// 4*bsel + e%4 with bsel as in dvec_reg.
+template <int D>
+__device__ __forceinline__ void gather_dvectors(f32x16& c) {
+  if (D == 4) return;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[r]),
+                                                    __float_as_uint(c[r + 8]), false, false);
+    c[r] = __uint_as_float(s[0]);
+    c[r + 8] = __uint_as_float(s[1]);
+  }
+}
+template <int D>
+__host__ __device__ constexpr int dvec_reg(int v, int e) {
+  const int j = e >> 2;
+  const int bsel = D == 4 ? v : D == 8 ? (j << 1) | v : ((j & 1) << 1) | (j >> 1);
+  return 4 * bsel + (e & 3);
+}
+// Row (index k within the block) of element e of local vector v in lane half h.
+template <int D>
+__device__ __forceinline__ int dvec_row(int v, int e, int h) {
+  const int g = D == 4 ? 2 * v + h : D == 8 ? 2 * h + v : h;
+  return g * D + e;
+}
+
 // dX[m, g*d+i] = 2 sum_j A[i][j] C[g*d+j, m] + (B[i] - 4 sum_j A[i][j]) r[m]
 // where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m).
-// Blocks are taken in pairs along k, so that each output row receives 128 contiguous
-// bytes (bf16) per store instruction.
+// The d x d product runs on whole vectors in registers (gather_dvectors); the results
+// go through the wave's LDS area only for the transposed store. Blocks are taken in
+// pairs along k, so that each output row receives 128 contiguous bytes (bf16) per
+// store instruction.
 constexpr int DX_WAVE_LDS = 64 * SROW * 4;   // per-wave staging area: 64 x 33 floats
 
 template <int D, int WI, int WJ>
 __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp, int wq,
                             int lane, float* S, const float* Alds) {
   static_assert(WI % 2 == 0, "k blocks are staged in pairs");
+  constexpr int NV = 16 / D;                  // whole vectors per lane and block
   float bp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -394,35 +429,42 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
     for (int j = 0; j < D; ++j) s += a.A[i * D + j];
     bp[i] = a.B[i] - 4.f * s;
   }
-  const int q = lane & 31;
+  const int q = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int j = 0; j < WJ; ++j)
 #pragma unroll
     for (int i2 = 0; i2 < WI / 2; ++i2) {
       const int kb = p0 + wp * 32 * WI + i2 * 64;
       const int mb = q0 + wq * 32 * WJ + j * 32;
-      wave_sync();
-      stage_block(S, acc[2 * i2][j], lane);
-      stage_block(S + 32 * SROW, acc[2 * i2 + 1][j], lane);
-      wave_sync();
       const int m = mb + q;
       const float rm = m < a.M ? a.rowvec[m] : 0.f;
-      // Re-read A from the scalar cache for every block pair instead of keeping d*d
-      // values live across the unrolled sequence.
-      const float* Ab = D == 16 ? Alds : a.A;
-      if (D == 16) asm volatile("" : "+v"(Ab));
-      else asm volatile("" : "+s"(Ab));
-      for (int sl = lane >> 5; sl < 64 / D; sl += 2) {
-        float T[D];
+      // Re-read A for every block pair instead of keeping d*d values live across the
+      // unrolled sequence: d <= 8 through a constant-address-space pointer, so that the
+      // reads are scalar loads from the scalar cache (through a generic pointer they would
+      // be vector loads, each waited for); d = 16 from the copy in LDS.
+      const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
+      const LCVQ_LDS float* Al = (const LCVQ_LDS float*)Alds;
+      if constexpr (D == 16) asm volatile("" : "+v"(Al));
+      else asm volatile("" : "+s"(Ac));
+      auto Aat = [&](int idx) -> float {
+        if constexpr (D == 16) return Al[idx];
+        else return Ac[idx];
+      };
+      wave_sync();
 #pragma unroll
-        for (int e = 0; e < D; ++e) T[e] = S[(sl * D + e) * SROW + q];
+      for (int half = 0; half < 2; ++half) {
+        f32x16& c = acc[2 * i2 + half][j];
+        gather_dvectors<D>(c);
+        float* Sh = S + half * 32 * SROW;
 #pragma unroll
-        for (int ii = 0; ii < D; ++ii) {
-          float s = 0.f;
+        for (int v = 0; v < NV; ++v)
 #pragma unroll
-          for (int e = 0; e < D; ++e) s = __builtin_fmaf(Ab[ii * D + e], T[e], s);
-          S[(sl * D + ii) * SROW + q] = __builtin_fmaf(2.f, s, bp[ii] * rm);
-        }
+          for (int ii = 0; ii < D; ++ii) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < D; ++e) s = __builtin_fmaf(Aat(ii * D + e), c[dvec_reg<D>(v, e)], s);
+            Sh[dvec_row<D>(v, ii, h) * SROW + q] = __builtin_fmaf(2.f, s, bp[ii] * rm);
+          }
       }
       wave_sync();
       store_block_rows64(S, a.out, a.out_f32, a.K, mb, a.M, kb, a.K, lane);
@@ -473,9 +515,15 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
         stage_block(S, acc[i][j], lane);
         wave_sync();
         const int n = nb + q;
-        const float* Ab = D == 16 ? Alds : a.A;
-        if (D == 16) asm volatile("" : "+v"(Ab));
-        else asm volatile("" : "+s"(Ab));
+        // A: scalar loads through a constant-address-space pointer (d = 16: LDS copy).
+        const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
+        const LCVQ_LDS float* Al = (const LCVQ_LDS float*)Alds;
+        if constexpr (D == 16) asm volatile("" : "+v"(Al));
+        else asm volatile("" : "+s"(Ac));
+        auto Aat = [&](int idx) -> float {
+          if constexpr (D == 16) return Al[idx];
+          else return Ac[idx];
+        };
         for (int sl = lane >> 5; sl < 32 / D; sl += 2) {
           const int kv = kb + sl * D;
           float T[D];
@@ -498,7 +546,7 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
             for (int jj = 0; jj < D; ++jj) {
               float sum = 0.f;
 #pragma unroll
-              for (int e = 0; e < D; ++e) sum = __builtin_fmaf(Ab[e * D + jj], T[e], sum);
+              for (int e = 0; e < D; ++e) sum = __builtin_fmaf(Aat(e * D + jj), T[e], sum);
               S[(sl * D + jj) * SROW + q] = ((mw >> jj) & 1u) ? sum : 0.f;
             }
 #pragma unroll

@@ -13,6 +13,8 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define LCVQ_LDS __attribute__((address_space(3)))
+// Constant address space: uniform reads through such a pointer become scalar loads.
+#define LCVQ_CONST __attribute__((address_space(4)))
 
 // Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
