@@ -496,7 +496,7 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
   float* S = reinterpret_cast<float*>(smem + wave * WREG);
   float* red = S;                              // reused after the blocks of a pass
   float* wsum = reinterpret_cast<float*>(smem + NW * WREG);      // [NP][NW][NR]
-  const int q = lane & 31;
+  const int q = lane & 31, h = lane >> 5;
   float dB[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) dB[e] = 0.f;
@@ -511,9 +511,6 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
       for (int j = 0; j < WJ; ++j) {
         const int kb = p0 + wp * 128 + i * 32;
         const int nb = q0 + wq * 32 * WJ + j * 32;
-        wave_sync();
-        stage_block(S, acc[i][j], lane);
-        wave_sync();
         const int n = nb + q;
         // A: scalar loads through a constant-address-space pointer (d = 16: LDS copy).
         const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
@@ -524,30 +521,40 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
           if constexpr (D == 16) return Al[idx];
           else return Ac[idx];
         };
-        for (int sl = lane >> 5; sl < 32 / D; sl += 2) {
-          const int kv = kb + sl * D;
+        f32x16& c = acc[i][j];
+        __builtin_amdgcn_sched_barrier(0);   // keep each block's work within its block
+        if (pass == 0) {
+          gather_dvectors<D>(c);        // whole d-vectors per lane from here on
+          wave_sync();                  // the previous block's store has read S
+        }
+#pragma unroll
+        for (int v = 0; v < 16 / D; ++v) {
+          const int kr = dvec_row<D>(v, 0, h);       // first row of this vector in the block
+          const int kv = kb + kr;
           float T[D];
 #pragma unroll
-          for (int e = 0; e < D; ++e) T[e] = S[(sl * D + e) * SROW + q];
-          uint32_t zw = 0, mw = 0;
-          // Rows and columns past the end of G hold clamped-operand values, not zeros:
-          // they must not reach dA or dB.
+          for (int e = 0; e < D; ++e) T[e] = c[dvec_reg<D>(v, e)];
+          // The tile's codes and mask bits were brought into LDS at kernel start; the
+          // offsets stay inside the tile's area (n - q0 < 256, kv - p0 < 256) whether or
+          // not the vector is inside G, so the reads need no branch. Rows and columns
+          // past the end of G hold clamped-operand values, not zeros: they must not
+          // reach dA or dB.
           const bool valid = n < a.N && kv < a.K;
-          if (valid) {
-            // the tile's codes and mask bits were brought into LDS at kernel start
-            const uint8_t* zp = smem + DW_CODES_OFF + (n - q0) * 64 + ((kv - p0) >> 2);
-            const uint8_t* mp = smem + DW_MASK_OFF + (n - q0) * 32 + ((kv - p0) >> 3);
-            if (D == 4) { zw = zp[0]; mw = (mp[0] >> (kv & 4)) & 0xFu; }
-            if (D == 8) { zw = *reinterpret_cast<const uint16_t*>(zp); mw = mp[0]; }
-            if (D == 16) { zw = *reinterpret_cast<const uint32_t*>(zp); mw = *reinterpret_cast<const uint16_t*>(mp); }
-          }
+          const uint8_t* zp = smem + DW_CODES_OFF + (n - q0) * 64 + ((kv - p0) >> 2);
+          const uint8_t* mp = smem + DW_MASK_OFF + (n - q0) * 32 + ((kv - p0) >> 3);
+          uint32_t zw, mw;
+          if (D == 4) { zw = zp[0]; mw = (mp[0] >> (kv & 4)) & 0xFu; }
+          if (D == 8) { zw = *reinterpret_cast<const uint16_t*>(zp); mw = mp[0]; }
+          if (D == 16) { zw = *reinterpret_cast<const uint32_t*>(zp); mw = *reinterpret_cast<const uint16_t*>(mp); }
+          zw = valid ? zw : 0u;
+          mw = valid ? mw : 0u;
           if (pass == 0) {
 #pragma unroll
             for (int jj = 0; jj < D; ++jj) {
               float sum = 0.f;
 #pragma unroll
               for (int e = 0; e < D; ++e) sum = __builtin_fmaf(Aat(e * D + jj), T[e], sum);
-              S[(sl * D + jj) * SROW + q] = ((mw >> jj) & 1u) ? sum : 0.f;
+              S[(kr + jj) * SROW + q] = ((mw >> jj) & 1u) ? sum : 0.f;
             }
 #pragma unroll
             for (int e = 0; e < D; ++e) dB[e] += valid ? T[e] : 0.f;
