@@ -247,9 +247,9 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
 // own codes, A, B and output: workgroups [wg0[i], wg0[i+1]) belong to matrix i.
 constexpr int GWF = 8;
 
-template <int D, int RG, int KSW>
+template <int D, int RG, int KSW, int M>
 __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restrict__ X,
-                                                         GemvBatch batch, int M, int K) {
+                                                         GemvBatch batch, int K) {
   extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -272,34 +272,62 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   float* As = reinterpret_cast<float*>(gsm + XB + nkb * 128);     // [D][D], then B [D]
   float* Bs = As + D * D;
 
-  // 1. the codes of this wave's blocks, for every row group
+  // 1. A, B and this thread's X chunks, before the codes: vector-memory loads complete in
+  //    issue order, so a wait for X or A issued after the code loads would also wait for
+  //    the whole code stream, and forming X' could not overlap it. Item i = (kb * M + m)
+  //    * 16 + kc covers 16 columns; the 16 items of a (kb, m) are 16 consecutive lanes.
+  //    The launch picks KSW >= nkb / GWF, so nkb * M * 16 <= XI * GWF * 64.
+  //    All loads here are unconditional, from clamped addresses: a load merged with a
+  //    default value across a branch, or counted differently on two paths, makes the
+  //    compiler wait for it (and for everything issued before it) right there.
+  constexpr int XI = KSW * M / 4 > 1 ? KSW * M / 4 : 1;
+  const int nitems = nkb * M * 16;
+  uint4 xv[XI][2];
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int i = min(t + j * GWF * 64, nitems - 1);     // threads past the end: not used
+    const int kc = i & 15, gm = i >> 4;
+    const int m = gm % M, kb = gm / M;
+    const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)m * K + kb * GK + kc * 16);
+    xv[j][0] = src[0];
+    xv[j][1] = src[1];
+  }
+  const uint16_t a16 = A16[min(t, D * D - 1)];
+  const uint16_t b16 = B16[min(t, D - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the codes of this wave's blocks, for every row group. Blocks past the end of K are
+  //    never used (the product loop stops first) and rows past N are not stored, so those
+  //    loads read the last block or the first row group instead.
   const u32x4* crow =
       reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 + nl) * rowb + kq * 16);
   u32x4 cw[KSW][RG];
 #pragma unroll
   for (int u = 0; u < KSW; ++u) {
-    const int kb = wave + GWF * u;
+    const int kb = min(wave + GWF * u, nkb - 1);
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
-      cw[u][g] = (kb < nkb && n0 + 16 * g < N)
-                     ? __builtin_nontemporal_load(crow + g * rowb + kb * 4)
-                     : u32x4{0, 0, 0, 0};
+    for (int g = 0; g < RG; ++g) {
+      const int gc = n0 + 16 * g < N ? g : 0;
+      cw[u][g] = __builtin_nontemporal_load(crow + gc * rowb + kb * 4);
+    }
   }
-  // 2. A, B, and zero block scales for the rows m >= M
-  if (t < D * D) As[t] = (float)__builtin_bit_cast(_Float16, A16[t]);
-  if (t < D) Bs[t] = (float)__builtin_bit_cast(_Float16, B16[t]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. A, B, zero block scales for the rows m >= M, then X' of rows m < M
+  if (t < D * D) As[t] = (float)__builtin_bit_cast(_Float16, a16);
+  if (t < D) Bs[t] = (float)__builtin_bit_cast(_Float16, b16);
   for (int i = t; i < nkb * 16; i += GWF * 64)
     if ((i & 15) >= M) ris[i] = make_float2(0.f, 0.f);
   __syncthreads();
-  // 3. X' of rows m < M: item i = (kb * M + m) * 16 + kc; the 16 items of a (kb, m)
-  //    are 16 consecutive lanes
-  for (int i = t; i < nkb * M * 16; i += GWF * 64) {
+#pragma unroll
+  for (int j = 0; j < XI; ++j) {
+    const int i = t + j * GWF * 64;
+    if (i >= nitems) break;
     const int kc = i & 15, gm = i >> 4;
     const int m = gm % M, kb = gm / M;
-    const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)m * K + kb * GK + kc * 16);
     uint32_t hi[4], lo[4];
     float scale, bsum;
-    xprime_chunk<D>(src[0], src[1], As, Bs, hi, lo, scale, bsum);
+    xprime_chunk<D>(xv[j][0], xv[j][1], As, Bs, hi, lo, scale, bsum);
     const int q = kc >> 2, s = kc & 3;
     *reinterpret_cast<uint4*>(gsm + (((kb * 8 + 2 * s) * 4 + q) * M + m) * 16) =
         make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -378,16 +406,16 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   }
 }
 
-template <int D, int RG, int KSW>
+template <int D, int RG, int KSW, int M>
 static void launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
-                         const GemvBatch& b, int M, int K) {
+                         const GemvBatch& b, int K) {
   static bool attr = false;                        // LDS beyond 64 KiB must be requested
   if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW, M>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr = true;
   }
-  LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW>), grid, dim3(GWF * 64), shm, s, X, b, M, K);
+  LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW, M>), grid, dim3(GWF * 64), shm, s, X, b, K);
 }
 
 template <int D>
@@ -395,15 +423,20 @@ static void launch_fused_d(int M, int K, bool two, size_t shm, hipStream_t s, co
                            const GemvBatch& b, int wgs) {
   const int pw = (K / GK + GWF - 1) / GWF;
   const dim3 grid(wgs);
+  static_assert(GEMV_FUSED_M == 2, "fused path instantiated for one and two tokens");
+#define LCVQ_FUSED(RG, KSW)                                              \
+  (M == 1 ? launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K)            \
+          : launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K))
   if (two) {
-    if (pw <= 2) launch_fused<D, 2, 2>(grid, shm, s, X, b, M, K);
-    else if (pw <= 4) launch_fused<D, 2, 4>(grid, shm, s, X, b, M, K);
-    else launch_fused<D, 2, 8>(grid, shm, s, X, b, M, K);
+    if (pw <= 2) LCVQ_FUSED(2, 2);
+    else if (pw <= 4) LCVQ_FUSED(2, 4);
+    else LCVQ_FUSED(2, 8);
   } else {
-    if (pw <= 2) launch_fused<D, 1, 2>(grid, shm, s, X, b, M, K);
-    else if (pw <= 4) launch_fused<D, 1, 4>(grid, shm, s, X, b, M, K);
-    else launch_fused<D, 1, 8>(grid, shm, s, X, b, M, K);
+    if (pw <= 2) LCVQ_FUSED(1, 2);
+    else if (pw <= 4) LCVQ_FUSED(1, 4);
+    else LCVQ_FUSED(1, 8);
   }
+#undef LCVQ_FUSED
 }
 
 // One fused launch over the matrices of `b` (count, packed, A16, B16, Y, N filled in).
