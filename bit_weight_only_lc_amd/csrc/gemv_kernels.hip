@@ -20,11 +20,16 @@
 namespace lcvq {
 
 constexpr int GK = 256;   // k per block (4 MFMA of k = 64)
-constexpr int GEMV_FUSED_M = 2;     // up to this many tokens one fused kernel does it all
+constexpr int GEMV_FUSED_M = 4;     // up to this many tokens one fused kernel can do it all
 
-// The fused path (X' formed in LDS by every workgroup) serves few tokens and K up to 64
-// blocks; otherwise a prologue kernel writes X' once and the product reads it.
-inline bool gemv_fused(int M, int K) { return M <= GEMV_FUSED_M && K / 256 <= 64; }
+// The fused path (X' formed in LDS by every workgroup) repeats M * K * d multiply-adds in
+// every workgroup; measured on the decode shapes, that beats a separate prologue launch
+// up to about M * K / 256 = 128. So: one or two tokens with K up to 64 blocks, three or
+// four with K up to 32; otherwise a prologue kernel writes X' once and the product reads it.
+inline bool gemv_fused(int M, int K) {
+  const int nkb = K / 256;
+  return M <= 2 ? nkb <= 64 : (M <= GEMV_FUSED_M && nkb <= 32);
+}
 bool gemv_fused_path(int M, int K) { return gemv_fused(M, K); }
 
 // X' limbs: each (block kb, MFMA step s, limb 0 = high / 1 = low, quarter kq, row m) is
@@ -280,7 +285,8 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   //    All loads here are unconditional, from clamped addresses: a load merged with a
   //    default value across a branch, or counted differently on two paths, makes the
   //    compiler wait for it (and for everything issued before it) right there.
-  constexpr int XI = KSW * M / 4 > 1 ? KSW * M / 4 : 1;
+  constexpr int XI = (KSW * M + 3) / 4;
+  static_assert(XI * GWF * 64 >= GWF * KSW * M * 16, "X items of nkb <= GWF * KSW blocks");
   const int nitems = nkb * M * 16;
   uint4 xv[XI][2];
 #pragma unroll
@@ -418,15 +424,25 @@ static void launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X
   LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW, M>), grid, dim3(GWF * 64), shm, s, X, b, K);
 }
 
+// M = 3, 4 take the fused path only for K up to 32 blocks, i.e. KSW <= 4.
+template <int D, int RG, int KSW>
+static void launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
+                           const GemvBatch& b, int K) {
+  static_assert(GEMV_FUSED_M == 4, "fused path instantiated for one to four tokens");
+  if (M == 1) launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K);
+  else if (M == 2) launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K);
+  else if constexpr (KSW <= 4) {
+    if (M == 3) launch_fused<D, RG, KSW, 3>(grid, shm, s, X, b, K);
+    else launch_fused<D, RG, KSW, 4>(grid, shm, s, X, b, K);
+  }
+}
+
 template <int D>
 static void launch_fused_d(int M, int K, bool two, size_t shm, hipStream_t s, const uint16_t* X,
                            const GemvBatch& b, int wgs) {
   const int pw = (K / GK + GWF - 1) / GWF;
   const dim3 grid(wgs);
-  static_assert(GEMV_FUSED_M == 2, "fused path instantiated for one and two tokens");
-#define LCVQ_FUSED(RG, KSW)                                              \
-  (M == 1 ? launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K)            \
-          : launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K))
+#define LCVQ_FUSED(RG, KSW) launch_fused_m<D, RG, KSW>(M, grid, shm, s, X, b, K)
   if (two) {
     if (pw <= 2) LCVQ_FUSED(2, 2);
     else if (pw <= 4) LCVQ_FUSED(2, 4);

@@ -170,8 +170,8 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
  * q, k and v projections, or gate and up, of one transformer layer; each matrix has its
  * own codes and its own A, B (LC-QAT summary, Methodology 1: A and B are shared within
  * one weight matrix). Every output equals what lcvq_gemv2b gives for that matrix, byte
- * for byte. With M <= 2 and K <= 16384 all of them run in one launch; otherwise one
- * matrix after the other, on `stream`.
+ * for byte. With M <= 2 and K <= 16384, or M <= 4 and K <= 8192, all of them run in
+ * one launch; otherwise one matrix after the other, on `stream`.
  *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 256
  *   mats    host array of `count` descriptors, 1 <= count <= 8; mats[i].N a multiple of
  *           16; packed uint8 [N, K/4], A16 float16 [d, d], B16 float16 [d] and the output

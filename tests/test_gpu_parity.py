@@ -195,6 +195,26 @@ def test_gemv(P, N, K, M):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("d", [4, 16])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (2048, 14336)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
+def test_gemv_d(P, N, K, M, d):
+    """The decode product at the other vector lengths, on both the one-launch path (few
+    tokens, K within its range) and the prologue + product path."""
+    note(f"gemv d={d} N={N} K={K} M={M}")
+    wp = SI.make_wp(N, K, seed=3200 + N + K, device="cuda")
+    A, B = SI.make_ab(d, seed=3200 + d + M)
+    X = SI.make_act(M, K, seed=3300 + M, device="cuda")
+    pk = torch.empty((N, K // 4), dtype=torch.uint8, device="cuda")
+    P.lcvq_quantize(wp, None, pk, None)
+    Y = P.gemv2b(X, pk, A.half().cuda(), B.half().cuda(), d)
+    torch.cuda.synchronize()
+    ref = O.gemv2b(host(X), host(pk), A.half().double().numpy(), B.half().double().numpy(), d)
+    e = rel(host(Y), ref)
+    note(f"  rel={e:.2e}")
+    assert e <= TOL
+
+
 @pytest.mark.parametrize("N,K,M", [(4096, 14336, 16), (14336, 4096, 1), (272, 8192, 5),
                                    (256, 16640, 2)])
 def test_gemv_repeat_shared_workspace(P, N, K, M):
