@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
-KERNELS = {1: "quantize_prologue", 2: "fwd_product", 3: "dx_product", 4: "dw_product"}
+KERNELS = {1: "quantize_prologue", 2: "fwd_product", 6: "bwd_prologue", 3: "dx_product",
+           4: "dw_product"}
 
 # HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE, each
 # scaled by what it reads for a copy of known size). They are valid only for the kernel
@@ -127,8 +128,8 @@ def main():
     for _ in range(args.warmup):
         step()
     # Per-kernel durations come from the timed steps themselves: step i arms the timing
-    # hook for kernel i mod 4, whose launch is then bracketed by two events on the
-    # library's stream. Under sustained back-to-back steps the clock runs lower than in
+    # hook for kernel number i mod 5 of KERNELS, whose launch is then bracketed by two
+    # events on the library's stream. Under sustained back-to-back steps the clock runs lower than in
     # an isolated step, so these are the durations that make up the measured step time.
     kern_ids = list(KERNELS.items())
     step_evs = timed_events(torch, args.steps)

@@ -93,7 +93,7 @@ bool lcvq::take_profile(int id, hipEvent_t* start, hipEvent_t* stop) {
 extern "C" {
 
 lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event) {
-  if (kernel_id < PROF_QUANTIZE || kernel_id > PROF_GEMV) return LCVQ_ERR_SHAPE;
+  if (kernel_id < PROF_QUANTIZE || kernel_id > PROF_BWD_PREP) return LCVQ_ERR_SHAPE;
   g_prof.id = (start_event && stop_event) ? kernel_id : 0;
   g_prof.start = static_cast<hipEvent_t>(start_event);
   g_prof.stop = static_cast<hipEvent_t>(stop_event);

@@ -6,7 +6,7 @@
 namespace lcvq {
 
 // Kernel ids of the profiling hook (lcvq_profile_next).
-enum { PROF_QUANTIZE = 1, PROF_FWD = 2, PROF_DX = 3, PROF_DW = 4, PROF_GEMV = 5 };
+enum { PROF_QUANTIZE = 1, PROF_FWD = 2, PROF_DX = 3, PROF_DW = 4, PROF_GEMV = 5, PROF_BWD_PREP = 6 };
 // True (once) if the calling thread armed timing for kernel `id`; returns the events.
 bool take_profile(int id, hipEvent_t* start, hipEvent_t* stop);
 

@@ -387,12 +387,41 @@ __device__ __forceinline__ void bwd_prologue_body(int64_t m, const T* __restrict
   if (threadIdx.x == 0) r[m] = s;
 }
 
+// r[m] = sum_n dY[m, n] for bf16 dY: one wave per row. Every lane issues all of its
+// 16-byte loads of a sweep before using any (clamped addresses, no branch, so none of
+// them is waited for early), then the wave adds its lanes. N is a multiple of 64.
+constexpr int ROWSUM_U = 8;                   // loads in flight per lane
+__device__ __forceinline__ void rowsum_bf16_wave(int64_t m, const uint16_t* __restrict__ dY,
+                                                 int64_t N, float* __restrict__ r, int lane) {
+  const uint4* row = reinterpret_cast<const uint4*>(dY + m * N);
+  const int64_t chunks = N >> 3;              // 8 bf16 per 16 bytes
+  float acc = 0.f;
+  for (int64_t c0 = 0; c0 < chunks; c0 += 64 * ROWSUM_U) {
+    uint4 v[ROWSUM_U];
+#pragma unroll
+    for (int u = 0; u < ROWSUM_U; ++u) v[u] = row[min(c0 + u * 64 + lane, chunks - 1)];
+#pragma unroll
+    for (int u = 0; u < ROWSUM_U; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t += bf16lo_to_f32(w[i]) + bf16hi_to_f32(w[i]);
+      acc += c0 + u * 64 + lane < chunks ? t : 0.f;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) r[m] = acc;
+}
+
 // ------------------------------------------------------------------ merged launches
 // Work that does not depend on each other shares one launch: block ranges of one grid
 // run the two parts, which saves a kernel boundary and lets the VALU-bound quantizer
 // overlap the memory-bound prologue.
 //   forward:  blocks [0, qblocks) quantize, then one block per activation row m;
-//   backward: one block per row m (r = dY 1), then the blocks of the transposed codes.
+//   backward: the blocks of the transposed codes (VALU work, first so that it overlaps
+//             the rest), then the row blocks (r = dY 1; bf16: 4 rows per block, one per
+//             wave; float32, which also writes the hi/lo splits: one row per block).
 template <typename T, int DQ, int D>
 __global__ __launch_bounds__(256) void k_fwd_prep(const float* __restrict__ wp, int64_t total,
                                                   int64_t K, uint8_t* __restrict__ packed,
@@ -411,6 +440,8 @@ __global__ __launch_bounds__(256) void k_fwd_prep(const float* __restrict__ wp, 
     fwd_prologue_body<T, D>((int64_t)blockIdx.x - qblocks, X, KX, A, B, xs, xs_lo, beta);
 }
 
+template <typename T> constexpr int bwd_rows_per_block() { return sizeof(T) == 2 ? 4 : 1; }
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ dY,
                                                   const T* __restrict__ X, int64_t M,
@@ -420,12 +451,20 @@ __global__ __launch_bounds__(256) void k_bwd_prep(const T* __restrict__ dY,
                                                   uint16_t* __restrict__ x_hi,
                                                   uint16_t* __restrict__ x_lo,
                                                   const uint8_t* __restrict__ packed,
-                                                  uint32_t* __restrict__ r16t, int kblocks) {
-  if ((int64_t)blockIdx.x < M) {
-    bwd_prologue_body<T>(blockIdx.x, dY, X, N, K, r, dy_hi, dy_lo, x_hi, x_lo);
-  } else {
-    const int vb = (int)((int64_t)blockIdx.x - M);
+                                                  uint32_t* __restrict__ r16t, int kblocks,
+                                                  int tblocks) {
+  constexpr int RPB = bwd_rows_per_block<T>();
+  if ((int64_t)blockIdx.x < tblocks) {
+    const int vb = (int)blockIdx.x;
     r16t_body(vb % kblocks, vb / kblocks, packed, N, K, r16t);
+  } else {
+    const int64_t rb = (int64_t)blockIdx.x - tblocks;
+    if constexpr (RPB == 4) {
+      const int64_t m = rb * 4 + (threadIdx.x >> 6);
+      if (m < M) rowsum_bf16_wave(m, dY, N, r, threadIdx.x & 63);
+    } else {
+      bwd_prologue_body<T>(rb, dY, X, N, K, r, dy_hi, dy_lo, x_hi, x_lo);
+    }
   }
 }
 
@@ -568,16 +607,17 @@ hipError_t launch_bwd_prep(const void* dY, const void* X, bool f32, int64_t M, i
                            uint32_t* r16t, hipStream_t s) {
   const int kblocks = (int)((K + 255) / 256);
   const int64_t rb = r16t ? (int64_t)kblocks * (N / 64) : 0;
-  const dim3 g((unsigned)(M + rb)), b(256);
+  const int rpb = f32 ? bwd_rows_per_block<float>() : bwd_rows_per_block<uint16_t>();
+  const dim3 g((unsigned)((M + rpb - 1) / rpb + rb)), b(256);
   if (f32)
-    hipLaunchKernelGGL(k_bwd_prep<float>, g, b, 0, s, static_cast<const float*>(dY),
-                       static_cast<const float*>(X), M, N, K, r, dy_hi, dy_lo, x_hi, x_lo,
-                       packed, r16t, kblocks);
+    LCVQ_LAUNCH(PROF_BWD_PREP, k_bwd_prep<float>, g, b, 0, s, static_cast<const float*>(dY),
+                static_cast<const float*>(X), M, N, K, r, dy_hi, dy_lo, x_hi, x_lo, packed,
+                r16t, kblocks, (int)rb);
   else
-    hipLaunchKernelGGL(k_bwd_prep<uint16_t>, g, b, 0, s, static_cast<const uint16_t*>(dY),
-                       static_cast<const uint16_t*>(X), M, N, K, r, (uint16_t*)nullptr,
-                       (uint16_t*)nullptr, (uint16_t*)nullptr, (uint16_t*)nullptr, packed,
-                       r16t, kblocks);
+    LCVQ_LAUNCH(PROF_BWD_PREP, k_bwd_prep<uint16_t>, g, b, 0, s,
+                static_cast<const uint16_t*>(dY), static_cast<const uint16_t*>(X), M, N, K, r,
+                (uint16_t*)nullptr, (uint16_t*)nullptr, (uint16_t*)nullptr, (uint16_t*)nullptr,
+                packed, r16t, kblocks, (int)rb);
   return hipGetLastError();
 }
 

@@ -195,7 +195,8 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
  * kernel by calls made from this host thread: the kernel is launched with
  * hipExtLaunchKernel between `start_event` and `stop_event` (hipEvent_t handles created
  * by the caller with timing enabled). kernel_id: 1 quantizer, 2 forward product,
- * 3 dX product, 4 dW product (with the straight-through epilogue), 5 decode product.
+ * 3 dX product, 4 dW product (with the straight-through epilogue), 5 decode product,
+ * 6 backward prologue (r = dY 1 and the transposed codes, lcvq_linear_bwd).
  * Passing NULL events disarms. Returns LCVQ_ERR_SHAPE for an unknown kernel_id.
  */
 lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event);
