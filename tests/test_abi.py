@@ -185,3 +185,11 @@ def test_workspace_sizes_grow_with_shape(L):
     assert L.lcvq_linear_fwd_workspace_size(0, 256, 256, 8) == 0
     assert L.lcvq_linear_bwd_workspace_size(64, 256, 256, 16) > \
         L.lcvq_linear_bwd_workspace_size(64, 256, 256, 4)
+
+
+def test_profile_hook_ids(L):
+    """The timing hook knows kernel ids 1..6; arming with NULL events disarms (no GPU call)."""
+    for kid in (0, 7, -1):
+        assert L.lcvq_profile_next(kid, None, None) == 2          # LCVQ_ERR_SHAPE
+    for kid in range(1, 7):
+        assert L.lcvq_profile_next(kid, None, None) == 0
