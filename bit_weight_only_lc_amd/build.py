@@ -32,6 +32,9 @@ def flags():
     return [
         f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # Let "#pragma unroll" unroll the large epilogue loops fully (d = 16): a loop left
+        # rolled indexes the accumulator arrays at run time and moves them to scratch.
+        "-mllvm", "-pragma-unroll-threshold=200000",
         "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     ]
 

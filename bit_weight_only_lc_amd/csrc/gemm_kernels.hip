@@ -421,6 +421,7 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
                             int lane, float* S, const float* Alds) {
   static_assert(WI % 2 == 0, "k blocks are staged in pairs");
   constexpr int NV = 16 / D;                  // whole vectors per lane and block
+  constexpr int IIU = D == 16 ? 4 : D;        // output rows unrolled together
   float bp[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -456,14 +457,17 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
         f32x16& c = acc[2 * i2 + half][j];
         gather_dvectors<D>(c);
         float* Sh = S + half * 32 * SROW;
+        // d = 16: the output rows go four at a time, with their A rows and row terms read
+        // from LDS, instead of all 256 coefficients at once (which spills).
 #pragma unroll
         for (int v = 0; v < NV; ++v)
-#pragma unroll
+#pragma unroll IIU
           for (int ii = 0; ii < D; ++ii) {
             float s = 0.f;
 #pragma unroll
             for (int e = 0; e < D; ++e) s = __builtin_fmaf(Aat(ii * D + e), c[dvec_reg<D>(v, e)], s);
-            Sh[dvec_row<D>(v, ii, h) * SROW + q] = __builtin_fmaf(2.f, s, bp[ii] * rm);
+            const float bpi = D == 16 ? Al[D * D + ii] : bp[ii];
+            Sh[dvec_row<D>(v, ii, h) * SROW + q] = __builtin_fmaf(2.f, s, bpi * rm);
           }
       }
       wave_sync();
@@ -486,7 +490,8 @@ constexpr int DW_SMEM = DW_MASK_OFF + 256 * 32;         // 152 KiB
 template <int D, int NW, int WJ>
 __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
                             int lane, int wave, int tile, uint8_t* smem, const float* Alds) {
-  constexpr int NP = D == 16 ? 4 : 1;          // passes over the columns j of dA
+  constexpr int NP = D == 16 ? 8 : 1;          // passes over the columns j of dA (d = 16: two
+                                               // columns a pass, so no partial sums spill)
   constexpr int JW = D / NP;
   constexpr int NA = D * JW;                   // dA partials per lane and pass
   constexpr int NR = NA + D;                   // + dB partials (first pass)
@@ -816,10 +821,15 @@ void k_gemm_ring(GemmArgs a) {
     epilogue_fwd<NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, wave, smem);
   } else {
     // The ring is free after the last barrier: per-wave staging areas of 8.25 KiB, and
-    // for d = 16 a copy of A at 120 KiB.
+    // for d = 16 a copy of A at 120 KiB followed by the row terms B[i] - 4 sum_j A[i][j].
     float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
     if (D == 16) {
       if (tid < D * D) Alds[tid] = a.A[tid];
+      if (tid < D) {
+        float sa = 0.f;
+        for (int j = 0; j < D; ++j) sa += a.A[tid * D + j];
+        Alds[D * D + tid] = a.B[tid] - 4.f * sa;
+      }
       __syncthreads();
     }
     static_assert(NW * DX_WAVE_LDS <= 120 * 1024, "dX staging below the copy of A");
