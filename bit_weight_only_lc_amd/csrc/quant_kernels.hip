@@ -254,6 +254,7 @@ __device__ __forceinline__ void fwd_prologue_body(int64_t m, const T* __restrict
                                                       float* __restrict__ beta) {
   __shared__ float red[4];
   __shared__ float Asm[D * D], Bsm[D];
+  __shared__ float xsl[D > 8 ? 256 * 17 : 1];     // d = 16: each thread's 16 inputs (padded)
   // A and B are the same for every lane: for d <= 8 they are read with scalar loads into
   // scalar registers (64 + 8 values), which keeps the vector registers for the data;
   // for d = 16 they are staged in LDS.
@@ -285,14 +286,17 @@ __device__ __forceinline__ void fwd_prologue_body(int64_t m, const T* __restrict
         }
       }
     } else {
-      // one row of A at a time from LDS, so that only the 16 outputs stay in registers
+      // One row of A at a time from LDS, so that only the 16 outputs stay in registers.
+      // The row index runs at run time, so x[i] is read back from the thread's own LDS
+      // slot rather than selected among 16 registers.
+      float* xt = xsl + threadIdx.x * 17;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) xt[j] = x[j];
 #pragma unroll
       for (int j = 0; j < 16; ++j) xp[j] = 0.f;
 #pragma unroll 1
       for (int i = 0; i < D; ++i) {
-        float xi = x[0];
-#pragma unroll
-        for (int q = 1; q < 16; ++q) xi = i == q ? x[q] : xi;
+        const float xi = xt[i];
 #pragma unroll
         for (int j = 0; j < 16; ++j) xp[j] = __builtin_fmaf(xi, As[i * D + j], xp[j]);
       }
