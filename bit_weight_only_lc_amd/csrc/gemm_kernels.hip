@@ -1,18 +1,18 @@
 // Matrix-core products of the LC-VQ layer on gfx950 (bf16 MFMA, float32 accumulate).
 //
 // The decode c = A z + B (LC-QAT summary, Methodology 1) is linear, so A and B are moved
-// off the weight operand and the products run directly on the 2-bit codes, as the
-// summary's training pipeline says ("restructured to use INT2-FP16 matmul kernels",
-// Methodology 3):
+// off the weight operand and the products run directly on the 2-bit codes; the summary's
+// training pipeline likewise reorganises the computation around INT2 x FP16 matrix
+// products (Methodology 3):
 //   forward  Y  = X What^T            = X' Z^T + (X (1 kron B)) 1^T,   X' = X (I kron A)
 //   dX          = dY What             = (dY Z)(I kron A^T) + (dY 1)(1 kron B)^T
 //   dWp, dA, dB from G = dY^T X       (straight-through epilogue on the accumulators)
 // A code c enters a product as v(c) = 2 + c/2, exact in bf16 (see r16_to_vbf16); the
 // constant part is removed through the row terms prepared by the prologue kernels.
 //
-// One kernel template covers the three products. C (P x Q) = sum_r L[p, r] R[q, r] is
-// computed in 256 x 256 tiles (32x32x16 bf16 MFMA, contraction staged through LDS in
-// steps of 64):
+// Two kernel templates cover the three products (k_gemm_ring: forward and dX; k_gemm_dw).
+// C (P x Q) = sum_r L[p, r] R[q, r] is computed in 256 x 256 tiles (32x32x16 bf16 MFMA,
+// contraction staged through LDS in steps of 64):
 //   FWD: L = X' (bf16 rows m),        R = codes (rows n)       8 waves, 4-slot LDS ring
 //   DX : L = codes transposed (rows k), R = dY (bf16 rows m)   8 waves, 4-slot LDS ring
 //   DW : L = X^T (rows k), R = dY^T (rows n); both tiles arrive in their natural layout
@@ -235,10 +235,12 @@ __device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, floa
 
 // ---- epilogues -----------------------------------------------------------------------
 // Accumulator layout (32x32 block): lane l holds column l%32 and, in register r, row
-// 8*(r/4) + 4*(l/32) + r%4. For DX and DW the rows run along the d-vectors, so each
-// block is first staged through a per-wave LDS area (32 x 33 floats); then every lane
-// takes whole d-vectors of one column, and finally the block is written back to HBM
-// with each group of 8 lanes covering 32 consecutive elements of one output row.
+// 8*(r/4) + 4*(l/32) + r%4. For DX and DW the rows run along the d-vectors: a swap of
+// register halves between lanes l and l^32 (gather_dvectors) gives every lane whole
+// d-vectors, the d x d mix runs in registers, and the results go through a per-wave
+// LDS area (rows of 33 floats) only to be written back transposed, each group of 8
+// lanes covering consecutive elements of one output row. The forward epilogue stages
+// row-major strips the same way for 16-byte stores.
 
 constexpr int SROW = 33;                  // padded row of the staging area (floats)
 constexpr int WAVE_LDS = 32768;           // LDS bytes per wave in the epilogue

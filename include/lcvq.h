@@ -59,7 +59,7 @@ const char* lcvq_status_string(lcvq_status_t s);
 
 /*
  * Quantizer: z = clamp(round(Wp), 0, 3) and the straight-through mask
- * (LC-QAT summary, Methodology 1 "rounding and clamping", Methodology 3 forward).
+ * (LC-QAT summary: Methodology 1, rounding and clamping; Methodology 3, forward).
  *   Wp      float [N, K]            in
  *   z_u8    uint8 [N, K]   or NULL  out: one code per byte
  *   packed  uint8 [N, K/4] or NULL  out: 4 codes per byte
