@@ -29,7 +29,7 @@ _lib = None
 class GemvMatrix(ctypes.Structure):
     """lcvq_gemv2b_matrix: one matrix of a batched decode product."""
     _fields_ = [("packed", ctypes.c_void_p), ("A16", ctypes.c_void_p), ("B16", ctypes.c_void_p),
-                ("Y", ctypes.c_void_p), ("N", ctypes.c_int64)]
+                ("Y", ctypes.c_void_p), ("N", ctypes.c_int64), ("layout", ctypes.c_int32)]
 
 
 class LcvqError(RuntimeError):
@@ -62,6 +62,8 @@ def lib():
             "lcvq_linear_bwd_dge": [vp, vp, i32, i64, i64, i64, i32, vp, vp, vp, f32, vp, vp,
                                     vp, vp, vp, vp, vp, sz, vp],
             "lcvq_gemv2b": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp],
+            "lcvq_gemv2b_shuffled": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp],
+            "lcvq_gemv2b_shuffle": [vp, i64, i64, vp, vp],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -228,6 +230,26 @@ def lcvq_linear_bwd_dge(dY, X, packed, mask, Wp, alpha, A, B, d, dX, dWp, dA, dB
 
 
 def lcvq_gemv2b(X, packed, A16, B16, d, Y, workspace=None):
+    _gemv2b("lcvq_gemv2b", X, packed, A16, B16, d, Y, workspace)
+
+
+def lcvq_gemv2b_shuffled(X, codes, A16, B16, d, Y, workspace=None):
+    """codes: the decode layout written by lcvq_gemv2b_shuffle, held as uint8 [N, K/4]."""
+    _gemv2b("lcvq_gemv2b_shuffled", X, codes, A16, B16, d, Y, workspace)
+
+
+def lcvq_gemv2b_shuffle(packed, codes):
+    dev = packed.device
+    _check(packed, "packed", torch.uint8, dev)
+    _check(codes, "codes", torch.uint8, dev)
+    if codes.shape != packed.shape:
+        raise ValueError("codes must have the shape of packed")
+    N, K4 = packed.shape
+    _ok(lib().lcvq_gemv2b_shuffle(_p(packed), N, K4 * 4, _p(codes), _stream(dev)),
+        "lcvq_gemv2b_shuffle")
+
+
+def _gemv2b(name, X, packed, A16, B16, d, Y, workspace):
     _check(X, "X", torch.bfloat16)
     dev = X.device
     _check(packed, "packed", torch.uint8, dev)
@@ -240,24 +262,27 @@ def lcvq_gemv2b(X, packed, A16, B16, d, Y, workspace=None):
         workspace = torch.empty(max(lcvq_gemv2b_workspace_size(M, N, K, d), 1),
                                 dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", torch.uint8, dev)
-    _ok(lib().lcvq_gemv2b(_p(X), M, N, K, d, _p(packed), _p(A16), _p(B16), _p(Y),
-                          _p(workspace), workspace.numel(), _stream(dev)), "lcvq_gemv2b")
+    _ok(getattr(lib(), name)(_p(X), M, N, K, d, _p(packed), _p(A16), _p(B16), _p(Y),
+                             _p(workspace), workspace.numel(), _stream(dev)), name)
 
 
 def lcvq_gemv2b_batched(X, mats, d, workspace=None):
-    """mats: list of (packed, A16, B16, Y) sharing the input X."""
+    """mats: list of (packed, A16, B16, Y) or (packed, A16, B16, Y, layout) sharing the
+    input X; layout 1 means codes in the decode layout of lcvq_gemv2b_shuffle."""
     _check(X, "X", torch.bfloat16)
     dev = X.device
     M, K = X.shape
     arr = (GemvMatrix * max(len(mats), 1))()
     nmax = 16
-    for i, (pk, a16, b16, y) in enumerate(mats):
+    for i, m in enumerate(mats):
+        pk, a16, b16, y = m[:4]
+        layout = m[4] if len(m) > 4 else 0
         _check(pk, "packed", torch.uint8, dev)
         _check(a16, "A16", torch.float16, dev)
         _check(b16, "B16", torch.float16, dev)
         _check(y, "Y", torch.bfloat16, dev)
         arr[i] = GemvMatrix(pk.data_ptr(), a16.data_ptr(), b16.data_ptr(), y.data_ptr(),
-                            pk.shape[0])
+                            pk.shape[0], int(layout))
         nmax = max(nmax, pk.shape[0])
     if workspace is None:
         workspace = torch.empty(max(lcvq_gemv2b_workspace_size(M, nmax, K, d), 1),
@@ -304,9 +329,17 @@ def linear_bwd(dY, X, packed, mask, A, B, d, want_dx=True, dge_wp=None, dge_alph
     return out
 
 
-def gemv2b(X, packed, A16, B16, d):
+def gemv2b(X, packed, A16, B16, d, shuffled=False):
+    """Allocates Y; `shuffled` says that `packed` holds the decode layout."""
     M = X.shape[0]
     N = packed.shape[0]
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
-    lcvq_gemv2b(X, packed, A16, B16, d, Y)
+    (lcvq_gemv2b_shuffled if shuffled else lcvq_gemv2b)(X, packed, A16, B16, d, Y)
     return Y
+
+
+def gemv2b_shuffle(packed):
+    """Allocates and returns the decode layout of canonical packed codes."""
+    codes = torch.empty_like(packed)
+    lcvq_gemv2b_shuffle(packed, codes)
+    return codes

@@ -136,6 +136,56 @@ __global__ __launch_bounds__(256) void k_gemv_prologue(const uint16_t* __restric
 // keeps each workgroup's chain to one HBM round trip plus the X' walk.
 constexpr int GW = 16;
 
+// Where a lane's 16 bytes of codes for (row group g of a workgroup, block kb) live, in
+// 16-byte units: base + g * gstride + kb * kstride. Lane l = 16 kq + nl takes row
+// n0 + 16 g + nl, codes 256 kb + 64 kq .. +63.
+//   canonical packed [N][K/4]: the row's bytes 64 kb + 16 kq;
+//   decode layout: one 1 KiB tile per (16-row group, 256-column block), tile index
+//   (n / 16) * (K / 256) + kb, lane l's bytes at 16 l, i.e. in the order the lanes load.
+// The layout choice is uniform, so the loads themselves carry no branch.
+struct CodeAddr {
+  const u32x4* base;
+  int64_t gstride, kstride;
+};
+__device__ __forceinline__ CodeAddr code_addr(const uint8_t* packed, int shuffled, int n0, int K,
+                                              int lane) {
+  const int64_t nkb = K / GK, rowb = K >> 2;
+  CodeAddr c;
+  if (shuffled) {
+    c.base = reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 >> 4) * nkb * 1024) + lane;
+    c.gstride = nkb * 64;
+    c.kstride = 64;
+  } else {
+    c.base = reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 + (lane & 15)) * rowb +
+                                            (lane >> 4) * 16);
+    c.gstride = rowb;
+    c.kstride = 4;
+  }
+  return c;
+}
+
+// Canonical packed codes -> decode layout (see code_addr): one 1 KiB tile per wave.
+__global__ __launch_bounds__(256) void k_gemv_shuffle(const uint8_t* __restrict__ packed,
+                                                      int64_t N, int64_t K,
+                                                      uint8_t* __restrict__ out) {
+  const int64_t nkb = K / GK, tiles = (N / 16) * nkb;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= tiles) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = t / nkb, kb = t - r * nkb;
+  const uint4 v = *reinterpret_cast<const uint4*>(packed + (r * 16 + (lane & 15)) * (K >> 2) +
+                                                  kb * 64 + (lane >> 4) * 16);
+  *reinterpret_cast<uint4*>(out + t * 1024 + lane * 16) = v;
+}
+
+hipError_t launch_gemv_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* out,
+                               hipStream_t s) {
+  const int64_t tiles = (N / 16) * (K / GK);
+  hipLaunchKernelGGL(k_gemv_shuffle, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, packed,
+                     N, K, out);
+  return hipGetLastError();
+}
+
 struct GemvA {
   i32x4 hi[4], lo[4];
   f32x4 r0, r1;
@@ -179,17 +229,16 @@ __device__ __forceinline__ void gemv_block(f32x4& acc, const GemvA& a, const u32
 template <int RG, int KSW>
 __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
                                                   const float2* __restrict__ rowinfo,
-                                                  const uint8_t* __restrict__ packed, int M,
-                                                  int N, int K, uint16_t* __restrict__ Y) {
+                                                  const uint8_t* __restrict__ packed,
+                                                  int shuffled, int M, int N, int K,
+                                                  uint16_t* __restrict__ Y) {
   __shared__ f32x4 red[GW][RG][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16 * RG;
   const int nl = lane & 15, kq = lane >> 4;
   const int nkb = K / GK;
-  const int64_t rowb = K >> 2;                     // also 16 rows, in 16-byte units
-  const u32x4* crow =
-      reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 + nl) * rowb + kq * 16);
+  const CodeAddr ca = code_addr(packed, shuffled, n0, K, lane);
   const i32x4* xa = reinterpret_cast<const i32x4*>(xq) + lane;
   const f32x4* ri = reinterpret_cast<const f32x4*>(rowinfo) + 2 * kq;
   const bool has_a = nl < M;                       // A-operand lane row m = lane % 16
@@ -204,7 +253,7 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
 #pragma unroll
       for (int g = 0; g < RG; ++g)
         cw[u][g] = (kb < nkb && n0 + 16 * g < N)
-                       ? __builtin_nontemporal_load(crow + g * rowb + kb * 4)
+                       ? __builtin_nontemporal_load(ca.base + g * ca.gstride + kb * ca.kstride)
                        : u32x4{0, 0, 0, 0};
     }
     GemvA a[2];
@@ -264,6 +313,7 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   for (int i = 1; i < GEMV_MAX_BATCH; ++i)
     if (i < batch.count && (int)blockIdx.x >= batch.wg0[i]) mi = i;
   const uint8_t* __restrict__ packed = batch.packed[mi];
+  const int shuffled = batch.shuffled[mi];
   const uint16_t* __restrict__ A16 = batch.A16[mi];
   const uint16_t* __restrict__ B16 = batch.B16[mi];
   uint16_t* __restrict__ Y = batch.Y[mi];
@@ -271,7 +321,6 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   const int n0 = ((int)blockIdx.x - batch.wg0[mi]) * 16 * RG;
   const int nl = lane & 15, kq = lane >> 4;
   const int nkb = K / GK;
-  const int64_t rowb = K >> 2;
   const int XB = nkb * 32 * M * 16;                // dense X' bytes
   float2* ris = reinterpret_cast<float2*>(gsm + XB);              // [nkb][16]
   float* As = reinterpret_cast<float*>(gsm + XB + nkb * 128);     // [D][D], then B [D]
@@ -305,8 +354,7 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   // 2. the codes of this wave's blocks, for every row group. Blocks past the end of K are
   //    never used (the product loop stops first) and rows past N are not stored, so those
   //    loads read the last block or the first row group instead.
-  const u32x4* crow =
-      reinterpret_cast<const u32x4*>(packed + (int64_t)(n0 + nl) * rowb + kq * 16);
+  const CodeAddr ca = code_addr(packed, shuffled, n0, K, lane);
   u32x4 cw[KSW][RG];
 #pragma unroll
   for (int u = 0; u < KSW; ++u) {
@@ -314,7 +362,7 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       const int gc = n0 + 16 * g < N ? g : 0;
-      cw[u][g] = __builtin_nontemporal_load(crow + gc * rowb + kb * 4);
+      cw[u][g] = __builtin_nontemporal_load(ca.base + gc * ca.gstride + kb * ca.kstride);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -479,8 +527,8 @@ hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b
 }
 
 hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,
-                       const uint16_t* B16, int d, const uint8_t* packed, uint16_t* Y,
-                       int8_t* xq, float* rowinfo, hipStream_t s) {
+                       const uint16_t* B16, int d, const uint8_t* packed, int shuffled,
+                       uint16_t* Y, int8_t* xq, float* rowinfo, hipStream_t s) {
   const int nkb = K / GK;
   // Two row groups per workgroup when N still gives a workgroup per CU.
   const bool two = N >= 2 * 16 * 256;
@@ -488,6 +536,7 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
     GemvBatch b = {};
     b.count = 1;
     b.packed[0] = packed; b.A16[0] = A16; b.B16[0] = B16; b.Y[0] = Y; b.N[0] = N;
+    b.shuffled[0] = shuffled;
     return launch_gemv_fused(X, M, K, d, b, s);
   }
   float2* ri = reinterpret_cast<float2*>(rowinfo);
@@ -502,7 +551,8 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
   const int per_wave = (nkb + GW - 1) / GW;
   const dim3 grid(two ? (N + 31) / 32 : N / 16), block(GW * 64);
 #define LCVQ_GEMV(RG, KSW) \
-  LCVQ_LAUNCH(PROF_GEMV, (k_gemv<RG, KSW>), grid, block, 0, s, xq, ri, packed, M, N, K, Y)
+  LCVQ_LAUNCH(PROF_GEMV, (k_gemv<RG, KSW>), grid, block, 0, s, xq, ri, packed, shuffled, M, N, \
+              K, Y)
   if (two) {
     if (per_wave <= 1) LCVQ_GEMV(2, 1);
     else LCVQ_GEMV(2, 2);

@@ -272,9 +272,14 @@ size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t N, int64_t K, int d) {
   return gemv_ws(K).total;
 }
 
-lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
-                          const uint8_t* packed, const void* A16, const void* B16, void* Y,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// lcvq_gemv2b and lcvq_gemv2b_shuffled: the codes in the canonical packed layout or in
+// the decode layout written by lcvq_gemv2b_shuffle.
+static lcvq_status_t gemv2b_impl(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                                 const uint8_t* packed, int shuffled, const void* A16,
+                                 const void* B16, void* Y, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   if (!X || !packed || !A16 || !B16 || !Y) return LCVQ_ERR_NULL;
   if (!d_ok(d)) return LCVQ_ERR_D;
   if (M < 1 || M > 16 || N < 16 || (N % 16) || K < 256 || (K % 256) || N > INT32_MAX ||
@@ -291,8 +296,33 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
   float* rowinfo = reinterpret_cast<float*>(ws + w.rowinfo);
   return from_hip(launch_gemv(static_cast<const uint16_t*>(X), (int)M, (int)N, (int)K,
                               static_cast<const uint16_t*>(A16),
-                              static_cast<const uint16_t*>(B16), d, packed,
+                              static_cast<const uint16_t*>(B16), d, packed, shuffled,
                               static_cast<uint16_t*>(Y), xq, rowinfo, s));
+}
+
+extern "C" {
+
+lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                          const uint8_t* packed, const void* A16, const void* B16, void* Y,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return gemv2b_impl(X, M, N, K, d, packed, 0, A16, B16, Y, workspace, workspace_bytes, stream);
+}
+
+lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                                   const uint8_t* codes, const void* A16, const void* B16,
+                                   void* Y, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return gemv2b_impl(X, M, N, K, d, codes, 1, A16, B16, Y, workspace, workspace_bytes, stream);
+}
+
+lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
+                                  void* stream) {
+  if (!packed || !codes) return LCVQ_ERR_NULL;
+  if (N < 16 || (N % 16) || K < 256 || (K % 256) || N > INT32_MAX || K > INT32_MAX ||
+      N * K >= (int64_t(1) << 40))
+    return LCVQ_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(codes)) return LCVQ_ERR_ALIGN;
+  return from_hip(launch_gemv_shuffle(packed, N, K, codes, as_stream(stream)));
 }
 
 lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
@@ -306,6 +336,7 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
   for (int i = 0; i < count; ++i) {
     const lcvq_gemv2b_matrix& m = mats[i];
     if (!m.packed || !m.A16 || !m.B16 || !m.Y) return LCVQ_ERR_NULL;
+    if (m.layout != 0 && m.layout != 1) return LCVQ_ERR_VALUE;
     if (m.N < 16 || (m.N % 16) || m.N > INT32_MAX || m.N * K >= (int64_t(1) << 40))
       return LCVQ_ERR_SHAPE;
     if (!aligned16(m.packed) || !aligned16(m.A16) || !aligned16(m.B16) || !aligned16(m.Y))
@@ -327,6 +358,7 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
       b.B16[i] = static_cast<const uint16_t*>(mats[i].B16);
       b.Y[i] = static_cast<uint16_t*>(mats[i].Y);
       b.N[i] = (int)mats[i].N;
+      b.shuffled[i] = mats[i].layout;
     }
     return from_hip(launch_gemv_fused(static_cast<const uint16_t*>(X), (int)M, (int)K, d, b, s));
   }
@@ -335,7 +367,8 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
     const hipError_t e = launch_gemv(static_cast<const uint16_t*>(X), (int)M, (int)mats[i].N,
                                      (int)K, static_cast<const uint16_t*>(mats[i].A16),
                                      static_cast<const uint16_t*>(mats[i].B16), d,
-                                     mats[i].packed, static_cast<uint16_t*>(mats[i].Y),
+                                     mats[i].packed, mats[i].layout,
+                                     static_cast<uint16_t*>(mats[i].Y),
                                      reinterpret_cast<int8_t*>(ws + w.xq),
                                      reinterpret_cast<float*>(ws + w.rowinfo), s);
     if (e != hipSuccess) return LCVQ_ERR_HIP;

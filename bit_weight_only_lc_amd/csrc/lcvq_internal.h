@@ -75,6 +75,7 @@ struct GemvBatch {
   const uint16_t* B16[GEMV_MAX_BATCH];
   uint16_t* Y[GEMV_MAX_BATCH];
   int N[GEMV_MAX_BATCH];
+  int shuffled[GEMV_MAX_BATCH];  // codes in the decode layout (lcvq_gemv2b_shuffle)
   int wg0[GEMV_MAX_BATCH];     // first workgroup of each matrix (set by the launcher)
   int count;
 };
@@ -86,7 +87,10 @@ hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b
 // Decode product. Few tokens: one fused kernel (xq and rowinfo unused); otherwise a
 // prologue writes X' limbs to xq and block scales to rowinfo, and the product reads them.
 hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,
-                       const uint16_t* B16, int d, const uint8_t* packed, uint16_t* Y,
-                       int8_t* xq, float* rowinfo, hipStream_t s);
+                       const uint16_t* B16, int d, const uint8_t* packed, int shuffled,
+                       uint16_t* Y, int8_t* xq, float* rowinfo, hipStream_t s);
+// Canonical packed codes [N][K/4] -> the decode layout read with shuffled = 1.
+hipError_t launch_gemv_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* out,
+                               hipStream_t s);
 
 }  // namespace lcvq

@@ -166,6 +166,30 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode layout of the codes, for deployment: the same bytes as the canonical packed
+ * [N, K/4] rearranged so that the decode product reads each 16-row x 256-column block as
+ * one contiguous 1 KiB tile. Tile t = (n / 16) * (K / 256) + kb; within it, the 16 bytes
+ * of row 16 (t / (K/256)) + j, columns 256 kb + 64 q .. +63, sit at byte 16 (16 q + j).
+ * The layout is this library's own (the pages fix only what the integer part holds).
+ *   packed  uint8 [N, K/4] canonical (2-bit fields, little-endian along K)         in
+ *   codes   uint8, N * K / 4 bytes, must not overlap packed                          out
+ *   N a multiple of 16, K a multiple of 256, N * K < 2^40; both pointers 16-byte aligned
+ * Errors: LCVQ_ERR_NULL, LCVQ_ERR_SHAPE, LCVQ_ERR_ALIGN, LCVQ_ERR_HIP.
+ */
+lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
+                                  void* stream);
+
+/*
+ * lcvq_gemv2b with the codes in the decode layout (lcvq_gemv2b_shuffle). Arguments,
+ * errors and numerics as for lcvq_gemv2b; the output is byte for byte the same as
+ * lcvq_gemv2b's on the canonical codes.
+ */
+lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                                   const uint8_t* codes, const void* A16, const void* B16,
+                                   void* Y, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Decode product of several matrices that share the input X (and K), for instance the
  * q, k and v projections, or gate and up, of one transformer layer; each matrix has its
  * own codes and its own A, B (LC-QAT summary, Methodology 1: A and B are shared within
@@ -174,10 +198,13 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
  * one launch; otherwise one matrix after the other, on `stream`.
  *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 256
  *   mats    host array of `count` descriptors, 1 <= count <= 8; mats[i].N a multiple of
- *           16; packed uint8 [N, K/4], A16 float16 [d, d], B16 float16 [d] and the output
- *           Y bfloat16 [M, N] are device pointers; outputs must not overlap anything
+ *           16; packed (N * K / 4 bytes: canonical [N, K/4] for layout 0, the decode
+ *           layout of lcvq_gemv2b_shuffle for layout 1), A16 float16 [d, d], B16 float16
+ *           [d] and the output Y bfloat16 [M, N] are device pointers; outputs must not
+ *           overlap anything
  *   workspace >= lcvq_gemv2b_workspace_size(M, largest N, K, d) bytes
- * Errors as for lcvq_gemv2b; LCVQ_ERR_SHAPE also for count outside 1..8.
+ * Errors as for lcvq_gemv2b; LCVQ_ERR_SHAPE also for count outside 1..8, LCVQ_ERR_VALUE
+ * for a layout other than 0 or 1.
  */
 typedef struct {
   const uint8_t* packed;
@@ -185,6 +212,7 @@ typedef struct {
   const void* B16;
   void* Y;
   int64_t N;
+  int32_t layout;              /* 0: canonical packed; 1: decode layout */
 } lcvq_gemv2b_matrix;
 lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
                                   const lcvq_gemv2b_matrix* mats, int count, void* workspace,

@@ -153,6 +153,28 @@ def test_gemv_errors(L):
     assert L.lcvq_gemv2b_workspace_size(1, 40, 256, 8) == 0
 
 
+def test_gemv_shuffle_errors(L):
+    def g(packed=P, N=256, K=256, codes=P):
+        return L.lcvq_gemv2b_shuffle(packed, N, K, codes, None)
+    assert g(packed=None) == 1
+    assert g(codes=None) == 1
+    assert g(N=40) == 2
+    assert g(N=0) == 2
+    assert g(K=320) == 2
+    assert g(K=128) == 2
+    assert g(codes=MIS) == 5
+
+    def s(**kw):
+        a = dict(X=P, M=1, N=256, K=256, d=8, codes=P, A=P, B=P, Y=P, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return L.lcvq_gemv2b_shuffled(a["X"], a["M"], a["N"], a["K"], a["d"], a["codes"],
+                                      a["A"], a["B"], a["Y"], a["ws"], a["wsb"], None)
+    assert s(codes=None) == 1
+    assert s(M=17) == 2
+    assert s(d=5) == 3
+    assert s(codes=MIS) == 5
+
+
 def test_gemv_batched_errors(L):
     import bit_weight_only_lc_amd as PK
     mats = (PK.GemvMatrix * 9)(*[PK.GemvMatrix(P, P, P, P, 256) for _ in range(9)])
@@ -174,6 +196,9 @@ def test_gemv_batched_errors(L):
     mats[2].Y = MIS
     assert g() == 5
     mats[2].Y = P
+    mats[1].layout = 2
+    assert g() == 8                                   # LCVQ_ERR_VALUE
+    mats[1].layout = 1
     mats[0].packed = None
     assert g() == 1
 

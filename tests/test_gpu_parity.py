@@ -317,6 +317,36 @@ def test_dge_backward(P, M, N, K, d, xdt, alpha):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("N,K", [(16, 256), (4096, 4096), (272, 14336)])
+def test_gemv_shuffle_layout(P, N, K):
+    """The decode layout holds the canonical bytes in the order its definition gives:
+    tile (n/16, kb), then 16-byte pieces q = 0..3 of the 64-byte block row, then rows."""
+    g = torch.Generator(device="cuda").manual_seed(7000 + N + K)
+    pk = torch.randint(0, 256, (N, K // 4), generator=g, dtype=torch.uint8, device="cuda")
+    codes = P.gemv2b_shuffle(pk)
+    torch.cuda.synchronize()
+    a = host(pk).reshape(N // 16, 16, K // 256, 4, 16)      # (r, j, kb, q, byte)
+    want = a.transpose(0, 2, 3, 1, 4).reshape(-1)           # (r, kb, q, j, byte)
+    assert np.array_equal(host(codes).reshape(-1), want)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (14336, 4096), (4096, 14336), (272, 8192)])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
+def test_gemv_shuffled_matches(P, N, K, M):
+    """The product on the decode layout gives the canonical product's bytes, on both the
+    one-launch and the prologue + product paths."""
+    d = 8
+    g = torch.Generator(device="cuda").manual_seed(7100 + N + K)
+    pk = torch.randint(0, 256, (N, K // 4), generator=g, dtype=torch.uint8, device="cuda")
+    A, B = SI.make_ab(d, seed=7200 + M)
+    A16, B16 = A.half().cuda(), B.half().cuda()
+    X = SI.make_act(M, K, seed=7300 + M, device="cuda")
+    y0 = P.gemv2b(X, pk, A16, B16, d)
+    y1 = P.gemv2b(X, P.gemv2b_shuffle(pk), A16, B16, d, shuffled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
 @pytest.mark.parametrize("shapes,K", [([4096, 1024, 1024], 4096), ([14336, 14336], 4096),
                                       ([8192, 272], 256), ([4096], 14336)])
 @pytest.mark.parametrize("M", [1, 2, 4])
@@ -337,8 +367,14 @@ def test_gemv_batched(P, shapes, K, M):
         singles.append(P.gemv2b(X, pk, A16, B16, d))
         refs.append((pk, A.half().double().numpy(), B.half().double().numpy()))
     P.lcvq_gemv2b_batched(X, mats, d)
+    # the same call with every other matrix in the decode layout
+    mixed = [(P.gemv2b_shuffle(pk), a16, b16, torch.empty_like(y), 1) if i % 2 else
+             (pk, a16, b16, torch.empty_like(y), 0)
+             for i, (pk, a16, b16, y) in enumerate(mats)]
+    P.lcvq_gemv2b_batched(X, mixed, d)
     torch.cuda.synchronize()
-    for (pk, _, _, Y), ys, (pkr, Ah, Bh) in zip(mats, singles, refs):
+    for (pk, _, _, Y), mx, ys, (pkr, Ah, Bh) in zip(mats, mixed, singles, refs):
         assert torch.equal(Y, ys)
+        assert torch.equal(mx[3], ys)
         e = rel(host(Y), O.gemv2b(host(X), host(pkr), Ah, Bh, d))
         assert e <= TOL, e
