@@ -226,43 +226,52 @@ def main():
             P.lcvq_quantize(wp, None, pk0, None)
             del wp
             copies = max(2, -(-(512 << 20) // pk0.numel()))
-            pool = [pk0.clone() for _ in range(copies)]
             A16, B16 = (t.half().to(dev) for t in SI.make_ab(8, seed=3000))
-            for m in SI.CONFIGS["c3_decode"]["Ms"]:
-                Xd = SI.make_act(m, k, seed=3100 + m, device=dev)
-                Yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-                ws = torch.empty(P.lcvq_gemv2b_workspace_size(m, n, k, 8), dtype=torch.uint8,
-                                 device=dev)
-                calls = 2 * copies
-                for i in range(copies):
-                    P.lcvq_gemv2b(Xd, pool[i], A16, B16, 8, Yd, ws)
-                evs = timed_events(torch, calls)
-                for i, (a, b) in enumerate(evs):
-                    L.lcvq_profile_next(5, a.cuda_event, b.cuda_event)
-                    P.lcvq_gemv2b(Xd, pool[i % copies], A16, B16, 8, Yd, ws)
-                torch.cuda.synchronize()
-                t_k = sum(a.elapsed_time(b) for a, b in evs) / calls * 1e-3
-                w0 = torch.cuda.Event(enable_timing=True)
-                w1 = torch.cuda.Event(enable_timing=True)
-                w0.record()
-                for i in range(calls):
-                    P.lcvq_gemv2b(Xd, pool[i % copies], A16, B16, 8, Yd, ws)
-                w1.record()
-                torch.cuda.synchronize()
-                t_w = w0.elapsed_time(w1) / calls * 1e-3
-                nbytes = n * k // 4 + 2 * m * k + 2 * m * n + 2 * (64 + 8)
-                decode[f"{n}x{k}_M{m}"] = {
-                    "bytes": nbytes, "kernel_us": round(t_k * 1e6, 2),
-                    "kernel_gbs": round(nbytes / t_k / 1e9, 1),
-                    "frac": round(nbytes / t_k / 1e9 / PEAK_HBM_GBS, 4),
-                    "call_us": round(t_w * 1e6, 2), "call_gbs": round(nbytes / t_w / 1e9, 1)}
+            # layout 0: canonical packed codes; layout 1: the decode layout written once by
+            # lcvq_gemv2b_shuffle (weight preparation, outside the timed calls)
+            for layout in (0, 1):
+                pool = [P.gemv2b_shuffle(pk0) if layout else pk0.clone() for _ in range(copies)]
+                call = P.lcvq_gemv2b_shuffled if layout else P.lcvq_gemv2b
+                for m in SI.CONFIGS["c3_decode"]["Ms"]:
+                    Xd = SI.make_act(m, k, seed=3100 + m, device=dev)
+                    Yd = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                    ws = torch.empty(P.lcvq_gemv2b_workspace_size(m, n, k, 8),
+                                     dtype=torch.uint8, device=dev)
+                    calls = 2 * copies
+                    for i in range(copies):
+                        call(Xd, pool[i], A16, B16, 8, Yd, ws)
+                    evs = timed_events(torch, calls)
+                    for i, (a, b) in enumerate(evs):
+                        L.lcvq_profile_next(5, a.cuda_event, b.cuda_event)
+                        call(Xd, pool[i % copies], A16, B16, 8, Yd, ws)
+                    torch.cuda.synchronize()
+                    t_k = sum(a.elapsed_time(b) for a, b in evs) / calls * 1e-3
+                    w0 = torch.cuda.Event(enable_timing=True)
+                    w1 = torch.cuda.Event(enable_timing=True)
+                    w0.record()
+                    for i in range(calls):
+                        call(Xd, pool[i % copies], A16, B16, 8, Yd, ws)
+                    w1.record()
+                    torch.cuda.synchronize()
+                    t_w = w0.elapsed_time(w1) / calls * 1e-3
+                    nbytes = n * k // 4 + 2 * m * k + 2 * m * n + 2 * (64 + 8)
+                    rec = {"bytes": nbytes, "kernel_us": round(t_k * 1e6, 2),
+                           "kernel_gbs": round(nbytes / t_k / 1e9, 1),
+                           "frac": round(nbytes / t_k / 1e9 / PEAK_HBM_GBS, 4),
+                           "call_us": round(t_w * 1e6, 2),
+                           "call_gbs": round(nbytes / t_w / 1e9, 1)}
+                    if layout:
+                        decode[f"{n}x{k}_M{m}"]["decode_layout"] = rec
+                    else:
+                        decode[f"{n}x{k}_M{m}"] = rec
             del pool
             torch.cuda.empty_cache()
 
     # ------------------------------------------------- decode step of an 8B-shaped stack
     # One token through all 7 projections of 32 layers (1.63 GiB of codes, far beyond the
-    # last-level cache), as 224 single calls and as 128 calls that group the matrices
-    # sharing an input (q, k, v and gate, up) into one launch each.
+    # last-level cache), as 224 single calls, as 128 calls that group the matrices sharing
+    # an input (q, k, v and gate, up) into one launch each, and as the same 128 calls on
+    # codes prepared once in the decode layout (lcvq_gemv2b_shuffle, outside the timing).
     decode_stack = None
     if not args.no_decode:
         shapes = SI.CONFIGS["c4_stack_8b_layer"]["mats"]     # q, k, v, o, gate, up, down
@@ -287,20 +296,30 @@ def main():
                 for pk, y, k in lay:
                     P.lcvq_gemv2b(xs[k], pk, A16, B16, dd, y, ws_s)
 
-        def run_grouped():
-            for lay in mats:
-                for g in groups:
-                    k = lay[g[0]][2]
-                    if len(g) == 1:
-                        pk, y, _ = lay[g[0]]
-                        P.lcvq_gemv2b(xs[k], pk, A16, B16, dd, y, ws_s)
-                    else:
-                        P.lcvq_gemv2b_batched(xs[k], [(lay[i][0], A16, B16, lay[i][1]) for i in g],
-                                              dd, ws_s)
+        def grouped(stack, layout):
+            one = P.lcvq_gemv2b_shuffled if layout else P.lcvq_gemv2b
+
+            def run():
+                for lay in stack:
+                    for g in groups:
+                        k = lay[g[0]][2]
+                        if len(g) == 1:
+                            pk, y, _ = lay[g[0]]
+                            one(xs[k], pk, A16, B16, dd, y, ws_s)
+                        else:
+                            P.lcvq_gemv2b_batched(
+                                xs[k], [(lay[i][0], A16, B16, lay[i][1], layout) for i in g],
+                                dd, ws_s)
+            return run
+
+        mats_dl = [[(P.gemv2b_shuffle(pk), y, k) for pk, y, k in lay] for lay in mats]
+        run_grouped = grouped(mats, 0)
 
         decode_stack = {"codes_bytes": total_bytes, "layers": layers, "tokens": 1}
         for name, fn, calls in (("single", run_single, layers * 7),
-                                ("grouped", run_grouped, layers * len(groups))):
+                                ("grouped", run_grouped, layers * len(groups)),
+                                ("grouped_decode_layout", grouped(mats_dl, 1),
+                                 layers * len(groups))):
             fn()
             torch.cuda.synchronize()
             e0 = torch.cuda.Event(enable_timing=True)
@@ -344,7 +363,7 @@ def main():
                                   "graph_ms": round(t_g * 1e3, 3),
                                   "graph_gbs": round(total_bytes / t_g / 1e9, 1),
                                   "graph_frac": round(total_bytes / t_g / 1e9 / PEAK_HBM_GBS, 4)}
-        del mats
+        del mats, mats_dl
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- HBM copy ceiling
