@@ -13,6 +13,7 @@
 // The order in which a lane's 16 codes reach the MFMA differs from their order in k;
 // the prologue writes X' limbs in that same order.
 #include <algorithm>
+#include <atomic>
 
 #include "lcvq_device.h"
 #include "lcvq_internal.h"
@@ -463,11 +464,16 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
 template <int D, int RG, int KSW, int M>
 static void launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
                          const GemvBatch& b, int K) {
-  static bool attr = false;                        // LDS beyond 64 KiB must be requested
-  if (!attr) {
+  // Dynamic LDS beyond 64 KiB must be requested for the kernel, once per device (the
+  // first 64 devices are remembered; beyond that it is requested on every launch).
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+  if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW, M>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
+    done.fetch_or(bit, std::memory_order_acq_rel);
   }
   LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW, M>), grid, dim3(GWF * 64), shm, s, X, b, K);
 }
