@@ -718,40 +718,30 @@ __device__ __forceinline__ void ring_expand(RingFrags<CODES_ARE_L, WI, WJ>& f, c
   for (int i = 0; i < RingFrags<CODES_ARE_L, WI, WJ>::NC; ++i) f.c[i] = codes_expand(f.w[i], k);
 }
 
+// The MFMAs of one sub-step on fragments fc, with the expansion of the next fragments fn
+// (whose LDS reads were issued just before) interleaved between them.
 template <bool CODES_ARE_L, int WI, int WJ>
-__device__ __forceinline__ void mma_ring_stage(const uint8_t* slot, f32x16 acc[WI][WJ], int wp,
-                                               int wq, int lane) {
+__device__ __forceinline__ void ring_mfma(const RingFrags<CODES_ARE_L, WI, WJ>& fc,
+                                          RingFrags<CODES_ARE_L, WI, WJ>& fn,
+                                          f32x16 acc[WI][WJ], const ExpandK& ek) {
   using F = RingFrags<CODES_ARE_L, WI, WJ>;
-  F f[2];
-  const ExpandK ek = expand_consts(lane);
-  ring_read<CODES_ARE_L, WI, WJ>(slot, 0, wp, wq, lane, f[0]);
-  ring_expand<CODES_ARE_L, WI, WJ>(f[0], ek);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = s & 1;
-    // LDS reads of the next sub-step go out before this sub-step's MFMAs; the code
-    // expansion of the next sub-step is interleaved with those MFMAs.
-    if (s < 3) ring_read<CODES_ARE_L, WI, WJ>(slot, s + 1, wp, wq, lane, f[c ^ 1]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < WI; ++i)
 #pragma unroll
-    for (int i = 0; i < WI; ++i)
-#pragma unroll
-      for (int j = 0; j < WJ; ++j) {
-        const bf16x8 av = CODES_ARE_L ? f[c].c[i] : f[c].b[i];
-        const bf16x8 bv = CODES_ARE_L ? f[c].b[j] : f[c].c[j];
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
-      }
-    if (s < 3) {
-      ring_expand<CODES_ARE_L, WI, WJ>(f[c ^ 1], ek);
-      constexpr int NV = (F::NC * 10 + WI * WJ - 1) / (WI * WJ);  // VALU per MFMA slot
-#pragma unroll
-      for (int g = 0; g < WI * WJ; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
-      }
+    for (int j = 0; j < WJ; ++j) {
+      const bf16x8 av = CODES_ARE_L ? fc.c[i] : fc.b[i];
+      const bf16x8 bv = CODES_ARE_L ? fc.b[j] : fc.c[j];
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[i][j], 0, 0, 0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  ring_expand<CODES_ARE_L, WI, WJ>(fn, ek);
+  constexpr int NV = (F::NC * 10 + WI * WJ - 1) / (WI * WJ);  // VALU per MFMA slot
+#pragma unroll
+  for (int g = 0; g < WI * WJ; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Wait until at most `stages_after` (0..2) stages of this wave's ring loads are still
@@ -803,18 +793,38 @@ void k_gemm_ring(GemmArgs a) {
       if (st < nk)
         issue_ring_stage<NW>(smem + st * SLOTB, mat, ld, row0, a.M, st * BK, a.codes, rowblock,
                              nk, st, wave, lane);
+    // The barrier of each stage sits before its last sub-step, so that the first
+    // fragments of the next stage are read and expanded under that sub-step's MFMAs
+    // instead of after a barrier at the stage boundary. Plain s_barrier: __syncthreads()
+    // would also wait for every outstanding load (a workgroup release fence), which would
+    // drain the ring; the memory clobber keeps LDS reads from moving across it.
+    using F = RingFrags<CL, WI, WJ>;
+    F f[2];
+    const ExpandK ek = expand_consts(lane);
+    wait_vm_stages<NW>(nk - 1 < 2 ? nk - 1 : 2);
+    asm volatile("s_barrier" ::: "memory");
+    ring_read<CL, WI, WJ>(smem, 0, wp, wq, lane, f[0]);
+    ring_expand<CL, WI, WJ>(f[0], ek);
     for (int kt = 0; kt < nk; ++kt) {
-      const int after = nk - 1 - kt;
-      wait_vm_stages<NW>(after < 2 ? after : 2);
-      // Plain s_barrier: __syncthreads() would also wait for every outstanding load
-      // (a workgroup release fence), which would drain the ring. The memory clobber
-      // keeps the compiler from moving LDS reads across it.
+      const uint8_t* slot = smem + (kt % RING) * SLOTB;
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        ring_read<CL, WI, WJ>(slot, s + 1, wp, wq, lane, f[(s & 1) ^ 1]);
+        ring_mfma<CL, WI, WJ>(f[s & 1], f[(s & 1) ^ 1], acc, ek);
+      }
+      // Stage kt + 1 must have landed (stage kt + 2 may still be in flight); after the
+      // barrier every wave is past sub-step 2 of stage kt, so stage kt - 1's slot is free
+      // for stage kt + 3.
+      wait_vm_stages<NW>(kt + 2 < nk ? 1 : 0);
       asm volatile("s_barrier" ::: "memory");
       if (kt + RING - 1 < nk)
         issue_ring_stage<NW>(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
                              (kt + RING - 1) * BK, a.codes, rowblock, nk, kt + RING - 1, wave,
                              lane);
-      mma_ring_stage<CL, WI, WJ>(smem + (kt % RING) * SLOTB, acc, wp, wq, lane);
+      // Sub-step 3, with stage kt + 1's first fragments read and expanded under it (on
+      // the last stage this reads a free slot; the values are not used).
+      ring_read<CL, WI, WJ>(smem + ((kt + 1) % RING) * SLOTB, 0, wp, wq, lane, f[0]);
+      ring_mfma<CL, WI, WJ>(f[1], f[0], acc, ek);
     }
     __syncthreads();
   }
