@@ -227,13 +227,16 @@ __device__ __forceinline__ void mma_stage(const uint8_t* Ls, const uint8_t* Rs, 
 
 __device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, float a, float b, float c, float d) {
   if (f32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = make_float4(a, b, c, d);
+    __builtin_nontemporal_store(f32x4{a, b, c, d},
+                                reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx));
   } else {
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
   }
 }
 
 // ---- epilogues -----------------------------------------------------------------------
+// Outputs (Y, dX, dWp) are written once and not read again by the kernel: they go out as
+// non-temporal stores, which measured 1-3 us faster per product than ordinary ones.
 // Accumulator layout (32x32 block): lane l holds column l%32 and, in register r, row
 // 8*(r/4) + 4*(l/32) + r%4. For DX and DW the rows run along the d-vectors: a swap of
 // register halves between lanes l and l^32 (gather_dvectors) gives every lane whole
@@ -295,11 +298,11 @@ __device__ __forceinline__ void store_block_rows_dge(const float* S, float* out,
     if (row < rows && k0 + kq < K) {
       const int64_t idx = (int64_t)row * ld + k0 + kq;
       const float4 w = *reinterpret_cast<const float4*>(wp + idx);
-      *reinterpret_cast<float4*>(out + idx) =
-          make_float4(S[(kq + 0) * SROW + rr] * dge_slope(w.x, alpha, c),
-                      S[(kq + 1) * SROW + rr] * dge_slope(w.y, alpha, c),
-                      S[(kq + 2) * SROW + rr] * dge_slope(w.z, alpha, c),
-                      S[(kq + 3) * SROW + rr] * dge_slope(w.w, alpha, c));
+      __builtin_nontemporal_store(f32x4{S[(kq + 0) * SROW + rr] * dge_slope(w.x, alpha, c),
+                                        S[(kq + 1) * SROW + rr] * dge_slope(w.y, alpha, c),
+                                        S[(kq + 2) * SROW + rr] * dge_slope(w.z, alpha, c),
+                                        S[(kq + 3) * SROW + rr] * dge_slope(w.w, alpha, c)},
+                                  reinterpret_cast<f32x4*>(out + idx));
     }
   }
 }
@@ -337,12 +340,13 @@ __device__ void epilogue_fwd(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int 
         const int64_t idx = (int64_t)p * a.N + q;
         if (a.out_f32) {
           float* o = static_cast<float*>(a.out) + idx;
-          *reinterpret_cast<f32x4*>(o) = x + b;
-          *reinterpret_cast<f32x4*>(o + 4) = y + b;
+          __builtin_nontemporal_store(x + b, reinterpret_cast<f32x4*>(o));
+          __builtin_nontemporal_store(y + b, reinterpret_cast<f32x4*>(o + 4));
         } else {
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + idx) =
-              make_uint4(pack_bf16x2(x[0] + b, x[1] + b), pack_bf16x2(x[2] + b, x[3] + b),
-                         pack_bf16x2(y[0] + b, y[1] + b), pack_bf16x2(y[2] + b, y[3] + b));
+          __builtin_nontemporal_store(
+              u32x4{pack_bf16x2(x[0] + b, x[1] + b), pack_bf16x2(x[2] + b, x[3] + b),
+                    pack_bf16x2(y[0] + b, y[1] + b), pack_bf16x2(y[2] + b, y[3] + b)},
+              reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + idx));
         }
       }
     }
@@ -367,12 +371,14 @@ __device__ __forceinline__ void store_block_rows64(const float* S, void* out, in
       const int64_t idx = (int64_t)row * ld + k0 + kq;
       if (f32) {
         float* o = static_cast<float*>(out) + idx;
-        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(o));
+        __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]},
+                                    reinterpret_cast<f32x4*>(o + 4));
       } else {
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + idx) =
-            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        __builtin_nontemporal_store(
+            u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                  pack_bf16x2(v[6], v[7])},
+            reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx));
       }
     }
   }
