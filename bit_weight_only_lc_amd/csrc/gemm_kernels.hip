@@ -78,6 +78,12 @@ struct GemmArgs {
   const uint8_t* mask;         // DW: mask bits [N][K/8]
   float* partials;             // DW: [ntiles][d*d + d]
   const float* dge_wp;         // DW with the DGE estimator: proxies [N][K], else NULL
+  // DX launched after DW: the DW tiles' dA/dB partials [red_tiles][d*d + d] to reduce
+  // into red_dA, red_dB (NULL: nothing to reduce)
+  const float* red_partials;
+  int red_tiles;
+  float* red_dA;
+  float* red_dB;
   float dge_alpha, dge_c;      // sharpness and alpha / (2 tanh(alpha / 2))
 };
 
@@ -750,6 +756,31 @@ __device__ __forceinline__ void ring_mfma(const RingFrags<CODES_ARE_L, WI, WJ>& 
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// dA and dB from the dW product's per-tile partials, summed in a fixed order: output o by
+// tile o mod ntiles; thread t adds partials t, t + NT, ... of it, then a tree over the NT
+// threads. Run by the dX product (launched after dW) once its own work is done, so that
+// the reduction needs no launch of its own.
+template <int D, int NT>
+__device__ void reduce_dw_partials(const GemmArgs& a, int tile, int ntiles, int tid, float* red) {
+  constexpr int NOUT = D * D + D;
+  for (int o = tile; o < NOUT; o += ntiles) {
+    float s = 0.f;
+    for (int i = tid; i < a.red_tiles; i += NT) s += a.red_partials[(int64_t)i * NOUT + o];
+    red[tid] = s;
+    __syncthreads();
+#pragma unroll
+    for (int w = NT / 2; w >= 1; w >>= 1) {
+      if (tid < w) red[tid] += red[tid + w];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      if (o < D * D) a.red_dA[o] = red[0];
+      else a.red_dB[o - D * D] = red[0];
+    }
+    __syncthreads();
+  }
+}
+
 // Wait until at most `stages_after` (0..2) stages of this wave's ring loads are still
 // outstanding; the other counters are not waited on.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -853,6 +884,10 @@ void k_gemm_ring(GemmArgs a) {
     static_assert(NW * DX_WAVE_LDS <= 120 * 1024, "dX staging below the copy of A");
     epilogue_dx<D, WI, WJ>(a, acc, p0, q0, wp, wq, lane,
                            reinterpret_cast<float*>(smem + wave * DX_WAVE_LDS), Alds);
+    // 2 KiB at 128 KiB: above the staging areas and the copy of A
+    if (a.red_partials)
+      reduce_dw_partials<D, NW * 64>(a, tile, a.ntiles, tid,
+                                     reinterpret_cast<float*>(smem + 128 * 1024));
   }
 }
 
@@ -1085,8 +1120,15 @@ hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint
 
 hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16_t* dy_lo,
                           const float* r, const float* A, const float* B, int M, int N, int K,
-                          int d, void* dX, bool f32, hipStream_t s) {
+                          int d, void* dX, bool f32, const float* dw_partials, float* dA,
+                          float* dB, hipStream_t s) {
   GemmArgs a = {};
+  if (dw_partials) {                         // the dW product's tiles: ceil(K/BT) x ceil(N/BT)
+    a.red_partials = dw_partials;
+    a.red_tiles = ((K + BT - 1) / BT) * ((N + BT - 1) / BT);
+    a.red_dA = dA;
+    a.red_dB = dB;
+  }
   a.P = K; a.Q = M; a.R = N;
   a.codes = r16t;
   a.Rmat[0] = dy; a.Rmat[1] = dy_lo;
@@ -1101,7 +1143,7 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
                           const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, const float* dge_wp,
-                          float dge_alpha, hipStream_t s) {
+                          float dge_alpha, bool reduce, hipStream_t s) {
   GemmArgs a = {};
   a.P = K; a.Q = N; a.R = M;
   a.Lmat[0] = x; a.Rmat[0] = dy;
@@ -1118,7 +1160,7 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
   a.dge_alpha = dge_alpha;
   a.dge_c = dge_wp ? (float)((double)dge_alpha / (2.0 * tanh((double)dge_alpha / 2.0))) : 0.f;
   hipError_t e = launch_op<OP_DW>(a, d, s);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !reduce) return e;
   hipLaunchKernelGGL(k_reduce_partials, dim3(d * d + d), dim3(256), 0, s, partials, a.ntiles,
                      d * d + d, dA, dB, d);
   return hipGetLastError();

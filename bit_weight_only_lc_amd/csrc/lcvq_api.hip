@@ -227,16 +227,21 @@ lcvq_status_t linear_bwd_impl(const void* dY, const void* X, lcvq_dtype_t dt, in
   if (e != hipSuccess) return LCVQ_ERR_HIP;
   const uint16_t* dyb = f32 ? dy_hi : static_cast<const uint16_t*>(dY);
   const uint16_t* xb = f32 ? x_hi : static_cast<const uint16_t*>(X);
+  // dW first; with dX wanted, the dX product then also reduces dW's dA/dB partials
+  // (saving the reduction's own launch), otherwise a small kernel does.
+  e = launch_gemm_dw(xb, x_lo, dyb, dy_lo, packed, mask, A, (int)M, (int)N, (int)K, d, dWp,
+                     partials, dA, dB, Wp, alpha, !dX, s);
+  if (e != hipSuccess) return LCVQ_ERR_HIP;
   if (dX) {
     if (!merged) {
       e = launch_codes_to_r16t(packed, N, K, r16t, s);
       if (e != hipSuccess) return LCVQ_ERR_HIP;
     }
-    e = launch_gemm_dx(r16t, dyb, dy_lo, r, A, B, (int)M, (int)N, (int)K, d, dX, f32, s);
+    e = launch_gemm_dx(r16t, dyb, dy_lo, r, A, B, (int)M, (int)N, (int)K, d, dX, f32, partials,
+                       dA, dB, s);
     if (e != hipSuccess) return LCVQ_ERR_HIP;
   }
-  return from_hip(launch_gemm_dw(xb, x_lo, dyb, dy_lo, packed, mask, A, (int)M, (int)N,
-                                 (int)K, d, dWp, partials, dA, dB, Wp, alpha, s));
+  return LCVQ_OK;
 }
 }  // namespace
 

@@ -58,14 +58,16 @@ int gemm_tiles(int64_t P, int64_t Q);
 hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint32_t* r16,
                            const float* beta, int M, int N, int K, int d, void* Y, bool y_f32,
                            hipStream_t s);
+// dX; with dw_partials (the dW product already enqueued) it also reduces them into dA, dB.
 hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16_t* dy_lo,
                           const float* r, const float* A, const float* B, int M, int N, int K,
-                          int d, void* dX, bool f32, hipStream_t s);
+                          int d, void* dX, bool f32, const float* dw_partials, float* dA,
+                          float* dB, hipStream_t s);
 hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_t* dy,
                           const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, const float* dge_wp,
-                          float dge_alpha, hipStream_t s);
+                          float dge_alpha, bool reduce, hipStream_t s);
 
 // Matrices that share X for one fused decode launch (kernel argument, by value).
 constexpr int GEMV_MAX_BATCH = 8;
