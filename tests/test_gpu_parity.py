@@ -140,6 +140,30 @@ def test_layer_shapes(P, d, xdt, M, N, K):
     check_layer(P, inp, d, f"M={M} N={N} K={K} d={d} {xdt}")
 
 
+@pytest.mark.parametrize("d,xdt", [(8, "bf16"), (16, "f32")])
+def test_backward_without_dx(P, d, xdt):
+    """Without dX the dA/dB partials are reduced by a launch of their own instead of by the
+    dX product's tiles: dWp is the same bytes, dA and dB the same sums in another order."""
+    M, N, K = 513, 576, 320
+    inp = SI.make_layer(N, K, M, d, seed=8100 + d, x_dtype=xdt, lo=-2.0, hi=5.0)
+    dev = {k: v.cuda() for k, v in inp.items()}
+    f = P.linear_fwd(dev["X"], dev["Wp"], dev["A"], dev["B"], d)
+    with_dx = P.linear_bwd(dev["dY"], dev["X"], f["packed"], f["mask"], dev["A"], dev["B"], d)
+    no_dx = P.linear_bwd(dev["dY"], dev["X"], f["packed"], f["mask"], dev["A"], dev["B"], d,
+                         want_dx=False)
+    torch.cuda.synchronize()
+    assert no_dx["dX"] is None
+    assert torch.equal(no_dx["dWp"], with_dx["dWp"])
+    for k in ("dA", "dB"):
+        assert rel(host(no_dx[k]), host(with_dx[k])) <= 1e-5, k
+    wp = inp["Wp"].numpy()
+    A, B = inp["A"].double().numpy(), inp["B"].double().numpy()
+    z, m = O.quantize(wp)
+    ob = O.linear_bwd(host(inp["dY"]), host(inp["X"]), z, m, A, B, d)
+    for k in ("dWp", "dA", "dB"):
+        assert rel(host(no_dx[k]), ob[k]) <= TOL, k
+
+
 def test_degenerate_A(P):
     """A = 0, negative and singular A are valid decodes (decoupleQ section 3.2 allows a
     zero or negative scale)."""
