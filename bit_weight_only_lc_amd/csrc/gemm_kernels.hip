@@ -952,31 +952,93 @@ __device__ __forceinline__ void issue_dw_stage(uint8_t* slot, const uint16_t* X,
   }
 }
 
-template <int WJ>
-__device__ __forceinline__ void mma_dw_stage(const uint8_t* slot, f32x16 acc[4][WJ], int wp, int wq,
-                                             int lane) {
-  const uint8_t* Xt = slot;
-  const uint8_t* Yt = slot + TTILEB;
-  bf16x8 af[2][4], bf[2][WJ];
-  auto load = [&](int s, bf16x8* fa, bf16x8* fb) {
+// Stages after the first: the two rows of each load instruction are uniform, so a load
+// is a scalar row base plus one of two per-lane byte offsets (the swizzle of rows 2i and
+// 2i + 1 alternates with i), which keeps few address registers live in the main loop.
+// In a stage that runs past M, a load whose pair of rows reaches M reads row
+// min(row, M - 1) into both halves (a valid row: such a stage is never the first, so
+// M > 64), and zero_dw_rows then clears the rows at or past M, which are contraction
+// terms.
+struct DwLaneOffsets {
+  uint32_t v[2][2];            // [operand][i & 1]
+};
+__device__ __forceinline__ DwLaneOffsets dw_lane_offsets(int N, int K, int p0, int q0, int lane) {
+  DwLaneOffsets o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = trans_frag(Xt, wp * 128 + i * 32, s, lane);
+  for (int op = 0; op < 2; ++op) {
+    const int ld = op == 0 ? K : N;
+    const int c0 = op == 0 ? p0 : q0;
 #pragma unroll
-    for (int j = 0; j < WJ; ++j) fb[j] = trans_frag(Yt, wq * 32 * WJ + j * 32, s, lane);
-  };
-  load(0, af[0], bf[0]);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = s & 1;
-    if (s < 3) load(s + 1, af[c ^ 1], bf[c ^ 1]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < WJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int par = 0; par < 2; ++par) {
+      const int r = par * 2 + (lane >> 5);             // row mod 4 of this lane's load
+      const int c = (lane & 31) ^ tswz(r);
+      int col = c0 + c * 8;
+      col = col < ld ? col : ld - 8;
+      o.v[op][par] = (uint32_t)(((lane >> 5) * ld + col) * 2);
+    }
   }
+  return o;
+}
+__device__ __forceinline__ void issue_dw_stage_rows(uint8_t* slot, const uint16_t* X,
+                                                    const uint16_t* dY, int M, int N, int K,
+                                                    int m0, const DwLaneOffsets& o, int wave,
+                                                    int lane) {
+#pragma unroll
+  for (int op = 0; op < 2; ++op) {
+    const uint16_t* mat = op == 0 ? X : dY;
+    const int ld = op == 0 ? K : N;
+    uint8_t* tile = slot + op * TTILEB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int row = m0 + wave * 8 + i * 2;                   // uniform
+      uint32_t off = o.v[op][i & 1];
+      if (row + 1 >= M) {
+        // the second row of the pair (or both) lies past M: both halves read row
+        // min(row, M - 1), whose copy in a row past M is cleared afterwards
+        row = row < M ? row : M - 1;
+        off -= (uint32_t)((lane >> 5) * ld * 2);
+      }
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(mat + (int64_t)row * ld);
+      __builtin_amdgcn_global_load_lds(base + off,
+                                       (LCVQ_LDS void*)(tile + (wave * 8 + i * 2) * TROWB), 16, 0, 0);
+    }
+  }
+}
+// Wave w clears its own rows [8w, 8w + 8) of both tiles where m0 + row >= M; called after
+// its loads have landed and before the stage's barrier.
+__device__ __forceinline__ void zero_dw_rows(uint8_t* slot, int m0, int M, int wave, int lane) {
+#pragma unroll
+  for (int op = 0; op < 2; ++op)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wave * 8 + i * 2 + (lane >> 5);
+      if (m0 + r >= M)
+        *reinterpret_cast<uint4*>(slot + op * TTILEB + r * TROWB + (lane & 31) * 16) =
+            make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <int WJ>
+struct DwFrags {
+  bf16x8 a[4], b[WJ];
+};
+
+template <int WJ>
+__device__ __forceinline__ void dw_read(const uint8_t* slot, int s, int wp, int wq, int lane,
+                                        DwFrags<WJ>& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = trans_frag(slot, wp * 128 + i * 32, s, lane);
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) f.b[j] = trans_frag(slot + TTILEB, wq * 32 * WJ + j * 32, s, lane);
+}
+
+template <int WJ>
+__device__ __forceinline__ void dw_mfma(const DwFrags<WJ>& f, f32x16 acc[4][WJ]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // Codes: 16-byte direct loads, 2 per lane; mask: 4-byte direct loads (mask rows are only
@@ -1016,9 +1078,11 @@ void k_gemm_dw(GemmArgs a) {
   int tp, tq, tile;
   if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
   const int p0 = tp * BT, q0 = tq * BT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WGQ, wq = wave % WGQ;
   const int nk = (a.R + BK - 1) / BK;
+  const DwLaneOffsets lo = dw_lane_offsets(a.N, a.K, p0, q0, lane);
   issue_dw_codes(smem, a.packed, a.mask, a.N, a.K, p0, q0, wave, lane);
 
   f32x16 acc[4][WJ];
@@ -1035,13 +1099,33 @@ void k_gemm_dw(GemmArgs a) {
     issue_dw_stage(smem, Lp, Rp, a.M, a.N, a.K, 0, p0, q0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // Every transposing LDS read of a stage is issued before the next stage's direct
+    // loads: the compiler makes an LDS read that follows a direct global->LDS load in
+    // program order wait for that load, which would serialize the two. Sub-steps 0-2 are
+    // read first, sub-step 3 into sub-step 0's registers once its MFMAs have issued, and
+    // the next stage's loads then run under the MFMAs of sub-steps 1-3.
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
+      const uint8_t* slot = smem + (kt & 1) * 2 * TTILEB;
+      DwFrags<WJ> f0, f1, f2;
+      dw_read<WJ>(slot, 0, wp, wq, lane, f0);
+      dw_read<WJ>(slot, 1, wp, wq, lane, f1);
+      dw_read<WJ>(slot, 2, wp, wq, lane, f2);
+      __builtin_amdgcn_sched_barrier(0);
+      dw_mfma<WJ>(f0, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      dw_read<WJ>(slot, 3, wp, wq, lane, f0);
+      __builtin_amdgcn_sched_barrier(0);
+      uint8_t* next = smem + ((kt & 1) ^ 1) * 2 * TTILEB;
       if (kt + 1 < nk)
-        issue_dw_stage(smem + (cur ^ 1) * 2 * TTILEB, Lp, Rp, a.M, a.N, a.K, (kt + 1) * BK, p0,
-                       q0, wave, lane);
-      mma_dw_stage<WJ>(smem + cur * 2 * TTILEB, acc, wp, wq, lane);
+        issue_dw_stage_rows(next, Lp, Rp, a.M, a.N, a.K, (kt + 1) * BK, lo, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      dw_mfma<WJ>(f1, acc);
+      dw_mfma<WJ>(f2, acc);
+      dw_mfma<WJ>(f0, acc);
+      __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
+      if (kt + 1 < nk && (kt + 1) * BK + wave * 8 + 8 > a.M)
+        zero_dw_rows(next, (kt + 1) * BK, a.M, wave, lane);
       __syncthreads();
     }
   }

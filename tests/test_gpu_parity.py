@@ -242,8 +242,8 @@ def test_gemv_d(P, N, K, M, d):
 @pytest.mark.parametrize("N,K,M", [(4096, 14336, 16), (14336, 4096, 1), (272, 8192, 5),
                                    (256, 16640, 2)])
 def test_gemv_repeat_shared_workspace(P, N, K, M):
-    """Calls that reuse one workspace (its row-set counters included) give identical
-    bytes, and the slices of long rows add up to the oracle's product."""
+    """Calls that reuse one workspace give identical bytes, and the partial sums of long
+    rows add up to the oracle's product."""
     d = 8
     note(f"gemv repeat N={N} K={K} M={M}")
     wp = SI.make_wp(N, K, seed=5000 + N + K, device="cuda")
@@ -311,6 +311,64 @@ def test_graph_replay_matches_eager(P):
         junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
+
+
+def test_decode_graph_replay_matches_eager(P):
+    """The decode calls (one-launch path, prologue + product path, decode layout and the
+    batched call) captured in one HIP graph give the eager calls' bytes on every replay,
+    with other GPU work and synchronizations between the replays."""
+    d, K = 8, 4096
+    note("decode graph replay")
+    g = torch.Generator(device="cuda").manual_seed(7700)
+    pks = [torch.randint(0, 256, (n, K // 4), generator=g, dtype=torch.uint8, device="cuda")
+           for n in (1024, 4096)]
+    A, B = SI.make_ab(d, seed=7701)
+    A16, B16 = A.half().cuda(), B.half().cuda()
+    x1 = SI.make_act(1, K, seed=7702, device="cuda")
+    x16 = SI.make_act(16, K, seed=7703, device="cuda")
+    codes = P.gemv2b_shuffle(pks[1])
+    ys = {"fused": torch.empty((1, 4096), dtype=torch.bfloat16, device="cuda"),
+          "two": torch.empty((16, 4096), dtype=torch.bfloat16, device="cuda"),
+          "layout": torch.empty((1, 4096), dtype=torch.bfloat16, device="cuda"),
+          "b0": torch.empty((16, 1024), dtype=torch.bfloat16, device="cuda"),
+          "b1": torch.empty((16, 4096), dtype=torch.bfloat16, device="cuda")}
+    ws = torch.empty(P.lcvq_gemv2b_workspace_size(16, 4096, K, d), dtype=torch.uint8,
+                     device="cuda")
+
+    def calls():
+        P.lcvq_gemv2b(x1, pks[1], A16, B16, d, ys["fused"], ws)
+        P.lcvq_gemv2b(x16, pks[1], A16, B16, d, ys["two"], ws)
+        P.lcvq_gemv2b_shuffled(x1, codes, A16, B16, d, ys["layout"], ws)
+        P.lcvq_gemv2b_batched(x16, [(pks[0], A16, B16, ys["b0"], 0),
+                                    (codes, A16, B16, ys["b1"], 1)], d, ws)
+
+    calls()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in ys.items()}
+    assert torch.equal(ref["fused"], ref["layout"])
+    assert torch.equal(ref["two"], ref["b1"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        calls()
+    for i in range(4):
+        for v in ys.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for k in ys:
+            assert torch.equal(ys[k], ref[k]), (i, k)
+        junk = torch.randn(1 << 20, device="cuda").sum()     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+    e = rel(host(ref["two"]), O.gemv2b(host(x16), host(pks[1]), A.half().double().numpy(),
+                                       B.half().double().numpy(), d))
+    assert e <= TOL, e
 
 
 @pytest.mark.parametrize("d,xdt,alpha", [(8, "bf16", 6.0), (4, "f32", 2.0), (16, "bf16", 20.0)])
