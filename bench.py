@@ -14,7 +14,12 @@ HBM. Also measured in the same run:
   * the CPU oracle on the same step (the full 4096-token step on the host cores).
 Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--clock-warmup-s 0.5]
+
+Before the W warmup steps the step runs untimed for --clock-warmup-s seconds of wall
+time: the GPU starts from its idle clock state, and the shader clock needs tens of
+milliseconds of load to reach its working level (with 5 warmup steps and no clock
+warm-up the timed steps ran about 18% slower than sustained back-to-back steps).
 """
 
 import argparse
@@ -70,8 +75,9 @@ def recorded_traffic(kernel):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--clock-warmup-s", type=float, default=0.5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=10)
@@ -89,6 +95,18 @@ def timed_events(torch, n):
         evs.append((a, b))
     torch.cuda.synchronize()
     return evs
+
+
+def clock_warmup(torch, fn, seconds):
+    """Runs fn, untimed, until `seconds` of wall time have passed; returns the call count."""
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        n += 10
+    return n
 
 
 def main():
@@ -125,14 +143,15 @@ def main():
         P.lcvq_linear_fwd(X, Wp, A, B, d, Y, packed, mask, None, wsf)
         P.lcvq_linear_bwd(dY, X, packed, mask, A, B, d, dX, dWp, dA, dB, wsb)
 
+    kern_ids = list(KERNELS.items())
+    step_evs = timed_events(torch, args.steps)
+    clock_steps = clock_warmup(torch, step, args.clock_warmup_s)
     for _ in range(args.warmup):
         step()
     # Per-kernel durations come from the timed steps themselves: step i arms the timing
     # hook for kernel number i mod 5 of KERNELS, whose launch is then bracketed by two
-    # events on the library's stream. Under sustained back-to-back steps the clock runs lower than in
-    # an isolated step, so these are the durations that make up the measured step time.
-    kern_ids = list(KERNELS.items())
-    step_evs = timed_events(torch, args.steps)
+    # events on the library's stream, so they are the durations that make up the measured
+    # step time.
     kern_evs = {name: [] for _, name in kern_ids}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -220,6 +239,7 @@ def main():
     decode = None
     if not args.no_decode:
         decode = {}
+        clock_warmup(torch, step, min(args.clock_warmup_s, 0.2))
         for (n, k) in SI.CONFIGS["c3_decode"]["mats"]:
             wp = SI.make_wp(n, k, seed=3000 + n + k, device=dev)
             pk0 = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
@@ -423,6 +443,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup": {"seconds": args.clock_warmup_s, "steps": clock_steps},
         "ms_per_step": round(ms, 4),
         "ms_per_step_eager": round(ms_eager, 4),
         "ms_per_step_graph": round(ms_graph, 4),

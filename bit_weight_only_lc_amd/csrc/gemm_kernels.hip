@@ -92,12 +92,12 @@ __device__ __forceinline__ int lds_off(int row, int chunk) { return row * ROWB +
 
 // Tiles are spread so that consecutive workgroup ids land on different XCDs (the
 // dispatcher deals workgroups round-robin over the 8 XCDs) while each XCD works on a
-// compact group of 4 tile-rows, which keeps its operand panels in its own L2.
+// compact group of GR tile-rows, which keeps its operand panels in its own L2.
+template <int GR>
 __device__ __forceinline__ bool map_tile(int b, int tilesP, int tilesQ, int ntiles, int& tp, int& tq, int& t) {
   const int per = (ntiles + 7) >> 3;
   t = (b & 7) * per + (b >> 3);
   if (t >= ntiles) return false;
-  const int GR = 4;
   const int group = t / (GR * tilesQ);
   const int within = t - group * GR * tilesQ;
   int rows = tilesP - group * GR;
@@ -803,7 +803,11 @@ void k_gemm_ring(GemmArgs a) {
   constexpr bool CL = OP == OP_DX;               // codes are the L operand for dX
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOTB];   // 144 KiB
   int tp, tq, tile;
-  if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
+  // The bf16 operand's panels (2 MiB each at K or N = 4096) outweigh the code panels
+  // (256 KiB), so each XCD takes few tiles along the bf16 operand: forward tile-rows
+  // are rows of X', dX tile-columns are rows of dY.
+  constexpr int GR = OP == OP_FWD ? 2 : 16;
+  if (!map_tile<GR>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wp = wave / T::WGQ, wq = wave % T::WGQ;
@@ -1076,7 +1080,8 @@ void k_gemm_dw(GemmArgs a) {
   constexpr int NW = 8, WGQ = 4, WJ = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[DW_SMEM];   // 152 KiB
   int tp, tq, tile;
-  if (!map_tile(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
+  // X and dY panels weigh the same: 4 x 8 tiles per XCD reads the fewest panels.
+  if (!map_tile<4>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
