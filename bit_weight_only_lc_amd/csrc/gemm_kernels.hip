@@ -7,7 +7,7 @@
 //   forward  Y  = X What^T            = X' Z^T + (X (1 kron B)) 1^T,   X' = X (I kron A)
 //   dX          = dY What             = (dY Z)(I kron A^T) + (dY 1)(1 kron B)^T
 //   dWp, dA, dB from G = dY^T X       (straight-through epilogue on the accumulators)
-// A code c enters a product as v(c) = 2 + c/2, exact in bf16 (see r16_to_vbf16); the
+// A code c enters a product as v(c) = 2 + c/2, exact in bf16 (see codes_expand); the
 // constant part is removed through the row terms prepared by the prologue kernels.
 //
 // Two kernel templates cover the three products (k_gemm_ring: forward and dX; k_gemm_dw).
@@ -107,130 +107,6 @@ __device__ __forceinline__ bool map_tile(int b, int tilesP, int tilesQ, int ntil
   return true;
 }
 
-// ---- loaders -------------------------------------------------------------------------
-// bf16 rows straight into LDS: wave w fills tile rows [64w, 64w+64), 8 rows per
-// instruction; lane l lands at byte 16*l of the instruction's 1 KiB, i.e. row l/8,
-// physical chunk l%8, so it fetches the logical chunk that the swizzle puts there.
-// Rows past the end are clamped to the last row (they only feed C entries that are
-// never stored).
-__device__ __forceinline__ void load_rows_direct(uint8_t* tile, const uint16_t* mat, int64_t ld,
-                                                 int row0, int rows_total, int k0, int wave,
-                                                 int lane) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = wave * 64 + i * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz(r);
-    int g = row0 + r;
-    g = g < rows_total ? g : rows_total - 1;
-    const uint16_t* src = mat + (int64_t)g * ld + k0 + c * 8;
-    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(tile + (wave * 64 + i * 8) * ROWB), 16, 0, 0);
-  }
-}
-
-// R16 codes: thread t owns tile row t; one 16-byte load holds the row's 64 codes.
-__device__ __forceinline__ uint4 load_codes(const uint32_t* codes, int rowblock, int nk, int kt, int tid) {
-  const uint4* src = reinterpret_cast<const uint4*>(codes + ((int64_t)rowblock * nk + kt) * 1024) + tid;
-  return *src;
-}
-__device__ __forceinline__ void store_codes(uint8_t* tile, uint4 w, int tid) {
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t o[8];
-    r16_to_vbf16(ws[q], o);
-    *reinterpret_cast<uint4*>(tile + lds_off(tid, 2 * q)) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4*>(tile + lds_off(tid, 2 * q + 1)) = make_uint4(o[4], o[5], o[6], o[7]);
-  }
-}
-
-// Transposing loader: tile row = a column c of the bf16 matrix (c in [c0, c0+256)),
-// tile column = contraction m in [m0, m0+64). Thread t reads an 8 x 8 block (8 rows m,
-// 8 columns) and writes it transposed. Out-of-range rows or columns read as zero.
-__device__ __forceinline__ void load_trans(uint4 v[8], const uint16_t* mat, int64_t ld, int m0,
-                                           int M, int c0, int cols, int tid) {
-  const int cc = tid & 31, mg = tid >> 5;
-  const int col = c0 + cc * 8;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int m = m0 + mg * 8 + r;
-    if (m < M && col < cols)
-      v[r] = *reinterpret_cast<const uint4*>(mat + (int64_t)m * ld + col);
-    else
-      v[r] = make_uint4(0, 0, 0, 0);
-  }
-}
-__device__ __forceinline__ void store_trans(uint8_t* tile, const uint4 v[8], int tid) {
-  const int cc = tid & 31, mg = tid >> 5;
-  uint32_t in[8][4];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) { in[r][0] = v[r].x; in[r][1] = v[r].y; in[r][2] = v[r].z; in[r][3] = v[r].w; }
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint32_t lo[4], hi[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      lo[q] = __builtin_amdgcn_perm(in[2 * q + 1][s], in[2 * q][s], 0x05040100u);
-      hi[q] = __builtin_amdgcn_perm(in[2 * q + 1][s], in[2 * q][s], 0x07060302u);
-    }
-    const int row = cc * 8 + 2 * s;
-    *reinterpret_cast<uint4*>(tile + lds_off(row, mg)) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    *reinterpret_cast<uint4*>(tile + lds_off(row + 1, mg)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  }
-}
-
-// ---- one contraction stage of 64 on the current LDS buffers --------------------------
-// Fragments are double-buffered in registers: the LDS reads of sub-step s+1 are issued
-// between the MFMAs of sub-step s (two MFMAs per read), so the matrix cores never wait
-// for LDS once the stage has started.
-template <int WJ>
-__device__ __forceinline__ void load_frags(const uint8_t* Ls, const uint8_t* Rs, int s, int wp,
-                                           int wq, int lane, bf16x8 af[4], bf16x8 bf[WJ]) {
-  const int chunk = 2 * s + (lane >> 5);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wp * 128 + i * 32 + (lane & 31);
-    af[i] = *reinterpret_cast<const bf16x8*>(Ls + lds_off(row, chunk));
-  }
-#pragma unroll
-  for (int j = 0; j < WJ; ++j) {
-    const int row = wq * 32 * WJ + j * 32 + (lane & 31);
-    bf[j] = *reinterpret_cast<const bf16x8*>(Rs + lds_off(row, chunk));
-  }
-}
-
-// Single-buffered variant for the dW product, whose transposing loaders already hold
-// 64 registers of prefetched data.
-__device__ __forceinline__ void mma_stage_single(const uint8_t* Ls, const uint8_t* Rs,
-                                                 f32x16 acc[4][4], int wp, int wq, int lane) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    bf16x8 af[4], bf[4];
-    load_frags<4>(Ls, Rs, s, wp, wq, lane, af, bf);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-template <int WJ>
-__device__ __forceinline__ void mma_stage(const uint8_t* Ls, const uint8_t* Rs, f32x16 acc[4][WJ],
-                                          int wp, int wq, int lane) {
-  bf16x8 af[2][4], bf[2][WJ];
-  load_frags<WJ>(Ls, Rs, 0, wp, wq, lane, af[0], bf[0]);
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int c = s & 1;
-    if (s < 3) load_frags<WJ>(Ls, Rs, s + 1, wp, wq, lane, af[c ^ 1], bf[c ^ 1]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < WJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
-  }
-}
-
 __device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, float a, float b, float c, float d) {
   if (f32) {
     __builtin_nontemporal_store(f32x4{a, b, c, d},
@@ -252,17 +128,10 @@ __device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, floa
 // row-major strips the same way for 16-byte stores.
 
 constexpr int SROW = 33;                  // padded row of the staging area (floats)
-constexpr int WAVE_LDS = 32768;           // LDS bytes per wave in the epilogue
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-}
-
-__device__ __forceinline__ void stage_block(float* S, const f32x16& acc, int lane) {
-  const int col = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) S[(8 * (r >> 2) + 4 * h + (r & 3)) * SROW + col] = acc[r];
 }
 
 // Writes a staged 32 x 32 block (rows = contraction-side index k, columns = output row)

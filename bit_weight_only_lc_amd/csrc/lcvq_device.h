@@ -44,22 +44,5 @@ __host__ __device__ __forceinline__ uint32_t r16_encode(const uint32_t c[16]) {
   const uint32_t hi = r16_place8(c + 8);
   return r16_place8(c) | (hi << 8) | (hi >> 24);
 }
-// W -> 8 dwords; dword p holds the bf16 pair (v(c2p), v(c2p+1)), low half first.
-__device__ __forceinline__ void r16_to_vbf16(uint32_t w, uint32_t out[8]) {
-  const uint32_t r = __builtin_amdgcn_alignbit(w, w, 8);   // rotate right by 8
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    out[p] = ((w >> (2 * p)) & 0x00600060u) | 0x40004000u;
-    out[p + 4] = ((r >> (2 * p)) & 0x00600060u) | 0x40004000u;
-  }
-}
-
-// LDS tile geometry shared by the GEMM kernels: rows of 64 bf16 (128 bytes = 8 chunks
-// of 16 bytes). A chunk is stored at a row-dependent XOR position so that both the
-// MFMA fragment reads (8 consecutive rows, same chunk) and the transposing writes
-// (rows 8 apart, same chunk) spread over all banks.
-__device__ __forceinline__ int swz_chunk(int row, int chunk) {
-  return chunk ^ ((row ^ (row >> 3)) & 7);
-}
 
 }  // namespace lcvq
