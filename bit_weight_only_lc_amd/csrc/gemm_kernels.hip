@@ -161,22 +161,33 @@ __device__ __forceinline__ float dge_slope(float w, float alpha, float c) {
 }
 
 // store_block_rows for dWp under the DGE estimator: each value is multiplied by the
-// slope at its proxy, read as the same 4 consecutive floats of Wp [N][K].
+// slope at its proxy, read as the same 4 consecutive floats of Wp [N][K]. All four
+// proxy loads are issued before the first store: the compiler cannot move a load of Wp
+// above a store to dWp (they might alias), and one HBM round trip per store would
+// serialize the epilogue. (Loading a block ahead of its store spills the epilogue.)
 __device__ __forceinline__ void store_block_rows_dge(const float* S, float* out, const float* wp,
                                                      float alpha, float c, int64_t ld, int row0,
                                                      int rows, int k0, int K, int lane) {
   const int kq = (lane & 7) * 4;
+  float4 w[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int row = row0 + it * 8 + (lane >> 3);
+    const bool in = row < rows && k0 + kq < K;
+    // a valid address either way; values of rows or columns past the end are not used
+    const int64_t idx = in ? (int64_t)row * ld + k0 + kq : 0;
+    w[it] = *reinterpret_cast<const float4*>(wp + idx);
+  }
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int rr = it * 8 + (lane >> 3);
     const int row = row0 + rr;
     if (row < rows && k0 + kq < K) {
       const int64_t idx = (int64_t)row * ld + k0 + kq;
-      const float4 w = *reinterpret_cast<const float4*>(wp + idx);
-      __builtin_nontemporal_store(f32x4{S[(kq + 0) * SROW + rr] * dge_slope(w.x, alpha, c),
-                                        S[(kq + 1) * SROW + rr] * dge_slope(w.y, alpha, c),
-                                        S[(kq + 2) * SROW + rr] * dge_slope(w.z, alpha, c),
-                                        S[(kq + 3) * SROW + rr] * dge_slope(w.w, alpha, c)},
+      __builtin_nontemporal_store(f32x4{S[(kq + 0) * SROW + rr] * dge_slope(w[it].x, alpha, c),
+                                        S[(kq + 1) * SROW + rr] * dge_slope(w[it].y, alpha, c),
+                                        S[(kq + 2) * SROW + rr] * dge_slope(w[it].z, alpha, c),
+                                        S[(kq + 3) * SROW + rr] * dge_slope(w[it].w, alpha, c)},
                                   reinterpret_cast<f32x4*>(out + idx));
     }
   }
