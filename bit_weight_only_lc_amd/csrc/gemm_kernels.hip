@@ -129,6 +129,10 @@ __device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, floa
 
 constexpr int SROW = 33;                  // padded row of the staging area (floats)
 
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding; the other counters are not waited on.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -206,6 +210,18 @@ __device__ void epilogue_fwd(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int 
   float* S = reinterpret_cast<float*>(smem) + wave * 32 * SR;
   const int col = lane & 31, h = lane >> 5;
   const int qb = q0 + wq * CW, c8 = (lane % LPR) * 8, q = qb + c8;
+  // All of this lane's beta values are loaded before the first store: vector loads and
+  // stores share one counter (vmcnt), so a load issued after a store can only be waited
+  // for together with that store.
+  constexpr int NIT = 32 / RPI;
+  float bv[WI][NIT];
+#pragma unroll
+  for (int i = 0; i < WI; ++i)
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int p = p0 + wp * 32 * WI + i * 32 + it * RPI + lane / LPR;
+      bv[i][it] = a.rowvec[p < a.M ? p : a.M - 1];
+    }
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
     const int pb = p0 + wp * 32 * WI + i * 32;
@@ -216,11 +232,14 @@ __device__ void epilogue_fwd(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int 
       for (int r = 0; r < 16; ++r)
         S[(8 * (r >> 2) + 4 * h + (r & 3)) * SR + j * 32 + col] = acc[i][j][r];
     wave_sync();
+    // Settle every beta load here, before the first store: a wait for one of them
+    // placed after stores would also wait for those stores to complete.
+    if (i == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 #pragma unroll
-    for (int it = 0; it < 32 / RPI; ++it) {
+    for (int it = 0; it < NIT; ++it) {
       const int rr = it * RPI + lane / LPR, p = pb + rr;
       if (p < a.M && q < a.N) {
-        const float b = a.rowvec[p];
+        const float b = bv[i][it];
         const f32x4 x = *reinterpret_cast<const f32x4*>(S + rr * SR + c8);
         const f32x4 y = *reinterpret_cast<const f32x4*>(S + rr * SR + c8 + 4);
         const int64_t idx = (int64_t)p * a.N + q;
@@ -316,23 +335,37 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
   static_assert(WI % 2 == 0, "k blocks are staged in pairs");
   constexpr int NV = 16 / D;                  // whole vectors per lane and block
   constexpr int IIU = D == 16 ? 4 : D;        // output rows unrolled together
+  // row terms B[i] - 4 sum_j A[i][j] (d <= 8; d = 16 keeps them in LDS), read as scalar
+  // loads through constant-address-space pointers
   float bp[D];
+  if constexpr (D != 16) {
+    const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
+    const LCVQ_CONST float* Bc = (const LCVQ_CONST float*)a.B;
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    float s = 0.f;
+    for (int i = 0; i < D; ++i) {
+      float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < D; ++j) s += a.A[i * D + j];
-    bp[i] = a.B[i] - 4.f * s;
+      for (int j = 0; j < D; ++j) s += Ac[i * D + j];
+      bp[i] = Bc[i] - 4.f * s;
+    }
   }
   const int q = lane & 31, h = lane >> 5;
+  // r of this lane's rows, loaded before the first store (vector loads and stores share
+  // one counter, so a load issued after a store is waited for together with it)
+  float rmv[WJ];
+#pragma unroll
+  for (int j = 0; j < WJ; ++j) {
+    const int m = q0 + wq * 32 * WJ + j * 32 + q;
+    const float r = a.rowvec[m < a.M ? m : a.M - 1];
+    rmv[j] = m < a.M ? r : 0.f;
+  }
 #pragma unroll
   for (int j = 0; j < WJ; ++j)
 #pragma unroll
     for (int i2 = 0; i2 < WI / 2; ++i2) {
       const int kb = p0 + wp * 32 * WI + i2 * 64;
       const int mb = q0 + wq * 32 * WJ + j * 32;
-      const int m = mb + q;
-      const float rm = m < a.M ? a.rowvec[m] : 0.f;
+      const float rm = rmv[j];
       // Re-read A for every block pair instead of keeping d*d values live across the
       // unrolled sequence: d <= 8 through a constant-address-space pointer, so that the
       // reads are scalar loads from the scalar cache (through a generic pointer they would
@@ -365,6 +398,10 @@ __device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q
           }
       }
       wave_sync();
+      // Settle the loads issued before the epilogue (r, and dW's partials when this tile
+      // reduces them) before the first store: a wait for them placed after stores would
+      // also wait for those stores to complete.
+      if (j == 0 && i2 == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       store_block_rows64(S, a.out, a.out_f32, a.K, mb, a.M, kb, a.K, lane);
     }
 }
@@ -637,33 +674,38 @@ __device__ __forceinline__ void ring_mfma(const RingFrags<CODES_ARE_L, WI, WJ>& 
 }
 
 // dA and dB from the dW product's per-tile partials, summed in a fixed order: output o by
-// tile o mod ntiles; thread t adds partials t, t + NT, ... of it, then a tree over the NT
-// threads. Run by the dX product (launched after dW) once its own work is done, so that
-// the reduction needs no launch of its own.
+// tile o mod ntiles; thread t adds partials t, t + NT, ... of it, each wave adds its 64
+// thread sums by a butterfly of lane exchanges, and thread 0 adds the NT / 64 wave sums
+// in wave order. `first` is thread tid's sum for output `tile` when the caller loaded it
+// ahead (`have_first`). Barriers are plain s_barrier: __syncthreads() would also wait for
+// the epilogue's outstanding stores.
 template <int D, int NT>
-__device__ void reduce_dw_partials(const GemmArgs& a, int tile, int ntiles, int tid, float* red) {
+__device__ void reduce_dw_partials(const GemmArgs& a, int tile, int ntiles, int tid, float* red,
+                                   float first, bool have_first) {
   constexpr int NOUT = D * D + D;
   for (int o = tile; o < NOUT; o += ntiles) {
     float s = 0.f;
-    for (int i = tid; i < a.red_tiles; i += NT) s += a.red_partials[(int64_t)i * NOUT + o];
-    red[tid] = s;
-    __syncthreads();
+    if (o == tile && have_first) {
+      s = first;
+    } else {
+      for (int i = tid; i < a.red_tiles; i += NT) s += a.red_partials[(int64_t)i * NOUT + o];
+    }
 #pragma unroll
-    for (int w = NT / 2; w >= 1; w >>= 1) {
-      if (tid < w) red[tid] += red[tid + w];
-      __syncthreads();
-    }
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    if ((tid & 63) == 0) red[tid >> 6] = s;
+    __builtin_amdgcn_s_waitcnt(0xC07F);                   // lgkmcnt(0): the LDS write
+    asm volatile("s_barrier" ::: "memory");
     if (tid == 0) {
-      if (o < D * D) a.red_dA[o] = red[0];
-      else a.red_dB[o - D * D] = red[0];
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < NT / 64; ++w) t += red[w];
+      if (o < D * D) a.red_dA[o] = t;
+      else a.red_dB[o - D * D] = t;
     }
-    __syncthreads();
+    asm volatile("s_barrier" ::: "memory");               // red is reused next round
   }
 }
 
-// Wait until at most `stages_after` (0..2) stages of this wave's ring loads are still
-// outstanding; the other counters are not waited on.
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 template <int NW>
 __device__ __forceinline__ void wait_vm_stages(int stages_after) {
   constexpr int L = ring_loads<NW>();
@@ -766,12 +808,24 @@ void k_gemm_ring(GemmArgs a) {
       __syncthreads();
     }
     static_assert(NW * DX_WAVE_LDS <= 120 * 1024, "dX staging below the copy of A");
+    // This tile's first dA/dB output (o = tile) from dW's partials: loaded here, before
+    // the epilogue's stores, when one load per thread covers the partials.
+    // The load is unconditional, from a valid address (A when there is nothing to
+    // reduce): a load inside a branch would be waited for at once where the branch joins.
+    constexpr int NOUT = D * D + D;
+    const bool have_first = a.red_partials && tile < NOUT && a.red_tiles <= NW * 64;
+    const float* fsrc = a.red_partials
+                            ? a.red_partials + (int64_t)(tid < a.red_tiles ? tid : 0) * NOUT +
+                                  (tile < NOUT ? tile : 0)
+                            : a.A;
+    const float fv = *fsrc;
     epilogue_dx<D, WI, WJ>(a, acc, p0, q0, wp, wq, lane,
                            reinterpret_cast<float*>(smem + wave * DX_WAVE_LDS), Alds);
-    // 2 KiB at 128 KiB: above the staging areas and the copy of A
+    // wave sums at 128 KiB: above the staging areas and the copy of A
     if (a.red_partials)
       reduce_dw_partials<D, NW * 64>(a, tile, a.ntiles, tid,
-                                     reinterpret_cast<float*>(smem + 128 * 1024));
+                                     reinterpret_cast<float*>(smem + 128 * 1024),
+                                     tid < a.red_tiles ? fv : 0.f, have_first);
   }
 }
 
