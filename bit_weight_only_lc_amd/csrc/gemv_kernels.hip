@@ -462,41 +462,46 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
 }
 
 template <int D, int RG, int KSW, int M>
-static void launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
-                         const GemvBatch& b, int K) {
-  // Dynamic LDS beyond 64 KiB must be requested for the kernel, once per device (the
-  // first 64 devices are remembered; beyond that it is requested on every launch).
+static hipError_t launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
+                               const GemvBatch& b, int K) {
+  // Dynamic LDS beyond 64 KiB must be requested for the kernel, once per device: a
+  // process-wide cache of the devices done (the first 64; beyond that it is requested on
+  // every launch). A failed request is returned, and not cached.
   static std::atomic<uint64_t> done{0};
   int dev = 0;
-  (void)hipGetDevice(&dev);
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
   if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW, M>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW, M>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
     done.fetch_or(bit, std::memory_order_acq_rel);
   }
   LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW, M>), grid, dim3(GWF * 64), shm, s, X, b, K);
+  return hipGetLastError();
 }
 
 // M = 3, 4 take the fused path only for K up to 32 blocks, i.e. KSW <= 4.
 template <int D, int RG, int KSW>
-static void launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
-                           const GemvBatch& b, int K) {
+static hipError_t launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
+                                 const GemvBatch& b, int K) {
   static_assert(GEMV_FUSED_M == 4, "fused path instantiated for one to four tokens");
-  if (M == 1) launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K);
-  else if (M == 2) launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K);
-  else if constexpr (KSW <= 4) {
-    if (M == 3) launch_fused<D, RG, KSW, 3>(grid, shm, s, X, b, K);
-    else launch_fused<D, RG, KSW, 4>(grid, shm, s, X, b, K);
+  if (M == 1) return launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K);
+  if (M == 2) return launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K);
+  if constexpr (KSW <= 4) {
+    if (M == 3) return launch_fused<D, RG, KSW, 3>(grid, shm, s, X, b, K);
+    return launch_fused<D, RG, KSW, 4>(grid, shm, s, X, b, K);
   }
+  return hipErrorInvalidValue;       // not reached: gemv_fused() keeps M > 2 to KSW <= 4
 }
 
 template <int D>
-static void launch_fused_d(int M, int K, bool two, size_t shm, hipStream_t s, const uint16_t* X,
-                           const GemvBatch& b, int wgs) {
+static hipError_t launch_fused_d(int M, int K, bool two, size_t shm, hipStream_t s,
+                                 const uint16_t* X, const GemvBatch& b, int wgs) {
   const int pw = (K / GK + GWF - 1) / GWF;
   const dim3 grid(wgs);
-#define LCVQ_FUSED(RG, KSW) launch_fused_m<D, RG, KSW>(M, grid, shm, s, X, b, K)
+#define LCVQ_FUSED(RG, KSW) return launch_fused_m<D, RG, KSW>(M, grid, shm, s, X, b, K)
   if (two) {
     if (pw <= 2) LCVQ_FUSED(2, 2);
     else if (pw <= 4) LCVQ_FUSED(2, 4);
@@ -525,11 +530,10 @@ hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b
   const size_t base = (size_t)nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
   const size_t shm = std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
   switch (d) {
-    case 4: launch_fused_d<4>(M, K, two, shm, s, X, b, wgs); break;
-    case 8: launch_fused_d<8>(M, K, two, shm, s, X, b, wgs); break;
-    default: launch_fused_d<16>(M, K, two, shm, s, X, b, wgs); break;
+    case 4: return launch_fused_d<4>(M, K, two, shm, s, X, b, wgs);
+    case 8: return launch_fused_d<8>(M, K, two, shm, s, X, b, wgs);
+    default: return launch_fused_d<16>(M, K, two, shm, s, X, b, wgs);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,

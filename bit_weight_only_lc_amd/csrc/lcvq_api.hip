@@ -17,13 +17,36 @@ inline bool d_ok(int d) { return d == 4 || d == 8 || d == 16; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 inline lcvq_status_t from_hip(hipError_t e) { return e == hipSuccess ? LCVQ_OK : LCVQ_ERR_HIP; }
 
+// Launch limits. A HIP grid holds at most 2^32 - 1 work-items per dimension. The largest
+// grids of a layer call are the products (one 512-thread workgroup per 256 x 256 tile,
+// rounded up to a multiple of 8) and the row prologues (256-thread blocks, one per row
+// or per few rows, after at most 65535 quantizer blocks); the transposed-code kernel
+// has a (K / 256) x (N / 64) grid. These limits keep every one of them inside the range.
+constexpr int64_t kMaxRows = (int64_t(1) << 24) - (int64_t(1) << 17);   // M
+constexpr int64_t kMaxDim = int64_t(1) << 21;                           // N, K
+constexpr int64_t kMaxTiles = (int64_t(1) << 23) - 8;                   // per product
+constexpr int64_t kMaxBlocks256 = (int64_t(1) << 24) - 1;              // 256-thread grids
+// Decode: one 1024- or 512-thread workgroup per 16 or 32 output rows, and the
+// layout kernel's one 256-thread block per four 1 KiB tiles.
+constexpr int64_t kMaxDecodeRows = int64_t(1) << 26;                    // N, sum over a batch
+constexpr int64_t kMaxDecodeWeights = int64_t(1) << 36;                 // N * K
+
+inline int64_t tiles(int64_t P, int64_t Q) { return ((P + 255) / 256) * ((Q + 255) / 256); }
+
 // Linear-layer shapes: M rows of activations, weight [N, K].
 inline bool layer_shape_ok(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || M > INT32_MAX) return false;
+  if (M < 1 || M > kMaxRows) return false;
   if (N < 64 || K < 64 || (N % 64) || (K % 64)) return false;
-  if (N > INT32_MAX || K > INT32_MAX) return false;
+  if (N > kMaxDim || K > kMaxDim) return false;
   if (N * K >= (int64_t(1) << 40)) return false;
+  if (tiles(M, N) > kMaxTiles || tiles(K, N) > kMaxTiles || tiles(K, M) > kMaxTiles)
+    return false;
   return true;
+}
+
+inline bool decode_shape_ok(int64_t N, int64_t K) {
+  return N >= 16 && (N % 16) == 0 && K >= 256 && (K % 256) == 0 && N <= kMaxDecodeRows &&
+         K <= INT32_MAX && N * K <= kMaxDecodeWeights;
 }
 
 // Blocked R16 code words for `rows` operand rows and a contraction of length `kc`.
@@ -171,7 +194,7 @@ lcvq_status_t lcvq_linear_fwd(const void* X, lcvq_dtype_t xdt, int64_t M, int64_
   float* beta = reinterpret_cast<float*>(ws + w.beta);
   uint32_t* r16 = reinterpret_cast<uint32_t*>(ws + w.r16);
   hipError_t e;
-  if (M + 65536 < INT32_MAX) {                     // quantizer and prologue in one launch
+  if (M + 65536 <= kMaxBlocks256) {                // quantizer and prologue in one launch
     e = launch_fwd_prep(Wp, N, K, packed_out, mask_out, r16, What_out, X, f32, M, A, B, d, xs,
                         xs_lo, beta, s);
   } else {
@@ -219,7 +242,7 @@ lcvq_status_t linear_bwd_impl(const void* dY, const void* X, lcvq_dtype_t dt, in
   uint16_t* x_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.x_lo) : nullptr;
   // prologue and (when dX is wanted) the transposed codes in one launch
   const int64_t rblocks = dX ? ((K + 255) / 256) * (N / 64) : 0;
-  const bool merged = M + rblocks < INT32_MAX;
+  const bool merged = M + rblocks <= kMaxBlocks256;
   hipError_t e = merged ? launch_bwd_prep(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi, x_lo,
                                           packed, dX ? r16t : nullptr, s)
                         : launch_bwd_prologue(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi,
@@ -271,9 +294,7 @@ lcvq_status_t lcvq_linear_bwd_dge(const void* dY, const void* X, lcvq_dtype_t dt
 
 size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t N, int64_t K, int d) {
   (void)d;
-  if (M < 1 || M > 16 || N < 16 || (N % 16) || N > INT32_MAX || K < 256 || (K % 256) ||
-      K > INT32_MAX)
-    return 0;
+  if (M < 1 || M > 16 || !decode_shape_ok(N, K)) return 0;
   return gemv_ws(K).total;
 }
 
@@ -287,9 +308,7 @@ static lcvq_status_t gemv2b_impl(const void* X, int64_t M, int64_t N, int64_t K,
                                  size_t workspace_bytes, void* stream) {
   if (!X || !packed || !A16 || !B16 || !Y) return LCVQ_ERR_NULL;
   if (!d_ok(d)) return LCVQ_ERR_D;
-  if (M < 1 || M > 16 || N < 16 || (N % 16) || K < 256 || (K % 256) || N > INT32_MAX ||
-      K > INT32_MAX || N * K >= (int64_t(1) << 40))
-    return LCVQ_ERR_SHAPE;
+  if (M < 1 || M > 16 || !decode_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(A16) || !aligned16(B16) ||
       !aligned16(Y) || !aligned16(workspace))
     return LCVQ_ERR_ALIGN;
@@ -323,9 +342,7 @@ lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t 
 lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
                                   void* stream) {
   if (!packed || !codes) return LCVQ_ERR_NULL;
-  if (N < 16 || (N % 16) || K < 256 || (K % 256) || N > INT32_MAX || K > INT32_MAX ||
-      N * K >= (int64_t(1) << 40))
-    return LCVQ_ERR_SHAPE;
+  if (!decode_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
   if (!aligned16(packed) || !aligned16(codes)) return LCVQ_ERR_ALIGN;
   return from_hip(launch_gemv_shuffle(packed, N, K, codes, as_stream(stream)));
 }
@@ -336,20 +353,19 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
   if (!X || !mats) return LCVQ_ERR_NULL;
   if (!d_ok(d)) return LCVQ_ERR_D;
   if (count < 1 || count > GEMV_MAX_BATCH) return LCVQ_ERR_SHAPE;
-  if (M < 1 || M > 16 || K < 256 || (K % 256) || K > INT32_MAX) return LCVQ_ERR_SHAPE;
+  if (M < 1 || M > 16 || !decode_shape_ok(16, K)) return LCVQ_ERR_SHAPE;
   int64_t nmax = 0, groups = 0;
   for (int i = 0; i < count; ++i) {
     const lcvq_gemv2b_matrix& m = mats[i];
     if (!m.packed || !m.A16 || !m.B16 || !m.Y) return LCVQ_ERR_NULL;
     if (m.layout != 0 && m.layout != 1) return LCVQ_ERR_VALUE;
-    if (m.N < 16 || (m.N % 16) || m.N > INT32_MAX || m.N * K >= (int64_t(1) << 40))
-      return LCVQ_ERR_SHAPE;
+    if (!decode_shape_ok(m.N, K)) return LCVQ_ERR_SHAPE;
     if (!aligned16(m.packed) || !aligned16(m.A16) || !aligned16(m.B16) || !aligned16(m.Y))
       return LCVQ_ERR_ALIGN;
     nmax = m.N > nmax ? m.N : nmax;
     groups += m.N / 16;
   }
-  if (groups > INT32_MAX) return LCVQ_ERR_SHAPE;
+  if (groups * 16 > kMaxDecodeRows) return LCVQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(workspace)) return LCVQ_ERR_ALIGN;
   const GemvWs w = gemv_ws(K);
   if (!workspace || workspace_bytes < w.total) return LCVQ_ERR_WORKSPACE;

@@ -41,8 +41,9 @@ hipError_t launch_bwd_prologue(const void* dY, const void* X, bool f32, int64_t 
                                uint16_t* x_hi, uint16_t* x_lo, hipStream_t s);
 
 // One launch each for the forward's quantizer + prologue and the backward's prologue +
-// transposed codes (r16t may be NULL when dX is not wanted). The grid must fit in
-// 2^31 - 1 blocks (launch_*_prep_fits).
+// transposed codes (r16t may be NULL when dX is not wanted). Their grids are 256-thread
+// blocks, so the callers use them only while the block count stays below 2^24 (2^32
+// work-items); otherwise they launch the parts separately.
 hipError_t launch_fwd_prep(const float* wp, int64_t N, int64_t K, uint8_t* packed, uint8_t* mask,
                            uint32_t* r16, float* what, const void* X, bool x_f32, int64_t M,
                            const float* A, const float* B, int d, uint16_t* xs,

@@ -22,13 +22,18 @@
  *  - Packed codes: 4 per byte, code k = 4b + t in bits [2t, 2t+1] of byte b of its row.
  *    Mask: 8 per byte, bit k = 8c + t in bit t of byte c of its row.
  *  - All pointers must be 16-byte aligned. Outputs must not overlap inputs or each other.
- *  - Shape limits: d in {4, 8, 16}; 1 <= M <= 2^31 - 1; N, K >= 64 and multiples of 64;
- *    N * K < 2^40. (lcvq_quantize / pack / unpack need only K a multiple of 16.)
+ *  - Shape limits of the layer calls: d in {4, 8, 16}; 1 <= M <= 2^24 - 2^17; N and K
+ *    multiples of 64 in [64, 2^21]; N * K < 2^40; and at most 2^23 - 8 tiles of 256 x 256
+ *    in each of the products (M x N, K x N, K x M). These keep every kernel grid within
+ *    HIP's 2^32 - 1 work-items. (lcvq_quantize / pack / unpack need only K a multiple
+ *    of 16 and N * K < 2^40.) Shapes outside them return LCVQ_ERR_SHAPE.
  *  - Errors are returned synchronously from host-side checks, before anything is
  *    enqueued. LCVQ_ERR_HIP reports a failed launch; faults inside kernels surface at the
  *    caller's next synchronization, as with any HIP work.
- *  - Calls are re-entrant; the library keeps no state between calls (apart from the
- *    per-thread profiling hook at the end of this file).
+ *  - Calls are re-entrant. State kept between calls: the per-thread profiling hook at
+ *    the end of this file, and a process-wide record of the devices on which the decode
+ *    kernels' dynamic LDS size has been requested (hipFuncSetAttribute, once per device
+ *    and kernel; a failed request returns LCVQ_ERR_HIP and is not recorded).
  */
 #ifndef LCVQ_H
 #define LCVQ_H
@@ -150,7 +155,7 @@ lcvq_status_t lcvq_linear_bwd_dge(const void* dY, const void* X, lcvq_dtype_t dt
  * Y = X What^T for a few tokens (decoupleQ, section 3.2: one linear transform turns the
  * integer part back into weights; LC-QAT summary, Methodology 3).
  *   X   bfloat16 [M, K], 1 <= M <= 16;  packed uint8 [N, K/4]
- *   N a multiple of 16, K a multiple of 256
+ *   N a multiple of 16, at most 2^26; K a multiple of 256; N * K <= 2^36
  *   A16 float16 [d, d];  B16 float16 [d]
  *   Y   bfloat16 [M, N]                                          out
  *   workspace >= lcvq_gemv2b_workspace_size(M, N, K, d) bytes (0 for invalid shapes)
@@ -173,7 +178,8 @@ lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
  * The layout is this library's own (the pages fix only what the integer part holds).
  *   packed  uint8 [N, K/4] canonical (2-bit fields, little-endian along K)         in
  *   codes   uint8, N * K / 4 bytes, must not overlap packed                          out
- *   N a multiple of 16, K a multiple of 256, N * K < 2^40; both pointers 16-byte aligned
+ *   N a multiple of 16, at most 2^26; K a multiple of 256; N * K <= 2^36; both pointers
+ *   16-byte aligned
  * Errors: LCVQ_ERR_NULL, LCVQ_ERR_SHAPE, LCVQ_ERR_ALIGN, LCVQ_ERR_HIP.
  */
 lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
@@ -198,10 +204,11 @@ lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t 
  * one launch; otherwise one matrix after the other, on `stream`.
  *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 256
  *   mats    host array of `count` descriptors, 1 <= count <= 8; mats[i].N a multiple of
- *           16; packed (N * K / 4 bytes: canonical [N, K/4] for layout 0, the decode
- *           layout of lcvq_gemv2b_shuffle for layout 1), A16 float16 [d, d], B16 float16
- *           [d] and the output Y bfloat16 [M, N] are device pointers; outputs must not
- *           overlap anything
+ *           16, the N summed over the matrices at most 2^26, each N * K <= 2^36; packed
+ *           (N * K / 4 bytes: canonical [N, K/4] for layout 0, the decode layout of
+ *           lcvq_gemv2b_shuffle for layout 1), A16 float16 [d, d], B16 float16 [d] and the
+ *           output Y bfloat16 [M, N] are device pointers; outputs must not overlap
+ *           anything
  *   workspace >= lcvq_gemv2b_workspace_size(M, largest N, K, d) bytes
  * Errors as for lcvq_gemv2b; LCVQ_ERR_SHAPE also for count outside 1..8, LCVQ_ERR_VALUE
  * for a layout other than 0 or 1.

@@ -218,3 +218,32 @@ def test_profile_hook_ids(L):
         assert L.lcvq_profile_next(kid, None, None) == 2          # LCVQ_ERR_SHAPE
     for kid in range(1, 7):
         assert L.lcvq_profile_next(kid, None, None) == 0
+
+
+def test_launch_limits_are_shape_errors(L):
+    """Shapes whose kernel grids would exceed 2^32 - 1 work-items are rejected on the host
+    (LCVQ_ERR_SHAPE, workspace size 0) instead of failing at launch; the largest
+    accepted ones still report a workspace size. No GPU call is made."""
+    max_m = (1 << 24) - (1 << 17)
+    assert L.lcvq_linear_fwd_workspace_size(max_m, 256, 256, 8) > 0
+    assert L.lcvq_linear_fwd_workspace_size(max_m + 1, 256, 256, 8) == 0
+    assert L.lcvq_linear_bwd_workspace_size(max_m + 1, 256, 256, 8) == 0
+    assert _fwd(L, M=max_m + 1) == 2
+    assert _bwd(L, M=1 << 24) == 2
+    assert L.lcvq_linear_fwd_workspace_size(64, 1 << 21, 256, 8) > 0
+    assert L.lcvq_linear_fwd_workspace_size(64, (1 << 21) + 64, 256, 8) == 0
+    assert _fwd(L, N=(1 << 21) + 64) == 2
+    assert _bwd(L, K=(1 << 21) + 64) == 2
+    # M x N product tiles beyond 2^23 - 8 with every dimension inside its own limit
+    assert L.lcvq_linear_fwd_workspace_size(max_m, 1 << 20, 64, 8) == 0
+    assert _fwd(L, M=max_m, N=1 << 20, K=64) == 2
+    # decode: N <= 2^26, N * K <= 2^36, and the batch's rows summed <= 2^26
+    assert L.lcvq_gemv2b_workspace_size(1, 1 << 26, 256, 8) > 0
+    assert L.lcvq_gemv2b_workspace_size(1, (1 << 26) + 16, 256, 8) == 0
+    assert L.lcvq_gemv2b_workspace_size(1, 1 << 20, 1 << 17, 8) == 0
+    assert L.lcvq_gemv2b_shuffle(P, (1 << 26) + 16, 256, P, None) == 2
+    import bit_weight_only_lc_amd as PK
+    mats = (PK.GemvMatrix * 2)(*[PK.GemvMatrix(P, P, P, P, 1 << 25) for _ in range(2)])
+    ws = L.lcvq_gemv2b_workspace_size(1, 256, 256, 8)
+    mats[1].N = (1 << 25) + 16                      # 2^26 + 16 rows in all
+    assert L.lcvq_gemv2b_batched(P, 1, 256, 8, mats, 2, P, ws, None) == 2

@@ -1,9 +1,13 @@
-"""Pins of the CPU oracle against things other than itself.
+"""Pins of the CPU oracles against things other than themselves.
 
 Each test checks an oracle function against a fact the pages or the mathematics fix:
 hand-worked values, brute-force search, the decoupleQ scalar special case, closed
 forms computed by a different route, exact finite differences, and torch autograd on
-the literal formula. All run on the CPU.
+the literal formula. All run on the CPU, once for each oracle: the plain C++ loops
+(oracle/lcvq_oracle.cpp through oracle/coracle.py, the oracle of record) and the numpy
+one (oracle/lcvq_oracle.py, a second opinion that uses library matmuls as steps).
+Helpers that are routes of their own (brute-force codeword search, the decoupleQ
+eq. (3)/(4) routine, the smooth-rounding curve) come from the numpy module in both.
 """
 
 import json
@@ -14,7 +18,16 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import lcvq_oracle as O
+from oracle import coracle
+from oracle import lcvq_oracle as H
+
+
+@pytest.fixture(params=["cxx", "numpy"], scope="module")
+def O(request):
+    if request.param == "cxx":
+        coracle.lib()
+        return coracle
+    return H
 
 
 def _load(golden_dir, name):
@@ -23,7 +36,7 @@ def _load(golden_dir, name):
 
 
 # ---------------------------------------------------------------- hand-worked values
-def test_hand_example_d2(golden_dir):
+def test_hand_example_d2(O, golden_dir):
     g = _load(golden_dir, "hand_example_d2.json")
     d = g["d"]
     A, B = np.array(g["A"]), np.array(g["B"])
@@ -42,7 +55,7 @@ def test_hand_example_d2(golden_dir):
     np.testing.assert_allclose(b["dB"], e["dB"], rtol=0, atol=1e-12)
 
 
-def test_quantize_edge_values(golden_dir):
+def test_quantize_edge_values(O, golden_dir):
     g = _load(golden_dir, "quantize_edge_values.json")
     wp = np.array([float(v) for v in g["wp"]], dtype=np.float32)
     z, m = O.quantize(wp)
@@ -50,7 +63,7 @@ def test_quantize_edge_values(golden_dir):
     assert m.tolist() == g["mask"]
 
 
-def test_quantize_matches_torch_round_clamp():
+def test_quantize_matches_torch_round_clamp(O):
     # torch.round is round-half-to-even; an independent route to the same codes.
     gen = torch.Generator().manual_seed(3)
     wp = (torch.rand(4096, generator=gen) * 7 - 2).float()
@@ -63,14 +76,14 @@ def test_quantize_matches_torch_round_clamp():
 
 
 # ---------------------------------------------------------------- packing
-def test_pack_worked_example():
+def test_pack_worked_example(O):
     # codes [1, 2, 3, 0] -> 1 | 2<<2 | 3<<4 | 0<<6 = 0x39
     assert O.pack2b(np.array([[1, 2, 3, 0]], dtype=np.uint8)).tolist() == [[0x39]]
     # mask bits [1,0,1,1,0,0,0,1] -> 1 + 4 + 8 + 128 = 0x8D
     assert O.pack_mask(np.array([[1, 0, 1, 1, 0, 0, 0, 1]], dtype=np.uint8)).tolist() == [[0x8D]]
 
 
-def test_pack_roundtrips():
+def test_pack_roundtrips(O):
     allbytes = np.arange(256, dtype=np.uint8).reshape(1, 256)
     assert np.array_equal(O.pack2b(O.unpack2b(allbytes, 1024)), allbytes)
     assert np.array_equal(O.pack_mask(O.unpack_mask(allbytes, 2048)), allbytes)
@@ -96,7 +109,7 @@ def _away_from_ties(rng, n, d):
 
 
 @pytest.mark.parametrize("d", [2, 4, 8])
-def test_round_clamp_is_nearest_codeword_for_orthogonal_columns(d):
+def test_round_clamp_is_nearest_codeword_for_orthogonal_columns(O, d):
     """Nearest-codeword search over all 4^d codes equals round/clamp when A has
     orthogonal columns (the distance then separates per coordinate)."""
     rng = np.random.default_rng(11 + d)
@@ -111,10 +124,10 @@ def test_round_clamp_is_nearest_codeword_for_orthogonal_columns(d):
         B = rng.normal(size=d)
         z, _ = O.quantize(W)
         for r in range(n):
-            assert np.array_equal(O.nearest_codeword(W[r], A, B), z[r]), (case, r)
+            assert np.array_equal(H.nearest_codeword(W[r], A, B), z[r]), (case, r)
 
 
-def test_general_A_is_not_nearest_codeword():
+def test_general_A_is_not_nearest_codeword(O):
     """For a general A the two rules differ (so LC-VQ is not nearest-codeword VQ):
     the brute force must find a strictly closer codeword on some inputs."""
     rng = np.random.default_rng(1)
@@ -125,7 +138,7 @@ def test_general_A_is_not_nearest_codeword():
     z, _ = O.quantize(W)
     differ = 0
     for r in range(200):
-        zb = O.nearest_codeword(W[r], A, B)
+        zb = H.nearest_codeword(W[r], A, B)
         if not np.array_equal(zb, z[r]):
             t = A @ W[r].astype(np.float64)
             db = np.sum((A @ zb - t) ** 2)
@@ -136,7 +149,7 @@ def test_general_A_is_not_nearest_codeword():
 
 
 # ---------------------------------------------------------------- decoupleQ special case
-def test_diagonal_A_is_decoupleq_uniform_quantization():
+def test_diagonal_A_is_decoupleq_uniform_quantization(O):
     """A = s I, B = b 1 reduces LC-VQ to per-tensor uniform 2-bit quantization,
     decoupleQ eq. (3)/(4) with alpha=-2, beta=1, after the code offset z = W^ + 2."""
     rng = np.random.default_rng(2)
@@ -146,7 +159,7 @@ def test_diagonal_A_is_decoupleq_uniform_quantization():
         zero = k * s
         wp = (rng.integers(-4 * 65536, 8 * 65536, size=(16, 64)) / 65536.0).astype(np.float32)
         W0 = s * (wp.astype(np.float64) - 2.0 + k)
-        q, wt = O.decoupleq_quant(W0, s, zero)
+        q, wt = H.decoupleq_quant(W0, s, zero)
         z, m = O.quantize(wp)
         assert np.array_equal(z.astype(np.int64), q.astype(np.int64) + 2)
         b = zero - 2 * s
@@ -169,7 +182,7 @@ def _layer(seed, M=5, N=12, K=48, d=8, lo=-2.0, hi=5.0):
 
 
 @pytest.mark.parametrize("d", [4, 8, 16])
-def test_fold_identities(d):
+def test_fold_identities(O, d):
     """Y = X' Z^T + beta 1^T with X' = X (I kron A), beta = X (1 kron B); and
     dX = (dY Z)(I kron A^T) + (dY 1)(1 kron B)^T; dB = sum_g (r^T X)_g, r = dY 1."""
     wp, A, B, X, dY = _layer(7 + d, d=d, K=64)
@@ -188,7 +201,7 @@ def test_fold_identities(d):
     np.testing.assert_allclose(b["dB"], dB2, rtol=1e-12, atol=1e-10)
 
 
-def test_gemv_matches_forward():
+def test_gemv_matches_forward(O):
     wp, A, B, X, _ = _layer(31, M=3, N=16, K=64, d=8)
     f = O.linear_fwd(X, wp, A, B, 8)
     np.testing.assert_allclose(O.gemv2b(X, f["packed"], A, B, 8), f["Y"], rtol=1e-13, atol=1e-12)
@@ -196,7 +209,7 @@ def test_gemv_matches_forward():
 
 # ---------------------------------------------------------------- exact finite differences
 @pytest.mark.parametrize("d", [2, 8])
-def test_finite_differences_exact(d):
+def test_finite_differences_exact(O, d):
     """L = <dY, X What^T> is affine in A, B, X and in the (continuous) codes, so a
     central difference with a unit step is exact up to rounding. The STE gradient of Wp
     is the code gradient where the mask is 1 and zero elsewhere."""
@@ -238,7 +251,7 @@ def test_finite_differences_exact(d):
 
 # ---------------------------------------------------------------- third opinion: torch autograd
 @pytest.mark.parametrize("d", [4, 8, 16])
-def test_torch_autograd_literal_formula(d):
+def test_torch_autograd_literal_formula(O, d):
     """PyTorch CPU float64 autograd of clamp(Wp + (round(Wp) - Wp).detach(), 0, 3),
     decoded by A z + B and multiplied by X, gives the same forward and gradients."""
     wp, A, B, X, dY = _layer(200 + d, M=4, N=8, K=64, d=d)
@@ -261,7 +274,7 @@ def test_torch_autograd_literal_formula(d):
     np.testing.assert_allclose(Bt.grad.numpy(), b["dB"], rtol=1e-12, atol=1e-12)
 
 
-def test_mask_zero_outside_clamp_range():
+def test_mask_zero_outside_clamp_range(O):
     wp = np.array([[-0.51, -0.5, 3.49, 3.5, 10.0, -3.0, 1.0, 2.0]], dtype=np.float32)
     z, m = O.quantize(wp)
     assert m.tolist() == [[0, 1, 1, 0, 0, 0, 1, 1]]
@@ -275,33 +288,33 @@ def test_mask_zero_outside_clamp_range():
 # definition by other routes: derivative by finite differences, its limits, and torch
 # autograd through the literal smooth-rounding formula.
 @pytest.mark.parametrize("alpha", [0.5, 4.0, 12.0])
-def test_dge_slope_is_derivative_of_curve(alpha):
+def test_dge_slope_is_derivative_of_curve(O, alpha):
     w = np.random.default_rng(5).uniform(-1.0, 4.0, 2000)
     h = 1e-6
-    fd = (O.dge_curve(w + h, alpha) - O.dge_curve(w - h, alpha)) / (2 * h)
+    fd = (H.dge_curve(w + h, alpha) - H.dge_curve(w - h, alpha)) / (2 * h)
     np.testing.assert_allclose(O.dge_slope(w, alpha), fd, rtol=1e-6, atol=1e-6)
 
 
-def test_dge_curve_limits_and_fixed_points():
+def test_dge_curve_limits_and_fixed_points(O):
     ints = np.arange(-2.0, 6.0)
-    np.testing.assert_allclose(O.dge_curve(ints, 7.0), ints, atol=1e-14)
-    np.testing.assert_allclose(O.dge_curve(ints + 0.5, 7.0), ints + 0.5, atol=1e-14)
+    np.testing.assert_allclose(H.dge_curve(ints, 7.0), ints, atol=1e-14)
+    np.testing.assert_allclose(H.dge_curve(ints + 0.5, 7.0), ints + 0.5, atol=1e-14)
     w = np.random.default_rng(6).uniform(-1.0, 4.0, 1000)
     # alpha -> 0: the straight-through estimator (identity curve, slope 1)
-    np.testing.assert_allclose(O.dge_curve(w, 1e-6), w, atol=1e-9)
+    np.testing.assert_allclose(H.dge_curve(w, 1e-6), w, atol=1e-9)
     np.testing.assert_allclose(O.dge_slope(w, 1e-6), 1.0, atol=1e-9)
     # alpha -> infinity: rounding, away from the half-integers
     far = w[np.abs(w - np.floor(w) - 0.5) > 0.1]
-    np.testing.assert_allclose(O.dge_curve(far, 200.0), np.rint(far), atol=1e-12)
+    np.testing.assert_allclose(H.dge_curve(far, 200.0), np.rint(far), atol=1e-12)
     # monotone, and the slope integrates to 1 over a cell
     x = np.linspace(0.0, 1.0, 200001)
-    assert np.all(np.diff(O.dge_curve(x, 9.0)) > 0)
+    assert np.all(np.diff(H.dge_curve(x, 9.0)) > 0)
     assert abs(np.trapezoid(O.dge_slope(x, 9.0), x) - 1.0) < 1e-8
     assert np.all(O.dge_slope(np.array([np.nan, np.inf, -np.inf]), 3.0) == 0.0)
 
 
 @pytest.mark.parametrize("d", [4, 8])
-def test_dge_backward_matches_torch_autograd(d):
+def test_dge_backward_matches_torch_autograd(O, d):
     """Forward rounds; the backward differentiates the smooth curve (value of round,
     gradient of s): zs = s(Wp) + (round(Wp) - s(Wp)).detach(), then clamp and decode."""
     alpha = 6.0
