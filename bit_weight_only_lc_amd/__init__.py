@@ -6,8 +6,8 @@ declared in include/lcvq.h. All arithmetic runs in the library's HIP kernels; if
 library is missing the import of any entry point raises.
 
 Names follow the C ABI (lcvq_quantize, lcvq_pack2b, lcvq_unpack2b, lcvq_linear_fwd,
-lcvq_linear_bwd, lcvq_linear_bwd_dge, lcvq_gemv2b, lcvq_gemv2b_batched and the
-*_workspace_size helpers).
+lcvq_linear_bwd, lcvq_linear_bwd_dge, lcvq_gemv2b, lcvq_gemv2b_noalloc,
+lcvq_gemv2b_batched and the *_workspace_size helpers).
 """
 
 import ctypes
@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_HERE, "liblcvq.so")
 LCVQ_F32, LCVQ_BF16 = 0, 1
 _STATUS = {0: "LCVQ_OK", 1: "LCVQ_ERR_NULL", 2: "LCVQ_ERR_SHAPE", 3: "LCVQ_ERR_D",
            4: "LCVQ_ERR_DTYPE", 5: "LCVQ_ERR_ALIGN", 6: "LCVQ_ERR_WORKSPACE", 7: "LCVQ_ERR_HIP",
-           8: "LCVQ_ERR_VALUE"}
+           8: "LCVQ_ERR_VALUE", 9: "LCVQ_ERR_SCRATCH"}
 
 _lib = None
 
@@ -64,6 +64,7 @@ def lib():
             "lcvq_gemv2b": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp],
             "lcvq_gemv2b_shuffled": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp],
             "lcvq_gemv2b_shuffle": [vp, i64, i64, vp, vp],
+            "lcvq_gemv2b_noalloc": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -231,6 +232,20 @@ def lcvq_linear_bwd_dge(dY, X, packed, mask, Wp, alpha, A, B, d, dX, dWp, dA, dB
 
 def lcvq_gemv2b(X, packed, A16, B16, d, Y, workspace=None):
     _gemv2b("lcvq_gemv2b", X, packed, A16, B16, d, Y, workspace)
+
+
+def lcvq_gemv2b_noalloc(X, packed, A16, B16, d, Y):
+    """lcvq_gemv2b on the library's fixed scratch: no workspace, nothing allocated."""
+    _check(X, "X", torch.bfloat16)
+    dev = X.device
+    _check(packed, "packed", torch.uint8, dev)
+    _check(A16, "A16", torch.float16, dev)
+    _check(B16, "B16", torch.float16, dev)
+    _check(Y, "Y", torch.bfloat16, dev)
+    M, K = X.shape
+    N = packed.shape[0]
+    _ok(lib().lcvq_gemv2b_noalloc(_p(X), M, N, K, d, _p(packed), _p(A16), _p(B16), _p(Y),
+                                  _stream(dev)), "lcvq_gemv2b_noalloc")
 
 
 def lcvq_gemv2b_shuffled(X, codes, A16, B16, d, Y, workspace=None):

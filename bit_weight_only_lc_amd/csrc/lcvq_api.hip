@@ -6,12 +6,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <vector>
+
 using namespace lcvq;
 
 namespace {
 
 constexpr size_t kAlign = 256;
-inline size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool d_ok(int d) { return d == 4 || d == 8 || d == 16; }
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -88,14 +91,19 @@ inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int d, bool f32) {
 struct GemvWs {
   size_t xq, rowinfo, total;
 };
-inline GemvWs gemv_ws(int64_t K) {
-  GemvWs w;
+constexpr GemvWs gemv_ws(int64_t K) {
   const size_t nkb = (size_t)(K / 256);
-  w.xq = 0;
+  GemvWs w{0, 0, 0};
   w.rowinfo = up(nkb * 4 * 2 * 1024);
   w.total = w.rowinfo + up(nkb * 16 * 8);
   return w;
 }
+
+// The decode product without a caller workspace (lcvq_gemv2b_noalloc): its X' limbs and
+// block scales live in a file-scope device array of fixed size, enough for K up to
+// kNoAllocMaxK. Every GPU the library runs on holds one copy until the process ends.
+constexpr int64_t kNoAllocMaxK = 65536;
+constexpr size_t kScratchBytes = gemv_ws(kNoAllocMaxK).total;   // 2,129,920 bytes
 
 struct ProfSlot {
   int id = 0;
@@ -103,6 +111,31 @@ struct ProfSlot {
 };
 thread_local ProfSlot g_prof;
 
+}  // namespace
+
+// Device-side scratch of lcvq_gemv2b_noalloc. In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the address that hipGetSymbolAddress returns
+// for the current device (scratch_ptr below), never the symbol itself.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+// Address of this device's copy of `scratch`, looked up once per device with that
+// device current and kept for later calls.
+lcvq_status_t scratch_ptr(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LCVQ_ERR_HIP;
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((size_t)dev >= ptrs.size()) ptrs.resize((size_t)dev + 1, nullptr);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LCVQ_ERR_HIP;
+    ptrs[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(ptrs[dev]);
+  return LCVQ_OK;
+}
 }  // namespace
 
 bool lcvq::take_profile(int id, hipEvent_t* start, hipEvent_t* stop) {
@@ -134,6 +167,7 @@ const char* lcvq_status_string(lcvq_status_t s) {
     case LCVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case LCVQ_ERR_HIP: return "kernel launch failed";
     case LCVQ_ERR_VALUE: return "a scalar argument is out of range";
+    case LCVQ_ERR_SCRATCH: return "shape larger than the no-allocation scratch serves";
   }
   return "unknown status";
 }
@@ -337,6 +371,20 @@ lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t 
                                    void* Y, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   return gemv2b_impl(X, M, N, K, d, codes, 1, A16, B16, Y, workspace, workspace_bytes, stream);
+}
+
+lcvq_status_t lcvq_gemv2b_noalloc(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                                  const uint8_t* packed, const void* A16, const void* B16,
+                                  void* Y, void* stream) {
+  if (!X || !packed || !A16 || !B16 || !Y) return LCVQ_ERR_NULL;
+  if (!d_ok(d)) return LCVQ_ERR_D;
+  if (M < 1 || M > 16 || !decode_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
+  if (K > kNoAllocMaxK) return LCVQ_ERR_SCRATCH;
+  static_assert(gemv_ws(kNoAllocMaxK).total <= kScratchBytes, "scratch covers the largest K");
+  uint8_t* ws = nullptr;
+  const lcvq_status_t st = scratch_ptr(&ws);
+  if (st != LCVQ_OK) return st;
+  return gemv2b_impl(X, M, N, K, d, packed, 0, A16, B16, Y, ws, kScratchBytes, stream);
 }
 
 lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,

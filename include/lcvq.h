@@ -54,7 +54,8 @@ typedef enum {
   LCVQ_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
   LCVQ_ERR_WORKSPACE = 6,  /* workspace NULL or smaller than the *_workspace_size() */
   LCVQ_ERR_HIP = 7,        /* a kernel launch failed */
-  LCVQ_ERR_VALUE = 8       /* a scalar argument is out of range */
+  LCVQ_ERR_VALUE = 8,      /* a scalar argument is out of range */
+  LCVQ_ERR_SCRATCH = 9     /* shape beyond what lcvq_gemv2b_noalloc's fixed scratch holds */
 } lcvq_status_t;
 
 typedef enum { LCVQ_F32 = 0, LCVQ_BF16 = 1 } lcvq_dtype_t;
@@ -169,6 +170,25 @@ size_t lcvq_gemv2b_workspace_size(int64_t M, int64_t N, int64_t K, int d);
 lcvq_status_t lcvq_gemv2b(const void* X, int64_t M, int64_t N, int64_t K, int d,
                           const uint8_t* packed, const void* A16, const void* B16, void* Y,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lcvq_gemv2b for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same product, the
+ * same kernels and the same output bytes as lcvq_gemv2b, without a workspace argument.
+ * Its scratch (X' limbs and block scales of the few-token path that writes them) is a
+ * fixed device array in the library, 2,129,920 bytes per GPU, held from the first call
+ * on that GPU until the process ends; its address is looked up once per device. The
+ * call allocates and frees nothing.
+ *   Arguments as for lcvq_gemv2b, less the workspace; K at most 65536.
+ * Errors as for lcvq_gemv2b; LCVQ_ERR_SCRATCH for K > 65536; LCVQ_ERR_HIP if the
+ * scratch address cannot be had. Every call on one GPU shares that GPU's scratch, which
+ * keeps the last call's contents (no part of it needs to start at zero): calls that
+ * overlap in time on one GPU (other streams, other host threads) race and must not be
+ * made.
+ */
+lcvq_status_t lcvq_gemv2b_noalloc(const void* X, int64_t M, int64_t N, int64_t K, int d,
+                                  const uint8_t* packed, const void* A16, const void* B16,
+                                  void* Y, void* stream);
 
 /*
  * Decode layout of the codes, for deployment: the same bytes as the canonical packed

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for s in range(9):
+    for s in range(10):
         assert L.lcvq_status_string(s) != b"unknown status"
     assert L.lcvq_status_string(99) == b"unknown status"
 
@@ -247,3 +247,22 @@ def test_launch_limits_are_shape_errors(L):
     ws = L.lcvq_gemv2b_workspace_size(1, 256, 256, 8)
     mats[1].N = (1 << 25) + 16                      # 2^26 + 16 rows in all
     assert L.lcvq_gemv2b_batched(P, 1, 256, 8, mats, 2, P, ws, None) == 2
+
+
+def test_gemv_noalloc_errors(L):
+    """The no-allocation decode call: argument errors as lcvq_gemv2b's, and K beyond its
+    fixed scratch is LCVQ_ERR_SCRATCH, all reported before any GPU call."""
+    def g(**kw):
+        a = dict(X=P, M=1, N=256, K=256, d=8, packed=P, A=P, B=P, Y=P)
+        a.update(kw)
+        return L.lcvq_gemv2b_noalloc(a["X"], a["M"], a["N"], a["K"], a["d"], a["packed"],
+                                     a["A"], a["B"], a["Y"], None)
+    assert g(X=None) == 1
+    assert g(Y=None) == 1
+    assert g(M=17) == 2
+    assert g(N=40) == 2
+    assert g(K=320) == 2
+    assert g(d=5) == 3
+    assert g(K=65536 + 256) == 9                     # LCVQ_ERR_SCRATCH
+    assert g(K=1 << 20, N=16) == 9
+    assert L.lcvq_status_string(9) != b"unknown status"
