@@ -11,8 +11,9 @@ HBM. Also measured in the same run:
   * the packed 2-bit decode product on {4096x4096, 14336x4096, 4096x14336} x M in
     {1, 4, 16}, cycling over >= 512 MiB of distinct code copies so the 256 MB
     last-level cache cannot serve them, against the HBM peak;
-  * the plain C++ CPU oracle on a bounded sample of the same step (2048 of the 4096
-    tokens) on the host cores.
+  * the plain C++ CPU oracle on the same step (all 4096 tokens; a few seconds on the
+    host cores);
+  * the same fwd + bwd on the MLP chain and on one 8B-shaped layer at 8192 tokens.
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--clock-warmup-s 0.5]
@@ -34,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak
-CPU_TOKENS = 2048              # tokens of the CPU oracle's sample of the step
+CPU_TOKENS = 4096              # tokens of the CPU oracle's sample of the step (all of them)
 KERNELS = {1: "quantize_prologue", 2: "fwd_product", 6: "bwd_prologue", 3: "dx_product",
            4: "dw_product"}
 
@@ -84,6 +85,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--no-copy-probe", action="store_true")
+    ap.add_argument("--no-layers", action="store_true")
+    ap.add_argument("--layer-reps", type=int, default=10)
     return ap.parse_args()
 
 
@@ -109,6 +112,85 @@ def clock_warmup(torch, fn, seconds):
         torch.cuda.synchronize()
         n += 10
     return n
+
+
+def read_probe(torch, pool, calls):
+    """Same-size read ceiling: one torch reduction (a streaming read of every byte) per
+    buffer of the rotating pool, each bracketed by its own events like the decode
+    kernels. Returns its mean time and rate."""
+    views = [p.view(torch.int32) for p in pool]
+    for v in views:
+        v.sum()
+    evs = timed_events(torch, calls)
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        views[i % len(views)].sum()
+        b.record()
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in evs) / calls * 1e-3
+    nb = pool[0].numel()
+    return {"bytes": nb, "us": round(t * 1e6, 2), "gbs": round(nb / t / 1e9, 1),
+            "kind": "torch int32 sum over the same rotating pool"}
+
+
+def time_layers(torch, P, L, mats, M, d, dev, seed, reps, warm_s):
+    """Forward + straight-through backward of each weight shape in `mats` (a list of
+    (name, N, K)) at M bf16 tokens: every matrix's step timed with events over `reps` steps
+    after a clock warm-up, and its three products timed with the library's hook inside
+    further steps. Returns per-matrix records and the sum over the list."""
+    import synth_inputs as SI
+    out = {}
+    for i, (name, N, K) in enumerate(mats):
+        inp = {"Wp": SI.make_wp(N, K, seed=seed + i, device=dev)}
+        inp["A"], inp["B"] = (t.to(dev) for t in SI.make_ab(d, seed=seed + i))
+        inp["X"] = SI.make_act(M, K, seed=seed + 100 + i, device=dev)
+        inp["dY"] = SI.make_act(M, N, seed=seed + 200 + i, device=dev)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        pk = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+        mk = torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        dWp = torch.empty((N, K), dtype=torch.float32, device=dev)
+        dA = torch.empty((d, d), dtype=torch.float32, device=dev)
+        dB = torch.empty((d,), dtype=torch.float32, device=dev)
+        wsf = torch.empty(P.lcvq_linear_fwd_workspace_size(M, N, K, d), dtype=torch.uint8,
+                          device=dev)
+        wsb = torch.empty(P.lcvq_linear_bwd_workspace_size(M, N, K, d), dtype=torch.uint8,
+                          device=dev)
+        X, Wp, A, B, dY = (inp[k] for k in ("X", "Wp", "A", "B", "dY"))
+
+        def step():
+            P.lcvq_linear_fwd(X, Wp, A, B, d, Y, pk, mk, None, wsf)
+            P.lcvq_linear_bwd(dY, X, pk, mk, A, B, d, dX, dWp, dA, dB, wsb)
+
+        clock_warmup(torch, step, warm_s)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        prod = {}
+        for kid, pname in ((2, "fwd"), (3, "dx"), (4, "dw")):
+            evs = timed_events(torch, 3)
+            for a, b in evs:
+                L.lcvq_profile_next(kid, a.cuda_event, b.cuda_event)
+                step()
+            torch.cuda.synchronize()
+            t = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+            prod[pname] = {"ms": round(t, 4),
+                           "tflops": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 1)}
+        fl = 6.0 * M * N * K
+        out[name] = {"N": N, "K": K, "ms": round(ms, 4),
+                     "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "tiles_fwd_dx_dw": [-(-M // 256) * -(-N // 256),
+                                         -(-K // 256) * -(-M // 256),
+                                         -(-K // 256) * -(-N // 256)],
+                     "products": prod}
+        del inp, X, Wp, A, B, dY, Y, pk, mk, dX, dWp, wsf, wsb
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -241,8 +323,48 @@ def main():
     q_bytes = N * K * (4 + 0.25 + 0.125 + 0.25) + M * K * (2 + 2) + M * 4
     roofline["quantize_prologue_gbs"] = round(q_bytes / (kern["quantize_prologue"] * 1e-3) / 1e9, 1)
 
+    # ------------------------------------------- MLP chain and 8B-shaped layer steps
+    # The same fwd + bwd on the Llama-7B MLP (gate and up 11008 x 4096, down 4096 x 11008)
+    # and on one layer of an 8B-shaped stack (q, k, v, o, gate, up, down) at 8192 tokens,
+    # d = 8 (MLP) and d in {4, 8, 16} (layer); the 32-layer step is 32 times one layer
+    # (every layer has the same shapes and work), labelled as such. The SiLU gating between
+    # the MLP's matrices is torch elementwise glue outside the library and outside the
+    # flops; it is left out of these timings.
+    layer_steps = None
+    if not args.no_layers:
+        layer_steps = {}
+        c2 = SI.CONFIGS["c2_mlp_7b"]
+        names2 = ["gate", "up", "down"]
+        r2 = time_layers(torch, P, L, [(nm, n, k) for nm, (n, k) in zip(names2, c2["mats"])],
+                         c2["M"], c2["d"], dev, 2000, args.layer_reps, 0.2)
+        ms2 = sum(v["ms"] for v in r2.values())
+        fl2 = 6.0 * c2["M"] * sum(n * k for n, k in c2["mats"])
+        layer_steps["mlp_7b_d8"] = {"tokens": c2["M"], "ms": round(ms2, 3),
+                                    "tflops": round(fl2 / (ms2 * 1e-3) / 1e12, 1),
+                                    "frac": round(fl2 / (ms2 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                    "matrices": r2}
+        c4 = SI.CONFIGS["c4_stack_8b_layer"]
+        names4 = ["q", "k", "v", "o", "gate", "up", "down"]
+        # k and v (and gate and up) have the same shape: timed once, counted twice
+        uniq = [("q_o", 4096, 4096), ("k_v", 1024, 4096), ("gate_up", 14336, 4096),
+                ("down", 4096, 14336)]
+        count = {"q_o": 2, "k_v": 2, "gate_up": 2, "down": 1}
+        fl4 = 6.0 * c4["M"] * sum(n * k for n, k in c4["mats"])
+        for dd in c4["ds"]:
+            r4 = time_layers(torch, P, L, uniq, c4["M"], dd, dev, 4000 + dd,
+                             args.layer_reps, 0.2)
+            ms4 = sum(count[k] * v["ms"] for k, v in r4.items())
+            layer_steps[f"stack_8b_layer_d{dd}"] = {
+                "tokens": c4["M"], "matrices_per_layer": len(names4),
+                "ms_layer": round(ms4, 3),
+                "ms_32_layers_scaled": round(32 * ms4, 2),
+                "tflops": round(fl4 / (ms4 * 1e-3) / 1e12, 1),
+                "frac": round(fl4 / (ms4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "shapes": r4}
+
     # ---------------------------------------------------------------- decode product
     decode = None
+    read_ceiling = {}
     if not args.no_decode:
         decode = {}
         clock_warmup(torch, step, min(args.clock_warmup_s, 0.2))
@@ -281,9 +403,13 @@ def main():
                     torch.cuda.synchronize()
                     t_w = w0.elapsed_time(w1) / calls * 1e-3
                     nbytes = n * k // 4 + 2 * m * k + 2 * m * n + 2 * (64 + 8)
+                    if layout == 0 and f"{n}x{k}" not in read_ceiling:
+                        read_ceiling[f"{n}x{k}"] = read_probe(torch, pool, calls)
+                    rc = read_ceiling[f"{n}x{k}"]
                     rec = {"bytes": nbytes, "kernel_us": round(t_k * 1e6, 2),
                            "kernel_gbs": round(nbytes / t_k / 1e9, 1),
                            "frac": round(nbytes / t_k / 1e9 / PEAK_HBM_GBS, 4),
+                           "frac_of_read_ceiling": round(rc["us"] * 1e-6 / t_k, 4),
                            "call_us": round(t_w * 1e6, 2),
                            "call_gbs": round(nbytes / t_w / 1e9, 1)}
                     if layout:
@@ -292,6 +418,46 @@ def main():
                         decode[f"{n}x{k}_M{m}"] = rec
             del pool
             torch.cuda.empty_cache()
+        decode["read_ceiling"] = read_ceiling
+
+        # The largest single decode launch of the 8B-shaped layer: gate and up (2 x 14336 x
+        # 4096, 28 MiB of codes) in one batched call at one token, over a rotating pool.
+        n, k, m = 14336, 4096, 1
+        gen = torch.Generator(device=dev).manual_seed(3500)
+        pair_bytes = 2 * n * k // 4
+        copies = max(2, -(-(512 << 20) // pair_bytes))
+        pool = [[torch.randint(0, 256, (n, k // 4), generator=gen, dtype=torch.uint8, device=dev)
+                 for _ in range(2)] for _ in range(copies)]
+        A16, B16 = (t.half().to(dev) for t in SI.make_ab(8, seed=3501))
+        Xd = SI.make_act(m, k, seed=3502, device=dev)
+        ys = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        ws = torch.empty(P.lcvq_gemv2b_workspace_size(m, n, k, 8), dtype=torch.uint8,
+                         device=dev)
+
+        def gate_up(i):
+            P.lcvq_gemv2b_batched(Xd, [(pool[i][0], A16, B16, ys[0]),
+                                       (pool[i][1], A16, B16, ys[1])], 8, ws)
+
+        calls = 2 * copies
+        for i in range(copies):
+            gate_up(i)
+        evs = timed_events(torch, calls)
+        for i, (a, b) in enumerate(evs):
+            L.lcvq_profile_next(5, a.cuda_event, b.cuda_event)
+            gate_up(i % copies)
+        torch.cuda.synchronize()
+        t_k = sum(a.elapsed_time(b) for a, b in evs) / calls * 1e-3
+        nbytes = pair_bytes + 2 * m * k + 2 * 2 * m * n + 2 * 2 * (64 + 8)
+        flat = [torch.cat([pl[0].view(-1), pl[1].view(-1)]) for pl in pool]
+        del pool
+        rc = read_probe(torch, flat, calls)
+        decode["gate_up_batched_M1"] = {
+            "bytes": nbytes, "kernel_us": round(t_k * 1e6, 2),
+            "kernel_gbs": round(nbytes / t_k / 1e9, 1),
+            "frac": round(nbytes / t_k / 1e9 / PEAK_HBM_GBS, 4),
+            "read_ceiling": rc, "frac_of_read_ceiling": round(rc["us"] * 1e-6 / t_k, 4)}
+        del flat
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------- decode step of an 8B-shaped stack
     # One token through all 7 projections of 32 layers (1.63 GiB of codes, far beyond the
@@ -462,6 +628,7 @@ def main():
                                "quantize + forward + straight-through backward",
                    "M": M, "N": N, "K": K, "d": d},
         "roofline": roofline,
+        "layer_steps": layer_steps,
         "decode": decode,
         "decode_stack_8b": decode_stack,
         "hbm_copy_probe": copy_probe,
