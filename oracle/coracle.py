@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(_HERE, "liblcvq_oracle.so")
 _lib = None
 
 __all__ = ["quantize", "pack2b", "unpack2b", "pack_mask", "unpack_mask", "reconstruct",
-           "linear_fwd", "linear_bwd", "gemv2b", "dge_slope", "threads", "lib"]
+           "linear_fwd", "linear_bwd", "gemv2b", "dge_slope", "threads", "lib",
+           "hessian", "damp", "udu", "ptq_objective", "ptq_sweep", "ptq_solve_sb", "ptq_init"]
 
 
 def lib():
@@ -48,6 +49,13 @@ def lib():
                                 vp, vp], None),
             "oc_dge_slope": ([vp, i64, f64, vp], None),
             "oc_gemv2b": ([vp, i64, i64, vp, i64, i32, vp, vp, vp, i64, vp], None),
+            "oc_hessian": ([vp, i64, i64, vp], None),
+            "oc_damp": ([vp, i64, f64, vp], None),
+            "oc_udu": ([vp, i64, vp, vp], i32),
+            "oc_ptq_objective": ([vp, vp, i64, i64, vp, f64, f64], f64),
+            "oc_ptq_sweep": ([vp, i64, i64, vp, f64, f64, vp, vp], None),
+            "oc_ptq_solve_sb": ([vp, vp, i64, i64, vp, vp, vp], i32),
+            "oc_ptq_init": ([vp, i64, i64, vp, f64, i32, vp, vp, vp, vp], i32),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -200,3 +208,80 @@ def gemv2b(X, packed, A, B, d, rows=None):
     Y = np.empty((M, nr if r is not None else N), np.float64)
     lib().oc_gemv2b(_p(Xc), M, K, _p(pk), N, d, _p(Ac), _p(Bc), _p(r), nr, _p(Y))
     return Y
+
+
+# ---------------------------------------------------------------- PTQ initialisation
+def hessian(X):
+    """H = X^T X for calibration activations X [M, K]."""
+    Xc = _c(X, np.float64)
+    M, K = Xc.shape
+    H = np.empty((K, K), np.float64)
+    lib().oc_hessian(_p(Xc), M, K, _p(H))
+    return H
+
+
+def damp(H, dmp):
+    """H + dmp * mean(diag(H)) I."""
+    Hc = _c(H, np.float64)
+    out = np.empty_like(Hc)
+    lib().oc_damp(_p(Hc), Hc.shape[0], float(dmp), _p(out))
+    return out
+
+
+def udu(Hd):
+    """(U, D) with Hd = U diag(D) U^T, U unit upper triangular."""
+    Hc = _c(Hd, np.float64)
+    K = Hc.shape[0]
+    U = np.empty((K, K), np.float64)
+    D = np.empty(K, np.float64)
+    bad = lib().oc_udu(_p(Hc), K, _p(U), _p(D))
+    if bad:
+        raise ValueError(f"matrix not positive definite (pivot {bad - 1})")
+    return U, D
+
+
+def ptq_objective(W0, c, Hd, s, b):
+    W = _c(W0, np.float64)
+    cc = _c(c, np.uint8)
+    Hc = _c(Hd, np.float64)
+    N, K = W.shape
+    return float(lib().oc_ptq_objective(_p(W), _p(cc), N, K, _p(Hc), float(s), float(b)))
+
+
+def ptq_sweep(W0, U, s, b, want_t=False):
+    """The integer step for fixed (s, b): codes [N, K] (and the continuous targets t)."""
+    W = _c(W0, np.float64)
+    Uc = _c(U, np.float64)
+    N, K = W.shape
+    c = np.empty((N, K), np.uint8)
+    t = np.empty((N, K), np.float64) if want_t else None
+    lib().oc_ptq_sweep(_p(W), N, K, _p(Uc), float(s), float(b), _p(c), _p(t))
+    return (c, t) if want_t else c
+
+
+def ptq_solve_sb(W0, c, Hd, s=1.0, b=0.0):
+    """The (s, b) step for fixed codes; returns (s, b, singular)."""
+    W = _c(W0, np.float64)
+    cc = _c(c, np.uint8)
+    Hc = _c(Hd, np.float64)
+    N, K = W.shape
+    sv = ctypes.c_double(s)
+    bv = ctypes.c_double(b)
+    sing = lib().oc_ptq_solve_sb(_p(W), _p(cc), N, K, _p(Hc), ctypes.byref(sv), ctypes.byref(bv))
+    return sv.value, bv.value, bool(sing)
+
+
+def ptq_init(W0, H, dmp, iters):
+    """The whole initialisation from H = X^T X: returns codes [N, K], s, b and the
+    objective after each of the 2 * iters steps."""
+    W = _c(W0, np.float64)
+    Hc = _c(H, np.float64)
+    N, K = W.shape
+    c = np.empty((N, K), np.uint8)
+    sv, bv = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    obj = np.empty(2 * iters, np.float64)
+    bad = lib().oc_ptq_init(_p(W), N, K, _p(Hc), float(dmp), int(iters), _p(c),
+                            ctypes.byref(sv), ctypes.byref(bv), _p(obj))
+    if bad:
+        raise ValueError(f"damped H not positive definite (pivot {bad - 1})")
+    return {"codes": c, "s": sv.value, "b": bv.value, "obj": obj}

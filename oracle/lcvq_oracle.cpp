@@ -272,4 +272,203 @@ void oc_gemv2b(const double* X, int64_t M, int64_t K, const uint8_t* packed, int
   }
 }
 
+// ---------------------------------------------------------------- PTQ initialisation
+// Layer-wise initialisation of a per-tensor code (A = s I, B = b 1: one scale and one
+// offset per matrix), the starting point that [LCQAT-M2] takes from post-training
+// quantization. The objective is [DQ-3] eq. (5)/(7) in this layout (W[N, K], X [M, K],
+// layer output X W^T), summed over the N output rows:
+//   g(c; s, b) = 1/2 sum_n (s c_n + b 1 - w0_n)^T H (s c_n + b 1 - w0_n),  c_n in {0..3}^K
+// with H = X^T X damped as H + delta I, delta = damp * mean(diag(X^T X)) (a reading: the
+// pages give no regularisation, and without one X^T X from fewer calibration tokens than
+// inputs is singular and eq. (11)'s minimiser is not unique). LC's codes {0..3} are
+// decoupleQ's {-2..1} shifted by 2, so s c + b is eq. (4) with z = b + 2 s.
+// [DQ-3] section 3.3 alternates two steps:
+//  * (s, b): with c fixed, g is an unconstrained quadratic in (s, b); its stationary point
+//    solves [S1 S2; S2 S3] [s; b] = [T1; T2] with S1 = sum c^T H c, S2 = sum c^T H 1,
+//    S3 = N 1^T H 1, T1 = sum c^T H w0, T2 = sum 1^T H w0 (eq. (7) differentiated);
+//  * c: element by element in index order, round and clip element k of the current
+//    continuous solution, then re-solve the elements after k without the integer and box
+//    constraints (eq. (11)). Written with H = U D U^T (U unit upper triangular), the
+//    continuous value of element k once elements 0..k-1 are fixed is
+//      t_k = v_k + sum_{i<k} U_ik (v_i - c_i),   v = (w0 - b) / s,
+//    (for fixed d_P = c_P - v_P the minimiser is d_F = -H_FF^-1 H_FP d_P, and with the
+//    factorisation H_FF^-1 H_FP = U_FF^-T U_PF^T, whose first row gives the sum above),
+//    and c_k = clip(round(t_k), 0, 3).
+
+// H = X^T X, plain loops (row i of H in parallel).
+void oc_hessian(const double* X, int64_t M, int64_t K, double* H) {
+#pragma omp parallel for schedule(dynamic, 4)
+  for (int64_t i = 0; i < K; ++i)
+    for (int64_t j = 0; j < K; ++j) {
+      double s = 0.0;
+      for (int64_t m = 0; m < M; ++m) s += X[m * K + i] * X[m * K + j];
+      H[i * K + j] = s;
+    }
+}
+
+// The damped matrix: Hd = H + damp * mean(diag(H)) I.
+void oc_damp(const double* H, int64_t K, double damp, double* Hd) {
+  double tr = 0.0;
+  for (int64_t i = 0; i < K; ++i) tr += H[i * K + i];
+  const double delta = damp * tr / (double)K;
+  for (int64_t i = 0; i < K * K; ++i) Hd[i] = H[i];
+  for (int64_t i = 0; i < K; ++i) Hd[i * K + i] += delta;
+}
+
+// Hd = U diag(D) U^T with U unit upper triangular (the last index is eliminated first):
+//   D_k = Hd_kk - sum_{j>k} U_kj^2 D_j;  U_ik = (Hd_ik - sum_{j>k} U_ij D_j U_kj) / D_k, i < k.
+// Returns 0, or k + 1 if D_k <= 0 (Hd not positive definite).
+int oc_udu(const double* Hd, int64_t K, double* U, double* D) {
+  for (int64_t i = 0; i < K * K; ++i) U[i] = 0.0;
+  for (int64_t k = K - 1; k >= 0; --k) {
+    double d = Hd[k * K + k];
+    for (int64_t j = k + 1; j < K; ++j) d -= U[k * K + j] * U[k * K + j] * D[j];
+    if (!(d > 0.0)) return (int)(k + 1);
+    D[k] = d;
+    U[k * K + k] = 1.0;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < k; ++i) {
+      double v = Hd[i * K + k];
+      for (int64_t j = k + 1; j < K; ++j) v -= U[i * K + j] * D[j] * U[k * K + j];
+      U[i * K + k] = v / d;
+    }
+  }
+  return 0;
+}
+
+// g(c; s, b) computed straight from its definition with Hd (rows in parallel, added in
+// row order).
+double oc_ptq_objective(const double* W0, const uint8_t* c, int64_t N, int64_t K,
+                        const double* Hd, double s, double b) {
+  std::vector<double> rowg((size_t)N);
+#pragma omp parallel
+  {
+    std::vector<double> r((size_t)K);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; ++n) {
+      for (int64_t k = 0; k < K; ++k) r[k] = s * (double)c[n * K + k] + b - W0[n * K + k];
+      double acc = 0.0;
+      for (int64_t i = 0; i < K; ++i) {
+        double hr = 0.0;
+        for (int64_t j = 0; j < K; ++j) hr += Hd[i * K + j] * r[j];
+        acc += r[i] * hr;
+      }
+      rowg[n] = 0.5 * acc;
+    }
+  }
+  double g = 0.0;
+  for (int64_t n = 0; n < N; ++n) g += rowg[n];
+  return g;
+}
+
+// The integer step for fixed (s, b): codes c [N][K]; t (optional, [N][K]) receives the
+// continuous value t_k each element was rounded from.
+void oc_ptq_sweep(const double* W0, int64_t N, int64_t K, const double* U, double s, double b,
+                  uint8_t* c, double* t) {
+  std::fesetround(FE_TONEAREST);
+#pragma omp parallel
+  {
+    std::vector<double> v((size_t)K), e((size_t)K);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; ++n) {
+      for (int64_t k = 0; k < K; ++k) v[k] = (W0[n * K + k] - b) / s;
+      for (int64_t k = 0; k < K; ++k) {
+        double tk = v[k];
+        for (int64_t i = 0; i < k; ++i) tk += U[i * K + k] * e[i];
+        const double r = std::nearbyint(tk);
+        const double q = r < 0.0 ? 0.0 : (r > 3.0 ? 3.0 : r);
+        c[n * K + k] = (uint8_t)q;
+        e[k] = v[k] - q;
+        if (t) t[n * K + k] = tk;
+      }
+    }
+  }
+}
+
+// The (s, b) step for fixed codes: the stationary point of g, computed from the sums of
+// its normal equations (each a plain double loop over H). Leaves s, b unchanged and
+// returns 1 when the system is singular or gives s = 0 (the next integer step divides by
+// s); returns 0 otherwise.
+int oc_ptq_solve_sb(const double* W0, const uint8_t* c, int64_t N, int64_t K, const double* Hd,
+                    double* s, double* b) {
+  std::vector<double> h1((size_t)K, 0.0);
+  for (int64_t i = 0; i < K; ++i)
+    for (int64_t j = 0; j < K; ++j) h1[i] += Hd[i * K + j];
+  double one_h_one = 0.0;
+  for (int64_t i = 0; i < K; ++i) one_h_one += h1[i];
+  std::vector<double> rs((size_t)N * 4);
+#pragma omp parallel
+  {
+    std::vector<double> hc((size_t)K);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; ++n) {
+      const uint8_t* cn = c + n * K;
+      const double* wn = W0 + n * K;
+      for (int64_t i = 0; i < K; ++i) {
+        double v = 0.0;
+        for (int64_t j = 0; j < K; ++j) v += Hd[i * K + j] * (double)cn[j];
+        hc[i] = v;
+      }
+      double s1 = 0.0, s2 = 0.0, t1 = 0.0, t2 = 0.0;
+      for (int64_t i = 0; i < K; ++i) {
+        s1 += (double)cn[i] * hc[i];      // c^T H c
+        s2 += hc[i];                      // 1^T H c
+        t1 += hc[i] * wn[i];              // c^T H w0
+        t2 += h1[i] * wn[i];              // 1^T H w0
+      }
+      rs[n * 4 + 0] = s1; rs[n * 4 + 1] = s2; rs[n * 4 + 2] = t1; rs[n * 4 + 3] = t2;
+    }
+  }
+  double S1 = 0.0, S2 = 0.0, T1 = 0.0, T2 = 0.0;
+  for (int64_t n = 0; n < N; ++n) {
+    S1 += rs[n * 4 + 0]; S2 += rs[n * 4 + 1]; T1 += rs[n * 4 + 2]; T2 += rs[n * 4 + 3];
+  }
+  const double S3 = (double)N * one_h_one;
+  const double det = S1 * S3 - S2 * S2;
+  if (!(std::fabs(det) > 1e-12 * std::fabs(S1 * S3)) || !std::isfinite(det)) return 1;
+  const double sn = (T1 * S3 - S2 * T2) / det;
+  const double bn = (S1 * T2 - S2 * T1) / det;
+  if (sn == 0.0 || !std::isfinite(sn) || !std::isfinite(bn)) return 1;
+  *s = sn;
+  *b = bn;
+  return 0;
+}
+
+// The whole initialisation: start from the uniform grid over the weight's range (s =
+// (max - min) / 3, b = min; s = 1 for a constant matrix), then `iters` alternations of
+// the integer step and the (s, b) step. The integer step's codes replace the current
+// ones only if they do not raise g at the current (s, b) (the first always does), so the
+// objective never increases. obj (2 * iters values, optional): g after each step.
+// H is X^T X; it is damped here. Returns 0, or the oc_udu failure index.
+int oc_ptq_init(const double* W0, int64_t N, int64_t K, const double* H, double damp,
+                int iters, uint8_t* codes, double* s_out, double* b_out, double* obj) {
+  std::vector<double> Hd((size_t)K * K), U((size_t)K * K), D((size_t)K);
+  oc_damp(H, K, damp, Hd.data());
+  const int bad = oc_udu(Hd.data(), K, U.data(), D.data());
+  if (bad) return bad;
+  double lo = W0[0], hi = W0[0];
+  for (int64_t i = 1; i < N * K; ++i) {
+    lo = W0[i] < lo ? W0[i] : lo;
+    hi = W0[i] > hi ? W0[i] : hi;
+  }
+  double s = hi > lo ? (hi - lo) / 3.0 : 1.0, b = lo;
+  std::vector<uint8_t> cand((size_t)N * K);
+  double gcur = 0.0;
+  for (int it = 0; it < iters; ++it) {
+    oc_ptq_sweep(W0, N, K, U.data(), s, b, cand.data(), nullptr);
+    const double gc = oc_ptq_objective(W0, cand.data(), N, K, Hd.data(), s, b);
+    if (it == 0 || gc <= gcur) {
+      std::memcpy(codes, cand.data(), (size_t)N * K);
+      gcur = gc;
+    }
+    if (obj) obj[2 * it] = gcur;
+    oc_ptq_solve_sb(W0, codes, N, K, Hd.data(), &s, &b);
+    gcur = oc_ptq_objective(W0, codes, N, K, Hd.data(), s, b);
+    if (obj) obj[2 * it + 1] = gcur;
+  }
+  *s_out = s;
+  *b_out = b;
+  return 0;
+}
+
 }  // extern "C"

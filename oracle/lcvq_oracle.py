@@ -44,7 +44,7 @@ import numpy as np
 __all__ = [
     "quantize", "pack2b", "unpack2b", "pack_mask", "unpack_mask", "reconstruct",
     "linear_fwd", "linear_bwd", "gemv2b", "nearest_codeword", "decoupleq_quant",
-    "dge_curve", "dge_slope",
+    "dge_curve", "dge_slope", "ptq_objective", "ptq_sweep_literal",
 ]
 
 
@@ -235,3 +235,33 @@ def decoupleq_quant(W0, s, zero, alpha=-2, beta=1):
     W0 = np.asarray(W0, dtype=np.float64)
     q = np.clip(np.rint((W0 - zero) / s), alpha, beta)
     return q, q * s + zero
+
+
+def ptq_objective(W0, c, Hd, s, b):
+    """[DQ-3.1] eq. (5)/(7) per output row, summed: 1/2 sum_n r_n^T Hd r_n with
+    r_n = s c_n + b - w0_n (the decoded weight's error; LC codes c = W^ + 2)."""
+    R = s * np.asarray(c, np.float64) + b - np.asarray(W0, np.float64)
+    return 0.5 * float(np.sum((R @ np.asarray(Hd, np.float64)) * R))
+
+
+def ptq_sweep_literal(W0, Hd, s, b):
+    """decoupleQ section 3.3's integer step taken literally, for small K only: element j
+    is rounded and clipped to {0..3} from the current continuous solution, then the
+    elements after j are re-solved by the unconstrained minimiser of the objective with
+    elements 0..j fixed (eq. (11)), by a linear solve at every step."""
+    W0 = np.asarray(W0, np.float64)
+    Hd = np.asarray(Hd, np.float64)
+    N, K = W0.shape
+    out = np.zeros((N, K), np.uint8)
+    for n in range(N):
+        v = (W0[n] - b) / s                 # minimiser with nothing fixed: s c + b = w0
+        x = v.copy()
+        c = np.zeros(K)
+        for j in range(K):
+            c[j] = np.clip(np.rint(x[j]), 0, 3)
+            if j + 1 < K:
+                P, F = slice(0, j + 1), slice(j + 1, K)
+                d_p = c[P] - v[P]
+                x[F] = v[F] - np.linalg.solve(Hd[F, F], Hd[F, P] @ d_p)
+        out[n] = c.astype(np.uint8)
+    return out
