@@ -7,7 +7,7 @@ library is missing the import of any entry point raises.
 
 Names follow the C ABI (lcvq_quantize, lcvq_pack2b, lcvq_unpack2b, lcvq_linear_fwd,
 lcvq_linear_bwd, lcvq_linear_bwd_dge, lcvq_gemv2b, lcvq_gemv2b_noalloc,
-lcvq_gemv2b_batched and the *_workspace_size helpers).
+lcvq_gemv2b_batched, lcvq_hessian, lcvq_ptq_init and the *_workspace_size helpers).
 """
 
 import ctypes
@@ -65,6 +65,8 @@ def lib():
             "lcvq_gemv2b_shuffled": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp],
             "lcvq_gemv2b_shuffle": [vp, i64, i64, vp, vp],
             "lcvq_gemv2b_noalloc": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp],
+            "lcvq_hessian": [vp, i64, i64, vp, vp],
+            "lcvq_ptq_init": [vp, vp, i64, i64, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -77,6 +79,8 @@ def lib():
         L.lcvq_gemv2b_batched.restype = i32
         L.lcvq_gemv2b_batched.argtypes = [vp, i64, i64, i32, ctypes.POINTER(GemvMatrix), i32,
                                           vp, sz, vp]
+        L.lcvq_ptq_workspace_size.restype = sz
+        L.lcvq_ptq_workspace_size.argtypes = [i64, i64]
         L.lcvq_gemv2b_workspace_size.restype = sz
         L.lcvq_gemv2b_workspace_size.argtypes = [i64, i64, i64, i32]
         L.lcvq_profile_next.restype = i32
@@ -305,6 +309,55 @@ def lcvq_gemv2b_batched(X, mats, d, workspace=None):
     _check(workspace, "workspace", torch.uint8, dev)
     _ok(lib().lcvq_gemv2b_batched(_p(X), M, K, d, arr, len(mats), _p(workspace),
                                   workspace.numel(), _stream(dev)), "lcvq_gemv2b_batched")
+
+
+def lcvq_hessian(X, H):
+    """H = X^T X (X bf16 [M, K], H float32 [K, K])."""
+    _check(X, "X", torch.bfloat16)
+    _check(H, "H", torch.float32, X.device)
+    M, K = X.shape
+    _ok(lib().lcvq_hessian(_p(X), M, K, _p(H), _stream(X.device)), "lcvq_hessian")
+
+
+def lcvq_ptq_workspace_size(N, K):
+    return int(lib().lcvq_ptq_workspace_size(N, K))
+
+
+def lcvq_ptq_init(H, W0, damp, iters, packed_out, sb_out, obj_out=None, U_out=None,
+                  D_out=None, workspace=None):
+    _check(H, "H", torch.float32)
+    dev = H.device
+    _check(W0, "W0", torch.float32, dev)
+    _check(packed_out, "packed_out", torch.uint8, dev)
+    _check(sb_out, "sb_out", torch.float32, dev)
+    for t, n in ((obj_out, "obj_out"), (U_out, "U_out"), (D_out, "D_out")):
+        _check(t, n, torch.float32, dev)
+    N, K = W0.shape
+    if workspace is None:
+        workspace = torch.empty(max(lcvq_ptq_workspace_size(N, K), 1), dtype=torch.uint8,
+                                device=dev)
+    _check(workspace, "workspace", torch.uint8, dev)
+    _ok(lib().lcvq_ptq_init(_p(H), _p(W0), N, K, float(damp), int(iters), _p(packed_out),
+                            _p(sb_out), _p(obj_out), _p(U_out), _p(D_out), _p(workspace),
+                            workspace.numel(), _stream(dev)), "lcvq_ptq_init")
+
+
+def ptq_init(X, W0, damp=0.01, iters=4, want_ud=False):
+    """Allocating helper: H = X^T X, then the initialisation. Returns a dict with H, the
+    packed codes, s, b, the objective history (and U, D with want_ud)."""
+    dev = X.device
+    M, K = X.shape
+    N = W0.shape[0]
+    H = torch.empty((K, K), dtype=torch.float32, device=dev)
+    lcvq_hessian(X, H)
+    out = {"H": H,
+           "packed": torch.empty((N, K // 4), dtype=torch.uint8, device=dev),
+           "sb": torch.empty(2, dtype=torch.float32, device=dev),
+           "obj": torch.empty(2 * iters, dtype=torch.float32, device=dev),
+           "U": torch.empty((K, K), dtype=torch.float32, device=dev) if want_ud else None,
+           "D": torch.empty(K, dtype=torch.float32, device=dev) if want_ud else None}
+    lcvq_ptq_init(H, W0, damp, iters, out["packed"], out["sb"], out["obj"], out["U"], out["D"])
+    return out
 
 
 # ------------------------------------------------------------------ allocating helpers

@@ -1078,6 +1078,96 @@ void k_gemm_dw(GemmArgs a) {
   epilogue_dw<D, NW, WJ>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
 }
 
+// ---- Gram matrix H = X^T X of calibration activations --------------------------------
+// The dW product's main loop with X as both operands: C[p, q] = sum_m X[m, p] X[m, q] on
+// 256 x 256 tiles, computed only for tile-row <= tile-column. Every element with p <= q
+// is written to H[p][q] and H[q][p] (elements p > q of a diagonal tile are skipped), so H
+// is exactly symmetric. Rows m past M are contraction terms and are cleared; columns past
+// K are clamped reads whose results are not stored.
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_gram(const uint16_t* __restrict__ X, int M, int K, float* __restrict__ H) {
+  constexpr int WGQ = 4, WJ = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TTILEB];   // 128 KiB
+  const int T = (K + BT - 1) / BT;
+  int t = blockIdx.x, tp = 0;                     // upper tile t -> (tp, tq), row by row
+  while (t >= T - tp) {
+    t -= T - tp;
+    ++tp;
+  }
+  const int tq = tp + t;
+  const int p0 = tp * BT, q0 = tq * BT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wp = wave / WGQ, wq = wave % WGQ;
+  const int nk = (M + BK - 1) / BK;
+  const DwLaneOffsets lo = dw_lane_offsets(K, K, p0, q0, lane);
+  f32x16 acc[4][WJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  issue_dw_stage(smem, X, X, M, K, K, 0, p0, q0, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {                // the dW product's stage order
+    const uint8_t* slot = smem + (kt & 1) * 2 * TTILEB;
+    DwFrags<WJ> f0, f1, f2;
+    dw_read<WJ>(slot, 0, wp, wq, lane, f0);
+    dw_read<WJ>(slot, 1, wp, wq, lane, f1);
+    dw_read<WJ>(slot, 2, wp, wq, lane, f2);
+    __builtin_amdgcn_sched_barrier(0);
+    dw_mfma<WJ>(f0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    dw_read<WJ>(slot, 3, wp, wq, lane, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    uint8_t* next = smem + ((kt & 1) ^ 1) * 2 * TTILEB;
+    if (kt + 1 < nk) issue_dw_stage_rows(next, X, X, M, K, K, (kt + 1) * BK, lo, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    dw_mfma<WJ>(f1, acc);
+    dw_mfma<WJ>(f2, acc);
+    dw_mfma<WJ>(f0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (kt + 1 < nk && (kt + 1) * BK + wave * 8 + 8 > M) zero_dw_rows(next, (kt + 1) * BK, M, wave, lane);
+    __syncthreads();
+  }
+  // accumulator block (i, j): lane column q = l % 32; register r holds row
+  // 8 (r / 4) + 4 (l / 32) + r % 4, so registers 4g .. 4g + 3 are four consecutive rows:
+  // H[q][p .. p + 3] is one 16-byte store when all four rows are at or above the diagonal.
+  const int col = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int q = q0 + wq * 32 * WJ + j * 32 + col;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int p = p0 + wp * 128 + i * 32 + 8 * g + 4 * h;
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
+        if (q >= K) continue;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (p + u < K && p + u <= q) H[(int64_t)(p + u) * K + q] = v[u];
+        if (p + 3 < q && p + 3 < K) {
+          *reinterpret_cast<f32x4*>(H + (int64_t)q * K + p) = v;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (p + u < K && p + u < q) H[(int64_t)q * K + p + u] = v[u];
+        }
+      }
+    }
+}
+
+hipError_t launch_gram(const uint16_t* X, int M, int K, float* H, hipStream_t s) {
+  const int T = (K + BT - 1) / BT;
+  LCVQ_LAUNCH(PROF_GRAM, k_gram, dim3(T * (T + 1) / 2), dim3(512), 0, s, X, M, K, H);
+  return hipGetLastError();
+}
+
 // One block per output: thread t adds tiles t, t+256, ... in order, then a fixed
 // binary tree in LDS combines the 256 thread sums.
 __global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ partials,

@@ -36,6 +36,14 @@ constexpr int64_t kMaxDecodeWeights = int64_t(1) << 36;                 // N * K
 
 inline int64_t tiles(int64_t P, int64_t Q) { return ((P + 255) / 256) * ((Q + 255) / 256); }
 
+// PTQ initialisation: K a multiple of 64 up to 16384 (the sweep keeps a workgroup's 16
+// rows of codes in LDS); N a multiple of 16 up to 2^20.
+constexpr int64_t kPtqMaxK = 16384;
+inline bool ptq_shape_ok(int64_t N, int64_t K) {
+  return N >= 16 && (N % 16) == 0 && N <= (int64_t(1) << 20) && K >= 64 && (K % 64) == 0 &&
+         K <= kPtqMaxK;
+}
+
 // Linear-layer shapes: M rows of activations, weight [N, K].
 inline bool layer_shape_ok(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || M > kMaxRows) return false;
@@ -149,7 +157,7 @@ bool lcvq::take_profile(int id, hipEvent_t* start, hipEvent_t* stop) {
 extern "C" {
 
 lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event) {
-  if (kernel_id < PROF_QUANTIZE || kernel_id > PROF_BWD_PREP) return LCVQ_ERR_SHAPE;
+  if (kernel_id < PROF_QUANTIZE || kernel_id > PROF_LAST) return LCVQ_ERR_SHAPE;
   g_prof.id = (start_event && stop_event) ? kernel_id : 0;
   g_prof.start = static_cast<hipEvent_t>(start_event);
   g_prof.stop = static_cast<hipEvent_t>(stop_event);
@@ -385,6 +393,34 @@ lcvq_status_t lcvq_gemv2b_noalloc(const void* X, int64_t M, int64_t N, int64_t K
   const lcvq_status_t st = scratch_ptr(&ws);
   if (st != LCVQ_OK) return st;
   return gemv2b_impl(X, M, N, K, d, packed, 0, A16, B16, Y, ws, kScratchBytes, stream);
+}
+
+lcvq_status_t lcvq_hessian(const void* X, int64_t M, int64_t K, float* H, void* stream) {
+  if (!X || !H) return LCVQ_ERR_NULL;
+  if (M < 1 || M > kMaxRows || K < 64 || (K % 64) || K > kPtqMaxK) return LCVQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(H)) return LCVQ_ERR_ALIGN;
+  return from_hip(launch_gram(static_cast<const uint16_t*>(X), (int)M, (int)K, H,
+                              as_stream(stream)));
+}
+
+size_t lcvq_ptq_workspace_size(int64_t N, int64_t K) {
+  if (!ptq_shape_ok(N, K)) return 0;
+  return ptq_workspace_bytes(N, K);
+}
+
+lcvq_status_t lcvq_ptq_init(const float* H, const float* W0, int64_t N, int64_t K, float damp,
+                            int iters, uint8_t* packed_out, float* sb_out, float* obj_out,
+                            float* U_out, float* D_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!H || !W0 || !packed_out || !sb_out) return LCVQ_ERR_NULL;
+  if (!ptq_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
+  if (!(damp > 0.f) || !(damp <= 1.f) || iters < 1 || iters > 64) return LCVQ_ERR_VALUE;
+  if (!aligned16(H) || !aligned16(W0) || !aligned16(packed_out) || !aligned16(sb_out) ||
+      !aligned16(obj_out) || !aligned16(U_out) || !aligned16(D_out) || !aligned16(workspace))
+    return LCVQ_ERR_ALIGN;
+  if (!workspace || workspace_bytes < ptq_workspace_bytes(N, K)) return LCVQ_ERR_WORKSPACE;
+  return from_hip(launch_ptq_init(H, W0, (int)N, (int)K, damp, iters, packed_out, sb_out,
+                                  obj_out, U_out, D_out, workspace, as_stream(stream)));
 }
 
 lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,

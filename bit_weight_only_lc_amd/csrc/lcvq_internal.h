@@ -6,7 +6,8 @@
 namespace lcvq {
 
 // Kernel ids of the profiling hook (lcvq_profile_next).
-enum { PROF_QUANTIZE = 1, PROF_FWD = 2, PROF_DX = 3, PROF_DW = 4, PROF_GEMV = 5, PROF_BWD_PREP = 6 };
+enum { PROF_QUANTIZE = 1, PROF_FWD = 2, PROF_DX = 3, PROF_DW = 4, PROF_GEMV = 5, PROF_BWD_PREP = 6,
+       PROF_GRAM = 7, PROF_PTQ_SWEEP = 8, PROF_LAST = 8 };
 // True (once) if the calling thread armed timing for kernel `id`; returns the events.
 bool take_profile(int id, hipEvent_t* start, hipEvent_t* stop);
 
@@ -69,6 +70,15 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, const float* dge_wp,
                           float dge_alpha, bool reduce, hipStream_t s);
+
+// PTQ initialisation: H = X^T X (bf16 X [M][K], K a multiple of 64, float H [K][K]).
+hipError_t launch_gram(const uint16_t* X, int M, int K, float* H, hipStream_t s);
+// The rest of the initialisation (damped factorisation, alternation, packed output); the
+// workspace is carved by ptq_workspace().
+size_t ptq_workspace_bytes(int64_t N, int64_t K);
+hipError_t launch_ptq_init(const float* H, const float* W0, int N, int K, float damp, int iters,
+                           uint8_t* packed_out, float* sb_out, float* obj_out, float* U_out,
+                           float* D_out, void* workspace, hipStream_t s);
 
 // Matrices that share X for one fused decode launch (kernel argument, by value).
 constexpr int GEMV_MAX_BATCH = 8;

@@ -246,12 +246,63 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * Gram matrix of calibration activations for the PTQ initialisation: H = X^T X
+ * (decoupleQ, section 3.1: H = X^T X of the layer input over a small calibration set).
+ *   X  bfloat16 [M, K], 1 <= M <= 2^24 - 2^17, K a multiple of 64 up to 16384
+ *   H  float [K, K]                                                    out, overwritten
+ * Products of bf16 values are exact; sums are float32 on the matrix cores. H is exactly
+ * symmetric (each off-diagonal pair is written from one sum).
+ * Errors: LCVQ_ERR_NULL, LCVQ_ERR_SHAPE, LCVQ_ERR_ALIGN, LCVQ_ERR_HIP.
+ */
+lcvq_status_t lcvq_hessian(const void* X, int64_t M, int64_t K, float* H, void* stream);
+
+/*
+ * PTQ initialisation of one matrix with a per-tensor code, A = s I and B = b 1 (the
+ * starting point LC-QAT takes from post-training quantization: LC-QAT summary,
+ * Methodology 2; the problem and its alternating solver: decoupleQ, sections 3.1-3.3,
+ * eq. (5)-(11), with decoupleQ's integers {-2..1} as codes {0..3}, z = b + 2 s).
+ * It minimises
+ *   g(c; s, b) = 1/2 sum_n (s c_n + b 1 - w0_n)^T Hd (s c_n + b 1 - w0_n)
+ * over codes c in {0..3}^[N, K] and floats s, b, with Hd = H + damp * mean(diag H) I.
+ * Start: s = (max W0 - min W0) / 3, b = min W0. Then `iters` times:
+ *  1. integer step at the current (s, b): for every row, element by element in index
+ *     order, round half to even and clip to {0..3} the element's value, then re-solve the
+ *     later elements of the row without constraints (decoupleQ eq. (11)); computed as
+ *     t_k = (q_k - b e_k) / s - sum_{i<k} U_ik c_i with Hd = U D U^T (U unit upper), q =
+ *     U^T w0, e = U^T 1. These codes replace the current ones unless they raise g at this
+ *     (s, b) (on the first iteration they always do);
+ *  2. (s, b) step: the least-squares (s, b) of the current codes (eq. (7) set to zero);
+ *     kept unchanged if that system is singular or gives s = 0.
+ * The objective therefore never increases.
+ *   H          float [K, K], symmetric (lcvq_hessian's output)                       in
+ *   W0         float [N, K], the weight to initialise (N outputs, K inputs)          in
+ *   N          a multiple of 16 up to 2^20;  K a multiple of 64 up to 16384
+ *   damp       0 < damp <= 1 (LCVQ_ERR_VALUE otherwise);  iters in 1..64
+ *   packed_out uint8 [N, K/4], the codes in the canonical packed layout              out
+ *   sb_out     float [2]: s, b (both NaN if Hd's factorisation met a pivot <= 0)     out
+ *   obj_out    float [2 * iters] or NULL: g after each step                          out
+ *   U_out      float [K, K] or NULL: U (unit upper triangular), row-major            out
+ *   D_out      float [K] or NULL: D                                                  out
+ *   workspace  >= lcvq_ptq_workspace_size(N, K) bytes (0 for invalid shapes)
+ * Numerics: float32 factorisation and sums (double for the workgroup and final sums);
+ * the sweep's sums over earlier codes run on the bf16 matrix cores with U split into bf16
+ * hi + lo halves (about 16 significant bits) and the codes exact. A code decided from a
+ * value within a few 1e-5 of a half-integer may differ from a float64 computation.
+ */
+size_t lcvq_ptq_workspace_size(int64_t N, int64_t K);
+lcvq_status_t lcvq_ptq_init(const float* H, const float* W0, int64_t N, int64_t K, float damp,
+                            int iters, uint8_t* packed_out, float* sb_out, float* obj_out,
+                            float* U_out, float* D_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Profiling hook (changes no result). Arms a one-shot timing of the next launch of one
  * kernel by calls made from this host thread: the kernel is launched with
  * hipExtLaunchKernel between `start_event` and `stop_event` (hipEvent_t handles created
  * by the caller with timing enabled). kernel_id: 1 quantizer, 2 forward product,
  * 3 dX product, 4 dW product (with the straight-through epilogue), 5 decode product,
- * 6 backward prologue (r = dY 1 and the transposed codes, lcvq_linear_bwd).
+ * 6 backward prologue (r = dY 1 and the transposed codes, lcvq_linear_bwd), 7 Gram
+ * product (lcvq_hessian), 8 PTQ integer step (lcvq_ptq_init; each call times the first).
  * Passing NULL events disarms. Returns LCVQ_ERR_SHAPE for an unknown kernel_id.
  */
 lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event);

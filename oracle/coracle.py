@@ -24,7 +24,8 @@ _lib = None
 
 __all__ = ["quantize", "pack2b", "unpack2b", "pack_mask", "unpack_mask", "reconstruct",
            "linear_fwd", "linear_bwd", "gemv2b", "dge_slope", "threads", "lib",
-           "hessian", "damp", "udu", "ptq_objective", "ptq_sweep", "ptq_solve_sb", "ptq_init"]
+           "hessian", "damp", "udu", "ptq_objective", "ptq_sweep", "ptq_solve_sb", "ptq_init",
+           "ptq_targets"]
 
 
 def lib():
@@ -55,6 +56,7 @@ def lib():
             "oc_ptq_objective": ([vp, vp, i64, i64, vp, f64, f64], f64),
             "oc_ptq_sweep": ([vp, i64, i64, vp, f64, f64, vp, vp], None),
             "oc_ptq_solve_sb": ([vp, vp, i64, i64, vp, vp, vp], i32),
+            "oc_ptq_targets": ([vp, i64, i64, vp, f64, f64, vp, vp], None),
             "oc_ptq_init": ([vp, i64, i64, vp, f64, i32, vp, vp, vp, vp], i32),
         }
         for name, (args, res) in sigs.items():
@@ -257,6 +259,17 @@ def ptq_sweep(W0, U, s, b, want_t=False):
     t = np.empty((N, K), np.float64) if want_t else None
     lib().oc_ptq_sweep(_p(W), N, K, _p(Uc), float(s), float(b), _p(c), _p(t))
     return (c, t) if want_t else c
+
+
+def ptq_targets(W0, U, s, b, c):
+    """The values t the integer step rounds, driven by the given codes c (teacher forcing)."""
+    W = _c(W0, np.float64)
+    Uc = _c(U, np.float64)
+    cc = _c(c, np.uint8)
+    N, K = W.shape
+    t = np.empty((N, K), np.float64)
+    lib().oc_ptq_targets(_p(W), N, K, _p(Uc), float(s), float(b), _p(cc), _p(t))
+    return t
 
 
 def ptq_solve_sb(W0, c, Hd, s=1.0, b=0.0):

@@ -385,6 +385,27 @@ void oc_ptq_sweep(const double* W0, int64_t N, int64_t K, const double* U, doubl
   }
 }
 
+// The continuous values the integer step rounds, given the codes that were decided:
+// t_k = v_k + sum_{i<k} U_ik (v_i - c_i), v = (w0 - b) / s, for codes c [N][K] from any
+// source (used to check another implementation's decisions one by one).
+void oc_ptq_targets(const double* W0, int64_t N, int64_t K, const double* U, double s,
+                    double b, const uint8_t* c, double* t) {
+#pragma omp parallel
+  {
+    std::vector<double> v((size_t)K), e((size_t)K);
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < N; ++n) {
+      for (int64_t k = 0; k < K; ++k) v[k] = (W0[n * K + k] - b) / s;
+      for (int64_t k = 0; k < K; ++k) {
+        double tk = v[k];
+        for (int64_t i = 0; i < k; ++i) tk += U[i * K + k] * e[i];
+        t[n * K + k] = tk;
+        e[k] = v[k] - (double)c[n * K + k];
+      }
+    }
+  }
+}
+
 // The (s, b) step for fixed codes: the stationary point of g, computed from the sums of
 // its normal equations (each a plain double loop over H). Leaves s, b unchanged and
 // returns 1 when the system is singular or gives s = 0 (the next integer step divides by

@@ -213,10 +213,10 @@ def test_workspace_sizes_grow_with_shape(L):
 
 
 def test_profile_hook_ids(L):
-    """The timing hook knows kernel ids 1..6; arming with NULL events disarms (no GPU call)."""
-    for kid in (0, 7, -1):
+    """The timing hook knows kernel ids 1..8; arming with NULL events disarms (no GPU call)."""
+    for kid in (0, 9, -1):
         assert L.lcvq_profile_next(kid, None, None) == 2          # LCVQ_ERR_SHAPE
-    for kid in range(1, 7):
+    for kid in range(1, 9):
         assert L.lcvq_profile_next(kid, None, None) == 0
 
 
@@ -266,3 +266,34 @@ def test_gemv_noalloc_errors(L):
     assert g(K=65536 + 256) == 9                     # LCVQ_ERR_SCRATCH
     assert g(K=1 << 20, N=16) == 9
     assert L.lcvq_status_string(9) != b"unknown status"
+
+
+def test_ptq_errors(L):
+    """lcvq_hessian and lcvq_ptq_init argument checks, all before any GPU call."""
+    assert L.lcvq_hessian(None, 16, 64, P, None) == 1
+    assert L.lcvq_hessian(P, 0, 64, P, None) == 2
+    assert L.lcvq_hessian(P, 16, 96, P, None) == 2                 # K % 64
+    assert L.lcvq_hessian(P, 16, 16384 + 64, P, None) == 2
+    assert L.lcvq_hessian(P, 16, 64, MIS, None) == 5
+    ws = L.lcvq_ptq_workspace_size(64, 256)
+    assert ws > 0 and L.lcvq_ptq_workspace_size(40, 256) == 0
+    assert L.lcvq_ptq_workspace_size(64, 16384 + 64) == 0
+
+    def g(**kw):
+        a = dict(H=P, W0=P, N=64, K=256, damp=0.01, iters=2, pk=P, sb=P, obj=None, U=None,
+                 D=None, ws=P, wsb=ws)
+        a.update(kw)
+        return L.lcvq_ptq_init(a["H"], a["W0"], a["N"], a["K"], a["damp"], a["iters"], a["pk"],
+                               a["sb"], a["obj"], a["U"], a["D"], a["ws"], a["wsb"], None)
+    assert g(H=None) == 1
+    assert g(sb=None) == 1
+    assert g(N=40) == 2
+    assert g(K=96) == 2
+    assert g(damp=0.0) == 8
+    assert g(damp=float("nan")) == 8
+    assert g(damp=2.0) == 8
+    assert g(iters=0) == 8
+    assert g(iters=65) == 8
+    assert g(U=MIS) == 5
+    assert g(wsb=ws - 1) == 6
+    assert g(ws=None) == 6

@@ -89,6 +89,22 @@ def test_sweep_equals_literal_eq11(K):
     assert done >= 4
 
 
+def test_targets_follow_the_given_codes():
+    """ptq_targets driven by the sweep's own codes returns the sweep's own t; driven by
+    other codes, each t_k depends only on the codes before k."""
+    rng = np.random.default_rng(12)
+    K, N = 40, 6
+    _, H = spd(rng, K)
+    U, _ = C.udu(C.damp(H, 0.01))
+    W0 = rng.normal(size=(N, K)) * 0.3
+    c, t = C.ptq_sweep(W0, U, 0.2, -0.3, want_t=True)
+    assert np.array_equal(C.ptq_targets(W0, U, 0.2, -0.3, c), t)
+    c2 = c.copy()
+    c2[:, 20] = (c2[:, 20] + 1) % 4
+    t2 = C.ptq_targets(W0, U, 0.2, -0.3, c2)
+    assert np.array_equal(t2[:, :21], t[:, :21]) and not np.array_equal(t2[:, 21:], t[:, 21:])
+
+
 @pytest.mark.parametrize("K", [1, 4, 6])
 def test_diagonal_H_sweep_is_brute_force_optimum(K):
     """With a diagonal H the objective separates per element: the sweep (no feedback)
