@@ -13,7 +13,8 @@ HBM. Also measured in the same run:
     last-level cache cannot serve them, against the HBM peak;
   * the plain C++ CPU oracle on the same step (all 4096 tokens; a few seconds on the
     host cores);
-  * the same fwd + bwd on the MLP chain and on one 8B-shaped layer at 8192 tokens.
+  * the same fwd + bwd on the MLP chain and on one 8B-shaped layer at 8192 tokens;
+  * the PTQ initialisation of one 4096 x 4096 weight from 8192 calibration tokens.
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--clock-warmup-s 0.5]
@@ -86,6 +87,7 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--no-copy-probe", action="store_true")
     ap.add_argument("--no-layers", action="store_true")
+    ap.add_argument("--no-ptq", action="store_true")
     ap.add_argument("--layer-reps", type=int, default=10)
     return ap.parse_args()
 
@@ -114,23 +116,23 @@ def clock_warmup(torch, fn, seconds):
     return n
 
 
-def read_probe(torch, pool, calls):
-    """Same-size read ceiling: one torch reduction (a streaming read of every byte) per
-    buffer of the rotating pool, each bracketed by its own events like the decode
-    kernels. Returns its mean time and rate."""
-    views = [p.view(torch.int32) for p in pool]
+def read_probe(torch, P, L, pool, calls):
+    """Same-size read ceiling: the library's read probe (one launch streaming a buffer
+    once, with the decode kernels' loads) over the same rotating pool, each launch timed
+    by the profiling hook like the decode kernels. Returns its mean time and rate."""
+    sink = torch.zeros(1024, dtype=torch.int32, device=pool[0].device)
+    views = [p.view(-1) for p in pool]
     for v in views:
-        v.sum()
+        P.lcvq_read_probe(v, sink)
     evs = timed_events(torch, calls)
     for i, (a, b) in enumerate(evs):
-        a.record()
-        views[i % len(views)].sum()
-        b.record()
+        L.lcvq_profile_next(9, a.cuda_event, b.cuda_event)
+        P.lcvq_read_probe(views[i % len(views)], sink)
     torch.cuda.synchronize()
     t = sum(a.elapsed_time(b) for a, b in evs) / calls * 1e-3
-    nb = pool[0].numel()
+    nb = views[0].numel()
     return {"bytes": nb, "us": round(t * 1e6, 2), "gbs": round(nb / t / 1e9, 1),
-            "kind": "torch int32 sum over the same rotating pool"}
+            "kind": "lcvq_read_probe over the same rotating pool"}
 
 
 def time_layers(torch, P, L, mats, M, d, dev, seed, reps, warm_s):
@@ -271,12 +273,21 @@ def main():
     for a_, b_ in zip(ref, (Y, dX, dWp, dA, dB)):
         if not torch.equal(a_, b_):
             raise RuntimeError("graph replay differs from the eager step")
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    host = 0.0
+    g0.record()
     for _ in range(args.steps):
+        h0 = time.perf_counter()
         graph.replay()
+        host += time.perf_counter() - h0
+    g1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ms_graph_device = g0.elapsed_time(g1) / args.steps   # the same loop on the device clock
     ms_graph = (t1 - t0) * 1e3 / args.steps
+    graph_host_ms = host * 1e3 / args.steps           # host time inside each replay() call
     ms = min(ms_eager, ms_graph)
     tflops = flops / (ms * 1e-3) / 1e12
 
@@ -362,6 +373,58 @@ def main():
                 "frac": round(fl4 / (ms4 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "shapes": r4}
 
+    # ------------------------------------------------------------ PTQ initialisation
+    # One 4096 x 4096 weight (W0 ~ 0.02 N(0, 1)) from 8192 calibration tokens (X ~ N(0, 1)
+    # in bf16): the Gram product H = X^T X, then the damped factorisation and 4 alternations.
+    ptq = None
+    if not args.no_ptq:
+        Mc, Kp, Np, iters = 8192, 4096, 4096, 4
+        Xc = SI.make_act(Mc, Kp, seed=6000, device=dev)
+        W0 = SI.make_act(Np, Kp, seed=6001, dtype="f32", device=dev) * 0.02
+        Hm = torch.empty((Kp, Kp), dtype=torch.float32, device=dev)
+        pk = torch.empty((Np, Kp // 4), dtype=torch.uint8, device=dev)
+        sb = torch.empty(2, dtype=torch.float32, device=dev)
+        obj = torch.empty(2 * iters, dtype=torch.float32, device=dev)
+        wsp = torch.empty(P.lcvq_ptq_workspace_size(Np, Kp), dtype=torch.uint8, device=dev)
+
+        def ptq_run():
+            P.lcvq_hessian(Xc, Hm)
+            P.lcvq_ptq_init(Hm, W0, 0.01, iters, pk, sb, obj, workspace=wsp)
+
+        clock_warmup(torch, ptq_run, 0.3)
+        reps = 5
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            ptq_run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_all = e0.elapsed_time(e1) / reps
+        kt = {}
+        for kid, name in ((7, "gram"), (8, "sweep")):
+            evs = timed_events(torch, 3)
+            for a, b in evs:
+                L.lcvq_profile_next(kid, a.cuda_event, b.cuda_event)
+                ptq_run()
+            torch.cuda.synchronize()
+            kt[name] = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+        gram_flops = float(Mc) * Kp * (Kp + 1)          # the distinct entries, 2 M flops each
+        sweep_flops = float(Np) * Kp * (Kp - 1)         # sum_{i<k} U_ik c_i for every row
+        ptq = {"workload": f"W0 {Np}x{Kp}, {Mc} calibration tokens, {iters} alternations, "
+                           "damp 0.01",
+               "ms_total": round(ms_all, 3),
+               "gram_ms": round(kt["gram"], 4),
+               "gram_tflops": round(gram_flops / (kt["gram"] * 1e-3) / 1e12, 1),
+               "gram_frac": round(gram_flops / (kt["gram"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "sweep_ms": round(kt["sweep"], 4),
+               "sweep_tflops": round(sweep_flops / (kt["sweep"] * 1e-3) / 1e12, 1),
+               "sweep_frac": round(sweep_flops / (kt["sweep"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "objective": [round(float(v), 4) for v in obj.cpu()],
+               "s_b": [float(v) for v in sb.cpu()]}
+        del Xc, W0, Hm, pk, wsp
+        torch.cuda.empty_cache()
+
     # ---------------------------------------------------------------- decode product
     decode = None
     read_ceiling = {}
@@ -404,7 +467,7 @@ def main():
                     t_w = w0.elapsed_time(w1) / calls * 1e-3
                     nbytes = n * k // 4 + 2 * m * k + 2 * m * n + 2 * (64 + 8)
                     if layout == 0 and f"{n}x{k}" not in read_ceiling:
-                        read_ceiling[f"{n}x{k}"] = read_probe(torch, pool, calls)
+                        read_ceiling[f"{n}x{k}"] = read_probe(torch, P, L, pool, calls)
                     rc = read_ceiling[f"{n}x{k}"]
                     rec = {"bytes": nbytes, "kernel_us": round(t_k * 1e6, 2),
                            "kernel_gbs": round(nbytes / t_k / 1e9, 1),
@@ -450,7 +513,7 @@ def main():
         nbytes = pair_bytes + 2 * m * k + 2 * 2 * m * n + 2 * 2 * (64 + 8)
         flat = [torch.cat([pl[0].view(-1), pl[1].view(-1)]) for pl in pool]
         del pool
-        rc = read_probe(torch, flat, calls)
+        rc = read_probe(torch, P, L, flat, calls)
         decode["gate_up_batched_M1"] = {
             "bytes": nbytes, "kernel_us": round(t_k * 1e6, 2),
             "kernel_gbs": round(nbytes / t_k / 1e9, 1),
@@ -617,6 +680,8 @@ def main():
         "ms_per_step": round(ms, 4),
         "ms_per_step_eager": round(ms_eager, 4),
         "ms_per_step_graph": round(ms_graph, 4),
+        "ms_per_step_graph_device": round(ms_graph_device, 4),
+        "graph_replay_host_ms": round(graph_host_ms, 4),
         "ms_per_step_dge": round(ms_dge, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -629,6 +694,7 @@ def main():
                    "M": M, "N": N, "K": K, "d": d},
         "roofline": roofline,
         "layer_steps": layer_steps,
+        "ptq_init": ptq,
         "decode": decode,
         "decode_stack_8b": decode_stack,
         "hbm_copy_probe": copy_probe,

@@ -66,6 +66,7 @@ def lib():
             "lcvq_gemv2b_shuffle": [vp, i64, i64, vp, vp],
             "lcvq_gemv2b_noalloc": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp],
             "lcvq_hessian": [vp, i64, i64, vp, vp],
+            "lcvq_read_probe": [vp, i64, vp, vp],
             "lcvq_ptq_init": [vp, vp, i64, i64, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         }
         for name, args in sigs.items():
@@ -309,6 +310,14 @@ def lcvq_gemv2b_batched(X, mats, d, workspace=None):
     _check(workspace, "workspace", torch.uint8, dev)
     _ok(lib().lcvq_gemv2b_batched(_p(X), M, K, d, arr, len(mats), _p(workspace),
                                   workspace.numel(), _stream(dev)), "lcvq_gemv2b_batched")
+
+
+def lcvq_read_probe(buf, sink):
+    """Measurement helper: stream buf once (uint8 device tensor) into sink (int32 [1024])."""
+    _check(buf, "buf", torch.uint8)
+    _check(sink, "sink", torch.int32, buf.device)
+    _ok(lib().lcvq_read_probe(_p(buf), buf.numel(), _p(sink), _stream(buf.device)),
+        "lcvq_read_probe")
 
 
 def lcvq_hessian(X, H):

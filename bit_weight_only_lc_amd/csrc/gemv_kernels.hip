@@ -179,6 +179,36 @@ __global__ __launch_bounds__(256) void k_gemv_shuffle(const uint8_t* __restrict_
   *reinterpret_cast<uint4*>(out + t * 1024 + lane * 16) = v;
 }
 
+// Measurement helper: one launch that streams `bytes` (a multiple of 16) once, with the
+// decode kernels' non-temporal 16-byte loads, and writes one word per workgroup to `sink`
+// (so that the loads are kept). It gives the same-size read ceiling beside the decode
+// product; it is no step of the method.
+__global__ __launch_bounds__(256) void k_read_probe(const u32x4* __restrict__ p, int64_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * 256) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  acc = __reduce_xor_sync(~0ull, acc);   // wave-wide, then one store per wave-0 lane 0
+  __shared__ uint32_t w[4];
+  if ((threadIdx.x & 63) == 0) w[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x & 1023] = w[0] ^ w[1] ^ w[2] ^ w[3];
+}
+
+hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* sink, hipStream_t s) {
+  const int64_t n16 = bytes / 16;
+  // four 16-byte loads per thread, and no more workgroups than four per CU's worth of
+  // rounds would need
+  int64_t blocks = (n16 + 1023) / 1024;
+  if (blocks > 65536) blocks = 65536;
+  LCVQ_LAUNCH(PROF_READ_PROBE, k_read_probe, dim3((unsigned)blocks), dim3(256), 0, s,
+              static_cast<const u32x4*>(p), n16, sink);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* out,
                                hipStream_t s) {
   const int64_t tiles = (N / 16) * (K / GK);

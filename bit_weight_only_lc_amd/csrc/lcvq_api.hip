@@ -423,6 +423,13 @@ lcvq_status_t lcvq_ptq_init(const float* H, const float* W0, int64_t N, int64_t 
                                   obj_out, U_out, D_out, workspace, as_stream(stream)));
 }
 
+lcvq_status_t lcvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return LCVQ_ERR_NULL;
+  if (bytes < 16 || (bytes % 16) || bytes > (int64_t(1) << 40)) return LCVQ_ERR_SHAPE;
+  if (!aligned16(buf) || !aligned16(sink)) return LCVQ_ERR_ALIGN;
+  return from_hip(launch_read_probe(buf, bytes, sink, as_stream(stream)));
+}
+
 lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
                                   void* stream) {
   if (!packed || !codes) return LCVQ_ERR_NULL;

@@ -296,13 +296,24 @@ lcvq_status_t lcvq_ptq_init(const float* H, const float* W0, int64_t N, int64_t 
                             size_t workspace_bytes, void* stream);
 
 /*
+ * Measurement helper, no step of the method: one launch that reads `bytes` of device
+ * memory once (16-byte non-temporal loads, as the decode kernels read codes) and writes
+ * one word per workgroup into `sink` (uint32 [1024], device). Timed with the profiling
+ * hook (kernel id 9), it is the same-size read ceiling the decode product is compared to.
+ *   bytes a multiple of 16, 16 <= bytes <= 2^40; buf and sink 16-byte aligned.
+ * Errors: LCVQ_ERR_NULL, LCVQ_ERR_SHAPE, LCVQ_ERR_ALIGN, LCVQ_ERR_HIP.
+ */
+lcvq_status_t lcvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * Profiling hook (changes no result). Arms a one-shot timing of the next launch of one
  * kernel by calls made from this host thread: the kernel is launched with
  * hipExtLaunchKernel between `start_event` and `stop_event` (hipEvent_t handles created
  * by the caller with timing enabled). kernel_id: 1 quantizer, 2 forward product,
  * 3 dX product, 4 dW product (with the straight-through epilogue), 5 decode product,
  * 6 backward prologue (r = dY 1 and the transposed codes, lcvq_linear_bwd), 7 Gram
- * product (lcvq_hessian), 8 PTQ integer step (lcvq_ptq_init; each call times the first).
+ * product (lcvq_hessian), 8 PTQ integer step (lcvq_ptq_init; each call times the first),
+ * 9 read probe (lcvq_read_probe).
  * Passing NULL events disarms. Returns LCVQ_ERR_SHAPE for an unknown kernel_id.
  */
 lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event);

@@ -213,10 +213,10 @@ def test_workspace_sizes_grow_with_shape(L):
 
 
 def test_profile_hook_ids(L):
-    """The timing hook knows kernel ids 1..8; arming with NULL events disarms (no GPU call)."""
-    for kid in (0, 9, -1):
+    """The timing hook knows kernel ids 1..9; arming with NULL events disarms (no GPU call)."""
+    for kid in (0, 10, -1):
         assert L.lcvq_profile_next(kid, None, None) == 2          # LCVQ_ERR_SHAPE
-    for kid in range(1, 9):
+    for kid in range(1, 10):
         assert L.lcvq_profile_next(kid, None, None) == 0
 
 
@@ -297,3 +297,10 @@ def test_ptq_errors(L):
     assert g(U=MIS) == 5
     assert g(wsb=ws - 1) == 6
     assert g(ws=None) == 6
+
+
+def test_read_probe_errors(L):
+    assert L.lcvq_read_probe(None, 64, P, None) == 1
+    assert L.lcvq_read_probe(P, 60, P, None) == 2
+    assert L.lcvq_read_probe(P, 0, P, None) == 2
+    assert L.lcvq_read_probe(MIS, 64, P, None) == 5

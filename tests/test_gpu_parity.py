@@ -447,3 +447,17 @@ def test_gemv_batched(P, shapes, K, M):
         assert torch.equal(Y, ys)
         assert torch.equal(mx[3], ys)
         check(host(Y), O.gemv2b(host(X), host(pkr), Ah, Bh, d), TOL, "gemv batched")
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 1 << 20, 14 << 20])
+def test_read_probe_reads_every_word(P, nbytes):
+    """The measurement helper streams every 16-byte word once: the XOR of its per-block
+    words equals the XOR of the buffer's 32-bit words (at most 1024 blocks here)."""
+    g = torch.Generator(device="cuda").manual_seed(nbytes)
+    buf = torch.randint(0, 256, (nbytes,), generator=g, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    P.lcvq_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
