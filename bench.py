@@ -621,6 +621,52 @@ def main():
         del mats, mats_dl
         torch.cuda.empty_cache()
 
+    # ------------------------------------------------ standalone quantizer and packer
+    # lcvq_quantize (Wp -> packed codes and mask bits: 4 + 0.25 + 0.125 B per weight) and
+    # lcvq_pack2b (one code per byte -> packed: 1 + 0.25 B per weight) on the 4096 x 4096 and
+    # 14336 x 4096 weights, each call on another buffer of a pool of >= 512 MiB, timed with
+    # the profiling hook (kernel id 1 covers lcvq_quantize's launch; the packer is timed by
+    # events around its own launch).
+    hbm_kernels = None
+    if not args.no_decode:
+        hbm_kernels = {}
+        for (n, k) in ((4096, 4096), (14336, 4096)):
+            per = n * k * 4
+            copies = max(2, -(-(512 << 20) // per))
+            wps = [SI.make_wp(n, k, seed=8000 + i, device=dev) for i in range(copies)]
+            pk_ = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
+            mk_ = torch.empty((n, k // 8), dtype=torch.uint8, device=dev)
+            for w_ in wps:
+                P.lcvq_quantize(w_, None, pk_, mk_)
+            evs = timed_events(torch, 2 * copies)
+            for i, (a, b) in enumerate(evs):
+                L.lcvq_profile_next(1, a.cuda_event, b.cuda_event)
+                P.lcvq_quantize(wps[i % copies], None, pk_, mk_)
+            torch.cuda.synchronize()
+            tq = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e-3
+            qb = n * k * (4 + 0.25 + 0.125)
+            del wps
+            zs = [torch.randint(0, 4, (n, k), dtype=torch.uint8, device=dev)
+                  for _ in range(max(2, -(-(512 << 20) // (n * k))))]
+            for z_ in zs:
+                P.lcvq_pack2b(z_, pk_)
+            evs = timed_events(torch, 2 * len(zs))
+            for i, (a, b) in enumerate(evs):
+                a.record()
+                P.lcvq_pack2b(zs[i % len(zs)], pk_)
+                b.record()
+            torch.cuda.synchronize()
+            tp = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e-3
+            pb = n * k * 1.25
+            del zs
+            torch.cuda.empty_cache()
+            hbm_kernels[f"quantize_{n}x{k}"] = {
+                "bytes": int(qb), "us": round(tq * 1e6, 2), "gbs": round(qb / tq / 1e9, 1),
+                "frac": round(qb / tq / 1e9 / PEAK_HBM_GBS, 4)}
+            hbm_kernels[f"pack2b_{n}x{k}"] = {
+                "bytes": int(pb), "us": round(tp * 1e6, 2), "gbs": round(pb / tp / 1e9, 1),
+                "frac": round(pb / tp / 1e9 / PEAK_HBM_GBS, 4)}
+
     # ---------------------------------------------------------------- HBM copy ceiling
     # A plain device-to-device copy of 1 GiB: the streaming ceiling measured beside the
     # decode product, and the kernel of known size that scales the HBM byte counters.
@@ -695,6 +741,7 @@ def main():
         "roofline": roofline,
         "layer_steps": layer_steps,
         "ptq_init": ptq,
+        "quantize_pack": hbm_kernels,
         "decode": decode,
         "decode_stack_8b": decode_stack,
         "hbm_copy_probe": copy_probe,

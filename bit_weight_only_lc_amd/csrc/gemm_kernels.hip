@@ -85,6 +85,13 @@ struct GemmArgs {
   float* red_dA;
   float* red_dB;
   float dge_alpha, dge_c;      // sharpness and alpha / (2 tanh(alpha / 2))
+  // Split contraction (launches with few tiles): `splits` workgroups share each tile;
+  // their float32 partial tiles go to split_ws [ntiles][splits][256 * 256], and split_cnt
+  // [ntiles] (zero at launch) counts arrivals, so the last one adds them and runs the
+  // epilogue. splits = 1: one workgroup per tile, nothing else used.
+  int splits;
+  float* split_ws;
+  int* split_cnt;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -105,6 +112,84 @@ __device__ __forceinline__ bool map_tile(int b, int tilesP, int tilesQ, int ntil
   tp = group * GR + within % rows;
   tq = within / rows;
   return true;
+}
+
+// Split launches: job b -> (tile b mod ntiles, split b / ntiles). The dispatcher deals
+// workgroups round-robin over the 8 XCDs, so the jobs of one tile share an XCD whenever
+// ntiles is a multiple of 8 and exchange their partials through its L2.
+__device__ __forceinline__ bool map_split(int b, int tilesQ, int ntiles, int splits, int& tp,
+                                          int& tq, int& tile, int& split) {
+  if (b >= ntiles * splits) return false;
+  tile = b % ntiles;
+  split = b / ntiles;
+  tp = tile / tilesQ;
+  tq = tile % tilesQ;
+  return true;
+}
+
+// Stages [kt0, kt1) of nk that job `split` of `splits` contracts over.
+__device__ __forceinline__ void split_range(int nk, int split, int splits, int& kt0, int& kt1) {
+  kt0 = (int)((int64_t)nk * split / splits);
+  kt1 = (int)((int64_t)nk * (split + 1) / splits);
+}
+
+// After a split job's main loop: writes its accumulators as this job's partial tile
+// (float4 [block][register quad][thread], so each store instruction covers 1 KiB), then
+// counts its arrival. Every job but the last returns false. The last one (release and
+// acquire fences at device scope order the partials before the count) replaces its
+// accumulators with the sum of all partials, taken in split order so that the result
+// does not depend on which job arrived last, resets the count for the next launch and
+// returns true. `flag` is one int of LDS, free at this point.
+template <int WI, int WJ>
+__device__ __forceinline__ bool split_join(const GemmArgs& a, f32x16 (&acc)[WI][WJ], int tile,
+                                           int split, int tid, int* flag) {
+  const int nt = blockDim.x;
+  constexpr int NQ = WI * WJ * 4;                    // float4 per thread
+  f32x4* tile_ws = reinterpret_cast<f32x4*>(a.split_ws) + (int64_t)tile * a.splits * NQ * nt;
+  f32x4* mine = tile_ws + (int64_t)split * NQ * nt;
+#pragma unroll
+  for (int i = 0; i < WI; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mine[((i * WJ + j) * 4 + q) * nt + tid] =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) *flag = atomicAdd(a.split_cnt + tile, 1);
+  __syncthreads();
+  if (*flag != a.splits - 1) return false;
+  __threadfence();
+#pragma unroll
+  for (int i = 0; i < WI; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int sp = 0; sp < a.splits; ++sp) {
+    const f32x4* src = tile_ws + (int64_t)sp * NQ * nt;
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+#pragma unroll
+      for (int j = 0; j < WJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = src[((i * WJ + j) * 4 + q) * nt + tid];
+          acc[i][j][4 * q] += v[0];
+          acc[i][j][4 * q + 1] += v[1];
+          acc[i][j][4 * q + 2] += v[2];
+          acc[i][j][4 * q + 3] += v[3];
+        }
+  }
+  if (tid == 0) a.split_cnt[tile] = 0;
+  __syncthreads();                                   // every thread has read `flag`
+  return true;
+}
+
+__global__ __launch_bounds__(256) void k_zero_ints(int* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 __device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, float a, float b, float c, float d) {
@@ -729,11 +814,19 @@ void k_gemm_ring(GemmArgs a) {
   // (256 KiB), so each XCD takes few tiles along the bf16 operand: forward tile-rows
   // are rows of X', dX tile-columns are rows of dY.
   constexpr int GR = OP == OP_FWD ? 2 : 16;
-  if (!map_tile<GR>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
+  int split = 0;
+  if (a.splits > 1) {
+    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+  } else if (!map_tile<GR>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
+    return;
+  }
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wp = wave / T::WGQ, wq = wave % T::WGQ;
-  const int nk = (a.R + BK - 1) / BK;
+  const int nkt = (a.R + BK - 1) / BK;               // stages of the whole contraction
+  int kt0, kt1;
+  split_range(nkt, split, a.splits, kt0, kt1);
+  const int nk = kt1 - kt0;                          // stages of this job
 
   f32x16 acc[WI][WJ];
 #pragma unroll
@@ -754,8 +847,8 @@ void k_gemm_ring(GemmArgs a) {
 #pragma unroll
     for (int st = 0; st < RING - 1; ++st)
       if (st < nk)
-        issue_ring_stage<NW>(smem + st * SLOTB, mat, ld, row0, a.M, st * BK, a.codes, rowblock,
-                             nk, st, wave, lane);
+        issue_ring_stage<NW>(smem + st * SLOTB, mat, ld, row0, a.M, (kt0 + st) * BK, a.codes,
+                             rowblock, nkt, kt0 + st, wave, lane);
     // The barrier of each stage sits before its last sub-step, so that the first
     // fragments of the next stage are read and expanded under that sub-step's MFMAs
     // instead of after a barrier at the stage boundary. Plain s_barrier: __syncthreads()
@@ -782,8 +875,8 @@ void k_gemm_ring(GemmArgs a) {
       asm volatile("s_barrier" ::: "memory");
       if (kt + RING - 1 < nk)
         issue_ring_stage<NW>(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
-                             (kt + RING - 1) * BK, a.codes, rowblock, nk, kt + RING - 1, wave,
-                             lane);
+                             (kt0 + kt + RING - 1) * BK, a.codes, rowblock, nkt,
+                             kt0 + kt + RING - 1, wave, lane);
       // Sub-step 3, with stage kt + 1's first fragments read and expanded under it (on
       // the last stage this reads a free slot; the values are not used).
       ring_read<CL, WI, WJ>(smem + ((kt + 1) % RING) * SLOTB, 0, wp, wq, lane, f[0]);
@@ -791,6 +884,9 @@ void k_gemm_ring(GemmArgs a) {
     }
     __syncthreads();
   }
+  if (OP == OP_FWD && a.splits > 1 &&
+      !split_join<WI, WJ>(a, acc, tile, split, tid, reinterpret_cast<int*>(smem)))
+    return;
 
   if (OP == OP_FWD) {
     epilogue_fwd<NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, wave, smem);
@@ -1015,12 +1111,18 @@ void k_gemm_dw(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[DW_SMEM];   // 152 KiB
   int tp, tq, tile;
   // X and dY panels weigh the same: 4 x 8 tiles per XCD reads the fewest panels.
-  if (!map_tile<4>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) return;
+  int split = 0;
+  if (a.splits > 1) {
+    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+  } else if (!map_tile<4>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
+    return;
+  }
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WGQ, wq = wave % WGQ;
-  const int nk = (a.R + BK - 1) / BK;
+  int kt0, kt1;
+  split_range((a.R + BK - 1) / BK, split, a.splits, kt0, kt1);
   const DwLaneOffsets lo = dw_lane_offsets(a.N, a.K, p0, q0, lane);
   issue_dw_codes(smem, a.packed, a.mask, a.N, a.K, p0, q0, wave, lane);
 
@@ -1035,7 +1137,7 @@ void k_gemm_dw(GemmArgs a) {
   for (int pass = 0; pass < a.npass; ++pass) {
     const uint16_t* Lp = pass == 0 ? a.Lmat[0] : (pass == 1 ? a.Lmat[1] : a.Lmat[2]);
     const uint16_t* Rp = pass == 0 ? a.Rmat[0] : (pass == 1 ? a.Rmat[1] : a.Rmat[2]);
-    issue_dw_stage(smem, Lp, Rp, a.M, a.N, a.K, 0, p0, q0, wave, lane);
+    issue_dw_stage(smem, Lp, Rp, a.M, a.N, a.K, kt0 * BK, p0, q0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Every transposing LDS read of a stage is issued before the next stage's direct
@@ -1043,8 +1145,8 @@ void k_gemm_dw(GemmArgs a) {
     // program order wait for that load, which would serialize the two. Sub-steps 0-2 are
     // read first, sub-step 3 into sub-step 0's registers once its MFMAs have issued, and
     // the next stage's loads then run under the MFMAs of sub-steps 1-3.
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint8_t* slot = smem + (kt & 1) * 2 * TTILEB;
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const uint8_t* slot = smem + ((kt - kt0) & 1) * 2 * TTILEB;
       DwFrags<WJ> f0, f1, f2;
       dw_read<WJ>(slot, 0, wp, wq, lane, f0);
       dw_read<WJ>(slot, 1, wp, wq, lane, f1);
@@ -1054,8 +1156,8 @@ void k_gemm_dw(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       dw_read<WJ>(slot, 3, wp, wq, lane, f0);
       __builtin_amdgcn_sched_barrier(0);
-      uint8_t* next = smem + ((kt & 1) ^ 1) * 2 * TTILEB;
-      if (kt + 1 < nk)
+      uint8_t* next = smem + (((kt - kt0) & 1) ^ 1) * 2 * TTILEB;
+      if (kt + 1 < kt1)
         issue_dw_stage_rows(next, Lp, Rp, a.M, a.N, a.K, (kt + 1) * BK, lo, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
       dw_mfma<WJ>(f1, acc);
@@ -1063,11 +1165,14 @@ void k_gemm_dw(GemmArgs a) {
       dw_mfma<WJ>(f0, acc);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
-      if (kt + 1 < nk && (kt + 1) * BK + wave * 8 + 8 > a.M)
+      if (kt + 1 < kt1 && (kt + 1) * BK + wave * 8 + 8 > a.M)
         zero_dw_rows(next, (kt + 1) * BK, a.M, wave, lane);
       __syncthreads();
     }
   }
+  if (a.splits > 1 &&
+      !split_join<4, WJ>(a, acc, tile, split, tid, reinterpret_cast<int*>(smem)))
+    return;
   // The buffers are free after the last barrier: per-wave areas of 12 KiB from 0, the
   // per-wave sums after them, and for d = 16 a copy of A at 120 KiB.
   float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
@@ -1192,12 +1297,33 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict
 }
 
 // ---- launchers -----------------------------------------------------------------------
+int gemm_splits(int64_t P, int64_t Q, int64_t R) {
+  const int64_t nt = ((P + BT - 1) / BT) * ((Q + BT - 1) / BT);
+  const int64_t nk = (R + BK - 1) / BK;
+  if (nt > 128) return 1;
+  int64_t sp = 256 / nt;
+  if (sp > 4) sp = 4;
+  if (sp > nk / 8) sp = nk / 8;                      // at least 8 stages per job
+  return sp < 1 ? 1 : (int)sp;
+}
+
+size_t gemm_split_bytes(int64_t P, int64_t Q, int64_t R) {
+  const int sp = gemm_splits(P, Q, R);
+  if (sp == 1) return 0;
+  const size_t nt = (size_t)(((P + BT - 1) / BT) * ((Q + BT - 1) / BT));
+  return nt * sp * BT * BT * 4 + ((nt * 4 + 255) / 256) * 256;
+}
+
 template <int OP>
 static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   a.tilesP = (a.P + BT - 1) / BT;
   a.tilesQ = (a.Q + BT - 1) / BT;
   a.ntiles = a.tilesP * a.tilesQ;
-  const int grid = ((a.ntiles + 7) / 8) * 8;
+  if (a.splits > 1) {
+    hipLaunchKernelGGL(k_zero_ints, dim3((a.ntiles + 255) / 256), dim3(256), 0, s, a.split_cnt,
+                       a.ntiles);
+  }
+  const int grid = ((a.ntiles * (a.splits > 1 ? a.splits : 1) + 7) / 8) * 8;
   if constexpr (OP == OP_DW) {
     switch (d) {
       case 4: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<4>, dim3(grid), dim3(512), 0, s, a); break;
@@ -1218,10 +1344,22 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
 
 int gemm_tiles(int64_t P, int64_t Q) { return (int)(((P + BT - 1) / BT) * ((Q + BT - 1) / BT)); }
 
+// Split contraction for launches of few tiles; split_ws holds gemm_split_bytes(P, Q, R):
+// the partial tiles, then the arrival counts.
+static void set_splits(GemmArgs& a, int64_t P, int64_t Q, int64_t R, void* split_ws) {
+  a.splits = split_ws ? gemm_splits(P, Q, R) : 1;
+  if (a.splits > 1) {
+    const size_t nt = (size_t)gemm_tiles(P, Q);
+    a.split_ws = static_cast<float*>(split_ws);
+    a.split_cnt = reinterpret_cast<int*>(static_cast<uint8_t*>(split_ws) + nt * a.splits * BT * BT * 4);
+  }
+}
+
 hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint32_t* r16,
                            const float* beta, int M, int N, int K, int d, void* Y, bool y_f32,
-                           hipStream_t s) {
+                           void* split_ws, hipStream_t s) {
   GemmArgs a = {};
+  set_splits(a, M, N, K, split_ws);
   a.P = M; a.Q = N; a.R = K;
   a.Lmat[0] = xs; a.Lmat[1] = xs_lo;
   a.npass = xs_lo ? 2 : 1;
@@ -1242,6 +1380,7 @@ hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16
     a.red_dA = dA;
     a.red_dB = dB;
   }
+  a.splits = 1;
   a.P = K; a.Q = M; a.R = N;
   a.codes = r16t;
   a.Rmat[0] = dy; a.Rmat[1] = dy_lo;
@@ -1256,8 +1395,9 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
                           const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, const float* dge_wp,
-                          float dge_alpha, bool reduce, hipStream_t s) {
+                          float dge_alpha, bool reduce, void* split_ws, hipStream_t s) {
   GemmArgs a = {};
+  set_splits(a, K, N, M, split_ws);
   a.P = K; a.Q = N; a.R = M;
   a.Lmat[0] = x; a.Rmat[0] = dy;
   a.npass = 1;

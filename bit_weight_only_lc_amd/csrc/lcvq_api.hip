@@ -66,7 +66,7 @@ inline size_t r16_bytes(int64_t rows, int64_t kc) {
 }
 
 struct FwdWs {
-  size_t xs, beta, r16, xs_lo, total;
+  size_t xs, beta, r16, xs_lo, split, total;
 };
 inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, bool f32) {
   FwdWs w;
@@ -74,12 +74,13 @@ inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, bool f32) {
   w.beta = w.xs + up((size_t)M * K * 2);
   w.r16 = w.beta + up((size_t)M * 4);
   w.xs_lo = w.r16 + up(r16_bytes(N, K));
-  w.total = w.xs_lo + (f32 ? up((size_t)M * K * 2) : 0);
+  w.split = w.xs_lo + (f32 ? up((size_t)M * K * 2) : 0);
+  w.total = w.split + up(gemm_split_bytes(M, N, K));   // split partials of few-tile shapes
   return w;
 }
 
 struct BwdWs {
-  size_t r, r16t, partials, dy_hi, dy_lo, x_hi, x_lo, total;
+  size_t r, r16t, partials, dy_hi, dy_lo, x_hi, x_lo, split, total;
 };
 inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int d, bool f32) {
   BwdWs w;
@@ -92,7 +93,8 @@ inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int d, bool f32) {
   w.dy_lo = w.dy_hi + dyb;
   w.x_hi = w.dy_lo + dyb;
   w.x_lo = w.x_hi + xb;
-  w.total = w.x_lo + xb;
+  w.split = w.x_lo + xb;
+  w.total = w.split + up(gemm_split_bytes(K, N, M));   // dW's split partials, few-tile shapes
   return w;
 }
 
@@ -244,7 +246,9 @@ lcvq_status_t lcvq_linear_fwd(const void* X, lcvq_dtype_t xdt, int64_t M, int64_
     if (e == hipSuccess) e = launch_fwd_prologue(X, f32, M, K, A, B, d, xs, xs_lo, beta, s);
   }
   if (e != hipSuccess) return LCVQ_ERR_HIP;
-  return from_hip(launch_gemm_fwd(xs, xs_lo, r16, beta, (int)M, (int)N, (int)K, d, Y, f32, s));
+  void* split = gemm_split_bytes(M, N, K) ? static_cast<void*>(ws + w.split) : nullptr;
+  return from_hip(launch_gemm_fwd(xs, xs_lo, r16, beta, (int)M, (int)N, (int)K, d, Y, f32, split,
+                                  s));
 }
 
 size_t lcvq_linear_bwd_workspace_size(int64_t M, int64_t N, int64_t K, int d) {
@@ -294,8 +298,9 @@ lcvq_status_t linear_bwd_impl(const void* dY, const void* X, lcvq_dtype_t dt, in
   const uint16_t* xb = f32 ? x_hi : static_cast<const uint16_t*>(X);
   // dW first; with dX wanted, the dX product then also reduces dW's dA/dB partials
   // (saving the reduction's own launch), otherwise a small kernel does.
+  void* split = gemm_split_bytes(K, N, M) ? static_cast<void*>(ws + w.split) : nullptr;
   e = launch_gemm_dw(xb, x_lo, dyb, dy_lo, packed, mask, A, (int)M, (int)N, (int)K, d, dWp,
-                     partials, dA, dB, Wp, alpha, !dX, s);
+                     partials, dA, dB, Wp, alpha, !dX, split, s);
   if (e != hipSuccess) return LCVQ_ERR_HIP;
   if (dX) {
     if (!merged) {

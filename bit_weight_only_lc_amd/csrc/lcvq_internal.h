@@ -55,11 +55,17 @@ hipError_t launch_bwd_prep(const void* dY, const void* X, bool f32, int64_t M, i
                            uint32_t* r16t, hipStream_t s);
 
 int gemm_tiles(int64_t P, int64_t Q);
+// Launches with at most 128 tiles (of 256 x 256) split their contraction over up to four
+// workgroups per tile: gemm_splits() of them (1: no split), and gemm_split_bytes() of
+// workspace (0 without a split) for the forward (P = M, Q = N, R = K) and dW (P = K,
+// Q = N, R = M) products.
+int gemm_splits(int64_t P, int64_t Q, int64_t R);
+size_t gemm_split_bytes(int64_t P, int64_t Q, int64_t R);
 // Products. `*_lo` operands are NULL for bf16 activations; for float32 activations
 // they hold the low bf16 half of each value and add the cross terms in extra passes.
 hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint32_t* r16,
                            const float* beta, int M, int N, int K, int d, void* Y, bool y_f32,
-                           hipStream_t s);
+                           void* split_ws, hipStream_t s);
 // dX; with dw_partials (the dW product already enqueued) it also reduces them into dA, dB.
 hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16_t* dy_lo,
                           const float* r, const float* A, const float* B, int M, int N, int K,
@@ -69,7 +75,7 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
                           const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, const float* dge_wp,
-                          float dge_alpha, bool reduce, hipStream_t s);
+                          float dge_alpha, bool reduce, void* split_ws, hipStream_t s);
 
 // PTQ initialisation: H = X^T X (bf16 X [M][K], K a multiple of 64, float H [K][K]).
 hipError_t launch_gram(const uint16_t* X, int M, int K, float* H, hipStream_t s);

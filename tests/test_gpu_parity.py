@@ -461,3 +461,35 @@ def test_read_probe_reads_every_word(P, nbytes):
     want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == want
+
+
+# Shapes whose forward and dW products have few tiles: their contraction is split over up
+# to four workgroups per tile (partials added in a fixed order by the last to arrive).
+SPLIT_SHAPES = [(1100, 320, 2112, 8, "bf16"),     # forward 4 ways, dW 2 ways, ragged M, K
+                (2500, 192, 1216, 16, "f32"),     # forward 2 ways, dW 4 ways, float32
+                (1031, 64, 4096, 4, "bf16")]      # one tile column, forward 4 ways
+
+
+@pytest.mark.parametrize("M,N,K,d,xdt", SPLIT_SHAPES)
+def test_split_contraction_shapes(P, M, N, K, d, xdt):
+    inp = SI.make_layer(N, K, M, d, seed=M + 3 * N + K, x_dtype=xdt, lo=-2.0, hi=5.0)
+    check_layer(P, inp, d, f"split M={M} N={N} K={K} d={d} {xdt}")
+
+
+def test_split_contraction_dge_and_determinism(P):
+    M, N, K, d = 1100, 320, 2112, 8
+    inp = SI.make_layer(N, K, M, d, seed=4242, lo=-2.0, hi=5.0)
+    X, Wp, A, B, dY = (inp[k].cuda() for k in ("X", "Wp", "A", "B", "dY"))
+    f1 = P.linear_fwd(X, Wp, A, B, d)
+    f2 = P.linear_fwd(X, Wp, A, B, d)
+    g1 = P.linear_bwd(dY, X, f1["packed"], f1["mask"], A, B, d, dge_wp=Wp, dge_alpha=5.0)
+    g2 = P.linear_bwd(dY, X, f1["packed"], f1["mask"], A, B, d, dge_wp=Wp, dge_alpha=5.0)
+    torch.cuda.synchronize()
+    assert torch.equal(f1["Y"], f2["Y"])
+    for k in ("dX", "dWp", "dA", "dB"):
+        assert torch.equal(g1[k], g2[k]), k
+    wp = inp["Wp"].numpy()
+    z, m = O.quantize(wp)
+    ob = O.linear_bwd(host(inp["dY"]), host(inp["X"]), z, m, inp["A"].double().numpy(),
+                      inp["B"].double().numpy(), d, wp=wp, dge_alpha=5.0)
+    note(f"split dge: dWp {fmt(check(host(g1['dWp']), ob['dWp'], TOL, 'split dge dWp'))}")
