@@ -85,13 +85,13 @@ struct GemmArgs {
   float* red_dA;
   float* red_dB;
   float dge_alpha, dge_c;      // sharpness and alpha / (2 tanh(alpha / 2))
-  // Split contraction (launches with few tiles): `splits` workgroups share each tile;
-  // their float32 partial tiles go to split_ws [ntiles][splits][256 * 256], and split_cnt
-  // [ntiles] (zero at launch) counts arrivals, so the last one adds them and runs the
-  // epilogue. splits = 1: one workgroup per tile, nothing else used.
+  // Split contraction (launches with few tiles), in two launches of the same kernel:
+  // phase 1 runs `splits` workgroups per tile, each over its share of the contraction,
+  // and writes its float32 partial tile to split_ws [ntiles][splits][256 * 256]; phase 2
+  // runs one workgroup per tile, which adds the partials in split order and runs the
+  // epilogue. splits = 1: one launch, one workgroup per tile.
   int splits;
   float* split_ws;
-  int* split_cnt;
 };
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -133,20 +133,14 @@ __device__ __forceinline__ void split_range(int nk, int split, int splits, int& 
   kt1 = (int)((int64_t)nk * (split + 1) / splits);
 }
 
-// After a split job's main loop: writes its accumulators as this job's partial tile
-// (float4 [block][register quad][thread], so each store instruction covers 1 KiB), then
-// counts its arrival. Every job but the last returns false. The last one (release and
-// acquire fences at device scope order the partials before the count) replaces its
-// accumulators with the sum of all partials, taken in split order so that the result
-// does not depend on which job arrived last, resets the count for the next launch and
-// returns true. `flag` is one int of LDS, free at this point.
+// Partial tiles of a split launch: float4 [tile][split][block][register quad][thread], so
+// that each store or load instruction of a workgroup covers 1 KiB.
 template <int WI, int WJ>
-__device__ __forceinline__ bool split_join(const GemmArgs& a, f32x16 (&acc)[WI][WJ], int tile,
-                                           int split, int tid, int* flag) {
+__device__ __forceinline__ void split_store(const GemmArgs& a, const f32x16 (&acc)[WI][WJ],
+                                            int tile, int split, int tid) {
   const int nt = blockDim.x;
   constexpr int NQ = WI * WJ * 4;                    // float4 per thread
-  f32x4* tile_ws = reinterpret_cast<f32x4*>(a.split_ws) + (int64_t)tile * a.splits * NQ * nt;
-  f32x4* mine = tile_ws + (int64_t)split * NQ * nt;
+  f32x4* mine = reinterpret_cast<f32x4*>(a.split_ws) + ((int64_t)tile * a.splits + split) * NQ * nt;
 #pragma unroll
   for (int i = 0; i < WI; ++i)
 #pragma unroll
@@ -155,20 +149,17 @@ __device__ __forceinline__ bool split_join(const GemmArgs& a, f32x16 (&acc)[WI][
       for (int q = 0; q < 4; ++q)
         mine[((i * WJ + j) * 4 + q) * nt + tid] =
             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) *flag = atomicAdd(a.split_cnt + tile, 1);
-  __syncthreads();
-  if (*flag != a.splits - 1) return false;
-  __threadfence();
-#pragma unroll
-  for (int i = 0; i < WI; ++i)
-#pragma unroll
-    for (int j = 0; j < WJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// Phase 2: the tile's accumulators as the sum of its partials, added in split order.
+template <int WI, int WJ>
+__device__ __forceinline__ void split_load(const GemmArgs& a, f32x16 (&acc)[WI][WJ], int tile,
+                                           int tid) {
+  const int nt = blockDim.x;
+  constexpr int NQ = WI * WJ * 4;
+  const f32x4* base = reinterpret_cast<const f32x4*>(a.split_ws) + (int64_t)tile * a.splits * NQ * nt;
   for (int sp = 0; sp < a.splits; ++sp) {
-    const f32x4* src = tile_ws + (int64_t)sp * NQ * nt;
+    const f32x4* src = base + (int64_t)sp * NQ * nt;
 #pragma unroll
     for (int i = 0; i < WI; ++i)
 #pragma unroll
@@ -182,14 +173,6 @@ __device__ __forceinline__ bool split_join(const GemmArgs& a, f32x16 (&acc)[WI][
           acc[i][j][4 * q + 3] += v[3];
         }
   }
-  if (tid == 0) a.split_cnt[tile] = 0;
-  __syncthreads();                                   // every thread has read `flag`
-  return true;
-}
-
-__global__ __launch_bounds__(256) void k_zero_ints(int* p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0;
 }
 
 __device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, float a, float b, float c, float d) {
@@ -287,7 +270,7 @@ __device__ __forceinline__ void store_block_rows_dge(const float* S, float* out,
 // free by now), then written with 16-byte stores, so that every store instruction
 // covers whole 32*WJ-element runs of 16 / WJ output rows.
 template <int NW, int WI, int WJ>
-__device__ void epilogue_fwd(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp,
+__device__ __forceinline__ void epilogue_fwd(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp,
                              int wq, int lane, int wave, uint8_t* smem) {
   constexpr int CW = 32 * WJ, SR = CW + 4;             // strip width, padded LDS row
   constexpr int LPR = CW / 8, RPI = 64 / LPR;          // lanes per row, rows per store
@@ -415,7 +398,7 @@ __device__ __forceinline__ int dvec_row(int v, int e, int h) {
 constexpr int DX_WAVE_LDS = 64 * SROW * 4;   // per-wave staging area: 64 x 33 floats
 
 template <int D, int WI, int WJ>
-__device__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp, int wq,
+__device__ __forceinline__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp, int wq,
                             int lane, float* S, const float* Alds) {
   static_assert(WI % 2 == 0, "k blocks are staged in pairs");
   constexpr int NV = 16 / D;                  // whole vectors per lane and block
@@ -503,8 +486,10 @@ constexpr int DW_CODES_OFF = 128 * 1024;
 constexpr int DW_MASK_OFF = DW_CODES_OFF + 256 * 64;    // 144 KiB
 constexpr int DW_SMEM = DW_MASK_OFF + 256 * 32;         // 152 KiB
 
-template <int D, int NW, int WJ>
-__device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
+// ALDS: A is read from its copy in LDS (d = 16, and the second phase of a split launch)
+// rather than as scalar loads.
+template <int D, int NW, int WJ, bool ALDS>
+__device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
                             int lane, int wave, int tile, uint8_t* smem, const float* Alds) {
   constexpr int NP = D == 16 ? 8 : 1;          // passes over the columns j of dA (d = 16: two
                                                // columns a pass, so no partial sums spill)
@@ -536,10 +521,10 @@ __device__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0
         // A: scalar loads through a constant-address-space pointer (d = 16: LDS copy).
         const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
         const LCVQ_LDS float* Al = (const LCVQ_LDS float*)Alds;
-        if constexpr (D == 16) asm volatile("" : "+v"(Al));
+        if constexpr (ALDS) asm volatile("" : "+v"(Al));
         else asm volatile("" : "+s"(Ac));
         auto Aat = [&](int idx) -> float {
-          if constexpr (D == 16) return Al[idx];
+          if constexpr (ALDS) return Al[idx];
           else return Ac[idx];
         };
         f32x16& c = acc[i][j];
@@ -765,7 +750,7 @@ __device__ __forceinline__ void ring_mfma(const RingFrags<CODES_ARE_L, WI, WJ>& 
 // ahead (`have_first`). Barriers are plain s_barrier: __syncthreads() would also wait for
 // the epilogue's outstanding stores.
 template <int D, int NT>
-__device__ void reduce_dw_partials(const GemmArgs& a, int tile, int ntiles, int tid, float* red,
+__device__ __forceinline__ void reduce_dw_partials(const GemmArgs& a, int tile, int ntiles, int tid, float* red,
                                    float first, bool have_first) {
   constexpr int NOUT = D * D + D;
   for (int o = tile; o < NOUT; o += ntiles) {
@@ -802,7 +787,8 @@ __device__ __forceinline__ void wait_vm_stages(int stages_after) {
 
 // ---- the kernel ----------------------------------------------------------------------
 // FWD and dX: NW waves (4 or 8), 4-slot ring of direct global->LDS loads.
-template <int OP, int D, int NW>
+// SPL: 0 one workgroup per tile; 1 and 2 the two phases of a split launch (forward only).
+template <int OP, int D, int NW, int SPL = 0>
 __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_gemm_ring(GemmArgs a) {
   using T = Tiling<OP, NW>;
@@ -815,8 +801,9 @@ void k_gemm_ring(GemmArgs a) {
   // are rows of X', dX tile-columns are rows of dY.
   constexpr int GR = OP == OP_FWD ? 2 : 16;
   int split = 0;
-  if (a.splits > 1) {
-    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+  if constexpr (SPL != 0) {
+    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, SPL == 1 ? a.splits : 1, tp, tq, tile, split))
+      return;
   } else if (!map_tile<GR>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
     return;
   }
@@ -824,8 +811,8 @@ void k_gemm_ring(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wp = wave / T::WGQ, wq = wave % T::WGQ;
   const int nkt = (a.R + BK - 1) / BK;               // stages of the whole contraction
-  int kt0, kt1;
-  split_range(nkt, split, a.splits, kt0, kt1);
+  int kt0 = 0, kt1 = nkt;
+  if constexpr (SPL == 1) split_range(nkt, split, a.splits, kt0, kt1);
   const int nk = kt1 - kt0;                          // stages of this job
 
   f32x16 acc[WI][WJ];
@@ -838,7 +825,7 @@ void k_gemm_ring(GemmArgs a) {
 
   // One pipelined pass over the contraction per bf16 operand (bf16 activations: one
   // pass; float32 activations: hi and lo halves in two passes).
-  for (int pass = 0; pass < a.npass; ++pass) {
+  for (int pass = 0; pass < (SPL == 2 ? 0 : a.npass); ++pass) {
     const uint16_t* mat = CL ? (pass == 0 ? a.Rmat[0] : a.Rmat[1])
                              : (pass == 0 ? a.Lmat[0] : a.Lmat[1]);
     const int64_t ld = CL ? a.N : a.K;
@@ -884,9 +871,11 @@ void k_gemm_ring(GemmArgs a) {
     }
     __syncthreads();
   }
-  if (OP == OP_FWD && a.splits > 1 &&
-      !split_join<WI, WJ>(a, acc, tile, split, tid, reinterpret_cast<int*>(smem)))
+  if constexpr (SPL == 1) {
+    split_store<WI, WJ>(a, acc, tile, split, tid);
     return;
+  }
+  if constexpr (SPL == 2) split_load<WI, WJ>(a, acc, tile, tid);
 
   if (OP == OP_FWD) {
     epilogue_fwd<NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, wave, smem);
@@ -1104,7 +1093,7 @@ __device__ __forceinline__ void issue_dw_codes(uint8_t* smem, const uint8_t* pac
 }
 
 // dW: 8 waves (512 threads), double-buffered direct loads into LDS (2 x 64 KiB).
-template <int D>
+template <int D, int SPL = 0>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_dw(GemmArgs a) {
   constexpr int NW = 8, WGQ = 4, WJ = 2;
@@ -1112,8 +1101,9 @@ void k_gemm_dw(GemmArgs a) {
   int tp, tq, tile;
   // X and dY panels weigh the same: 4 x 8 tiles per XCD reads the fewest panels.
   int split = 0;
-  if (a.splits > 1) {
-    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+  if constexpr (SPL != 0) {
+    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, SPL == 1 ? a.splits : 1, tp, tq, tile, split))
+      return;
   } else if (!map_tile<4>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
     return;
   }
@@ -1121,10 +1111,12 @@ void k_gemm_dw(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / WGQ, wq = wave % WGQ;
-  int kt0, kt1;
-  split_range((a.R + BK - 1) / BK, split, a.splits, kt0, kt1);
+  int kt0 = 0, kt1 = (a.R + BK - 1) / BK;
+  if constexpr (SPL == 1) split_range(kt1, split, a.splits, kt0, kt1);
+  if constexpr (SPL == 2) kt1 = 0;                   // no stages: the partials hold them
   const DwLaneOffsets lo = dw_lane_offsets(a.N, a.K, p0, q0, lane);
-  issue_dw_codes(smem, a.packed, a.mask, a.N, a.K, p0, q0, wave, lane);
+  if constexpr (SPL != 1)                            // for the epilogue
+    issue_dw_codes(smem, a.packed, a.mask, a.N, a.K, p0, q0, wave, lane);
 
   f32x16 acc[4][WJ];
 #pragma unroll
@@ -1134,7 +1126,7 @@ void k_gemm_dw(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int pass = 0; pass < a.npass; ++pass) {
+  for (int pass = 0; pass < (kt1 > kt0 ? a.npass : 0); ++pass) {
     const uint16_t* Lp = pass == 0 ? a.Lmat[0] : (pass == 1 ? a.Lmat[1] : a.Lmat[2]);
     const uint16_t* Rp = pass == 0 ? a.Rmat[0] : (pass == 1 ? a.Rmat[1] : a.Rmat[2]);
     issue_dw_stage(smem, Lp, Rp, a.M, a.N, a.K, kt0 * BK, p0, q0, wave, lane);
@@ -1170,17 +1162,24 @@ void k_gemm_dw(GemmArgs a) {
       __syncthreads();
     }
   }
-  if (a.splits > 1 &&
-      !split_join<4, WJ>(a, acc, tile, split, tid, reinterpret_cast<int*>(smem)))
+  if constexpr (SPL == 1) {
+    split_store<4, WJ>(a, acc, tile, split, tid);
     return;
+  }
+  if constexpr (SPL == 2) {
+    split_load<4, WJ>(a, acc, tile, tid);
+    __builtin_amdgcn_s_waitcnt(0);                   // the codes and mask in LDS
+    __syncthreads();
+  }
   // The buffers are free after the last barrier: per-wave areas of 12 KiB from 0, the
   // per-wave sums after them, and for d = 16 a copy of A at 120 KiB.
   float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
-  if (D == 16) {
+  constexpr bool ALDS = D == 16 || SPL == 2;
+  if (ALDS) {
     if (tid < D * D) Alds[tid] = a.A[tid];
     __syncthreads();
   }
-  epilogue_dw<D, NW, WJ>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
+  epilogue_dw<D, NW, WJ, ALDS>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
 }
 
 // ---- Gram matrix H = X^T X of calibration activations --------------------------------
@@ -1300,7 +1299,9 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict
 int gemm_splits(int64_t P, int64_t Q, int64_t R) {
   const int64_t nt = ((P + BT - 1) / BT) * ((Q + BT - 1) / BT);
   const int64_t nk = (R + BK - 1) / BK;
-  if (nt > 128) return 1;
+  // Measured on k/v-shaped layers: with 128 tiles (half the chip) the split's per-stage
+  // cost and its second phase cancel the gain; with 64 tiles it pays (dW 176 -> 121 us).
+  if (nt > 64) return 1;
   int64_t sp = 256 / nt;
   if (sp > 4) sp = 4;
   if (sp > nk / 8) sp = nk / 8;                      // at least 8 stages per job
@@ -1311,32 +1312,50 @@ size_t gemm_split_bytes(int64_t P, int64_t Q, int64_t R) {
   const int sp = gemm_splits(P, Q, R);
   if (sp == 1) return 0;
   const size_t nt = (size_t)(((P + BT - 1) / BT) * ((Q + BT - 1) / BT));
-  return nt * sp * BT * BT * 4 + ((nt * 4 + 255) / 256) * 256;
+  return nt * sp * BT * BT * 4;
 }
+
+template <int OP, int SPL>
+static hipError_t launch_op1(GemmArgs& a, int d, int grid, hipStream_t s);
 
 template <int OP>
 static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   a.tilesP = (a.P + BT - 1) / BT;
   a.tilesQ = (a.Q + BT - 1) / BT;
   a.ntiles = a.tilesP * a.tilesQ;
-  if (a.splits > 1) {
-    hipLaunchKernelGGL(k_zero_ints, dim3((a.ntiles + 255) / 256), dim3(256), 0, s, a.split_cnt,
-                       a.ntiles);
+  if constexpr (OP == OP_DX) {
+    return launch_op1<OP, 0>(a, d, ((a.ntiles + 7) / 8) * 8, s);
+  } else {
+    if (a.splits <= 1) return launch_op1<OP, 0>(a, d, ((a.ntiles + 7) / 8) * 8, s);
+    // Split launch: the timing hook, when armed for this product, brackets both phases
+    // with events on the stream.
+    constexpr int id = OP == OP_FWD ? PROF_FWD : PROF_DW;
+    hipEvent_t e0, e1;
+    const bool timed = take_profile(id, &e0, &e1);
+    if (timed) (void)hipEventRecord(e0, s);
+    hipError_t e = launch_op1<OP, 1>(a, d, a.ntiles * a.splits, s);
+    if (e != hipSuccess) return e;
+    e = launch_op1<OP, 2>(a, d, a.ntiles, s);
+    if (timed) (void)hipEventRecord(e1, s);
+    return e;
   }
-  const int grid = ((a.ntiles * (a.splits > 1 ? a.splits : 1) + 7) / 8) * 8;
+}
+
+template <int OP, int SPL>
+static hipError_t launch_op1(GemmArgs& a, int d, int grid, hipStream_t s) {
   if constexpr (OP == OP_DW) {
     switch (d) {
-      case 4: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<4>, dim3(grid), dim3(512), 0, s, a); break;
-      case 8: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<8>, dim3(grid), dim3(512), 0, s, a); break;
-      default: LCVQ_LAUNCH(PROF_DW, k_gemm_dw<16>, dim3(grid), dim3(512), 0, s, a); break;
+      case 4: LCVQ_LAUNCH(PROF_DW, (k_gemm_dw<4, SPL>), dim3(grid), dim3(512), 0, s, a); break;
+      case 8: LCVQ_LAUNCH(PROF_DW, (k_gemm_dw<8, SPL>), dim3(grid), dim3(512), 0, s, a); break;
+      default: LCVQ_LAUNCH(PROF_DW, (k_gemm_dw<16, SPL>), dim3(grid), dim3(512), 0, s, a); break;
     }
   } else {
     constexpr int id = OP == OP_FWD ? PROF_FWD : PROF_DX;
     constexpr int NW = OP == OP_FWD ? LCVQ_FWD_WAVES : LCVQ_DX_WAVES;
     switch (d) {
-      case 4: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 4, NW>), dim3(grid), dim3(NW * 64), 0, s, a); break;
-      case 8: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 8, NW>), dim3(grid), dim3(NW * 64), 0, s, a); break;
-      default: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 16, NW>), dim3(grid), dim3(NW * 64), 0, s, a); break;
+      case 4: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 4, NW, SPL>), dim3(grid), dim3(NW * 64), 0, s, a); break;
+      case 8: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 8, NW, SPL>), dim3(grid), dim3(NW * 64), 0, s, a); break;
+      default: LCVQ_LAUNCH(id, (k_gemm_ring<OP, 16, NW, SPL>), dim3(grid), dim3(NW * 64), 0, s, a); break;
     }
   }
   return hipGetLastError();
@@ -1344,15 +1363,11 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
 
 int gemm_tiles(int64_t P, int64_t Q) { return (int)(((P + BT - 1) / BT) * ((Q + BT - 1) / BT)); }
 
-// Split contraction for launches of few tiles; split_ws holds gemm_split_bytes(P, Q, R):
-// the partial tiles, then the arrival counts.
+// Split contraction for launches of few tiles; split_ws holds gemm_split_bytes(P, Q, R)
+// of partial tiles.
 static void set_splits(GemmArgs& a, int64_t P, int64_t Q, int64_t R, void* split_ws) {
   a.splits = split_ws ? gemm_splits(P, Q, R) : 1;
-  if (a.splits > 1) {
-    const size_t nt = (size_t)gemm_tiles(P, Q);
-    a.split_ws = static_cast<float*>(split_ws);
-    a.split_cnt = reinterpret_cast<int*>(static_cast<uint8_t*>(split_ws) + nt * a.splits * BT * BT * 4);
-  }
+  if (a.splits > 1) a.split_ws = static_cast<float*>(split_ws);
 }
 
 hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint32_t* r16,
