@@ -88,6 +88,10 @@ def parse():
     ap.add_argument("--no-copy-probe", action="store_true")
     ap.add_argument("--no-layers", action="store_true")
     ap.add_argument("--no-ptq", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 8B-stack decode step")
+    ap.add_argument("--no-quant-pack", action="store_true")
+    ap.add_argument("--decode-copies", type=int, default=0,
+                    help="code copies per decode shape (default: enough for 512 MiB)")
     ap.add_argument("--layer-reps", type=int, default=10)
     return ap.parse_args()
 
@@ -436,7 +440,7 @@ def main():
             pk0 = torch.empty((n, k // 4), dtype=torch.uint8, device=dev)
             P.lcvq_quantize(wp, None, pk0, None)
             del wp
-            copies = max(2, -(-(512 << 20) // pk0.numel()))
+            copies = args.decode_copies or max(2, -(-(512 << 20) // pk0.numel()))
             A16, B16 = (t.half().to(dev) for t in SI.make_ab(8, seed=3000))
             # layout 0: canonical packed codes; layout 1: the decode layout written once by
             # lcvq_gemv2b_shuffle (weight preparation, outside the timed calls)
@@ -488,7 +492,7 @@ def main():
         n, k, m = 14336, 4096, 1
         gen = torch.Generator(device=dev).manual_seed(3500)
         pair_bytes = 2 * n * k // 4
-        copies = max(2, -(-(512 << 20) // pair_bytes))
+        copies = args.decode_copies or max(2, -(-(512 << 20) // pair_bytes))
         pool = [[torch.randint(0, 256, (n, k // 4), generator=gen, dtype=torch.uint8, device=dev)
                  for _ in range(2)] for _ in range(copies)]
         A16, B16 = (t.half().to(dev) for t in SI.make_ab(8, seed=3501))
@@ -528,7 +532,7 @@ def main():
     # an input (q, k, v and gate, up) into one launch each, and as the same 128 calls on
     # codes prepared once in the decode layout (lcvq_gemv2b_shuffle, outside the timing).
     decode_stack = None
-    if not args.no_decode:
+    if not args.no_decode and not args.no_stack:
         shapes = SI.CONFIGS["c4_stack_8b_layer"]["mats"]     # q, k, v, o, gate, up, down
         layers = SI.CONFIGS["c4_stack_8b_layer"]["layers"]
         dd = 8
@@ -628,7 +632,7 @@ def main():
     # the profiling hook (kernel id 1 covers lcvq_quantize's launch; the packer is timed by
     # events around its own launch).
     hbm_kernels = None
-    if not args.no_decode:
+    if not args.no_decode and not args.no_quant_pack:
         hbm_kernels = {}
         for (n, k) in ((4096, 4096), (14336, 4096)):
             per = n * k * 4
