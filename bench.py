@@ -257,7 +257,7 @@ def main():
     flops = 6.0 * M * N * K
 
     # The same step captured once in a HIP graph and replayed: it removes the host-side
-    # launch path between the eight kernels. Replays are checked against the eager step
+    # launch path between the five kernels. Replays are checked against the eager step
     # (the library is deterministic, so the bytes must agree).
     ref = [t.clone() for t in (Y, dX, dWp, dA, dB)]
     graph = torch.cuda.CUDAGraph()
