@@ -152,26 +152,41 @@ __device__ __forceinline__ void split_store(const GemmArgs& a, const f32x16 (&ac
 }
 
 // Phase 2: the tile's accumulators as the sum of its partials, added in split order.
+// Addresses are one uniform base plus this thread's byte offset, so the loads need no
+// per-load address registers; split 0 is loaded straight into the accumulators (all its
+// loads in flight at once), each later split in two batches of WI*WJ*2 loads.
 template <int WI, int WJ>
 __device__ __forceinline__ void split_load(const GemmArgs& a, f32x16 (&acc)[WI][WJ], int tile,
                                            int tid) {
+  constexpr int NQ = WI * WJ * 4;                    // float4 per thread
+  constexpr int HQ = NQ / 2;
   const int nt = blockDim.x;
-  constexpr int NQ = WI * WJ * 4;
-  const f32x4* base = reinterpret_cast<const f32x4*>(a.split_ws) + (int64_t)tile * a.splits * NQ * nt;
-  for (int sp = 0; sp < a.splits; ++sp) {
-    const f32x4* src = base + (int64_t)sp * NQ * nt;
+  const int64_t step = (int64_t)nt * 16;             // bytes between a thread's float4s
+  const uint32_t lo = (uint32_t)tid * 16u;
+  const char* base = reinterpret_cast<const char*>(a.split_ws) + (int64_t)tile * a.splits * NQ * step;
 #pragma unroll
-    for (int i = 0; i < WI; ++i)
+  for (int k = 0; k < NQ; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(base + k * step + lo);
+    f32x16& c = acc[k / (WJ * 4)][(k / 4) % WJ];
 #pragma unroll
-      for (int j = 0; j < WJ; ++j)
+    for (int e = 0; e < 4; ++e) c[4 * (k % 4) + e] = v[e];
+  }
+  for (int sp = 1; sp < a.splits; ++sp) {
+    const char* src = base + (int64_t)sp * NQ * step;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = src[((i * WJ + j) * 4 + q) * nt + tid];
-          acc[i][j][4 * q] += v[0];
-          acc[i][j][4 * q + 1] += v[1];
-          acc[i][j][4 * q + 2] += v[2];
-          acc[i][j][4 * q + 3] += v[3];
-        }
+    for (int h = 0; h < 2; ++h) {
+      f32x4 t[HQ];
+#pragma unroll
+      for (int k = 0; k < HQ; ++k)
+        t[k] = *reinterpret_cast<const f32x4*>(src + (h * HQ + k) * step + lo);
+#pragma unroll
+      for (int k = 0; k < HQ; ++k) {
+        const int kk = h * HQ + k;
+        f32x16& c = acc[kk / (WJ * 4)][(kk / 4) % WJ];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[4 * (kk % 4) + e] += t[k][e];
+      }
+    }
   }
 }
 
