@@ -84,39 +84,64 @@ __global__ __launch_bounds__(256) void k_ptq_reverse(const float* __restrict__ H
 }
 
 // ------------------------------------------------------------------ blocked Cholesky
-// Step j0: the diagonal block (already updated by the earlier steps) is factored in LDS
-// by one workgroup. A pivot that is not positive is recorded in the state and replaced
-// by 1 so that the rest stays finite; the outputs are then flagged.
-__global__ __launch_bounds__(256) void k_chol_diag(float* __restrict__ A, int K, int j0,
-                                                   PtqState* st) {
-  __shared__ float L[PB][PB + 1];
+// Step j0: the diagonal block (already updated by the earlier steps) is factored by one
+// wave, row t of the block in lane t's registers. For column c the pivot is lane c's entry
+// c; the column is scaled (lanes t < c hold 0 there), and every later entry k > c of the
+// row subtracts the row's entry c times lane k's scaled entry c, broadcast with readlane
+// in groups of eight (so that few broadcast values are live at once). Entries above the
+// diagonal (k > t) take the same updates unmasked: no lane reads them before step c = k
+// sets them to 0, and they are written back as 0. A pivot that is not positive is
+// recorded in the state and replaced by 1 so that the rest stays finite; the outputs are
+// then flagged.
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+__global__ __launch_bounds__(PB) void k_chol_diag(float* __restrict__ A, int K, int j0,
+                                                  PtqState* st) {
   const int t = threadIdx.x;
-  for (int x = t; x < PB * PB; x += 256) {
-    const int i = x / PB, k = x % PB;
-    L[i][k] = k <= i ? A[(int64_t)(j0 + i) * K + j0 + k] : 0.f;
+  float* row = A + (int64_t)(j0 + t) * K + j0;
+  float x[PB];
+#pragma unroll
+  for (int v = 0; v < PB / 4; ++v) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * v + e] = 4 * v + e <= t ? a[e] : 0.f;   // lower part
   }
-  __syncthreads();
+  bool bad = false;
+#pragma unroll
   for (int c = 0; c < PB; ++c) {
-    const float piv = L[c][c];
+    const float piv = lane_value(x[c], c);
+    bad |= !(piv > 0.f);
     const float d = piv > 0.f ? sqrtf(piv) : 1.f;
-    __syncthreads();
-    if (t == 0) {
-      if (!(piv > 0.f)) st->bad = 1;
-      L[c][c] = d;
+    const float sc = x[c] / d;
+    x[c] = t == c ? d : (t > c ? sc : 0.f);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k0 = c + 1; k0 < PB; k0 += 8) {
+      float l[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < PB) l[u] = lane_value(x[c], k0 + u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < PB) x[k0 + u] = __builtin_fmaf(-x[c], l[u], x[k0 + u]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (t > c && t < PB) L[t][c] /= d;
-    __syncthreads();
-    // trailing update of the block: L[i][k] -= L[i][c] L[k][c], c < k <= i
-    for (int x = t; x < PB * PB; x += 256) {
-      const int i = x / PB, k = x % PB;
-      if (k > c && k <= i) L[i][k] -= L[i][c] * L[k][c];
-    }
-    __syncthreads();
+    // Materialise the row after each column: otherwise the compiler sinks every update
+    // of an entry to where the entry is next used, which keeps all earlier broadcasts
+    // live (in SGPRs, spilled).
+#pragma unroll
+    for (int k = c + 1; k < PB; ++k) asm volatile("" : "+v"(x[k]));
   }
-  for (int x = t; x < PB * PB; x += 256) {
-    const int i = x / PB, k = x % PB;
-    if (k <= i) A[(int64_t)(j0 + i) * K + j0 + k] = L[i][k];
+  // the upper part of the block (never read by the later steps) is written as zeros
+#pragma unroll
+  for (int v = 0; v < PB / 4; ++v) {
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = 4 * v + e <= t ? x[4 * v + e] : 0.f;
+    *reinterpret_cast<f32x4*>(row + 4 * v) = o;
   }
+  if (bad && t == 0) st->bad = 1;
 }
 
 // Rows i >= j0 + 64 of the panel: x L11^T = a, one row per thread, forward substitution
@@ -621,7 +646,7 @@ hipError_t launch_ptq_init(const float* H, const float* W0, int N, int K, float 
   hipLaunchKernelGGL(k_ptq_delta, dim3(1), dim3(256), 0, s, H, K, damp, st);
   hipLaunchKernelGGL(k_ptq_reverse, dim3(K), dim3(256), 0, s, H, K, st, A);
   for (int j0 = 0; j0 < K; j0 += PB) {
-    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(256), 0, s, A, K, j0, st);
+    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(PB), 0, s, A, K, j0, st);
     const int rows = K - j0 - PB;
     if (rows > 0) {
       hipLaunchKernelGGL(k_chol_panel, dim3((rows + 255) / 256), dim3(256), 0, s, A, K, j0);
