@@ -404,8 +404,8 @@ __global__ __launch_bounds__(256) void k_ptq_start(const double* __restrict__ pa
 // ------------------------------------------------------------------ the integer step
 // One workgroup sweeps 16 rows of W0 over K, 64 columns at a time. For a column block:
 //  1. its feedback from all earlier codes, F[r][j] = sum_{i < j0} c_ri U_ij, on the bf16
-//     matrix cores: codes (exact) times U^T's hi and lo halves, float32 accumulation;
-//     wave w covers the block's columns 16 w .. 16 w + 15;
+//     matrix cores: codes (exact) times U^T's hi and lo halves (summed in two float32
+//     accumulators, added at the end); wave w covers the block's columns 16 w .. 16 w + 15;
 //  2. wave 0 then walks the block's 64 columns in order, 4 lanes per row, each lane
 //     holding 16 columns' running value t = (q - b e) / s - F - (feedback inside the
 //     block): the owner of column k broadcasts t_k, every lane rounds it the same way
@@ -453,18 +453,50 @@ __global__ __launch_bounds__(256) void k_ptq_sweep(const float* __restrict__ Q,
   for (int j0 = 0; j0 < K; j0 += PB) {
     // 1. feedback of the earlier codes on this block's columns
     {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
       const int jc = j0 + 16 * wave + (lane & 15);               // B column of this lane
       const uint16_t* bh = Ut_hi + (int64_t)jc * K + 8 * (lane >> 4);
       const uint16_t* bl = Ut_lo + (int64_t)jc * K + 8 * (lane >> 4);
       const uint8_t* ca = cl + (lane & 15) * KB + 2 * (lane >> 4);
-      for (int i0 = 0; i0 < j0; i0 += 32) {
-        const bf16x8 a = codes8_bf16(*reinterpret_cast<const uint16_t*>(ca + i0 / 4));
-        const bf16x8 h = *reinterpret_cast<const bf16x8*>(bh + i0);
-        const bf16x8 l = *reinterpret_cast<const bf16x8*>(bl + i0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l, acc, 0, 0, 0);
+      // Steps of 32 rows in groups of FG: all of a group's loads are issued before its
+      // matrix-core products (one memory round trip per group, not two per step), and the
+      // hi and lo products go to separate accumulators.
+      constexpr int FG = 8;
+      int i0 = 0;
+      for (; i0 + 32 * FG <= j0; i0 += 32 * FG) {
+        bf16x8 h[FG], l[FG];
+        uint32_t cw[FG];
+#pragma unroll
+        for (int u = 0; u < FG; ++u) {
+          h[u] = *reinterpret_cast<const bf16x8*>(bh + i0 + 32 * u);
+          l[u] = *reinterpret_cast<const bf16x8*>(bl + i0 + 32 * u);
+          cw[u] = *reinterpret_cast<const uint16_t*>(ca + (i0 + 32 * u) / 4);
+        }
+#pragma unroll
+        for (int u = 0; u < FG; ++u) {
+          const bf16x8 a = codes8_bf16(cw[u]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h[u], acc, 0, 0, 0);
+          accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l[u], accl, 0, 0, 0);
+        }
       }
+      for (; i0 < j0; i0 += 64) {                                // j0 is a multiple of 64
+        bf16x8 h[2], l[2];
+        uint32_t cw[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          h[u] = *reinterpret_cast<const bf16x8*>(bh + i0 + 32 * u);
+          l[u] = *reinterpret_cast<const bf16x8*>(bl + i0 + 32 * u);
+          cw[u] = *reinterpret_cast<const uint16_t*>(ca + (i0 + 32 * u) / 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 a = codes8_bf16(cw[u]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h[u], acc, 0, 0, 0);
+          accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l[u], accl, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += accl[v];
       // D layout: lane l holds rows 4 (l / 16) + v, column l % 16
 #pragma unroll
       for (int v = 0; v < 4; ++v) F[4 * (lane >> 4) + v][16 * wave + (lane & 15)] = acc[v];
