@@ -1314,9 +1314,10 @@ __global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict
 int gemm_splits(int64_t P, int64_t Q, int64_t R) {
   const int64_t nt = ((P + BT - 1) / BT) * ((Q + BT - 1) / BT);
   const int64_t nk = (R + BK - 1) / BK;
-  // Measured on k/v-shaped layers: with 128 tiles (half the chip) the split's per-stage
-  // cost and its second phase cancel the gain; with 64 tiles it pays (dW 176 -> 121 us).
-  if (nt > 64) return 1;
+  // Measured on k/v-shaped layers (8192 tokens): with 64 tiles the split pays (dW 176 ->
+  // 121 us), and with 128 tiles (the forward, half the chip) too since the second phase
+  // loads its partials in one batch (95 -> 80 us).
+  if (nt > 128) return 1;
   int64_t sp = 256 / nt;
   if (sp > 4) sp = 4;
   if (sp > nk / 8) sp = nk / 8;                      // at least 8 stages per job

@@ -55,7 +55,7 @@ hipError_t launch_bwd_prep(const void* dY, const void* X, bool f32, int64_t M, i
                            uint32_t* r16t, hipStream_t s);
 
 int gemm_tiles(int64_t P, int64_t Q);
-// Launches with at most 64 tiles (of 256 x 256) split their contraction over up to four
+// Launches with at most 128 tiles (of 256 x 256) split their contraction over up to four
 // workgroups per tile: gemm_splits() of them (1: no split), and gemm_split_bytes() of
 // workspace (0 without a split) for the forward (P = M, Q = N, R = K) and dW (P = K,
 // Q = N, R = M) products.

@@ -463,11 +463,13 @@ def test_read_probe_reads_every_word(P, nbytes):
     assert got == want
 
 
-# Shapes whose forward and dW products have few tiles: their contraction is split over up
-# to four workgroups per tile (partials added in a fixed order by the last to arrive).
+# Shapes whose forward and dW products have few tiles (at most 128): their contraction is
+# split over up to four workgroups per tile, whose partial tiles a second launch adds in
+# split order before the epilogue.
 SPLIT_SHAPES = [(1100, 320, 2112, 8, "bf16"),     # forward 4 ways, dW 2 ways, ragged M, K
                 (2500, 192, 1216, 16, "f32"),     # forward 2 ways, dW 4 ways, float32
-                (1031, 64, 4096, 4, "bf16")]      # one tile column, forward 4 ways
+                (1031, 64, 4096, 4, "bf16"),      # one tile column, forward 4 ways
+                (4000, 1280, 1024, 8, "bf16")]    # forward 80 tiles 2 ways, dW 4 ways
 
 
 @pytest.mark.parametrize("M,N,K,d,xdt", SPLIT_SHAPES)
