@@ -155,12 +155,12 @@ __device__ __forceinline__ void split_store(const GemmArgs& a, const f32x16 (&ac
 // Addresses are one uniform base plus this thread's byte offset, so the loads need no
 // per-load address registers; split 0 is loaded straight into the accumulators (all its
 // loads in flight at once), each later split in two batches of WI*WJ*2 loads.
+// nt: the phase-1 workgroup size; tid: the phase-1 thread whose accumulators are loaded.
 template <int WI, int WJ>
 __device__ __forceinline__ void split_load(const GemmArgs& a, f32x16 (&acc)[WI][WJ], int tile,
-                                           int tid) {
+                                           int tid, int nt) {
   constexpr int NQ = WI * WJ * 4;                    // float4 per thread
   constexpr int HQ = NQ / 2;
-  const int nt = blockDim.x;
   const int64_t step = (int64_t)nt * 16;             // bytes between a thread's float4s
   const uint32_t lo = (uint32_t)tid * 16u;
   const char* base = reinterpret_cast<const char*>(a.split_ws) + (int64_t)tile * a.splits * NQ * step;
@@ -503,9 +503,11 @@ constexpr int DW_SMEM = DW_MASK_OFF + 256 * 32;         // 152 KiB
 
 // ALDS: A is read from its copy in LDS (d = 16, and the second phase of a split launch)
 // rather than as scalar loads.
-template <int D, int NW, int WJ, bool ALDS>
+// CO, MO: LDS offsets of the tile's codes and mask bits; `prow`: the partial row its dA/dB
+// sums go to.
+template <int D, int NW, int WJ, bool ALDS, int CO = DW_CODES_OFF, int MO = DW_MASK_OFF>
 __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
-                            int lane, int wave, int tile, uint8_t* smem, const float* Alds) {
+                            int lane, int wave, int prow, uint8_t* smem, const float* Alds) {
   constexpr int NP = D == 16 ? 8 : 1;          // passes over the columns j of dA (d = 16: two
                                                // columns a pass, so no partial sums spill)
   constexpr int JW = D / NP;
@@ -514,6 +516,8 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
   constexpr int RROW = NR + 1;
   constexpr int WREG = 12 * 1024;              // per-wave LDS area: staging, then reduction
   static_assert(32 * RROW * 4 <= WREG && 32 * SROW * 4 <= WREG, "per-wave LDS area");
+  static_assert(NW * WREG + NP * NW * NR * 4 <= (CO == DW_CODES_OFF ? 120 : 28) * 1024,
+                "per-wave areas and sums below A's copy");
   float* S = reinterpret_cast<float*>(smem + wave * WREG);
   float* red = S;                              // reused after the blocks of a pass
   float* wsum = reinterpret_cast<float*>(smem + NW * WREG);      // [NP][NW][NR]
@@ -561,8 +565,8 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
           // past the end of G hold clamped-operand values, not zeros: they must not
           // reach dA or dB.
           const bool valid = n < a.N && kv < a.K;
-          const uint8_t* zp = smem + DW_CODES_OFF + (n - q0) * 64 + ((kv - p0) >> 2);
-          const uint8_t* mp = smem + DW_MASK_OFF + (n - q0) * 32 + ((kv - p0) >> 3);
+          const uint8_t* zp = smem + CO + (n - q0) * 64 + ((kv - p0) >> 2);
+          const uint8_t* mp = smem + MO + (n - q0) * 32 + ((kv - p0) >> 3);
           uint32_t zw, mw;
           if (D == 4) { zw = zp[0]; mw = (mp[0] >> (kv & 4)) & 0xFu; }
           if (D == 8) { zw = *reinterpret_cast<const uint16_t*>(zp); mw = mp[0]; }
@@ -628,7 +632,7 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
       const int x = NA + (o - D * D);
       for (int w = 0; w < NW; ++w) sum += wsum[w * NR + x];
     }
-    a.partials[(int64_t)tile * (D * D + D) + o] = sum;
+    a.partials[(int64_t)prow * (D * D + D) + o] = sum;
   }
 }
 
@@ -890,7 +894,7 @@ void k_gemm_ring(GemmArgs a) {
     split_store<WI, WJ>(a, acc, tile, split, tid);
     return;
   }
-  if constexpr (SPL == 2) split_load<WI, WJ>(a, acc, tile, tid);
+  if constexpr (SPL == 2) split_load<WI, WJ>(a, acc, tile, tid, blockDim.x);
 
   if (OP == OP_FWD) {
     epilogue_fwd<NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, wave, smem);
@@ -1082,9 +1086,10 @@ __device__ __forceinline__ void dw_mfma(const DwFrags<WJ>& f, f32x16 acc[4][WJ])
 // Codes: 16-byte direct loads, 2 per lane; mask: 4-byte direct loads (mask rows are only
 // 8-byte aligned), 4 per lane. Columns past N and k past K read a valid address; those
 // entries are never used.
-__device__ __forceinline__ void issue_dw_codes(uint8_t* smem, const uint8_t* packed,
-                                               const uint8_t* mask, int N, int K, int p0,
-                                               int q0, int wave, int lane) {
+__device__ __forceinline__ void issue_dw_codes(uint8_t* codes_lds, uint8_t* mask_lds,
+                                               const uint8_t* packed, const uint8_t* mask,
+                                               int N, int K, int p0, int q0, int wave,
+                                               int lane) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int c = (wave * 2 + i) * 64 + lane;            // 16-byte chunk of the code tile
@@ -1093,7 +1098,7 @@ __device__ __forceinline__ void issue_dw_codes(uint8_t* smem, const uint8_t* pac
     int kb = p0 + (c & 3) * 64;
     kb = kb < K ? kb : 0;
     const uint8_t* src = packed + (int64_t)n * (K >> 2) + (kb >> 2);
-    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(smem + DW_CODES_OFF + (wave * 2 + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(codes_lds + (wave * 2 + i) * 1024), 16, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1103,22 +1108,24 @@ __device__ __forceinline__ void issue_dw_codes(uint8_t* smem, const uint8_t* pac
     int kb = p0 + (c & 7) * 32;
     kb = kb < K ? kb : 0;
     const uint8_t* src = mask + (int64_t)n * (K >> 3) + (kb >> 3);
-    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(smem + DW_MASK_OFF + (wave * 4 + i) * 256), 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(mask_lds + (wave * 4 + i) * 256), 4, 0, 0);
   }
 }
 
 // dW: 8 waves (512 threads), double-buffered direct loads into LDS (2 x 64 KiB).
+// SPL = 0: one workgroup per tile, with the epilogue; SPL = 1: phase 1 of a split launch
+// (partial tiles out; phase 2 is k_gemm_dw_epi).
 template <int D, int SPL = 0>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_dw(GemmArgs a) {
+  static_assert(SPL == 0 || SPL == 1, "phase 2 of a split dW is k_gemm_dw_epi");
   constexpr int NW = 8, WGQ = 4, WJ = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[DW_SMEM];   // 152 KiB
   int tp, tq, tile;
   // X and dY panels weigh the same: 4 x 8 tiles per XCD reads the fewest panels.
   int split = 0;
-  if constexpr (SPL != 0) {
-    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, SPL == 1 ? a.splits : 1, tp, tq, tile, split))
-      return;
+  if constexpr (SPL == 1) {
+    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
   } else if (!map_tile<4>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
     return;
   }
@@ -1128,10 +1135,10 @@ void k_gemm_dw(GemmArgs a) {
   const int wp = wave / WGQ, wq = wave % WGQ;
   int kt0 = 0, kt1 = (a.R + BK - 1) / BK;
   if constexpr (SPL == 1) split_range(kt1, split, a.splits, kt0, kt1);
-  if constexpr (SPL == 2) kt1 = 0;                   // no stages: the partials hold them
   const DwLaneOffsets lo = dw_lane_offsets(a.N, a.K, p0, q0, lane);
-  if constexpr (SPL != 1)                            // for the epilogue
-    issue_dw_codes(smem, a.packed, a.mask, a.N, a.K, p0, q0, wave, lane);
+  if constexpr (SPL == 0)                            // for the epilogue
+    issue_dw_codes(smem + DW_CODES_OFF, smem + DW_MASK_OFF, a.packed, a.mask, a.N, a.K, p0, q0,
+                   wave, lane);
 
   f32x16 acc[4][WJ];
 #pragma unroll
@@ -1181,20 +1188,60 @@ void k_gemm_dw(GemmArgs a) {
     split_store<4, WJ>(a, acc, tile, split, tid);
     return;
   }
-  if constexpr (SPL == 2) {
-    split_load<4, WJ>(a, acc, tile, tid);
-    __builtin_amdgcn_s_waitcnt(0);                   // the codes and mask in LDS
-    __syncthreads();
-  }
   // The buffers are free after the last barrier: per-wave areas of 12 KiB from 0, the
   // per-wave sums after them, and for d = 16 a copy of A at 120 KiB.
   float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
-  constexpr bool ALDS = D == 16 || SPL == 2;
+  constexpr bool ALDS = D == 16;
   if (ALDS) {
     if (tid < D * D) Alds[tid] = a.A[tid];
     __syncthreads();
   }
   epilogue_dw<D, NW, WJ, ALDS>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
+}
+
+// Phase 2 of a split dW launch, spread over DW_EPI_G workgroups per tile so that few-tile
+// launches still fill the chip with the epilogue's VALU work: workgroup b takes tile
+// b mod ntiles (as the phase-1 jobs, so that a tile's workgroups of both phases share an
+// XCD, whose L2 holds the partials) and group g = b / ntiles, i.e. the tile's waves
+// v = DW_EPI_NW g .. + DW_EPI_NW - 1 of the 8-wave layout of phase 1. It adds their partial
+// accumulators in split order and runs their part of the straight-through epilogue; its
+// dA/dB sums go to partial row DW_EPI_G * tile + g. LDS: the waves' 12 KiB areas, their
+// sums, A, then the whole tile's codes and mask bits.
+constexpr int DW_EPI_NW = 2;
+constexpr int DW_EPI_G = 8 / DW_EPI_NW;
+constexpr int EPI_A_OFF = 28 * 1024;
+constexpr int EPI_CODES_OFF = 32 * 1024;
+constexpr int EPI_MASK_OFF = EPI_CODES_OFF + 256 * 64;
+constexpr int EPI_SMEM = EPI_MASK_OFF + 256 * 32;       // 56 KiB
+template <int D>
+__global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
+  constexpr int WGQ = 4, WJ = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[EPI_SMEM];
+  const int tile = (int)blockIdx.x % a.ntiles, g = (int)blockIdx.x / a.ntiles;
+  if (g >= DW_EPI_G) return;
+  const int tp = tile / a.tilesQ, tq = tile % a.tilesQ;   // as map_split
+  const int p0 = tp * BT, q0 = tq * BT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int v = DW_EPI_NW * g + lw;                       // wave of the 8-wave layout
+  const int wp = v / WGQ, wq = v % WGQ;
+  for (int vw = lw; vw < 8; vw += DW_EPI_NW)              // the whole tile's codes and mask
+    issue_dw_codes(smem + EPI_CODES_OFF, smem + EPI_MASK_OFF, a.packed, a.mask, a.N, a.K, p0,
+                   q0, vw, lane);
+  float* Alds = reinterpret_cast<float*>(smem + EPI_A_OFF);
+  for (int i = tid; i < D * D; i += DW_EPI_NW * 64) Alds[i] = a.A[i];
+  f32x16 acc[4][WJ];
+  split_load<4, WJ>(a, acc, tile, v * 64 + lane, 512);
+  __builtin_amdgcn_s_waitcnt(0);                          // the codes and mask in LDS
+  __syncthreads();
+  epilogue_dw<D, DW_EPI_NW, WJ, true, EPI_CODES_OFF, EPI_MASK_OFF>(
+      a, acc, p0, q0, wp, wq, lane, lw, DW_EPI_G * tile + g, smem, Alds);
+}
+
+// dA/dB partial rows the dW product of this shape writes (the reduction's input).
+int dw_partial_rows(int64_t M, int64_t N, int64_t K) {
+  const int nt = gemm_tiles(K, N);
+  return gemm_splits(K, N, M) > 1 ? nt * DW_EPI_G : nt;
 }
 
 // ---- Gram matrix H = X^T X of calibration activations --------------------------------
@@ -1351,7 +1398,7 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
     if (timed) (void)hipEventRecord(e0, s);
     hipError_t e = launch_op1<OP, 1>(a, d, a.ntiles * a.splits, s);
     if (e != hipSuccess) return e;
-    e = launch_op1<OP, 2>(a, d, a.ntiles, s);
+    e = launch_op1<OP, 2>(a, d, OP == OP_DW ? a.ntiles * DW_EPI_G : a.ntiles, s);
     if (timed) (void)hipEventRecord(e1, s);
     return e;
   }
@@ -1359,7 +1406,14 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
 
 template <int OP, int SPL>
 static hipError_t launch_op1(GemmArgs& a, int d, int grid, hipStream_t s) {
-  if constexpr (OP == OP_DW) {
+  if constexpr (OP == OP_DW && SPL == 2) {
+    const dim3 b(DW_EPI_NW * 64);
+    switch (d) {
+      case 4: LCVQ_LAUNCH(PROF_DW, k_gemm_dw_epi<4>, dim3(grid), b, 0, s, a); break;
+      case 8: LCVQ_LAUNCH(PROF_DW, k_gemm_dw_epi<8>, dim3(grid), b, 0, s, a); break;
+      default: LCVQ_LAUNCH(PROF_DW, k_gemm_dw_epi<16>, dim3(grid), b, 0, s, a); break;
+    }
+  } else if constexpr (OP == OP_DW) {
     switch (d) {
       case 4: LCVQ_LAUNCH(PROF_DW, (k_gemm_dw<4, SPL>), dim3(grid), dim3(512), 0, s, a); break;
       case 8: LCVQ_LAUNCH(PROF_DW, (k_gemm_dw<8, SPL>), dim3(grid), dim3(512), 0, s, a); break;
@@ -1407,7 +1461,7 @@ hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16
   GemmArgs a = {};
   if (dw_partials) {                         // the dW product's tiles: ceil(K/BT) x ceil(N/BT)
     a.red_partials = dw_partials;
-    a.red_tiles = ((K + BT - 1) / BT) * ((N + BT - 1) / BT);
+    a.red_tiles = dw_partial_rows(M, N, K);
     a.red_dA = dA;
     a.red_dB = dB;
   }
@@ -1445,7 +1499,8 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
   a.dge_c = dge_wp ? (float)((double)dge_alpha / (2.0 * tanh((double)dge_alpha / 2.0))) : 0.f;
   hipError_t e = launch_op<OP_DW>(a, d, s);
   if (e != hipSuccess || !reduce) return e;
-  hipLaunchKernelGGL(k_reduce_partials, dim3(d * d + d), dim3(256), 0, s, partials, a.ntiles,
+  hipLaunchKernelGGL(k_reduce_partials, dim3(d * d + d), dim3(256), 0, s, partials,
+                     dw_partial_rows(M, N, K),
                      d * d + d, dA, dB, d);
   return hipGetLastError();
 }

@@ -87,8 +87,8 @@ inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int d, bool f32) {
   w.r = 0;
   w.r16t = w.r + up((size_t)M * 4);
   w.partials = w.r16t + up(r16_bytes(K, N));
-  const size_t ntiles = (size_t)gemm_tiles(K, N);
-  w.dy_hi = w.partials + up(ntiles * (size_t)(d * d + d) * 4);
+  const size_t prows = (size_t)dw_partial_rows(M, N, K);
+  w.dy_hi = w.partials + up(prows * (size_t)(d * d + d) * 4);
   const size_t dyb = f32 ? up((size_t)M * N * 2) : 0, xb = f32 ? up((size_t)M * K * 2) : 0;
   w.dy_lo = w.dy_hi + dyb;
   w.x_hi = w.dy_lo + dyb;
