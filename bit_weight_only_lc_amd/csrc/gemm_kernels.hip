@@ -806,10 +806,12 @@ __device__ __forceinline__ void wait_vm_stages(int stages_after) {
 
 // ---- the kernel ----------------------------------------------------------------------
 // FWD and dX: NW waves (4 or 8), 4-slot ring of direct global->LDS loads.
-// SPL: 0 one workgroup per tile; 1 and 2 the two phases of a split launch (forward only).
+// SPL: 0 one workgroup per tile; 1 phase 1 of a split launch (forward only; phase 2 is
+// k_gemm_fwd_epi).
 template <int OP, int D, int NW, int SPL = 0>
 __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_gemm_ring(GemmArgs a) {
+  static_assert(SPL == 0 || (SPL == 1 && OP == OP_FWD), "phase 2 of a split forward is k_gemm_fwd_epi");
   using T = Tiling<OP, NW>;
   constexpr int WI = T::WI, WJ = T::WJ;
   constexpr bool CL = OP == OP_DX;               // codes are the L operand for dX
@@ -820,9 +822,8 @@ void k_gemm_ring(GemmArgs a) {
   // are rows of X', dX tile-columns are rows of dY.
   constexpr int GR = OP == OP_FWD ? 2 : 16;
   int split = 0;
-  if constexpr (SPL != 0) {
-    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, SPL == 1 ? a.splits : 1, tp, tq, tile, split))
-      return;
+  if constexpr (SPL == 1) {
+    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
   } else if (!map_tile<GR>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
     return;
   }
@@ -844,7 +845,7 @@ void k_gemm_ring(GemmArgs a) {
 
   // One pipelined pass over the contraction per bf16 operand (bf16 activations: one
   // pass; float32 activations: hi and lo halves in two passes).
-  for (int pass = 0; pass < (SPL == 2 ? 0 : a.npass); ++pass) {
+  for (int pass = 0; pass < a.npass; ++pass) {
     const uint16_t* mat = CL ? (pass == 0 ? a.Rmat[0] : a.Rmat[1])
                              : (pass == 0 ? a.Lmat[0] : a.Lmat[1]);
     const int64_t ld = CL ? a.N : a.K;
@@ -894,7 +895,6 @@ void k_gemm_ring(GemmArgs a) {
     split_store<WI, WJ>(a, acc, tile, split, tid);
     return;
   }
-  if constexpr (SPL == 2) split_load<WI, WJ>(a, acc, tile, tid, blockDim.x);
 
   if (OP == OP_FWD) {
     epilogue_fwd<NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, wave, smem);
@@ -931,6 +931,30 @@ void k_gemm_ring(GemmArgs a) {
                                      reinterpret_cast<float*>(smem + 128 * 1024),
                                      tid < a.red_tiles ? fv : 0.f, have_first);
   }
+}
+
+// Phase 2 of a split forward launch, spread over FWD_EPI_G workgroups per tile: workgroup
+// b takes tile b mod ntiles (as the phase-1 jobs, so that both phases of a tile share an
+// XCD, whose L2 holds the partials) and group g = b / ntiles, i.e. the tile's waves
+// v = FWD_EPI_NW g .. + FWD_EPI_NW - 1 of the 8-wave forward layout. It adds their partial
+// accumulators in split order and runs their part of the forward epilogue (per wave).
+constexpr int FWD_EPI_NW = 2;
+constexpr int FWD_EPI_G = 8 / FWD_EPI_NW;
+__global__ __launch_bounds__(FWD_EPI_NW * 64) void k_gemm_fwd_epi(GemmArgs a) {
+  using T = Tiling<OP_FWD, 8>;
+  constexpr int WI = T::WI, WJ = T::WJ;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[FWD_EPI_NW * 32 * (32 * WJ + 4) * 4];
+  const int tile = (int)blockIdx.x % a.ntiles, g = (int)blockIdx.x / a.ntiles;
+  if (g >= FWD_EPI_G) return;
+  const int tp = tile / a.tilesQ, tq = tile % a.tilesQ;   // as map_split
+  const int p0 = tp * BT, q0 = tq * BT;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lw = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int v = FWD_EPI_NW * g + lw;
+  const int wp = v / T::WGQ, wq = v % T::WGQ;
+  f32x16 acc[WI][WJ];
+  split_load<WI, WJ>(a, acc, tile, v * 64 + lane, 512);
+  epilogue_fwd<FWD_EPI_NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, lw, smem);
 }
 
 // ---- dW product: both operands arrive in their natural [m][column] layout ------------
@@ -1398,7 +1422,7 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
     if (timed) (void)hipEventRecord(e0, s);
     hipError_t e = launch_op1<OP, 1>(a, d, a.ntiles * a.splits, s);
     if (e != hipSuccess) return e;
-    e = launch_op1<OP, 2>(a, d, OP == OP_DW ? a.ntiles * DW_EPI_G : a.ntiles, s);
+    e = launch_op1<OP, 2>(a, d, a.ntiles * (OP == OP_DW ? DW_EPI_G : FWD_EPI_G), s);
     if (timed) (void)hipEventRecord(e1, s);
     return e;
   }
@@ -1419,6 +1443,9 @@ static hipError_t launch_op1(GemmArgs& a, int d, int grid, hipStream_t s) {
       case 8: LCVQ_LAUNCH(PROF_DW, (k_gemm_dw<8, SPL>), dim3(grid), dim3(512), 0, s, a); break;
       default: LCVQ_LAUNCH(PROF_DW, (k_gemm_dw<16, SPL>), dim3(grid), dim3(512), 0, s, a); break;
     }
+  } else if constexpr (OP == OP_FWD && SPL == 2) {
+    static_assert(LCVQ_FWD_WAVES == 8, "the forward's spread phase 2 follows the 8-wave layout");
+    LCVQ_LAUNCH(PROF_FWD, k_gemm_fwd_epi, dim3(grid), dim3(FWD_EPI_NW * 64), 0, s, a);
   } else {
     constexpr int id = OP == OP_FWD ? PROF_FWD : PROF_DX;
     constexpr int NW = OP == OP_FWD ? LCVQ_FWD_WAVES : LCVQ_DX_WAVES;
