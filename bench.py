@@ -120,6 +120,22 @@ def clock_warmup(torch, fn, seconds):
     return n
 
 
+def mfma_ceiling(torch, P, L, dev, iters=1000, calls=20):
+    """Matrix-core issue ceiling on this machine: the library's MFMA probe (the products' 8
+    waves per CU and 32x32x16 bf16 MFMAs, pseudo-random toggling operands), right after
+    the timed steps so that the clock is at its working level; each launch timed by the
+    profiling hook. Returns TFLOP/s."""
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    P.lcvq_mfma_probe(iters, sink)
+    evs = timed_events(torch, calls)
+    for a, b in evs:
+        L.lcvq_profile_next(10, a.cuda_event, b.cuda_event)
+        P.lcvq_mfma_probe(iters, sink)
+    torch.cuda.synchronize()
+    t = sum(a.elapsed_time(b) for a, b in evs) / calls * 1e-3
+    return iters * float(1 << 29) / t / 1e12
+
+
 def read_probe(torch, P, L, pool, calls):
     """Same-size read ceiling: the library's read probe (one launch streaming a buffer
     once, with the decode kernels' loads) over the same rotating pool, each launch timed
@@ -333,6 +349,10 @@ def main():
                 "per_kernel_ms": {k: round(v, 4) for k, v in kern.items()},
                 "per_product_tflops": {k: round(gemm_flops / (v * 1e-3) / 1e12, 1)
                                        for k, v in prods.items()}}
+    # the same products against the matrix-core issue ceiling measured now, on this machine
+    ceil = mfma_ceiling(torch, P, L, dev)
+    roofline["mfma_ceiling_tflops"] = round(ceil, 1)
+    roofline["frac_of_mfma_ceiling"] = round(achieved / ceil, 4)
     # one launch: Wp read; packed codes, mask bits, GEMM code words written; X read and
     # X' written (bf16), one float per row
     q_bytes = N * K * (4 + 0.25 + 0.125 + 0.25) + M * K * (2 + 2) + M * 4

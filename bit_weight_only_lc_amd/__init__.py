@@ -67,6 +67,7 @@ def lib():
             "lcvq_gemv2b_noalloc": [vp, i64, i64, i64, i32, vp, vp, vp, vp, vp],
             "lcvq_hessian": [vp, i64, i64, vp, vp],
             "lcvq_read_probe": [vp, i64, vp, vp],
+            "lcvq_mfma_probe": [i64, vp, vp],
             "lcvq_ptq_init": [vp, vp, i64, i64, f32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         }
         for name, args in sigs.items():
@@ -310,6 +311,12 @@ def lcvq_gemv2b_batched(X, mats, d, workspace=None):
     _check(workspace, "workspace", torch.uint8, dev)
     _ok(lib().lcvq_gemv2b_batched(_p(X), M, K, d, arr, len(mats), _p(workspace),
                                   workspace.numel(), _stream(dev)), "lcvq_gemv2b_batched")
+
+
+def lcvq_mfma_probe(iters, sink):
+    """Measurement helper: iters * 2^29 flops of bf16 MFMA issue into sink (int32 [1024])."""
+    _check(sink, "sink", torch.int32)
+    _ok(lib().lcvq_mfma_probe(int(iters), _p(sink), _stream(sink.device)), "lcvq_mfma_probe")
 
 
 def lcvq_read_probe(buf, sink):

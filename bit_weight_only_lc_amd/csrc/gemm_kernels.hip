@@ -1458,6 +1458,71 @@ static hipError_t launch_op1(GemmArgs& a, int d, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Measurement helper, no step of the method: the matrix-core issue ceiling the products
+// are compared to. One workgroup of 8 waves per CU (2 per SIMD, as in the products); each
+// wave runs `iters` rounds of the products' 8 independent 32x32x16 bf16 MFMAs (4 x 2
+// accumulator blocks). Operands are pseudo-random bf16 values of magnitude in [0.5, 1)
+// with random signs and mantissas, in two sets used on alternate rounds so that the
+// operand bits toggle as when data streams through (the matrix cores' power, and so their
+// clock, depend on data activity). One word per workgroup goes to sink so that nothing is
+// dropped. Flops: iters * 8 * 2 * 32 * 32 * 16 per wave.
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_mfma_probe(int iters, uint32_t* __restrict__ sink) {
+  const int tid = threadIdx.x;
+  uint32_t h = ((uint32_t)blockIdx.x * 512u + (uint32_t)tid) * 0x9E3779B9u + 0x7F4A7C15u;
+  auto next = [&h]() {
+    h ^= h << 13; h ^= h >> 17; h ^= h << 5;
+    return (h & 0x807F807Fu) | 0x3F003F00u;     // two bf16: sign, exponent -1, mantissa
+  };
+  bf16x8 a[2][4], b[2][2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[s2][i] = __builtin_bit_cast(bf16x8, u32x4{next(), next(), next(), next()});
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b[s2][j] = __builtin_bit_cast(bf16x8, u32x4{next(), next(), next(), next()});
+  }
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s2][i], b[s2][j], acc[i][j], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t += acc[i][j][r];
+  __shared__ float w[8];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+  if ((tid & 63) == 0) w[tid >> 6] = t;
+  __syncthreads();
+  if (tid == 0) {
+    float u = 0.f;
+    for (int k = 0; k < 8; ++k) u += w[k];
+    sink[blockIdx.x & 1023] = __builtin_bit_cast(uint32_t, u);
+  }
+}
+
+// iters (even) rounds on 256 workgroups: iters * 2^29 flops.
+hipError_t launch_mfma_probe(int iters, uint32_t* sink, hipStream_t s) {
+  LCVQ_LAUNCH(PROF_MFMA_PROBE, k_mfma_probe, dim3(256), dim3(512), 0, s, iters, sink);
+  return hipGetLastError();
+}
+
 int gemm_tiles(int64_t P, int64_t Q) { return (int)(((P + BT - 1) / BT) * ((Q + BT - 1) / BT)); }
 
 // Split contraction for launches of few tiles; split_ws holds gemm_split_bytes(P, Q, R)

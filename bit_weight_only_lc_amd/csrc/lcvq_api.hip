@@ -435,6 +435,13 @@ lcvq_status_t lcvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, vo
   return from_hip(launch_read_probe(buf, bytes, sink, as_stream(stream)));
 }
 
+lcvq_status_t lcvq_mfma_probe(int64_t iters, uint32_t* sink, void* stream) {
+  if (!sink) return LCVQ_ERR_NULL;
+  if (iters < 2 || iters > (int64_t(1) << 24) || (iters % 2)) return LCVQ_ERR_SHAPE;
+  if (!aligned16(sink)) return LCVQ_ERR_ALIGN;
+  return from_hip(launch_mfma_probe((int)iters, sink, as_stream(stream)));
+}
+
 lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
                                   void* stream) {
   if (!packed || !codes) return LCVQ_ERR_NULL;

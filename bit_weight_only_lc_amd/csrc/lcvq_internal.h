@@ -7,7 +7,8 @@ namespace lcvq {
 
 // Kernel ids of the profiling hook (lcvq_profile_next).
 enum { PROF_QUANTIZE = 1, PROF_FWD = 2, PROF_DX = 3, PROF_DW = 4, PROF_GEMV = 5, PROF_BWD_PREP = 6,
-       PROF_GRAM = 7, PROF_PTQ_SWEEP = 8, PROF_READ_PROBE = 9, PROF_LAST = 9 };
+       PROF_GRAM = 7, PROF_PTQ_SWEEP = 8, PROF_READ_PROBE = 9,
+       PROF_MFMA_PROBE = 10, PROF_LAST = 10 };
 // True (once) if the calling thread armed timing for kernel `id`; returns the events.
 bool take_profile(int id, hipEvent_t* start, hipEvent_t* stop);
 
@@ -113,6 +114,7 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
                        uint16_t* Y, int8_t* xq, float* rowinfo, hipStream_t s);
 // Measurement helper: stream `bytes` once in one launch (same-size read ceiling).
 hipError_t launch_read_probe(const void* p, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_mfma_probe(int iters, uint32_t* sink, hipStream_t s);
 // Canonical packed codes [N][K/4] -> the decode layout read with shuffled = 1.
 hipError_t launch_gemv_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* out,
                                hipStream_t s);

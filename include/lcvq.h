@@ -306,6 +306,19 @@ lcvq_status_t lcvq_ptq_init(const float* H, const float* W0, int64_t N, int64_t 
 lcvq_status_t lcvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 /*
+ * Measurement helper, no step of the method: the matrix-core issue ceiling the products are
+ * compared to. One launch of 256 workgroups of 8 waves (2 per SIMD, as the products run);
+ * each wave issues `iters` rounds of 8 independent 32x32x16 bf16 MFMAs (the products' 4 x 2
+ * accumulator blocks) on pseudo-random operands in [-1, -0.5] U [0.5, 1) that alternate
+ * between two sets every round, so that operand bits toggle as when data streams through.
+ * It performs iters * 2^29 floating-point operations and writes one word per workgroup into
+ * `sink` (uint32 [1024], device). Timed with the profiling hook (kernel id 10).
+ *   iters even, 2 <= iters <= 2^24; sink 16-byte aligned.
+ * Errors: LCVQ_ERR_NULL, LCVQ_ERR_SHAPE, LCVQ_ERR_ALIGN, LCVQ_ERR_HIP.
+ */
+lcvq_status_t lcvq_mfma_probe(int64_t iters, uint32_t* sink, void* stream);
+
+/*
  * Profiling hook (changes no result). Arms a one-shot timing of the next launch of one
  * kernel by calls made from this host thread: the kernel is launched with
  * hipExtLaunchKernel between `start_event` and `stop_event` (hipEvent_t handles created
@@ -313,7 +326,7 @@ lcvq_status_t lcvq_read_probe(const void* buf, int64_t bytes, uint32_t* sink, vo
  * 3 dX product, 4 dW product (with the straight-through epilogue), 5 decode product,
  * 6 backward prologue (r = dY 1 and the transposed codes, lcvq_linear_bwd), 7 Gram
  * product (lcvq_hessian), 8 PTQ integer step (lcvq_ptq_init; each call times the first),
- * 9 read probe (lcvq_read_probe).
+ * 9 read probe (lcvq_read_probe), 10 MFMA probe (lcvq_mfma_probe).
  * Passing NULL events disarms. Returns LCVQ_ERR_SHAPE for an unknown kernel_id.
  */
 lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event);

@@ -213,10 +213,10 @@ def test_workspace_sizes_grow_with_shape(L):
 
 
 def test_profile_hook_ids(L):
-    """The timing hook knows kernel ids 1..9; arming with NULL events disarms (no GPU call)."""
-    for kid in (0, 10, -1):
+    """The timing hook knows kernel ids 1..10; arming with NULL events disarms (no GPU call)."""
+    for kid in (0, 11, -1):
         assert L.lcvq_profile_next(kid, None, None) == 2          # LCVQ_ERR_SHAPE
-    for kid in range(1, 10):
+    for kid in range(1, 11):
         assert L.lcvq_profile_next(kid, None, None) == 0
 
 
@@ -297,6 +297,14 @@ def test_ptq_errors(L):
     assert g(U=MIS) == 5
     assert g(wsb=ws - 1) == 6
     assert g(ws=None) == 6
+
+
+def test_mfma_probe_errors(L):
+    assert L.lcvq_mfma_probe(4, None, None) == 1
+    assert L.lcvq_mfma_probe(3, P, None) == 2                  # odd
+    assert L.lcvq_mfma_probe(0, P, None) == 2
+    assert L.lcvq_mfma_probe((1 << 24) + 2, P, None) == 2
+    assert L.lcvq_mfma_probe(4, MIS, None) == 5
 
 
 def test_read_probe_errors(L):

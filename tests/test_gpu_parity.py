@@ -463,6 +463,19 @@ def test_read_probe_reads_every_word(P, nbytes):
     assert got == want
 
 
+def test_mfma_probe_runs_and_is_deterministic(P):
+    """The MFMA ceiling probe (a measurement helper) writes one finite word per workgroup,
+    the same on every call."""
+    s1 = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    s2 = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    P.lcvq_mfma_probe(64, s1)
+    P.lcvq_mfma_probe(64, s2)
+    torch.cuda.synchronize()
+    v = s1[:256].cpu().view(torch.float32)
+    assert torch.isfinite(v).all() and (v != 0).all()
+    assert torch.equal(s1, s2)
+
+
 # Shapes whose forward and dW products have few tiles (at most 128): their contraction is
 # split over up to four workgroups per tile, whose partial tiles a second launch adds in
 # split order before the epilogue.
