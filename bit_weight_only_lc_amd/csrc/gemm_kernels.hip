@@ -190,15 +190,6 @@ __device__ __forceinline__ void split_load(const GemmArgs& a, f32x16 (&acc)[WI][
   }
 }
 
-__device__ __forceinline__ void store_out4(void* out, int f32, int64_t idx, float a, float b, float c, float d) {
-  if (f32) {
-    __builtin_nontemporal_store(f32x4{a, b, c, d},
-                                reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx));
-  } else {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
-  }
-}
-
 // ---- epilogues -----------------------------------------------------------------------
 // Outputs (Y, dX, dWp) are written once and not read again by the kernel: they go out as
 // non-temporal stores, which measured 1-3 us faster per product than ordinary ones.
@@ -221,19 +212,22 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Writes a staged 32 x 32 block (rows = contraction-side index k, columns = output row)
-// transposed to out[row][k] (row stride ld elements), float32 or bf16.
-__device__ __forceinline__ void store_block_rows(const float* S, void* out, int f32, int64_t ld,
-                                                 int row0, int rows, int k0, int K, int lane) {
+// dW's staging area holds a 32 x 32 block as [n][k] (row stride SROWT floats, 16-byte
+// aligned), so that a lane's d-vector (consecutive k of one n) goes in with 16-byte writes
+// and each store's four consecutive k come out with one 16-byte read. The block's rows n
+// go to out[row0 + n][k0 .. k0 + 31]; each group of 8 lanes covers one row.
+constexpr int SROWT = 36;
+__device__ __forceinline__ void store_block_rows_t(const float* S, float* out, int64_t ld,
+                                                   int row0, int rows, int k0, int K,
+                                                   int lane) {
   const int kq = (lane & 7) * 4;
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int rr = it * 8 + (lane >> 3);
     const int row = row0 + rr;
     if (row < rows && k0 + kq < K) {
-      const float v0 = S[(kq + 0) * SROW + rr], v1 = S[(kq + 1) * SROW + rr];
-      const float v2 = S[(kq + 2) * SROW + rr], v3 = S[(kq + 3) * SROW + rr];
-      store_out4(out, f32, (int64_t)row * ld + k0 + kq, v0, v1, v2, v3);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(S + rr * SROWT + kq);
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + (int64_t)row * ld + k0 + kq));
     }
   }
 }
@@ -247,7 +241,7 @@ __device__ __forceinline__ float dge_slope(float w, float alpha, float c) {
   return c * (1.f - t * t);
 }
 
-// store_block_rows for dWp under the DGE estimator: each value is multiplied by the
+// store_block_rows_t for dWp under the DGE estimator: each value is multiplied by the
 // slope at its proxy, read as the same 4 consecutive floats of Wp [N][K]. All four
 // proxy loads are issued before the first store: the compiler cannot move a load of Wp
 // above a store to dWp (they might alias), and one HBM round trip per store would
@@ -271,10 +265,11 @@ __device__ __forceinline__ void store_block_rows_dge(const float* S, float* out,
     const int row = row0 + rr;
     if (row < rows && k0 + kq < K) {
       const int64_t idx = (int64_t)row * ld + k0 + kq;
-      __builtin_nontemporal_store(f32x4{S[(kq + 0) * SROW + rr] * dge_slope(w[it].x, alpha, c),
-                                        S[(kq + 1) * SROW + rr] * dge_slope(w[it].y, alpha, c),
-                                        S[(kq + 2) * SROW + rr] * dge_slope(w[it].z, alpha, c),
-                                        S[(kq + 3) * SROW + rr] * dge_slope(w[it].w, alpha, c)},
+      const f32x4 v = *reinterpret_cast<const f32x4*>(S + rr * SROWT + kq);
+      __builtin_nontemporal_store(f32x4{v[0] * dge_slope(w[it].x, alpha, c),
+                                        v[1] * dge_slope(w[it].y, alpha, c),
+                                        v[2] * dge_slope(w[it].z, alpha, c),
+                                        v[3] * dge_slope(w[it].w, alpha, c)},
                                   reinterpret_cast<f32x4*>(out + idx));
     }
   }
@@ -515,7 +510,7 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
   constexpr int NR = NA + D;                   // + dB partials (first pass)
   constexpr int RROW = NR + 1;
   constexpr int WREG = 12 * 1024;              // per-wave LDS area: staging, then reduction
-  static_assert(32 * RROW * 4 <= WREG && 32 * SROW * 4 <= WREG, "per-wave LDS area");
+  static_assert(32 * RROW * 4 <= WREG && 32 * SROWT * 4 <= WREG, "per-wave LDS area");
   static_assert(NW * WREG + NP * NW * NR * 4 <= (CO == DW_CODES_OFF ? 120 : 28) * 1024,
                 "per-wave areas and sums below A's copy");
   float* S = reinterpret_cast<float*>(smem + wave * WREG);
@@ -574,13 +569,18 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
           zw = valid ? zw : 0u;
           mw = valid ? mw : 0u;
           if (pass == 0) {
+            float o[D];
 #pragma unroll
             for (int jj = 0; jj < D; ++jj) {
               float sum = 0.f;
 #pragma unroll
               for (int e = 0; e < D; ++e) sum = __builtin_fmaf(Aat(e * D + jj), T[e], sum);
-              S[(kr + jj) * SROW + q] = ((mw >> jj) & 1u) ? sum : 0.f;
+              o[jj] = ((mw >> jj) & 1u) ? sum : 0.f;
             }
+#pragma unroll
+            for (int c4 = 0; c4 < D / 4; ++c4)
+              *reinterpret_cast<f32x4*>(S + q * SROWT + kr + 4 * c4) =
+                  f32x4{o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]};
 #pragma unroll
             for (int e = 0; e < D; ++e) dB[e] += valid ? T[e] : 0.f;
           }
@@ -597,7 +597,7 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
             store_block_rows_dge(S, a.dwp, a.dge_wp, a.dge_alpha, a.dge_c, a.K, nb, a.N, kb,
                                  a.K, lane);
           else
-            store_block_rows(S, a.dwp, 1, a.K, nb, a.N, kb, a.K, lane);
+            store_block_rows_t(S, a.dwp, a.K, nb, a.N, kb, a.K, lane);
         }
       }
     // Wave reduction: lanes l and l+32 hold the same entries for different vectors; add
