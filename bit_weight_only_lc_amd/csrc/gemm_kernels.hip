@@ -66,7 +66,7 @@ struct GemmArgs {
   const uint16_t* Lmat[3];     // FWD: X' [M][K]; DW: X [M][K]
   const uint16_t* Rmat[3];     // DX, DW: dY [M][N]
   int npass;
-  const uint32_t* codes;       // FWD: R16 of Z along k; DX: R16 of Z^T along n (blocked)
+  const uint32_t* codes;       // FWD: R16 of Z along k; DX, DW: R16 of Z^T along n (blocked)
   int M, N, K;
   const float* rowvec;         // FWD: beta [M]; DX: r [M]
   const float* A;              // [d][d]
@@ -74,7 +74,6 @@ struct GemmArgs {
   void* out;                   // FWD: Y [M][N]; DX: dX [M][K]
   int out_f32;
   float* dwp;                  // DW: [N][K]
-  const uint8_t* packed;       // DW: canonical codes [N][K/4]
   const uint8_t* mask;         // DW: mask bits [N][K/8]
   float* partials;             // DW: [ntiles][d*d + d]
   const float* dge_wp;         // DW with the DGE estimator: proxies [N][K], else NULL
@@ -482,158 +481,6 @@ __device__ __forceinline__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ
       if (j == 0 && i2 == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       store_block_rows64(S, a.out, a.out_f32, a.K, mb, a.M, kb, a.K, lane);
     }
-}
-
-// Straight-through epilogue on G (rows k, columns n):
-//   dWp[n, g*d+j] = mask * sum_i A[i][j] G[g*d+i, n]
-//   dA[i][j] += G[g*d+i, n] z[n, g*d+j],   dB[i] += G[g*d+i, n]
-// Per-lane partial sums are reduced over the wave through LDS, then over the waves,
-// in a fixed order, into this tile's slot of `partials`.
-// dW LDS map: the double buffer (2 x 64 KiB) during the main loop, then per-wave
-// epilogue areas below 128 KiB; the tile's codes (256 columns n x 64 bytes) and mask bits
-// (256 x 32 bytes) live above it from kernel start, for the straight-through epilogue.
-constexpr int DW_CODES_OFF = 128 * 1024;
-constexpr int DW_MASK_OFF = DW_CODES_OFF + 256 * 64;    // 144 KiB
-constexpr int DW_SMEM = DW_MASK_OFF + 256 * 32;         // 152 KiB
-
-// ALDS: A is read from its copy in LDS (d = 16, and the second phase of a split launch)
-// rather than as scalar loads.
-// CO, MO: LDS offsets of the tile's codes and mask bits; `prow`: the partial row its dA/dB
-// sums go to.
-template <int D, int NW, int WJ, bool ALDS, int CO = DW_CODES_OFF, int MO = DW_MASK_OFF>
-__device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
-                            int lane, int wave, int prow, uint8_t* smem, const float* Alds) {
-  constexpr int NP = D == 16 ? 8 : 1;          // passes over the columns j of dA (d = 16: two
-                                               // columns a pass, so no partial sums spill)
-  constexpr int JW = D / NP;
-  constexpr int NA = D * JW;                   // dA partials per lane and pass
-  constexpr int NR = NA + D;                   // + dB partials (first pass)
-  constexpr int RROW = NR + 1;
-  constexpr int WREG = 12 * 1024;              // per-wave LDS area: staging, then reduction
-  static_assert(32 * RROW * 4 <= WREG && 32 * SROWT * 4 <= WREG, "per-wave LDS area");
-  static_assert(NW * WREG + NP * NW * NR * 4 <= (CO == DW_CODES_OFF ? 120 : 28) * 1024,
-                "per-wave areas and sums below A's copy");
-  float* S = reinterpret_cast<float*>(smem + wave * WREG);
-  float* red = S;                              // reused after the blocks of a pass
-  float* wsum = reinterpret_cast<float*>(smem + NW * WREG);      // [NP][NW][NR]
-  const int q = lane & 31, h = lane >> 5;
-  float dB[D];
-#pragma unroll
-  for (int e = 0; e < D; ++e) dB[e] = 0.f;
-#pragma unroll
-  for (int pass = 0; pass < NP; ++pass) {
-    float dA[NA];
-#pragma unroll
-    for (int x = 0; x < NA; ++x) dA[x] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < WJ; ++j) {
-        const int kb = p0 + wp * 128 + i * 32;
-        const int nb = q0 + wq * 32 * WJ + j * 32;
-        const int n = nb + q;
-        // A: scalar loads through a constant-address-space pointer (d = 16: LDS copy).
-        const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
-        const LCVQ_LDS float* Al = (const LCVQ_LDS float*)Alds;
-        if constexpr (ALDS) asm volatile("" : "+v"(Al));
-        else asm volatile("" : "+s"(Ac));
-        auto Aat = [&](int idx) -> float {
-          if constexpr (ALDS) return Al[idx];
-          else return Ac[idx];
-        };
-        f32x16& c = acc[i][j];
-        __builtin_amdgcn_sched_barrier(0);   // keep each block's work within its block
-        if (pass == 0) {
-          gather_dvectors<D>(c);        // whole d-vectors per lane from here on
-          wave_sync();                  // the previous block's store has read S
-        }
-#pragma unroll
-        for (int v = 0; v < 16 / D; ++v) {
-          const int kr = dvec_row<D>(v, 0, h);       // first row of this vector in the block
-          const int kv = kb + kr;
-          float T[D];
-#pragma unroll
-          for (int e = 0; e < D; ++e) T[e] = c[dvec_reg<D>(v, e)];
-          // The tile's codes and mask bits were brought into LDS at kernel start; the
-          // offsets stay inside the tile's area (n - q0 < 256, kv - p0 < 256) whether or
-          // not the vector is inside G, so the reads need no branch. Rows and columns
-          // past the end of G hold clamped-operand values, not zeros: they must not
-          // reach dA or dB.
-          const bool valid = n < a.N && kv < a.K;
-          const uint8_t* zp = smem + CO + (n - q0) * 64 + ((kv - p0) >> 2);
-          const uint8_t* mp = smem + MO + (n - q0) * 32 + ((kv - p0) >> 3);
-          uint32_t zw, mw;
-          if (D == 4) { zw = zp[0]; mw = (mp[0] >> (kv & 4)) & 0xFu; }
-          if (D == 8) { zw = *reinterpret_cast<const uint16_t*>(zp); mw = mp[0]; }
-          if (D == 16) { zw = *reinterpret_cast<const uint32_t*>(zp); mw = *reinterpret_cast<const uint16_t*>(mp); }
-          zw = valid ? zw : 0u;
-          mw = valid ? mw : 0u;
-          if (pass == 0) {
-            float o[D];
-#pragma unroll
-            for (int jj = 0; jj < D; ++jj) {
-              float sum = 0.f;
-#pragma unroll
-              for (int e = 0; e < D; ++e) sum = __builtin_fmaf(Aat(e * D + jj), T[e], sum);
-              o[jj] = ((mw >> jj) & 1u) ? sum : 0.f;
-            }
-#pragma unroll
-            for (int c4 = 0; c4 < D / 4; ++c4)
-              *reinterpret_cast<f32x4*>(S + q * SROWT + kr + 4 * c4) =
-                  f32x4{o[4 * c4], o[4 * c4 + 1], o[4 * c4 + 2], o[4 * c4 + 3]};
-#pragma unroll
-            for (int e = 0; e < D; ++e) dB[e] += valid ? T[e] : 0.f;
-          }
-#pragma unroll
-          for (int jj = 0; jj < JW; ++jj) {
-            const float zj = (float)((zw >> (2 * (pass * JW + jj))) & 3u);
-#pragma unroll
-            for (int e = 0; e < D; ++e) dA[e * JW + jj] = __builtin_fmaf(T[e], zj, dA[e * JW + jj]);
-          }
-        }
-        if (pass == 0) {
-          wave_sync();
-          if (a.dge_wp)
-            store_block_rows_dge(S, a.dwp, a.dge_wp, a.dge_alpha, a.dge_c, a.K, nb, a.N, kb,
-                                 a.K, lane);
-          else
-            store_block_rows_t(S, a.dwp, a.K, nb, a.N, kb, a.K, lane);
-        }
-      }
-    // Wave reduction: lanes l and l+32 hold the same entries for different vectors; add
-    // them with one exchange, then lane l < 32 writes its row and lanes sum columns.
-#pragma unroll
-    for (int x = 0; x < NA; ++x) dA[x] += __shfl_xor(dA[x], 32);
-    float dBp[D];
-#pragma unroll
-    for (int x = 0; x < D; ++x) dBp[x] = pass == 0 ? dB[x] + __shfl_xor(dB[x], 32) : 0.f;
-    wave_sync();
-    if (lane < 32) {
-#pragma unroll
-      for (int x = 0; x < NA; ++x) red[lane * RROW + x] = dA[x];
-#pragma unroll
-      for (int x = 0; x < D; ++x) red[lane * RROW + NA + x] = dBp[x];
-    }
-    wave_sync();
-    for (int x = lane; x < NR; x += 64) {
-      float sum = 0.f;
-      for (int l = 0; l < 32; ++l) sum += red[l * RROW + x];
-      wsum[(pass * NW + wave) * NR + x] = sum;
-    }
-  }
-  __syncthreads();
-  for (int o = threadIdx.x; o < D * D + D; o += blockDim.x) {
-    float sum = 0.f;
-    if (o < D * D) {
-      const int e = o / D, jj = o % D;
-      const int pass = jj / JW, x = e * JW + (jj % JW);
-      for (int w = 0; w < NW; ++w) sum += wsum[(pass * NW + w) * NR + x];
-    } else {
-      const int x = NA + (o - D * D);
-      for (int w = 0; w < NW; ++w) sum += wsum[w * NR + x];
-    }
-    a.partials[(int64_t)prow * (D * D + D) + o] = sum;
-  }
 }
 
 // ---- ring pipeline for the products with one 2-bit operand (FWD, DX) -----------------
@@ -1107,21 +954,227 @@ __device__ __forceinline__ void dw_mfma(const DwFrags<WJ>& f, f32x16 acc[4][WJ])
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Codes: 16-byte direct loads, 2 per lane; mask: 4-byte direct loads (mask rows are only
-// 8-byte aligned), 4 per lane. Columns past N and k past K read a valid address; those
-// entries are never used.
+// Straight-through epilogue on G (rows k, columns n), its d x d contractions on the
+// matrix cores (idle by then):
+//   dWp[n, k] = mask * sum_k' Mix[k][k'] G[k', n],   Mix = I kron A^T (block diagonal)
+//   dA[i][j]  = sum G[g*d+i, n] z[n, g*d+j] = 2 sum G[g*d+i, n] v(z[n, g*d+j]) - 4 dB[i]
+//   dB[i]     = sum G[g*d+i, n]
+// with v(z) = 2 + z/2, the code operand of the other products. G enters the MFMAs as bf16
+// hi + lo halves, and Mix likewise (hi*hi + lo*hi + hi*lo), so both products keep about
+// 16 bits of G. The mix takes G in the accumulator layout as its B operand (contraction
+// over k). dA contracts over n, the lane index of G: each block's G halves go through the
+// wave's LDS area as [n][k] and come back with transposing reads as the A operand, against
+// v(z) fragments expanded from the tile's transposed code words (the dX product's code
+// layout). Each wave's sums run over all its blocks; the waves' sums are then added in a
+// fixed order into the tile's partial row `prow`.
+// dW LDS map: the double buffer (2 x 64 KiB) during the main loop, then per-wave
+// epilogue areas below 128 KiB; the tile's transposed code words (4 slabs of 256 rows k x
+// 16 bytes) and mask bits (256 columns n x 32 bytes) live above it from kernel start.
+constexpr int DW_CODES_OFF = 128 * 1024;
+constexpr int DW_MASK_OFF = DW_CODES_OFF + 4 * 4096;    // 144 KiB
+constexpr int DW_SMEM = DW_MASK_OFF + 256 * 32;         // 152 KiB
+constexpr int GTROWB = 72;                 // bytes per row n of a staged bf16 half of G
+
+// ALDS: A is read from its copy in LDS (d = 16, and the second phase of a split launch).
+// CO, MO: LDS offsets of the tile's code words and mask bits.
+template <int D, int NW, int WJ, bool ALDS, int CO = DW_CODES_OFF, int MO = DW_MASK_OFF>
+__device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
+                            int lane, int wave, int prow, uint8_t* smem, const float* Alds) {
+  constexpr int WREG = 12 * 1024;              // per-wave LDS area: staging, then reduction
+  constexpr int SBYTES = 32 * SROWT * 4;
+  constexpr int GTB = 32 * GTROWB;
+  constexpr int NO = D * D + D;
+  constexpr int DBS = D == 16 ? 8 : 4;         // dB partial sums per lane
+  constexpr int RRED = 17;                     // row of the wave reduction (16 + pad)
+  static_assert(SBYTES + 2 * GTB <= WREG && (64 * RRED + 16) * 4 <= WREG, "per-wave LDS area");
+  static_assert(NW * WREG + NW * NO * 4 <= (CO == DW_CODES_OFF ? 120 : 28) * 1024,
+                "per-wave areas and sums below A's copy");
+  uint8_t* area = smem + wave * WREG;
+  float* S = reinterpret_cast<float*>(area);
+  uint8_t* GTh = area + SBYTES;
+  uint8_t* GTl = GTh + GTB;
+  float* wsum = reinterpret_cast<float*>(smem + NW * WREG);      // [NW][NO]
+  const int q = lane & 31, h = lane >> 5;
+
+  // Mix operands. In the MFMA over accumulator registers 8t .. 8t+7, slot e of lane half h
+  // holds row k = 16t + 8(e/4) + 4h + e%4 of the block; lane (row q, half h) holds
+  // Mix[q][k] for those k: A[k % d][q % d] inside q's d-vector, else 0.
+  bf16x8 AMh[2], AMl[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+      const int idx = (k % D) * D + q % D;
+      const float av = ALDS ? Alds[idx] : a.A[idx];
+      const float m = k / D == q / D ? av : 0.f;
+      const __bf16 mh = (__bf16)m;
+      AMh[t][e] = mh;
+      AMl[t][e] = (__bf16)(m - (float)mh);
+    }
+  const ExpandK ek = expand_consts(lane);
+  const bool full = p0 + BT <= a.K && q0 + BT <= a.N;
+  f32x16 P;
+  float dBp[DBS];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) P[r] = 0.f;
+#pragma unroll
+  for (int x = 0; x < DBS; ++x) dBp[x] = 0.f;
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < WJ; ++j) {
+      const int kb = p0 + wp * 128 + i * 32;
+      const int nb = q0 + wq * 32 * WJ + j * 32;
+      const int n = nb + q;
+      __builtin_amdgcn_sched_barrier(0);   // keep each block's work within its block
+      f32x16 g = acc[i][j];
+      // Rows and columns past the end of G hold clamped-operand values: they must not
+      // reach dA or dB (their dWp entries are not stored).
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int k = kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          g[r] = n < a.N && k < a.K ? g[r] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int slot = D == 16 ? ((r >> 2) & 1) * 4 + (r & 3) : (r & 3);
+        dBp[slot] += g[r];
+      }
+      uint32_t gh[8], gl[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        gh[p] = pack_bf16x2(g[2 * p], g[2 * p + 1]);
+        gl[p] = pack_bf16x2(g[2 * p] - bf16lo_to_f32(gh[p]), g[2 * p + 1] - bf16hi_to_f32(gh[p]));
+      }
+      const bf16x8 Gh0 = __builtin_bit_cast(bf16x8, u32x4{gh[0], gh[1], gh[2], gh[3]});
+      const bf16x8 Gh1 = __builtin_bit_cast(bf16x8, u32x4{gh[4], gh[5], gh[6], gh[7]});
+      const bf16x8 Gl0 = __builtin_bit_cast(bf16x8, u32x4{gl[0], gl[1], gl[2], gl[3]});
+      const bf16x8 Gl1 = __builtin_bit_cast(bf16x8, u32x4{gl[4], gl[5], gl[6], gl[7]});
+      f32x16 o;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] = 0.f;
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[0], Gh0, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[1], Gh1, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMl[0], Gh0, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMl[1], Gh1, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[0], Gl0, o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[1], Gl1, o, 0, 0, 0);
+      // mask bits of (n, kb .. kb+31): register r of o is row 8(r/4) + 4h + r%4
+      const uint32_t mw =
+          *reinterpret_cast<const uint32_t*>(smem + MO + (n - q0) * 32 + ((kb - p0) >> 3)) >> (4 * h);
+      wave_sync();                    // the previous block's store and reads are done
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = ((mw >> (8 * qq + e)) & 1u) ? o[4 * qq + e] : 0.f;
+        *reinterpret_cast<f32x4*>(S + q * SROWT + 8 * qq + 4 * h) = v;
+        *reinterpret_cast<uint2*>(GTh + q * GTROWB + (8 * qq + 4 * h) * 2) =
+            make_uint2(gh[2 * qq], gh[2 * qq + 1]);
+        *reinterpret_cast<uint2*>(GTl + q * GTROWB + (8 * qq + 4 * h) * 2) =
+            make_uint2(gl[2 * qq], gl[2 * qq + 1]);
+      }
+      wave_sync();
+      // dA over the block's 32 n in two contraction steps of 16: the A operand (rows k,
+      // contraction n) by transposing reads of the staged halves, the B operand (rows n,
+      // columns k) from the code words of rows k = kb .. kb+31.
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int g4 = lane >> 4, t = lane & 15;
+        const int col = 16 * (g4 & 1) + 4 * (t & 3);
+        const int row = 16 * u + 8 * (g4 >> 1) + (t >> 2);
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const LCVQ_LDS uint8_t* bh = (const LCVQ_LDS uint8_t*)GTh;
+        const LCVQ_LDS uint8_t* bl = (const LCVQ_LDS uint8_t*)GTl;
+        const v4i16 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(bh + row * GTROWB + col * 2));
+        const v4i16 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(bh + (row + 4) * GTROWB + col * 2));
+        const v4i16 l0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(bl + row * GTROWB + col * 2));
+        const v4i16 l1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(bl + (row + 4) * GTROWB + col * 2));
+        const bf16x8 Ah = __builtin_bit_cast(bf16x8, v8i16{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]});
+        const bf16x8 Al = __builtin_bit_cast(bf16x8, v8i16{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]});
+        const int nl = nb - q0 + 16 * u;
+        const uint32_t w = codes_word(smem + CO + (nl >> 6) * 4096, kb - p0 + q, (nl >> 4) & 3);
+        const bf16x8 bv = codes_expand(w, ek);
+        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, bv, P, 0, 0, 0);
+        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al, bv, P, 0, 0, 0);
+      }
+      if (a.dge_wp)
+        store_block_rows_dge(S, a.dwp, a.dge_wp, a.dge_alpha, a.dge_c, a.K, nb, a.N, kb, a.K,
+                             lane);
+      else
+        store_block_rows_t(S, a.dwp, a.K, nb, a.N, kb, a.K, lane);
+    }
+
+  // The wave's sums. dB: the lanes of a half hold the same slots (both halves, d = 4).
+#pragma unroll
+  for (int x = 0; x < DBS; ++x) {
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) dBp[x] += __shfl_xor(dBp[x], off);
+    if (D == 4) dBp[x] += __shfl_xor(dBp[x], 32);
+  }
+  float* red = S;                              // [64][RRED] P, then dB of the two halves
+  wave_sync();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[lane * RRED + r] = P[r];
+  if (q == 0) {
+#pragma unroll
+    for (int x = 0; x < DBS; ++x) red[64 * RRED + h * 8 + x] = dBp[x];
+  }
+  wave_sync();
+  // P entry (row k, column k') sits in lane 32 h + k' % 32, register r with
+  // k = 8(r/4) + 4h + r%4; dA[i][j] adds the entries with k = g d + i, k' = g d + j.
+  auto dB_of = [&](int i) -> float {
+    if (D == 8) return red[64 * RRED + (i >> 2) * 8 + (i & 3)];
+    if (D == 4) return red[64 * RRED + i];
+    return red[64 * RRED + ((i >> 2) & 1) * 8 + 4 * (i >> 3) + (i & 3)];
+  };
+  for (int o = lane; o < NO; o += 64) {
+    float v;
+    if (o < D * D) {
+      const int i = o / D, j = o % D;
+      float sum = 0.f;
+      if (D == 8) {
+        for (int g2 = 0; g2 < 4; ++g2) sum += red[(32 * (i >> 2) + 8 * g2 + j) * RRED + 4 * g2 + (i & 3)];
+      } else if (D == 4) {
+        for (int g2 = 0; g2 < 8; ++g2) sum += red[(32 * (g2 & 1) + 4 * g2 + j) * RRED + 4 * (g2 >> 1) + i];
+      } else {
+        for (int g2 = 0; g2 < 2; ++g2)
+          sum += red[(32 * ((i >> 2) & 1) + 16 * g2 + j) * RRED + 4 * (2 * g2 + (i >> 3)) + (i & 3)];
+      }
+      v = 2.f * sum - 4.f * dB_of(i);
+    } else {
+      v = dB_of(o - D * D);
+    }
+    wsum[wave * NO + o] = v;
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < NO; o += blockDim.x) {
+    float sum = 0.f;
+    for (int w = 0; w < NW; ++w) sum += wsum[w * NO + o];
+    a.partials[(int64_t)prow * NO + o] = sum;
+  }
+}
+
+// The tile's transposed code words (the dX product's layout: per 256-row block of k and
+// 64-column stage of n, a 4 KiB slab of 256 rows x 4 R16 words): the four slabs of stages
+// q0/64 .. q0/64 + 3, 16-byte direct loads, 2 per lane. Stages past N read the last one
+// (their G columns are zero). Mask bits: 4-byte direct loads (mask rows are only 8-byte
+// aligned), 4 per lane; columns past N and k past K read a valid address, never used.
 __device__ __forceinline__ void issue_dw_codes(uint8_t* codes_lds, uint8_t* mask_lds,
-                                               const uint8_t* packed, const uint8_t* mask,
+                                               const uint32_t* r16t, const uint8_t* mask,
                                                int N, int K, int p0, int q0, int wave,
                                                int lane) {
+  const int nks = N >> 6;                                // stages along n
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int c = (wave * 2 + i) * 64 + lane;            // 16-byte chunk of the code tile
-    int n = q0 + (c >> 2);
-    n = n < N ? n : N - 1;
-    int kb = p0 + (c & 3) * 64;
-    kb = kb < K ? kb : 0;
-    const uint8_t* src = packed + (int64_t)n * (K >> 2) + (kb >> 2);
+    const int c = (wave * 2 + i) * 64 + lane;            // 16-byte chunk of the 16 KiB
+    int kt = (q0 >> 6) + (c >> 8);
+    kt = kt < nks ? kt : nks - 1;
+    const uint32_t* src = r16t + ((int64_t)(p0 >> 8) * nks + kt) * 1024 + (c & 255) * 4;
     __builtin_amdgcn_global_load_lds(src, (LCVQ_LDS void*)(codes_lds + (wave * 2 + i) * 1024), 16, 0, 0);
   }
 #pragma unroll
@@ -1161,7 +1214,7 @@ void k_gemm_dw(GemmArgs a) {
   if constexpr (SPL == 1) split_range(kt1, split, a.splits, kt0, kt1);
   const DwLaneOffsets lo = dw_lane_offsets(a.N, a.K, p0, q0, lane);
   if constexpr (SPL == 0)                            // for the epilogue
-    issue_dw_codes(smem + DW_CODES_OFF, smem + DW_MASK_OFF, a.packed, a.mask, a.N, a.K, p0, q0,
+    issue_dw_codes(smem + DW_CODES_OFF, smem + DW_MASK_OFF, a.codes, a.mask, a.N, a.K, p0, q0,
                    wave, lane);
 
   f32x16 acc[4][WJ];
@@ -1235,7 +1288,7 @@ constexpr int DW_EPI_NW = 2;
 constexpr int DW_EPI_G = 8 / DW_EPI_NW;
 constexpr int EPI_A_OFF = 28 * 1024;
 constexpr int EPI_CODES_OFF = 32 * 1024;
-constexpr int EPI_MASK_OFF = EPI_CODES_OFF + 256 * 64;
+constexpr int EPI_MASK_OFF = EPI_CODES_OFF + 4 * 4096;
 constexpr int EPI_SMEM = EPI_MASK_OFF + 256 * 32;       // 56 KiB
 template <int D>
 __global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
@@ -1250,7 +1303,7 @@ __global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
   const int v = DW_EPI_NW * g + lw;                       // wave of the 8-wave layout
   const int wp = v / WGQ, wq = v % WGQ;
   for (int vw = lw; vw < 8; vw += DW_EPI_NW)              // the whole tile's codes and mask
-    issue_dw_codes(smem + EPI_CODES_OFF, smem + EPI_MASK_OFF, a.packed, a.mask, a.N, a.K, p0,
+    issue_dw_codes(smem + EPI_CODES_OFF, smem + EPI_MASK_OFF, a.codes, a.mask, a.N, a.K, p0,
                    q0, vw, lane);
   float* Alds = reinterpret_cast<float*>(smem + EPI_A_OFF);
   for (int i = tid; i < D * D; i += DW_EPI_NW * 64) Alds[i] = a.A[i];
@@ -1569,7 +1622,7 @@ hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16
 }
 
 hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_t* dy,
-                          const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
+                          const uint16_t* dy_lo, const uint32_t* r16t, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, const float* dge_wp,
                           float dge_alpha, bool reduce, void* split_ws, hipStream_t s) {
@@ -1585,7 +1638,7 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
   }
   a.A = A;
   a.M = M; a.N = N; a.K = K;
-  a.dwp = dWp; a.packed = packed; a.mask = mask; a.partials = partials;
+  a.dwp = dWp; a.codes = r16t; a.mask = mask; a.partials = partials;
   a.dge_wp = dge_wp;
   a.dge_alpha = dge_alpha;
   a.dge_c = dge_wp ? (float)((double)dge_alpha / (2.0 * tanh((double)dge_alpha / 2.0))) : 0.f;

@@ -286,27 +286,24 @@ lcvq_status_t linear_bwd_impl(const void* dY, const void* X, lcvq_dtype_t dt, in
   uint16_t* dy_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.dy_lo) : nullptr;
   uint16_t* x_hi = f32 ? reinterpret_cast<uint16_t*>(ws + w.x_hi) : nullptr;
   uint16_t* x_lo = f32 ? reinterpret_cast<uint16_t*>(ws + w.x_lo) : nullptr;
-  // prologue and (when dX is wanted) the transposed codes in one launch
-  const int64_t rblocks = dX ? ((K + 255) / 256) * (N / 64) : 0;
+  // prologue and the transposed codes (read by dW's epilogue and by dX) in one launch
+  const int64_t rblocks = ((K + 255) / 256) * (N / 64);
   const bool merged = M + rblocks <= kMaxBlocks256;
   hipError_t e = merged ? launch_bwd_prep(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi, x_lo,
-                                          packed, dX ? r16t : nullptr, s)
+                                          packed, r16t, s)
                         : launch_bwd_prologue(dY, X, f32, M, N, K, r, dy_hi, dy_lo, x_hi,
                                               x_lo, s);
+  if (e == hipSuccess && !merged) e = launch_codes_to_r16t(packed, N, K, r16t, s);
   if (e != hipSuccess) return LCVQ_ERR_HIP;
   const uint16_t* dyb = f32 ? dy_hi : static_cast<const uint16_t*>(dY);
   const uint16_t* xb = f32 ? x_hi : static_cast<const uint16_t*>(X);
   // dW first; with dX wanted, the dX product then also reduces dW's dA/dB partials
   // (saving the reduction's own launch), otherwise a small kernel does.
   void* split = gemm_split_bytes(K, N, M) ? static_cast<void*>(ws + w.split) : nullptr;
-  e = launch_gemm_dw(xb, x_lo, dyb, dy_lo, packed, mask, A, (int)M, (int)N, (int)K, d, dWp,
+  e = launch_gemm_dw(xb, x_lo, dyb, dy_lo, r16t, mask, A, (int)M, (int)N, (int)K, d, dWp,
                      partials, dA, dB, Wp, alpha, !dX, split, s);
   if (e != hipSuccess) return LCVQ_ERR_HIP;
   if (dX) {
-    if (!merged) {
-      e = launch_codes_to_r16t(packed, N, K, r16t, s);
-      if (e != hipSuccess) return LCVQ_ERR_HIP;
-    }
     e = launch_gemm_dx(r16t, dyb, dy_lo, r, A, B, (int)M, (int)N, (int)K, d, dX, f32, partials,
                        dA, dB, s);
     if (e != hipSuccess) return LCVQ_ERR_HIP;

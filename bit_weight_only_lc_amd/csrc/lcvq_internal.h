@@ -75,8 +75,9 @@ hipError_t launch_gemm_dx(const uint32_t* r16t, const uint16_t* dy, const uint16
                           const float* r, const float* A, const float* B, int M, int N, int K,
                           int d, void* dX, bool f32, const float* dw_partials, float* dA,
                           float* dB, hipStream_t s);
+// dW reads the codes as the transposed code words r16t (launch_codes_to_r16t's layout).
 hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_t* dy,
-                          const uint16_t* dy_lo, const uint8_t* packed, const uint8_t* mask,
+                          const uint16_t* dy_lo, const uint32_t* r16t, const uint8_t* mask,
                           const float* A, int M, int N, int K, int d, float* dWp,
                           float* partials, float* dA, float* dB, const float* dge_wp,
                           float dge_alpha, bool reduce, void* split_ws, hipStream_t s);
