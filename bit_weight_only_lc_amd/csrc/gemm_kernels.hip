@@ -193,12 +193,12 @@ __device__ __forceinline__ void split_load(const GemmArgs& a, f32x16 (&acc)[WI][
 // Outputs (Y, dX, dWp) are written once and not read again by the kernel: they go out as
 // non-temporal stores, which measured 1-3 us faster per product than ordinary ones.
 // Accumulator layout (32x32 block): lane l holds column l%32 and, in register r, row
-// 8*(r/4) + 4*(l/32) + r%4. For DX and DW the rows run along the d-vectors: a swap of
-// register halves between lanes l and l^32 (gather_dvectors) gives every lane whole
-// d-vectors, the d x d mix runs in registers, and the results go through a per-wave
-// LDS area (rows of 33 floats) only to be written back transposed, each group of 8
-// lanes covering consecutive elements of one output row. The forward epilogue stages
-// row-major strips the same way for 16-byte stores.
+// 8*(r/4) + 4*(l/32) + r%4. For DX and DW the rows run along the d-vectors, and the d x d
+// mix of every 32-row block is one block-diagonal 32 x 32 matrix: it runs on the matrix
+// cores with the accumulator block as the B operand, and the results go through a
+// per-wave LDS area only to be written back transposed, each group of 8 lanes covering
+// consecutive elements of one output row. The forward epilogue stages row-major strips
+// the same way for 16-byte stores.
 
 constexpr int SROW = 33;                  // padded row of the staging area (floats)
 
@@ -366,67 +366,54 @@ __device__ __forceinline__ void store_block_rows64(const float* S, void* out, in
   }
 }
 
-// Whole d-vectors per lane. In a 32x32 accumulator block, lane (column l%32, half
-// h = l/32) holds rows 8*(r/4) + 4h + r%4 in register r: for d = 4 these are complete
-// d-vectors already, for d = 8 and 16 each vector is split between lanes l and l^32.
-// Swapping registers 0..7 of the upper half with registers 8..15 of the lower half
-// (v_permlane32_swap: the first operand's lanes 32..63 trade places with the second
-// operand's lanes 0..31) leaves every lane with whole vectors: d = 8, vectors 2h and
-// 2h+1; d = 16, vector h. Element e of local vector v then sits in register
-// 4*bsel + e%4 with bsel as in dvec_reg.
-template <int D>
-__device__ __forceinline__ void gather_dvectors(f32x16& c) {
-  if (D == 4) return;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(c[r]),
-                                                    __float_as_uint(c[r + 8]), false, false);
-    c[r] = __uint_as_float(s[0]);
-    c[r + 8] = __uint_as_float(s[1]);
-  }
-}
-template <int D>
-__host__ __device__ constexpr int dvec_reg(int v, int e) {
-  const int j = e >> 2;
-  const int bsel = D == 4 ? v : D == 8 ? (j << 1) | v : ((j & 1) << 1) | (j >> 1);
-  return 4 * bsel + (e & 3);
-}
-// Row (index k within the block) of element e of local vector v in lane half h.
-template <int D>
-__device__ __forceinline__ int dvec_row(int v, int e, int h) {
-  const int g = D == 4 ? 2 * v + h : D == 8 ? 2 * h + v : h;
-  return g * D + e;
-}
-
 // dX[m, g*d+i] = 2 sum_j A[i][j] C[g*d+j, m] + (B[i] - 4 sum_j A[i][j]) r[m]
-// where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m).
-// The d x d product runs on whole vectors in registers (gather_dvectors); the results
-// go through the wave's LDS area only for the transposed store. Blocks are taken in
-// pairs along k, so that each output row receives 128 contiguous bytes (bf16) per
-// store instruction.
+// where C = sum_n v(z[n, k]) dY[m, n] is the accumulator (rows k, columns m). The d x d
+// mix 2 (I kron A) runs on the matrix cores with C in the accumulator layout as its B
+// operand (bf16 hi + lo halves of C and of the mix: hi*hi + lo*hi + hi*lo, about 16 bits
+// of C kept); the results go through the wave's LDS area only for the transposed store.
+// Blocks are taken in pairs along k, so that each output row receives 128 contiguous
+// bytes (bf16) per store instruction.
 constexpr int DX_WAVE_LDS = 64 * SROW * 4;   // per-wave staging area: 64 x 33 floats
 
 template <int D, int WI, int WJ>
 __device__ __forceinline__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ], int p0, int q0, int wp, int wq,
                             int lane, float* S, const float* Alds) {
   static_assert(WI % 2 == 0, "k blocks are staged in pairs");
-  constexpr int NV = 16 / D;                  // whole vectors per lane and block
-  constexpr int IIU = D == 16 ? 4 : D;        // output rows unrolled together
-  // row terms B[i] - 4 sum_j A[i][j] (d <= 8; d = 16 keeps them in LDS), read as scalar
-  // loads through constant-address-space pointers
-  float bp[D];
-  if constexpr (D != 16) {
-    const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
-    const LCVQ_CONST float* Bc = (const LCVQ_CONST float*)a.B;
+  const int q = lane & 31, h = lane >> 5;
+  // Mix operands: lane (row q, half h) holds, for the MFMA over accumulator registers
+  // 8t .. 8t+7 (slot e: row k = 16t + 8(e/4) + 4h + e%4 of C), the entry 2 A[q % d][k % d]
+  // of 2 (I kron A) inside q's d-vector, else 0, as bf16 hi + lo halves. (d = 16: A from its
+  // LDS copy.)
+  bf16x8 AMh[2], AMl[2];
 #pragma unroll
-    for (int i = 0; i < D; ++i) {
-      float s = 0.f;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int j = 0; j < D; ++j) s += Ac[i * D + j];
-      bp[i] = Bc[i] - 4.f * s;
+    for (int e = 0; e < 8; ++e) {
+      const int k = 16 * t + 8 * (e >> 2) + 4 * h + (e & 3);
+      const int idx = (q % D) * D + k % D;
+      const float av = D == 16 ? Alds[idx] : a.A[idx];
+      const float m = k / D == q / D ? 2.f * av : 0.f;
+      const __bf16 mh = (__bf16)m;
+      AMh[t][e] = mh;
+      AMl[t][e] = (__bf16)(m - (float)mh);
+    }
+  // Row terms B[i] - 4 sum_j A[i][j] of this lane's output rows: register r holds row
+  // 8(r/4) + 4h + r%4, i.e. i = that row mod d, slot rslot(r).
+  constexpr int NBP = D == 16 ? 8 : 4;
+  auto rslot = [](int r) { return D == 16 ? ((r >> 2) & 1) * 4 + (r & 3) : (r & 3); };
+  float bpl[NBP];
+#pragma unroll
+  for (int x = 0; x < NBP; ++x) {
+    const int i = D == 16 ? 8 * (x >> 2) + 4 * h + (x & 3) : (D == 8 ? 4 * h + x : x);
+    if constexpr (D == 16) {
+      bpl[x] = Alds[D * D + i];
+    } else {
+      float sa = 0.f;
+#pragma unroll
+      for (int j = 0; j < D; ++j) sa += a.A[i * D + j];
+      bpl[x] = a.B[i] - 4.f * sa;
     }
   }
-  const int q = lane & 31, h = lane >> 5;
   // r of this lane's rows, loaded before the first store (vector loads and stores share
   // one counter, so a load issued after a store is waited for together with it)
   float rmv[WJ];
@@ -443,36 +430,33 @@ __device__ __forceinline__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ
       const int kb = p0 + wp * 32 * WI + i2 * 64;
       const int mb = q0 + wq * 32 * WJ + j * 32;
       const float rm = rmv[j];
-      // Re-read A for every block pair instead of keeping d*d values live across the
-      // unrolled sequence: d <= 8 through a constant-address-space pointer, so that the
-      // reads are scalar loads from the scalar cache (through a generic pointer they would
-      // be vector loads, each waited for); d = 16 from the copy in LDS.
-      const LCVQ_CONST float* Ac = (const LCVQ_CONST float*)a.A;
-      const LCVQ_LDS float* Al = (const LCVQ_LDS float*)Alds;
-      if constexpr (D == 16) asm volatile("" : "+v"(Al));
-      else asm volatile("" : "+s"(Ac));
-      auto Aat = [&](int idx) -> float {
-        if constexpr (D == 16) return Al[idx];
-        else return Ac[idx];
-      };
       wave_sync();
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        f32x16& c = acc[2 * i2 + half][j];
-        gather_dvectors<D>(c);
+        const f32x16 c = acc[2 * i2 + half][j];
+        uint32_t ch[8], cl[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          ch[p] = pack_bf16x2(c[2 * p], c[2 * p + 1]);
+          cl[p] = pack_bf16x2(c[2 * p] - bf16lo_to_f32(ch[p]), c[2 * p + 1] - bf16hi_to_f32(ch[p]));
+        }
+        const bf16x8 Ch0 = __builtin_bit_cast(bf16x8, u32x4{ch[0], ch[1], ch[2], ch[3]});
+        const bf16x8 Ch1 = __builtin_bit_cast(bf16x8, u32x4{ch[4], ch[5], ch[6], ch[7]});
+        const bf16x8 Cl0 = __builtin_bit_cast(bf16x8, u32x4{cl[0], cl[1], cl[2], cl[3]});
+        const bf16x8 Cl1 = __builtin_bit_cast(bf16x8, u32x4{cl[4], cl[5], cl[6], cl[7]});
+        f32x16 o;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] = 0.f;
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[0], Ch0, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[1], Ch1, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMl[0], Ch0, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMl[1], Ch1, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[0], Cl0, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[1], Cl1, o, 0, 0, 0);
         float* Sh = S + half * 32 * SROW;
-        // d = 16: the output rows go four at a time, with their A rows and row terms read
-        // from LDS, instead of all 256 coefficients at once (which spills).
 #pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll IIU
-          for (int ii = 0; ii < D; ++ii) {
-            float s = 0.f;
-#pragma unroll
-            for (int e = 0; e < D; ++e) s = __builtin_fmaf(Aat(ii * D + e), c[dvec_reg<D>(v, e)], s);
-            const float bpi = D == 16 ? Al[D * D + ii] : bp[ii];
-            Sh[dvec_row<D>(v, ii, h) * SROW + q] = __builtin_fmaf(2.f, s, bpi * rm);
-          }
+        for (int r = 0; r < 16; ++r)
+          Sh[(8 * (r >> 2) + 4 * h + (r & 3)) * SROW + q] = __builtin_fmaf(bpl[rslot(r)], rm, o[r]);
       }
       wave_sync();
       // Settle the loads issued before the epilogue (r, and dW's partials when this tile
