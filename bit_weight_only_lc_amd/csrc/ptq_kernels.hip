@@ -414,14 +414,16 @@ __global__ __launch_bounds__(256) void k_ptq_start(const double* __restrict__ pa
 // The codes of the workgroup's rows stay in LDS (2 bits each) for the later blocks'
 // feedback, and go out packed (canonical layout) at the end.
 __device__ __forceinline__ bf16x8 codes8_bf16(uint32_t two_bytes) {
-  // 8 codes (2 bits each, little-endian) -> 8 bf16 values 0, 1, 2, 3 (exact)
+  // 8 codes (2 bits each, little-endian) -> 8 bf16 values 0, 1, 2, 3 (exact), two per
+  // dword by a byte-table lookup (v_perm_b32): the low bytes of bf16 0, 1, 2, 3 are
+  // 00 80 00 40 (table LO, byte c) and the high bytes 00 3F 40 40 (table HI, byte 4 + c).
+  constexpr uint32_t LO = 0x40008000u, HI = 0x40403F00u;
   u32x4 o;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const uint32_t c0 = (two_bytes >> (4 * p)) & 3u, c1 = (two_bytes >> (4 * p + 2)) & 3u;
-    const uint32_t b0 = c0 ? (0x3F80u + ((c0 >> 1) << 7) + (c0 == 3u ? 0x40u : 0u)) : 0u;
-    const uint32_t b1 = c1 ? (0x3F80u + ((c1 >> 1) << 7) + (c1 == 3u ? 0x40u : 0u)) : 0u;
-    o[p] = b0 | (b1 << 16);
+    const uint32_t sel = (c0 | (c1 << 16)) * 0x0101u + 0x04000400u;   // c0, 4+c0, c1, 4+c1
+    o[p] = __builtin_amdgcn_perm(HI, LO, sel);
   }
   return __builtin_bit_cast(bf16x8, o);
 }
