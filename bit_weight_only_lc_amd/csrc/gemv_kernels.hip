@@ -80,16 +80,23 @@ __device__ __forceinline__ void xprime_chunk(uint4 a, uint4 b, const float* As, 
     frexpf(amax, &E);          // amax = f * 2^E, f in [0.5, 1)
     ex = 14 - E;               // |X' * 2^ex| < 2^14
   }
+  // q = rint(X' 2^ex) split as q = 256 h + l, l in [-128, 127]. Adding 1.5 * 2^23 + 128
+  // rounds X' 2^ex + 128 to an integer t = q + 128 in the float's low mantissa bits
+  // (|t| < 2^22; the bits are 0x4B400000 + t): byte 1 of them is h = t >> 8 (mod 256) and
+  // byte 0 is t mod 256 = l + 128, i.e. l with its top bit flipped. Column 4*bb + tt goes
+  // to dword tt, byte bb; v_perm_b32 gathers the bytes, two columns per step.
+  uint32_t fb[16];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) hi[t] = lo[t] = 0;
+  for (int u = 0; u < 16; ++u) fb[u] = __float_as_uint(ldexpf(xp[u], ex) + 12583040.f);
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int q = (int)__builtin_rintf(ldexpf(xp[u], ex));
-    const int l = ((q + 128) & 255) - 128;
-    const int h = (q - l) >> 8;
-    const int tt = u & 3, bb = u >> 2;          // column 4*bb + tt -> dword tt, byte bb
-    hi[tt] |= (uint32_t)(h & 255) << (8 * bb);
-    lo[tt] |= (uint32_t)(l & 255) << (8 * bb);
+  for (int tt = 0; tt < 4; ++tt) {
+    // bytes k of columns tt, 4 + tt (low half) and 8 + tt, 12 + tt (high half)
+    const uint32_t l01 = __builtin_amdgcn_perm(fb[4 + tt], fb[tt], 0x0c0c0400u);
+    const uint32_t l23 = __builtin_amdgcn_perm(fb[12 + tt], fb[8 + tt], 0x0c0c0400u);
+    const uint32_t h01 = __builtin_amdgcn_perm(fb[4 + tt], fb[tt], 0x0c0c0501u);
+    const uint32_t h23 = __builtin_amdgcn_perm(fb[12 + tt], fb[8 + tt], 0x0c0c0501u);
+    lo[tt] = __builtin_amdgcn_perm(l23, l01, 0x05040100u) ^ 0x80808080u;
+    hi[tt] = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
   }
   scale = ldexpf(1.f, -ex);
 }
