@@ -405,12 +405,17 @@ __global__ __launch_bounds__(256) void k_ptq_start(const double* __restrict__ pa
 // One workgroup sweeps 16 rows of W0 over K, 64 columns at a time. For a column block:
 //  1. its feedback from all earlier codes, F[r][j] = sum_{i < j0} c_ri U_ij, on the bf16
 //     matrix cores: codes (exact) times U^T's hi and lo halves (summed in two float32
-//     accumulators, added at the end); wave w covers the block's columns 16 w .. 16 w + 15;
-//  2. wave 0 then walks the block's 64 columns in order, 4 lanes per row, each lane
-//     holding 16 columns' running value t = (q - b e) / s - F - (feedback inside the
-//     block): the owner of column k broadcasts t_k, every lane rounds it the same way
+//     accumulators, added at the end); a feedback wave covers 16 of the block's columns;
+//  2. the walk over the block's columns in order, 4 lanes per row, each lane holding 16
+//     columns' running value t = (q - b e) / s - F - (feedback inside the block): the
+//     owner of column k broadcasts t_k, every lane rounds it the same way
 //     (c = clip(rint(t), 0, 3)), and the four lanes update their later columns with
 //     U's diagonal block (fp32, LDS). The owner accumulates the sums of a = U^T c.
+// The walk of block b (wave 0) runs while waves 1-3 form block b + 1's feedback from the
+// blocks before b (wave 1 two of the four 16-column tiles, waves 2 and 3 one each); after
+// a barrier they add block b's own codes (two steps) and write it.
+// F and the diagonal block are double-buffered. The feedback steps run in ascending order
+// either way, so F is the same as one pass over i < j0 would give.
 // The codes of the workgroup's rows stay in LDS (2 bits each) for the later blocks'
 // feedback, and go out packed (canonical layout) at the end.
 __device__ __forceinline__ bf16x8 codes8_bf16(uint32_t two_bytes) {
@@ -428,7 +433,8 @@ __device__ __forceinline__ bf16x8 codes8_bf16(uint32_t two_bytes) {
   return __builtin_bit_cast(bf16x8, o);
 }
 
-__global__ __launch_bounds__(256) void k_ptq_sweep(const float* __restrict__ Q,
+constexpr int SW_WAVES = 4;                 // wave 0 walks, waves 1-3 form the feedback
+__global__ __launch_bounds__(SW_WAVES * 64) void k_ptq_sweep(const float* __restrict__ Q,
                                                    const float* __restrict__ e,
                                                    const float* __restrict__ D,
                                                    const uint16_t* __restrict__ Ut_hi,
@@ -439,8 +445,8 @@ __global__ __launch_bounds__(256) void k_ptq_sweep(const float* __restrict__ Q,
                                                    double* __restrict__ part,
                                                    const PtqState* __restrict__ st) {
   __shared__ __attribute__((aligned(16))) uint8_t cl[SWR * (PTQ_MAX_K / 4)];   // 64 KiB
-  __shared__ float F[SWR][PB + 4];
-  __shared__ __attribute__((aligned(16))) float Ub[PB][PB];
+  __shared__ float F[2][SWR][PB + 4];
+  __shared__ __attribute__((aligned(16))) float Ub[2][PB][PB];
   __shared__ double red[64][4];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -449,67 +455,74 @@ __global__ __launch_bounds__(256) void k_ptq_sweep(const float* __restrict__ Q,
   const float s = (float)st->s, b = (float)st->b;
   const float inv_s = 1.f / s;
   uint8_t* out = st->cur ? codes0 : codes1;        // the candidate buffer
-  // sweep lanes (wave 0): row r = lane / 4, columns 16 sub .. 16 sub + 15 of each block
+  // walk lanes (wave 0): row r = lane / 4, columns 16 sub .. 16 sub + 15 of each block
   const int r = lane >> 2, sub = lane & 3;
+  // feedback waves: tiles ft0 (and 3 for wave 1) of 16 columns of the block
+  const int ft0 = wave - 1;
   float sG = 0.f, sS1 = 0.f, sS2 = 0.f, sT1 = 0.f;
-  for (int j0 = 0; j0 < K; j0 += PB) {
-    // 1. feedback of the earlier codes on this block's columns
-    {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
-      const int jc = j0 + 16 * wave + (lane & 15);               // B column of this lane
-      const uint16_t* bh = Ut_hi + (int64_t)jc * K + 8 * (lane >> 4);
-      const uint16_t* bl = Ut_lo + (int64_t)jc * K + 8 * (lane >> 4);
-      const uint8_t* ca = cl + (lane & 15) * KB + 2 * (lane >> 4);
-      // Steps of 32 rows in groups of FG: all of a group's loads are issued before its
-      // matrix-core products (one memory round trip per group, not two per step), and the
-      // hi and lo products go to separate accumulators.
-      constexpr int FG = 8;
-      int i0 = 0;
-      for (; i0 + 32 * FG <= j0; i0 += 32 * FG) {
-        bf16x8 h[FG], l[FG];
-        uint32_t cw[FG];
+  const int nb = K / PB;
+
+  // Feedback of the codes i in [ia, ib) on columns j1 + 16 ft .. + 15, accumulated in
+  // order into acc (U^T hi) and accl (U^T lo). Steps of 32 rows in groups of FG: all of a
+  // group's loads are issued before its matrix-core products.
+  auto feedback = [&](int ft, int j1, int ia, int ib, f32x4& acc, f32x4& accl) {
+    const int jc = j1 + 16 * ft + (lane & 15);                   // B column of this lane
+    const uint16_t* bh = Ut_hi + (int64_t)jc * K + 8 * (lane >> 4);
+    const uint16_t* bl = Ut_lo + (int64_t)jc * K + 8 * (lane >> 4);
+    const uint8_t* ca = cl + (lane & 15) * KB + 2 * (lane >> 4);
+    constexpr int FG = 8;
+    int i0 = ia;
+    for (; i0 + 32 * FG <= ib; i0 += 32 * FG) {
+      bf16x8 h[FG], l[FG];
+      uint32_t cw[FG];
 #pragma unroll
-        for (int u = 0; u < FG; ++u) {
-          h[u] = *reinterpret_cast<const bf16x8*>(bh + i0 + 32 * u);
-          l[u] = *reinterpret_cast<const bf16x8*>(bl + i0 + 32 * u);
-          cw[u] = *reinterpret_cast<const uint16_t*>(ca + (i0 + 32 * u) / 4);
-        }
-#pragma unroll
-        for (int u = 0; u < FG; ++u) {
-          const bf16x8 a = codes8_bf16(cw[u]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h[u], acc, 0, 0, 0);
-          accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l[u], accl, 0, 0, 0);
-        }
-      }
-      for (; i0 < j0; i0 += 64) {                                // j0 is a multiple of 64
-        bf16x8 h[2], l[2];
-        uint32_t cw[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          h[u] = *reinterpret_cast<const bf16x8*>(bh + i0 + 32 * u);
-          l[u] = *reinterpret_cast<const bf16x8*>(bl + i0 + 32 * u);
-          cw[u] = *reinterpret_cast<const uint16_t*>(ca + (i0 + 32 * u) / 4);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const bf16x8 a = codes8_bf16(cw[u]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h[u], acc, 0, 0, 0);
-          accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l[u], accl, 0, 0, 0);
-        }
+      for (int u = 0; u < FG; ++u) {
+        h[u] = *reinterpret_cast<const bf16x8*>(bh + i0 + 32 * u);
+        l[u] = *reinterpret_cast<const bf16x8*>(bl + i0 + 32 * u);
+        cw[u] = *reinterpret_cast<const uint16_t*>(ca + (i0 + 32 * u) / 4);
       }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] += accl[v];
-      // D layout: lane l holds rows 4 (l / 16) + v, column l % 16
-#pragma unroll
-      for (int v = 0; v < 4; ++v) F[4 * (lane >> 4) + v][16 * wave + (lane & 15)] = acc[v];
-      // U's diagonal block for this column block
-      const float* ud = Udiag + (int64_t)(j0 / PB) * PB * PB;
-      for (int x = tid; x < PB * PB / 4; x += 256)
-        reinterpret_cast<f32x4*>(&Ub[0][0])[x] = reinterpret_cast<const f32x4*>(ud)[x];
+      for (int u = 0; u < FG; ++u) {
+        const bf16x8 a = codes8_bf16(cw[u]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h[u], acc, 0, 0, 0);
+        accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l[u], accl, 0, 0, 0);
+      }
     }
-    __syncthreads();
-    // 2. the ordered walk over the block's columns
+    for (; i0 < ib; i0 += 64) {                                  // ia, ib multiples of 64
+      bf16x8 h[2], l[2];
+      uint32_t cw[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        h[u] = *reinterpret_cast<const bf16x8*>(bh + i0 + 32 * u);
+        l[u] = *reinterpret_cast<const bf16x8*>(bl + i0 + 32 * u);
+        cw[u] = *reinterpret_cast<const uint16_t*>(ca + (i0 + 32 * u) / 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 a = codes8_bf16(cw[u]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, h[u], acc, 0, 0, 0);
+        accl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, l[u], accl, 0, 0, 0);
+      }
+    }
+  };
+  auto load_diag = [&](int blk, int buf) {                       // waves 1-3
+    const float* ud = Udiag + (int64_t)blk * PB * PB;
+    for (int x = tid - 64; x < PB * PB / 4; x += (SW_WAVES - 1) * 64)
+      reinterpret_cast<f32x4*>(&Ub[buf][0][0])[x] = reinterpret_cast<const f32x4*>(ud)[x];
+  };
+
+  // block 0: no earlier codes
+  if (wave > 0) {
+    for (int x = tid - 64; x < SWR * (PB + 4); x += (SW_WAVES - 1) * 64) (&F[0][0][0])[x] = 0.f;
+    load_diag(0, 0);
+  }
+  __syncthreads();
+  for (int blk = 0; blk < nb; ++blk) {
+    const int j0 = blk * PB, cur = blk & 1;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, accl = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc3 = {0.f, 0.f, 0.f, 0.f}, accl3 = {0.f, 0.f, 0.f, 0.f};   // wave 1: tile 3
     if (wave == 0) {
+      // the ordered walk over this block's columns
       const int n = n0 + r;
       const int jl0 = 16 * sub;
       float t[16], qv[16], ev[16], dv[16];
@@ -519,7 +532,7 @@ __global__ __launch_bounds__(256) void k_ptq_sweep(const float* __restrict__ Q,
         qv[u] = Q[(int64_t)n * K + j];
         ev[u] = e[j];
         dv[u] = D[j];
-        t[u] = (qv[u] - b * ev[u]) * inv_s - F[r][jl0 + u];
+        t[u] = (qv[u] - b * ev[u]) * inv_s - F[cur][r][jl0 + u];
       }
       uint32_t packed = 0;                         // this lane's 16 codes, 2 bits each
 #pragma unroll
@@ -541,14 +554,34 @@ __global__ __launch_bounds__(256) void k_ptq_sweep(const float* __restrict__ Q,
         // later columns of this lane: t_j -= U_kj c. U_kj is 0 for j < k and 1 for
         // j = k, whose values have been used already, so no column test is needed.
 #pragma unroll
-        for (int u = 0; u < 16; ++u) t[u] -= Ub[k][jl0 + u] * c;
+        for (int u = 0; u < 16; ++u) t[u] -= Ub[cur][k][jl0 + u] * c;
       }
       *reinterpret_cast<uint32_t*>(cl + r * KB + (j0 + jl0) / 4) = packed;
+    } else if (blk + 1 < nb) {
+      // the next block's feedback from the blocks before this one, and its diagonal block
+      feedback(ft0, j0 + PB, 0, j0, acc, accl);
+      if (wave == 1) feedback(3, j0 + PB, 0, j0, acc3, accl3);
+      load_diag(blk + 1, cur ^ 1);
+    }
+    __syncthreads();
+    if (wave > 0 && blk + 1 < nb) {
+      // this block's codes (written by the walk) on the next block's columns
+      feedback(ft0, j0 + PB, j0, j0 + PB, acc, accl);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] += accl[v];
+      // D layout: lane l holds rows 4 (l / 16) + v, column l % 16
+#pragma unroll
+      for (int v = 0; v < 4; ++v) F[cur ^ 1][4 * (lane >> 4) + v][16 * ft0 + (lane & 15)] = acc[v];
+      if (wave == 1) {
+        feedback(3, j0 + PB, j0, j0 + PB, acc3, accl3);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) F[cur ^ 1][4 * (lane >> 4) + v][48 + (lane & 15)] = acc3[v] + accl3[v];
+      }
     }
     __syncthreads();
   }
   // 3. the codes out (canonical packed rows), and this workgroup's sums
-  for (int x = tid; x < SWR * KB / 16; x += 256) {
+  for (int x = tid; x < SWR * KB / 16; x += SW_WAVES * 64) {
     const int rr = x / (KB / 16), c16 = (x % (KB / 16)) * 16;
     *reinterpret_cast<uint4*>(out + (int64_t)(n0 + rr) * KB + c16) =
         *reinterpret_cast<const uint4*>(cl + rr * KB + c16);
@@ -697,7 +730,7 @@ hipError_t launch_ptq_init(const float* H, const float* W0, int N, int K, float 
                      e, N, K, st);
   const int nwg = N / SWR;
   for (int it = 0; it < iters; ++it) {
-    LCVQ_LAUNCH(PROF_PTQ_SWEEP, k_ptq_sweep, dim3(nwg), dim3(256), 0, s, Q, e, D, Ut_hi, Ut_lo,
+    LCVQ_LAUNCH(PROF_PTQ_SWEEP, k_ptq_sweep, dim3(nwg), dim3(SW_WAVES * 64), 0, s, Q, e, D, Ut_hi, Ut_lo,
                 Udiag, N, K, c0, c1, spart, st);
     hipLaunchKernelGGL(k_ptq_solve, dim3(1), dim3(256), 0, s, spart, nwg, it, st, obj_out);
   }
