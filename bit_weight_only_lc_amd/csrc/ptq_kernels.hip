@@ -96,9 +96,9 @@ __global__ __launch_bounds__(256) void k_ptq_reverse(const float* __restrict__ H
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
-__global__ __launch_bounds__(PB) void k_chol_diag(float* __restrict__ A, int K, int j0,
-                                                  PtqState* st) {
-  const int t = threadIdx.x;
+// Thread t < 64 (one wave) holds row j0 + t of the block.
+__device__ __forceinline__ void chol_diag_body(float* __restrict__ A, int K, int j0,
+                                               PtqState* st, int t) {
   float* row = A + (int64_t)(j0 + t) * K + j0;
   float x[PB];
 #pragma unroll
@@ -143,6 +143,10 @@ __global__ __launch_bounds__(PB) void k_chol_diag(float* __restrict__ A, int K, 
   }
   if (bad && t == 0) st->bad = 1;
 }
+__global__ __launch_bounds__(PB) void k_chol_diag(float* __restrict__ A, int K, int j0,
+                                                  PtqState* st) {
+  chol_diag_body(A, K, j0, st, threadIdx.x);
+}
 
 // Rows i >= j0 + 64 of the panel: x L11^T = a, one row per thread, forward substitution
 // with the factored diagonal block from LDS.
@@ -176,8 +180,12 @@ __global__ __launch_bounds__(256) void k_chol_panel(float* __restrict__ A, int K
 }
 
 // Trailing update A[i][k] -= sum_c L[i][j0+c] L[k][j0+c] for j0 + 64 <= k <= i, on
-// 64 x 64 tiles of the lower triangle; each thread updates a 4 x 4 patch.
-__global__ __launch_bounds__(256) void k_chol_update(float* __restrict__ A, int K, int j0) {
+// 64 x 64 tiles of the lower triangle; each thread updates a 4 x 4 patch. Workgroup 0
+// updates tile (0, 0), the next step's diagonal block, and then factors it (its first
+// wave, after a barrier): the look-ahead that keeps the serial factor of step s + 1 off the
+// critical path while the other workgroups finish step s's update.
+__global__ __launch_bounds__(256) void k_chol_update(float* __restrict__ A, int K, int j0,
+                                                     PtqState* st) {
   __shared__ float Li[PB][PB + 4];
   __shared__ float Lk[PB][PB + 4];
   const int j1 = j0 + PB;
@@ -216,6 +224,10 @@ __global__ __launch_bounds__(256) void k_chol_update(float* __restrict__ A, int 
       const int i = i0 + ri + u, k = k0 + rk + v;
       if (k <= i) A[(int64_t)i * K + k] -= acc[u][v];
     }
+  if (blockIdx.x == 0) {                          // uniform per workgroup
+    __syncthreads();                              // the tile's updated entries
+    if (tid < PB) chol_diag_body(A, K, j1, st, tid);
+  }
 }
 
 // ------------------------------------------------------------------ U, D from L
@@ -712,13 +724,15 @@ hipError_t launch_ptq_init(const float* H, const float* W0, int N, int K, float 
 
   hipLaunchKernelGGL(k_ptq_delta, dim3(1), dim3(256), 0, s, H, K, damp, st);
   hipLaunchKernelGGL(k_ptq_reverse, dim3(K), dim3(256), 0, s, H, K, st, A);
+  // The first diagonal block on its own; every later one is factored by the update of the
+  // step before (its workgroup 0).
+  hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(PB), 0, s, A, K, 0, st);
   for (int j0 = 0; j0 < K; j0 += PB) {
-    hipLaunchKernelGGL(k_chol_diag, dim3(1), dim3(PB), 0, s, A, K, j0, st);
     const int rows = K - j0 - PB;
     if (rows > 0) {
       hipLaunchKernelGGL(k_chol_panel, dim3((rows + 255) / 256), dim3(256), 0, s, A, K, j0);
       const int T = rows / PB;
-      hipLaunchKernelGGL(k_chol_update, dim3(T * (T + 1) / 2), dim3(256), 0, s, A, K, j0);
+      hipLaunchKernelGGL(k_chol_update, dim3(T * (T + 1) / 2), dim3(256), 0, s, A, K, j0, st);
     }
   }
   hipLaunchKernelGGL(k_ptq_udu_out, dim3(K / PB, K / PB), dim3(256), 0, s, A, K, Ut32, Ut_hi,
