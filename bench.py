@@ -204,9 +204,14 @@ def time_layers(torch, P, L, mats, M, d, dev, seed, reps, warm_s):
             prod[pname] = {"ms": round(t, 4),
                            "tflops": round(2.0 * M * N * K / (t * 1e-3) / 1e12, 1)}
         fl = 6.0 * M * N * K
+        # The library's tile rule: the forward takes 128 x 256 tiles where its 256 x 256
+        # tiles fill at most half of the 256 CUs and the 128-row ones more than half.
+        tq = -(-N // 256)
+        fwd_rows = 128 if -(-M // 256) * tq <= 128 < -(-M // 128) * tq else 256
         out[name] = {"N": N, "K": K, "ms": round(ms, 4),
                      "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
-                     "tiles_fwd_dx_dw": [-(-M // 256) * -(-N // 256),
+                     "fwd_tile": f"{fwd_rows}x256",
+                     "tiles_fwd_dx_dw": [-(-M // fwd_rows) * tq,
                                          -(-K // 256) * -(-M // 256),
                                          -(-K // 256) * -(-N // 256)],
                      "products": prod}

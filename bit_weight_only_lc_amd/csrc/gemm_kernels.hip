@@ -12,7 +12,8 @@
 //
 // Two kernel templates cover the three products (k_gemm_ring: forward and dX; k_gemm_dw).
 // C (P x Q) = sum_r L[p, r] R[q, r] is computed in 256 x 256 tiles (32x32x16 bf16 MFMA,
-// contraction staged through LDS in steps of 64):
+// contraction staged through LDS in steps of 64; the forward also in 128 x 256 tiles when
+// the larger ones would leave most CUs idle):
 //   FWD: L = X' (bf16 rows m),        R = codes (rows n)       8 waves, 4-slot LDS ring
 //   DX : L = codes transposed (rows k), R = dY (bf16 rows m)   8 waves, 4-slot LDS ring
 //   DW : L = X^T (rows k), R = dY^T (rows n); both tiles arrive in their natural layout
@@ -50,11 +51,13 @@ enum { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
 // With 4 waves (one per SIMD) each wave owns a 128 x 128 quarter of the tile: 16
 // accumulator blocks of 32 x 32 (256 values, held in the accumulation registers) and 4
 // + 4 operand fragments per contraction sub-step, i.e. fewer LDS bytes per MFMA.
-template <int OP, int NWV = 8> struct Tiling {
+// The forward can also run 128 x 256 tiles (BPT = 128 rows of X'), for launches whose
+// 256 x 256 tiles would leave most of the chip idle: 8 waves of 64 x 64 (2 x 2 blocks).
+template <int OP, int NWV = 8, int BPT = 256> struct Tiling {
   static constexpr int NW = NWV;
-  static constexpr int WGP = NW == 4 ? 2 : (OP == OP_DX ? 4 : LCVQ_FWD_WGP);
+  static constexpr int WGP = BPT == 128 ? 2 : (NW == 4 ? 2 : (OP == OP_DX ? 4 : LCVQ_FWD_WGP));
   static constexpr int WGQ = NW / WGP;
-  static constexpr int WI = 8 / WGP;
+  static constexpr int WI = BPT / 32 / WGP;
   static constexpr int WJ = 8 / WGQ;
 };
 
@@ -91,6 +94,7 @@ struct GemmArgs {
   // epilogue. splits = 1: one launch, one workgroup per tile.
   int splits;
   float* split_ws;
+  int bpt;                     // forward: tile rows along P, 256 or 128 (host side)
 };
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -478,17 +482,18 @@ __device__ __forceinline__ void epilogue_dx(const GemmArgs& a, f32x16 acc[WI][WJ
 constexpr int RING = 4;
 constexpr int CODEB = 256 * 16;
 constexpr int SLOTB = TILEB + CODEB;
-// Loads per lane and stage: RPW/8 bf16-tile loads (8 rows each) + RPW/16 code loads
-// (16 rows of 16 bytes each), RPW = 256 / NW rows per wave.
-template <int NW> constexpr int ring_loads() { return (256 / NW) / 8 + (256 / NW) / 16; }
+// Loads per lane and stage: RB/NW/8 bf16-tile loads (8 rows each) + 256/NW/16 code loads
+// (16 rows of 16 bytes each); the bf16 tile has RB rows (256, or 128 for the forward's
+// 128 x 256 tiles), the code tile always 256.
+template <int NW, int RB = 256> constexpr int ring_loads() { return (RB / NW) / 8 + (256 / NW) / 16; }
 
-// Wave w fills tile rows [RPW w, RPW (w+1)) and the code words of the same rows.
-template <int NW>
+// Wave w fills bf16-tile rows [RB/NW w, RB/NW (w+1)) and code rows [256/NW w, 256/NW (w+1)).
+template <int NW, int RB = 256>
 __device__ __forceinline__ void issue_ring_stage(uint8_t* slot, const uint16_t* mat, int64_t ld,
                                                  int row0, int rows_total, int k0,
                                                  const uint32_t* codes, int rowblock, int nk,
                                                  int kt, int wave, int lane) {
-  constexpr int RPW = 256 / NW;
+  constexpr int RPW = RB / NW, CPW = 256 / NW;
 #pragma unroll
   for (int i = 0; i < RPW / 8; ++i) {
     const int r = wave * RPW + i * 8 + (lane >> 3);
@@ -500,8 +505,8 @@ __device__ __forceinline__ void issue_ring_stage(uint8_t* slot, const uint16_t* 
   }
   const uint32_t* slab = codes + ((int64_t)rowblock * nk + kt) * 1024;
 #pragma unroll
-  for (int h = 0; h < RPW / 16; ++h) {
-    const int w0 = (wave * RPW + h * 16) * 4;           // first word of these 16 rows
+  for (int h = 0; h < CPW / 16; ++h) {
+    const int w0 = (wave * CPW + h * 16) * 4;           // first word of these 16 rows
     __builtin_amdgcn_global_load_lds(slab + w0 + lane, (LCVQ_LDS void*)(slot + TILEB + w0 * 4), 4, 0, 0);
   }
 }
@@ -626,9 +631,9 @@ __device__ __forceinline__ void reduce_dw_partials(const GemmArgs& a, int tile, 
   }
 }
 
-template <int NW>
+template <int NW, int RB = 256>
 __device__ __forceinline__ void wait_vm_stages(int stages_after) {
-  constexpr int L = ring_loads<NW>();
+  constexpr int L = ring_loads<NW, RB>();
   static_assert(2 * L < 64, "vmcnt range");
   if (stages_after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
   else if (stages_after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
@@ -638,14 +643,16 @@ __device__ __forceinline__ void wait_vm_stages(int stages_after) {
 // ---- the kernel ----------------------------------------------------------------------
 // FWD and dX: NW waves (4 or 8), 4-slot ring of direct global->LDS loads.
 // SPL: 0 one workgroup per tile; 1 phase 1 of a split launch (forward only; phase 2 is
-// k_gemm_fwd_epi).
-template <int OP, int D, int NW, int SPL = 0>
+// k_gemm_fwd_epi). BPT: tile rows along P (128 only for the forward without a split).
+template <int OP, int D, int NW, int SPL = 0, int BPT = 256>
 __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void k_gemm_ring(GemmArgs a) {
   static_assert(SPL == 0 || (SPL == 1 && OP == OP_FWD), "phase 2 of a split forward is k_gemm_fwd_epi");
-  using T = Tiling<OP, NW>;
+  static_assert(BPT == 256 || (BPT == 128 && OP == OP_FWD && SPL == 0 && NW == 8), "128-row tiles: forward only");
+  using T = Tiling<OP, NW, BPT>;
   constexpr int WI = T::WI, WJ = T::WJ;
   constexpr bool CL = OP == OP_DX;               // codes are the L operand for dX
+  constexpr int RB = CL ? 256 : BPT;             // rows of the bf16 operand's tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOTB];   // 144 KiB
   int tp, tq, tile;
   // The bf16 operand's panels (2 MiB each at K or N = 4096) outweigh the code panels
@@ -658,7 +665,7 @@ void k_gemm_ring(GemmArgs a) {
   } else if (!map_tile<GR>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
     return;
   }
-  const int p0 = tp * BT, q0 = tq * BT;
+  const int p0 = tp * BPT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wp = wave / T::WGQ, wq = wave % T::WGQ;
   const int nkt = (a.R + BK - 1) / BK;               // stages of the whole contraction
@@ -685,8 +692,8 @@ void k_gemm_ring(GemmArgs a) {
 #pragma unroll
     for (int st = 0; st < RING - 1; ++st)
       if (st < nk)
-        issue_ring_stage<NW>(smem + st * SLOTB, mat, ld, row0, a.M, (kt0 + st) * BK, a.codes,
-                             rowblock, nkt, kt0 + st, wave, lane);
+        issue_ring_stage<NW, RB>(smem + st * SLOTB, mat, ld, row0, a.M, (kt0 + st) * BK, a.codes,
+                                 rowblock, nkt, kt0 + st, wave, lane);
     // The barrier of each stage sits before its last sub-step, so that the first
     // fragments of the next stage are read and expanded under that sub-step's MFMAs
     // instead of after a barrier at the stage boundary. Plain s_barrier: __syncthreads()
@@ -695,7 +702,7 @@ void k_gemm_ring(GemmArgs a) {
     using F = RingFrags<CL, WI, WJ>;
     F f[2];
     const ExpandK ek = expand_consts(lane);
-    wait_vm_stages<NW>(nk - 1 < 2 ? nk - 1 : 2);
+    wait_vm_stages<NW, RB>(nk - 1 < 2 ? nk - 1 : 2);
     asm volatile("s_barrier" ::: "memory");
     ring_read<CL, WI, WJ>(smem, 0, wp, wq, lane, f[0]);
     ring_expand<CL, WI, WJ>(f[0], ek);
@@ -709,12 +716,12 @@ void k_gemm_ring(GemmArgs a) {
       // Stage kt + 1 must have landed (stage kt + 2 may still be in flight); after the
       // barrier every wave is past sub-step 2 of stage kt, so stage kt - 1's slot is free
       // for stage kt + 3.
-      wait_vm_stages<NW>(kt + 2 < nk ? 1 : 0);
+      wait_vm_stages<NW, RB>(kt + 2 < nk ? 1 : 0);
       asm volatile("s_barrier" ::: "memory");
       if (kt + RING - 1 < nk)
-        issue_ring_stage<NW>(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
-                             (kt0 + kt + RING - 1) * BK, a.codes, rowblock, nkt,
-                             kt0 + kt + RING - 1, wave, lane);
+        issue_ring_stage<NW, RB>(smem + ((kt + RING - 1) % RING) * SLOTB, mat, ld, row0, a.M,
+                                 (kt0 + kt + RING - 1) * BK, a.codes, rowblock, nkt,
+                                 kt0 + kt + RING - 1, wave, lane);
       // Sub-step 3, with stage kt + 1's first fragments read and expanded under it (on
       // the last stage this reads a free slot; the values are not used).
       ring_read<CL, WI, WJ>(smem + ((kt + 1) % RING) * SLOTB, 0, wp, wq, lane, f[0]);
@@ -1439,6 +1446,19 @@ size_t gemm_split_bytes(int64_t P, int64_t Q, int64_t R) {
   return nt * sp * BT * BT * 4;
 }
 
+// The forward runs 128 x 256 tiles, without a split, when its 256 x 256 tiles would
+// occupy at most half of the 256 CUs and the 128-row tiles occupy more than half: at
+// 8192 tokens and N = 1024 that is 256 tiles in one round, where the split's float32
+// partial tiles cost a write and a read of 64 MiB.
+bool gemm_fwd_half_tiles(int64_t M, int64_t N) {
+  const int64_t tq = (N + BT - 1) / BT;
+  return ((M + BT - 1) / BT) * tq <= 128 && ((M + 127) / 128) * tq > 128;
+}
+
+size_t gemm_fwd_split_bytes(int64_t M, int64_t N, int64_t K) {
+  return gemm_fwd_half_tiles(M, N) ? 0 : gemm_split_bytes(M, N, K);
+}
+
 template <int OP, int SPL>
 static hipError_t launch_op1(GemmArgs& a, int d, int grid, hipStream_t s);
 
@@ -1447,6 +1467,20 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   a.tilesP = (a.P + BT - 1) / BT;
   a.tilesQ = (a.Q + BT - 1) / BT;
   a.ntiles = a.tilesP * a.tilesQ;
+  if constexpr (OP == OP_FWD) {
+    if (a.bpt == 128) {
+      static_assert(LCVQ_FWD_WAVES == 8, "the forward's 128-row tiles use the 8-wave layout");
+      a.tilesP = (a.P + 127) / 128;
+      a.ntiles = a.tilesP * a.tilesQ;
+      const dim3 g(((a.ntiles + 7) / 8) * 8), b(8 * 64);
+      switch (d) {
+        case 4: LCVQ_LAUNCH(PROF_FWD, (k_gemm_ring<OP_FWD, 4, 8, 0, 128>), g, b, 0, s, a); break;
+        case 8: LCVQ_LAUNCH(PROF_FWD, (k_gemm_ring<OP_FWD, 8, 8, 0, 128>), g, b, 0, s, a); break;
+        default: LCVQ_LAUNCH(PROF_FWD, (k_gemm_ring<OP_FWD, 16, 8, 0, 128>), g, b, 0, s, a); break;
+      }
+      return hipGetLastError();
+    }
+  }
   if constexpr (OP == OP_DX) {
     return launch_op1<OP, 0>(a, d, ((a.ntiles + 7) / 8) * 8, s);
   } else {
@@ -1573,7 +1607,9 @@ hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint
                            const float* beta, int M, int N, int K, int d, void* Y, bool y_f32,
                            void* split_ws, hipStream_t s) {
   GemmArgs a = {};
-  set_splits(a, M, N, K, split_ws);
+  a.bpt = gemm_fwd_half_tiles(M, N) ? 128 : 256;
+  if (a.bpt == 256) set_splits(a, M, N, K, split_ws);
+  else a.splits = 1;
   a.P = M; a.Q = N; a.R = K;
   a.Lmat[0] = xs; a.Lmat[1] = xs_lo;
   a.npass = xs_lo ? 2 : 1;

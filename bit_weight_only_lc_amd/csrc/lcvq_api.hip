@@ -75,7 +75,7 @@ inline FwdWs fwd_ws(int64_t M, int64_t N, int64_t K, bool f32) {
   w.r16 = w.beta + up((size_t)M * 4);
   w.xs_lo = w.r16 + up(r16_bytes(N, K));
   w.split = w.xs_lo + (f32 ? up((size_t)M * K * 2) : 0);
-  w.total = w.split + up(gemm_split_bytes(M, N, K));   // split partials of few-tile shapes
+  w.total = w.split + up(gemm_fwd_split_bytes(M, N, K));   // split partials of few-tile shapes
   return w;
 }
 
@@ -246,7 +246,7 @@ lcvq_status_t lcvq_linear_fwd(const void* X, lcvq_dtype_t xdt, int64_t M, int64_
     if (e == hipSuccess) e = launch_fwd_prologue(X, f32, M, K, A, B, d, xs, xs_lo, beta, s);
   }
   if (e != hipSuccess) return LCVQ_ERR_HIP;
-  void* split = gemm_split_bytes(M, N, K) ? static_cast<void*>(ws + w.split) : nullptr;
+  void* split = gemm_fwd_split_bytes(M, N, K) ? static_cast<void*>(ws + w.split) : nullptr;
   return from_hip(launch_gemm_fwd(xs, xs_lo, r16, beta, (int)M, (int)N, (int)K, d, Y, f32, split,
                                   s));
 }

@@ -62,6 +62,10 @@ int gemm_tiles(int64_t P, int64_t Q);
 // Q = N, R = M) products.
 int gemm_splits(int64_t P, int64_t Q, int64_t R);
 size_t gemm_split_bytes(int64_t P, int64_t Q, int64_t R);
+// The forward instead runs 128 x 256 tiles without a split where those fill more than half
+// of the CUs (gemm_fwd_half_tiles); gemm_fwd_split_bytes is its workspace for partials.
+bool gemm_fwd_half_tiles(int64_t M, int64_t N);
+size_t gemm_fwd_split_bytes(int64_t M, int64_t N, int64_t K);
 // Rows of dA/dB partials ([rows][d*d + d] floats) the dW product writes for M tokens and a
 // weight [N, K]: one per tile, or DW_EPI_G per tile when its contraction is split.
 int dw_partial_rows(int64_t M, int64_t N, int64_t K);

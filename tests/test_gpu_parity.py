@@ -476,13 +476,15 @@ def test_mfma_probe_runs_and_is_deterministic(P):
     assert torch.equal(s1, s2)
 
 
-# Shapes whose forward and dW products have few tiles (at most 128): their contraction is
-# split over up to four workgroups per tile, whose partial tiles a second launch adds in
-# split order before the epilogue.
+# Shapes whose forward and dW products have few tiles (at most 128 of 256 x 256): their
+# contraction is split over up to four workgroups per tile, whose partial tiles a second
+# launch adds in split order before the epilogue; except that a forward whose 128 x 256
+# tiles occupy more than half of the CUs runs those, without a split.
 SPLIT_SHAPES = [(1100, 320, 2112, 8, "bf16"),     # forward 4 ways, dW 2 ways, ragged M, K
                 (2500, 192, 1216, 16, "f32"),     # forward 2 ways, dW 4 ways, float32
                 (1031, 64, 4096, 4, "bf16"),      # one tile column, forward 4 ways
-                (4000, 1280, 1024, 8, "bf16")]    # forward 80 tiles 2 ways, dW 4 ways
+                (4000, 1280, 1024, 8, "bf16"),    # forward 160 tiles of 128 x 256, dW 4 ways
+                (8100, 960, 1088, 16, "f32")]     # forward 256 tiles of 128 x 256, ragged M, N, K
 
 
 @pytest.mark.parametrize("M,N,K,d,xdt", SPLIT_SHAPES)
