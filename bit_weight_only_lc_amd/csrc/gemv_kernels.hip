@@ -429,27 +429,44 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   }
   __syncthreads();
 
-  // 4. the products
-  const bool has_a = nl < M;                       // A-operand lane row m = lane % 16
+  // 4. the products. A-operand lane row m = lane % 16: rows m >= M read row 0's X' (a
+  //    valid address); they only reach output rows m >= M, whose block scales are zero and
+  //    which are never stored. Each block's 8 fragments and scales are read one block
+  //    ahead, so that the LDS reads run under the previous block's MFMAs instead of each
+  //    step waiting for its own two.
   f32x4 acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint8_t* ri = gsm + XB + kq * 32;
-  const uint8_t* xl = gsm + (kq * M + nl) * 16;
+  const uint8_t* xl = gsm + (kq * M + (nl < M ? nl : 0)) * 16;
+  struct Frags {
+    i32x4 h[4], l[4];
+    f32x4 r0, r1;
+  };
+  auto read_frags = [&](int kb, Frags& f) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f.h[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s) * 4 * M * 16);
+      f.l[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s + 1) * 4 * M * 16);
+    }
+    f.r0 = *reinterpret_cast<const f32x4*>(ri + kb * 128);
+    f.r1 = *reinterpret_cast<const f32x4*>(ri + kb * 128 + 16);
+  };
+  Frags fr[2];
+  read_frags(min(wave, nkb - 1), fr[0]);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int u = 0; u < KSW; ++u) {
     const int kb = wave + GWF * u;
     if (kb >= nkb) break;
+    if (u + 1 < KSW) read_frags(min(kb + GWF, nkb - 1), fr[(u + 1) & 1]);
+    __builtin_amdgcn_sched_barrier(0);             // keep the reads ahead of the MFMAs
+    const Frags& f = fr[u & 1];
     i32x4 chi[RG], clo[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) chi[g] = clo[g] = i32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {                  // fragments read one step at a time
-      i32x4 h = {0, 0, 0, 0}, l = {0, 0, 0, 0};
-      if (has_a) {
-        h = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s) * 4 * M * 16);
-        l = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s + 1) * 4 * M * 16);
-      }
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
         const uint32_t w = cw[u][g][s];
@@ -458,19 +475,17 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
         bz[1] = (int)((w >> 2) & 0x03030303u);
         bz[2] = (int)((w >> 4) & 0x03030303u);
         bz[3] = (int)((w >> 6) & 0x03030303u);
-        chi[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(h, bz, chi[g], 0, 0, 0);
-        clo[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(l, bz, clo[g], 0, 0, 0);
+        chi[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.h[s], bz, chi[g], 0, 0, 0);
+        clo[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(f.l[s], bz, clo[g], 0, 0, 0);
       }
     }
-    const f32x4 r0 = *reinterpret_cast<const f32x4*>(ri + kb * 128);
-    const f32x4 r1 = *reinterpret_cast<const f32x4*>(ri + kb * 128 + 16);
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       f32x4& a = acc[g];
-      a[0] = __builtin_fmaf((float)(chi[g][0] * 256 + clo[g][0]), r0[0], a[0] + r0[1]);
-      a[1] = __builtin_fmaf((float)(chi[g][1] * 256 + clo[g][1]), r0[2], a[1] + r0[3]);
-      a[2] = __builtin_fmaf((float)(chi[g][2] * 256 + clo[g][2]), r1[0], a[2] + r1[1]);
-      a[3] = __builtin_fmaf((float)(chi[g][3] * 256 + clo[g][3]), r1[2], a[3] + r1[3]);
+      a[0] = __builtin_fmaf((float)(chi[g][0] * 256 + clo[g][0]), f.r0[0], a[0] + f.r0[1]);
+      a[1] = __builtin_fmaf((float)(chi[g][1] * 256 + clo[g][1]), f.r0[2], a[1] + f.r0[3]);
+      a[2] = __builtin_fmaf((float)(chi[g][2] * 256 + clo[g][2]), f.r1[0], a[2] + f.r1[1]);
+      a[3] = __builtin_fmaf((float)(chi[g][3] * 256 + clo[g][3]), f.r1[2], a[3] + f.r1[3]);
     }
   }
   // 5. the GWF partial sums of each row, in wave order
