@@ -46,6 +46,13 @@ bool gemv_fused_path(int M, int K) { return gemv_fused(M, K); }
 // X' = X (I kron A) and X (1 kron B) in float32, agree on the block's exponent
 // (|X' 2^e| < 2^14) and return the two int8 limbs in MFMA byte order (column 4b + t in
 // dword t, byte b), the scale 2^-e and the block's partial beta.
+// A lane move within rows of 16 lanes (DPP control CTRL; every source lane is valid).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+
 template <int D>
 __device__ __forceinline__ void xprime_chunk(uint4 a, uint4 b, const float* As, const float* Bs,
                                              uint32_t (&hi)[4], uint32_t (&lo)[4],
@@ -69,11 +76,19 @@ __device__ __forceinline__ void xprime_chunk(uint4 a, uint4 b, const float* As, 
 #pragma unroll
     for (int i = 0; i < D; ++i) bsum = __builtin_fmaf(x[v0 + i], Bs[i], bsum);
   }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    amax = fmaxf(amax, __shfl_xor(amax, o));
-    bsum += __shfl_xor(bsum, o);
-  }
+  // Max and sum over the 16 lanes, as the xor butterfly o = 8, 4, 2, 1 with DPP lane moves
+  // instead of LDS permutes: rotating a row of 16 lanes by 8 is xor 8; after that step
+  // lanes i and i ^ 8 hold the same value, so a rotation by 4 brings lane i the value of
+  // lane i ^ 4; xor 2 and xor 1 are quad permutations. Every lane ends with the same sum,
+  // bit for bit, as the butterfly gives.
+  amax = fmaxf(amax, dpp_f32<0x128>(amax));        // row_ror:8
+  bsum += dpp_f32<0x128>(bsum);
+  amax = fmaxf(amax, dpp_f32<0x124>(amax));        // row_ror:4
+  bsum += dpp_f32<0x124>(bsum);
+  amax = fmaxf(amax, dpp_f32<0x4E>(amax));         // quad_perm [2, 3, 0, 1]
+  bsum += dpp_f32<0x4E>(bsum);
+  amax = fmaxf(amax, dpp_f32<0xB1>(amax));         // quad_perm [1, 0, 3, 2]
+  bsum += dpp_f32<0xB1>(bsum);
   int ex = 0;
   if (amax > 0.f) {
     int E;
@@ -411,6 +426,18 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   for (int i = t; i < nkb * 16; i += GWF * 64)
     if ((i & 15) >= M) ris[i] = make_float2(0.f, 0.f);
   __syncthreads();
+  // With two or more chunks per thread, d <= 8 and one row group per workgroup (two row
+  // groups keep to 128 VGPRs), A and B are copied to registers once: read from LDS inside
+  // the loop they would be read again for every chunk (the X' stores in between may alias
+  // them, as far as the compiler can tell).
+  constexpr bool AREG = XI > 1 && D <= 8 && RG == 1;
+  float Ar[AREG ? D * D + D : 1];
+  if constexpr (AREG) {
+#pragma unroll
+    for (int i = 0; i < D * D + D; ++i) Ar[i] = As[i];   // B follows A in LDS
+  }
+  const float* Au = AREG ? Ar : As;
+  const float* Bu = AREG ? Ar + D * D : Bs;
 #pragma unroll
   for (int j = 0; j < XI; ++j) {
     const int i = t + j * GWF * 64;
@@ -419,7 +446,7 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
     const int m = gm % M, kb = gm / M;
     uint32_t hi[4], lo[4];
     float scale, bsum;
-    xprime_chunk<D>(xv[j][0], xv[j][1], As, Bs, hi, lo, scale, bsum);
+    xprime_chunk<D>(xv[j][0], xv[j][1], Au, Bu, hi, lo, scale, bsum);
     const int q = kc >> 2, s = kc & 3;
     *reinterpret_cast<uint4*>(gsm + (((kb * 8 + 2 * s) * 4 + q) * M + m) * 16) =
         make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -429,39 +456,23 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   }
   __syncthreads();
 
-  // 4. the products. A-operand lane row m = lane % 16: rows m >= M read row 0's X' (a
-  //    valid address); they only reach output rows m >= M, whose block scales are zero and
-  //    which are never stored. Each block's 8 fragments and scales are read one block
-  //    ahead, so that the LDS reads run under the previous block's MFMAs instead of each
-  //    step waiting for its own two.
+  // 4. the products. A-operand lane row m = lane % 16. With one row group per workgroup,
+  //    each block's 8 fragments and scales are read one block ahead, so that the LDS
+  //    reads run under the previous block's MFMAs instead of each step waiting for its
+  //    own two; rows m >= M then read row 0's X' (a valid address): they only reach
+  //    output rows m >= M, whose block scales are zero and which are never stored. With
+  //    two row groups the workgroups must fit two to a CU (128 VGPRs), which leaves no
+  //    room for the second set of fragments: those read each step's two fragments as it
+  //    comes, rows m >= M as zeros.
   f32x4 acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint8_t* ri = gsm + XB + kq * 32;
-  const uint8_t* xl = gsm + (kq * M + (nl < M ? nl : 0)) * 16;
   struct Frags {
     i32x4 h[4], l[4];
     f32x4 r0, r1;
   };
-  auto read_frags = [&](int kb, Frags& f) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      f.h[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s) * 4 * M * 16);
-      f.l[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s + 1) * 4 * M * 16);
-    }
-    f.r0 = *reinterpret_cast<const f32x4*>(ri + kb * 128);
-    f.r1 = *reinterpret_cast<const f32x4*>(ri + kb * 128 + 16);
-  };
-  Frags fr[2];
-  read_frags(min(wave, nkb - 1), fr[0]);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int u = 0; u < KSW; ++u) {
-    const int kb = wave + GWF * u;
-    if (kb >= nkb) break;
-    if (u + 1 < KSW) read_frags(min(kb + GWF, nkb - 1), fr[(u + 1) & 1]);
-    __builtin_amdgcn_sched_barrier(0);             // keep the reads ahead of the MFMAs
-    const Frags& f = fr[u & 1];
+  auto block_mfma = [&](const Frags& f, int u) {
     i32x4 chi[RG], clo[RG];
 #pragma unroll
     for (int g = 0; g < RG; ++g) chi[g] = clo[g] = i32x4{0, 0, 0, 0};
@@ -486,6 +497,49 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
       a[1] = __builtin_fmaf((float)(chi[g][1] * 256 + clo[g][1]), f.r0[2], a[1] + f.r0[3]);
       a[2] = __builtin_fmaf((float)(chi[g][2] * 256 + clo[g][2]), f.r1[0], a[2] + f.r1[1]);
       a[3] = __builtin_fmaf((float)(chi[g][3] * 256 + clo[g][3]), f.r1[2], a[3] + f.r1[3]);
+    }
+  };
+  if constexpr (RG == 1) {
+    const uint8_t* xl = gsm + (kq * M + (nl < M ? nl : 0)) * 16;
+    auto read_frags = [&](int kb, Frags& f) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f.h[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s) * 4 * M * 16);
+        f.l[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s + 1) * 4 * M * 16);
+      }
+      f.r0 = *reinterpret_cast<const f32x4*>(ri + kb * 128);
+      f.r1 = *reinterpret_cast<const f32x4*>(ri + kb * 128 + 16);
+    };
+    Frags fr[2];
+    read_frags(min(wave, nkb - 1), fr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < KSW; ++u) {
+      const int kb = wave + GWF * u;
+      if (kb >= nkb) break;
+      if (u + 1 < KSW) read_frags(min(kb + GWF, nkb - 1), fr[(u + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);           // keep the reads ahead of the MFMAs
+      block_mfma(fr[u & 1], u);
+    }
+  } else {
+    const bool has_a = nl < M;
+    const uint8_t* xl = gsm + (kq * M + nl) * 16;
+#pragma unroll
+    for (int u = 0; u < KSW; ++u) {
+      const int kb = wave + GWF * u;
+      if (kb >= nkb) break;
+      Frags f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f.h[s] = f.l[s] = i32x4{0, 0, 0, 0};
+        if (has_a) {
+          f.h[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s) * 4 * M * 16);
+          f.l[s] = *reinterpret_cast<const i32x4*>(xl + (kb * 8 + 2 * s + 1) * 4 * M * 16);
+        }
+      }
+      f.r0 = *reinterpret_cast<const f32x4*>(ri + kb * 128);
+      f.r1 = *reinterpret_cast<const f32x4*>(ri + kb * 128 + 16);
+      block_mfma(f, u);
     }
   }
   // 5. the GWF partial sums of each row, in wave order
