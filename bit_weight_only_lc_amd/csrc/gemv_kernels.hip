@@ -656,6 +656,11 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
     return launch_gemv_fused(X, M, K, d, b, s);
   }
   float2* ri = reinterpret_cast<float2*>(rowinfo);
+  // Two launches: the timing hook, when armed for the decode product, brackets both with
+  // events on the stream (the prologue's time is part of the product's).
+  hipEvent_t e0, e1;
+  const bool timed = take_profile(PROF_GEMV, &e0, &e1);
+  if (timed) (void)hipEventRecord(e0, s);
   const dim3 pgrid(nkb), pblock(256);
   switch (d) {
     case 4: hipLaunchKernelGGL(k_gemv_prologue<4>, pgrid, pblock, 0, s, X, M, K, A16, B16, xq, ri); break;
@@ -663,12 +668,14 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
     default: hipLaunchKernelGGL(k_gemv_prologue<16>, pgrid, pblock, 0, s, X, M, K, A16, B16, xq, ri); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess) {
+    if (timed) (void)hipEventRecord(e1, s);
+    return e;
+  }
   const int per_wave = (nkb + GW - 1) / GW;
   const dim3 grid(two ? (N + 31) / 32 : N / 16), block(GW * 64);
 #define LCVQ_GEMV(RG, KSW) \
-  LCVQ_LAUNCH(PROF_GEMV, (k_gemv<RG, KSW>), grid, block, 0, s, xq, ri, packed, shuffled, M, N, \
-              K, Y)
+  hipLaunchKernelGGL((k_gemv<RG, KSW>), grid, block, 0, s, xq, ri, packed, shuffled, M, N, K, Y)
   if (two) {
     if (per_wave <= 1) LCVQ_GEMV(2, 1);
     else LCVQ_GEMV(2, 2);
@@ -677,7 +684,9 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
     else LCVQ_GEMV(1, 2);
   }
 #undef LCVQ_GEMV
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (timed) (void)hipEventRecord(e1, s);
+  return e;
 }
 
 }  // namespace lcvq
