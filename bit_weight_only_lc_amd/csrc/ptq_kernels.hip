@@ -148,35 +148,40 @@ __global__ __launch_bounds__(PB) void k_chol_diag(float* __restrict__ A, int K, 
   chol_diag_body(A, K, j0, st, threadIdx.x);
 }
 
-// Rows i >= j0 + 64 of the panel: x L11^T = a, one row per thread, forward substitution
-// with the factored diagonal block from LDS.
-__global__ __launch_bounds__(256) void k_chol_panel(float* __restrict__ A, int K, int j0) {
+// Rows i >= j0 + 64 of the panel: x L11^T = a, forward substitution with the factored
+// diagonal block L11 (from LDS). One row per wave, lane c holding column c: column u is
+// solved by lane u and broadcast to the wave (readlane), and every lane then subtracts its
+// term x_u L11[c][u]. Each column's sum takes its terms in the order u = 0, 1, ... and
+// ends with the same division, exactly as a sequential solve of the row; the chain of one
+// row is 64 steps of a division, a broadcast and a multiply-add.
+constexpr int PANEL_ROWS = 16;                   // rows (waves) per workgroup
+__global__ __launch_bounds__(PANEL_ROWS * 64) void k_chol_panel(float* __restrict__ A, int K,
+                                                                int j0) {
   __shared__ float L[PB][PB + 1];
   const int t = threadIdx.x;
-  for (int x = t; x < PB * PB; x += 256) {
+  for (int x = t; x < PB * PB; x += PANEL_ROWS * 64) {
     const int i = x / PB, k = x % PB;
     L[i][k] = k <= i ? A[(int64_t)(j0 + i) * K + j0 + k] : 0.f;
   }
   __syncthreads();
-  const int i = j0 + PB + blockIdx.x * 256 + t;
-  if (i >= K) return;
+  const int lane = t & 63;
+  const int i = j0 + PB + blockIdx.x * PANEL_ROWS + (t >> 6);
+  if (i >= K) return;                            // uniform within the wave
   float* row = A + (int64_t)i * K + j0;
-  float x[PB];
+  float v = row[lane];
+  float Lr[PB];                                  // this lane's row of L11 (zeros above it)
 #pragma unroll
-  for (int v = 0; v < PB / 4; ++v) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(row + 4 * v);
-    x[4 * v] = a[0]; x[4 * v + 1] = a[1]; x[4 * v + 2] = a[2]; x[4 * v + 3] = a[3];
+  for (int u = 0; u < PB; ++u) Lr[u] = L[lane][u];
+  const float dg = L[lane][lane];
+  float res = 0.f;
+#pragma unroll
+  for (int u = 0; u < PB; ++u) {
+    const float xa = v / dg;                     // final in lane u: x_u
+    const float xu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xa), u));
+    res = lane == u ? xu : res;
+    v -= xu * Lr[u];                             // lanes c > u: their next term
   }
-#pragma unroll
-  for (int c = 0; c < PB; ++c) {
-    float v = x[c];
-#pragma unroll
-    for (int u = 0; u < c; ++u) v -= x[u] * L[c][u];
-    x[c] = v / L[c][c];
-  }
-#pragma unroll
-  for (int v = 0; v < PB / 4; ++v)
-    *reinterpret_cast<f32x4*>(row + 4 * v) = f32x4{x[4 * v], x[4 * v + 1], x[4 * v + 2], x[4 * v + 3]};
+  row[lane] = res;
 }
 
 // Trailing update A[i][k] -= sum_c L[i][j0+c] L[k][j0+c] for j0 + 64 <= k <= i, on
@@ -730,7 +735,8 @@ hipError_t launch_ptq_init(const float* H, const float* W0, int N, int K, float 
   for (int j0 = 0; j0 < K; j0 += PB) {
     const int rows = K - j0 - PB;
     if (rows > 0) {
-      hipLaunchKernelGGL(k_chol_panel, dim3((rows + 255) / 256), dim3(256), 0, s, A, K, j0);
+      hipLaunchKernelGGL(k_chol_panel, dim3((rows + PANEL_ROWS - 1) / PANEL_ROWS),
+                         dim3(PANEL_ROWS * 64), 0, s, A, K, j0);
       const int T = rows / PB;
       hipLaunchKernelGGL(k_chol_update, dim3(T * (T + 1) / 2), dim3(256), 0, s, A, K, j0, st);
     }
