@@ -97,8 +97,10 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 // Thread t < 64 (one wave) holds row j0 + t of the block.
+// colbuf: 64 floats of LDS, 16-byte aligned, through which each column of L reaches the
+// wave (the lanes read it back as broadcast 16-byte reads).
 __device__ __forceinline__ void chol_diag_body(float* __restrict__ A, int K, int j0,
-                                               PtqState* st, int t) {
+                                               PtqState* st, int t, float* colbuf) {
   float* row = A + (int64_t)(j0 + t) * K + j0;
   float x[PB];
 #pragma unroll
@@ -115,18 +117,22 @@ __device__ __forceinline__ void chol_diag_body(float* __restrict__ A, int K, int
     const float d = piv > 0.f ? sqrtf(piv) : 1.f;
     const float sc = x[c] / d;
     x[c] = t == c ? d : (t > c ? sc : 0.f);
+    // Column c of L (lane k holds L[k][c]) to all lanes: written to LDS once and read back
+    // as broadcast 16-byte reads. The wave's LDS operations complete in order, so the
+    // reads see this column, and the next column's write follows them.
+    colbuf[t] = x[c];
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int Q = PB / 4;
+    f32x4 l[Q];
 #pragma unroll
-    for (int k0 = c + 1; k0 < PB; k0 += 8) {
-      float l[8];
+    for (int q = (c + 1) >> 2; q < Q; ++q) l[q] = *reinterpret_cast<const f32x4*>(colbuf + 4 * q);
+    __builtin_amdgcn_sched_barrier(0);           // all of the column's reads in flight first
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (k0 + u < PB) l[u] = lane_value(x[c], k0 + u);
+    for (int q = (c + 1) >> 2; q < Q; ++q)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (k0 + u < PB) x[k0 + u] = __builtin_fmaf(-x[c], l[u], x[k0 + u]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int e = 0; e < 4; ++e)
+        if (4 * q + e > c) x[4 * q + e] = __builtin_fmaf(-x[c], l[q][e], x[4 * q + e]);
+    __builtin_amdgcn_sched_barrier(0);
     // Materialise the row after each column: otherwise the compiler sinks every update
     // of an entry to where the entry is next used, which keeps all earlier broadcasts
     // live (in SGPRs, spilled).
@@ -145,7 +151,8 @@ __device__ __forceinline__ void chol_diag_body(float* __restrict__ A, int K, int
 }
 __global__ __launch_bounds__(PB) void k_chol_diag(float* __restrict__ A, int K, int j0,
                                                   PtqState* st) {
-  chol_diag_body(A, K, j0, st, threadIdx.x);
+  __shared__ __attribute__((aligned(16))) float colbuf[PB];
+  chol_diag_body(A, K, j0, st, threadIdx.x, colbuf);
 }
 
 // Rows i >= j0 + 64 of the panel: x L11^T = a, forward substitution with the factored
@@ -193,6 +200,7 @@ __global__ __launch_bounds__(256) void k_chol_update(float* __restrict__ A, int 
                                                      PtqState* st) {
   __shared__ float Li[PB][PB + 4];
   __shared__ float Lk[PB][PB + 4];
+  __shared__ __attribute__((aligned(16))) float colbuf[PB];
   const int j1 = j0 + PB;
   int t = blockIdx.x, ti = 0;                     // lower tile t -> (ti, tk), tk <= ti
   while (t > ti) {
@@ -231,7 +239,7 @@ __global__ __launch_bounds__(256) void k_chol_update(float* __restrict__ A, int 
     }
   if (blockIdx.x == 0) {                          // uniform per workgroup
     __syncthreads();                              // the tile's updated entries
-    if (tid < PB) chol_diag_body(A, K, j1, st, tid);
+    if (tid < PB) chol_diag_body(A, K, j1, st, tid, colbuf);
   }
 }
 
