@@ -121,18 +121,22 @@ __device__ __forceinline__ void chol_diag_body(float* __restrict__ A, int K, int
     // as broadcast 16-byte reads. The wave's LDS operations complete in order, so the
     // reads see this column, and the next column's write follows them.
     colbuf[t] = x[c];
+    // The next pivot's column first, with its one entry of column c taken straight from
+    // lane c + 1: the next column's square root and division then need not wait for the
+    // LDS round trip, and run under this column's other updates (the same multiply-add
+    // as through LDS).
+    if (c + 1 < PB) x[c + 1] = __builtin_fmaf(-x[c], lane_value(x[c], c + 1), x[c + 1]);
     __builtin_amdgcn_sched_barrier(0);
     constexpr int Q = PB / 4;
     f32x4 l[Q];
 #pragma unroll
-    for (int q = (c + 1) >> 2; q < Q; ++q) l[q] = *reinterpret_cast<const f32x4*>(colbuf + 4 * q);
+    for (int q = (c + 2) >> 2; q < Q; ++q) l[q] = *reinterpret_cast<const f32x4*>(colbuf + 4 * q);
     __builtin_amdgcn_sched_barrier(0);           // all of the column's reads in flight first
 #pragma unroll
-    for (int q = (c + 1) >> 2; q < Q; ++q)
+    for (int q = (c + 2) >> 2; q < Q; ++q)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * q + e > c) x[4 * q + e] = __builtin_fmaf(-x[c], l[q][e], x[4 * q + e]);
-    __builtin_amdgcn_sched_barrier(0);
+        if (4 * q + e > c + 1) x[4 * q + e] = __builtin_fmaf(-x[c], l[q][e], x[4 * q + e]);
     // Materialise the row after each column: otherwise the compiler sinks every update
     // of an entry to where the entry is next used, which keeps all earlier broadcasts
     // live (in SGPRs, spilled).
