@@ -657,8 +657,7 @@ def main():
     # lcvq_quantize (Wp -> packed codes and mask bits: 4 + 0.25 + 0.125 B per weight) and
     # lcvq_pack2b (one code per byte -> packed: 1 + 0.25 B per weight) on the 4096 x 4096 and
     # 14336 x 4096 weights, each call on another buffer of a pool of >= 512 MiB, timed with
-    # the profiling hook (kernel id 1 covers lcvq_quantize's launch; the packer is timed by
-    # events around its own launch).
+    # the profiling hook (kernel id 1: lcvq_quantize's launch; 11: lcvq_pack2b's).
     hbm_kernels = None
     if not args.no_decode and not args.no_quant_pack:
         hbm_kernels = {}
@@ -684,9 +683,8 @@ def main():
                 P.lcvq_pack2b(z_, pk_)
             evs = timed_events(torch, 2 * len(zs))
             for i, (a, b) in enumerate(evs):
-                a.record()
+                L.lcvq_profile_next(11, a.cuda_event, b.cuda_event)
                 P.lcvq_pack2b(zs[i % len(zs)], pk_)
-                b.record()
             torch.cuda.synchronize()
             tp = sum(a.elapsed_time(b) for a, b in evs) / len(evs) * 1e-3
             pb = n * k * 1.25

@@ -21,17 +21,38 @@
 namespace lcvq {
 
 constexpr int GK = 256;   // k per block (4 MFMA of k = 64)
-constexpr int GEMV_FUSED_M = 4;     // up to this many tokens one fused kernel can do it all
+constexpr int GWF = 8;    // waves per workgroup of the fused kernel
+constexpr size_t GEMV_LDS_MAX = 160 * 1024;
 
-// The fused path (X' formed in LDS by every workgroup) repeats M * K * d multiply-adds in
-// every workgroup; measured on the decode shapes, that beats a separate prologue launch
-// up to about M * K / 256 = 128. So: one or two tokens with K up to 64 blocks, three or
-// four with K up to 32; otherwise a prologue kernel writes X' once and the product reads it.
-inline bool gemv_fused(int M, int K) {
-  const int nkb = K / 256;
-  return M <= 2 ? nkb <= 64 : (M <= GEMV_FUSED_M && nkb <= 32);
+// Dynamic LDS of the fused kernel: the dense X' limbs (nkb * 32 * M * 16 bytes), the block
+// scales (nkb * 128) and A, B; at least the final reduction's area.
+inline size_t gemv_fused_lds(int M, int K, int d, bool two) {
+  const size_t nkb = K / GK;
+  const size_t base = nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
+  return std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
 }
-bool gemv_fused_path(int M, int K) { return gemv_fused(M, K); }
+
+// The fused path (X' formed in LDS by every workgroup) repeats the M * K * d multiply-adds
+// of X' in every workgroup, under the code stream; the two-kernel path pays a second
+// launch and the X' round trip through memory instead. Fused: one or two tokens with K
+// up to 64 blocks; three or four with K up to 32 blocks (one or two row groups per
+// workgroup); and where each workgroup takes one row group, its LDS fits, the grid runs
+// in one round of one workgroup per CU (rows / 16 <= 256) and the X' work per workgroup,
+// M * (K / 256) * d, is at most 1792: three or four tokens with K up to 64 blocks, five
+// to twelve tokens with K up to 16 blocks. (Measured on 4096 x 4096, 1024 x 4096 and
+// 4096 x 14336 at d = 4, 8, 16, one build against the other on one GPU: within that
+// bound the fused launch took 0.56-0.91x the two launches; beyond it 1.0-1.28x.)
+constexpr int GEMV_FUSED_WORK = 1792;
+inline bool gemv_fused(int M, int K, int64_t rows, int d) {
+  const int nkb = K / GK;
+  if (M <= 2) return nkb <= 64;
+  if (M <= 4 && nkb <= 32) return true;
+  const bool two = rows >= 2 * 16 * 256;
+  if (two || rows / 16 > 256 || gemv_fused_lds(M, K, d, false) > GEMV_LDS_MAX) return false;
+  if (M > 12 || M * nkb * d > GEMV_FUSED_WORK) return false;
+  return M <= 4 ? nkb <= 64 : nkb <= 16;
+}
+bool gemv_fused_path(int M, int K, int64_t rows, int d) { return gemv_fused(M, K, rows, d); }
 
 // X' limbs: each (block kb, MFMA step s, limb 0 = high / 1 = low, quarter kq, row m) is
 // a 16-byte chunk whose dword t, byte b holds column 64*kq + 16*s + 4*b + t of the block.
@@ -342,7 +363,7 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
   }
 }
 
-// Fused path for M <= GEMV_FUSED_M tokens: one launch. A workgroup of GWF waves covers
+// Fused path (the cases of gemv_fused): one launch. A workgroup of GWF waves covers
 // RG groups of 16 rows n over the whole of K. It first issues the code loads of all its
 // waves' blocks (they stream from HBM meanwhile), then forms X' of rows m < M for the
 // whole of K in LDS (dense chunk order, M * K * 2 bytes, at most 64 KiB) plus the block
@@ -352,12 +373,13 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
 // and the X' round trip through memory.
 // One launch can serve up to GEMV_MAX_BATCH matrices that share X (and K), each with its
 // own codes, A, B and output: workgroups [wg0[i], wg0[i+1]) belong to matrix i.
-constexpr int GWF = 8;
-
-template <int D, int RG, int KSW, int M>
+// MT is the token count, or for MT = 8 and 12 a bound on the run-time count Mrt (5..8,
+// 9..12), which then sets the LDS layout and the X' work.
+template <int D, int RG, int KSW, int MT>
 __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restrict__ X,
-                                                         GemvBatch batch, int K) {
+                                                         GemvBatch batch, int K, int Mrt) {
   extern __shared__ __attribute__((aligned(16))) uint8_t gsm[];
+  const int M = MT <= 4 ? MT : Mrt;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -387,8 +409,8 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   //    All loads here are unconditional, from clamped addresses: a load merged with a
   //    default value across a branch, or counted differently on two paths, makes the
   //    compiler wait for it (and for everything issued before it) right there.
-  constexpr int XI = (KSW * M + 3) / 4;
-  static_assert(XI * GWF * 64 >= GWF * KSW * M * 16, "X items of nkb <= GWF * KSW blocks");
+  constexpr int XI = (KSW * MT + 3) / 4;
+  static_assert(XI * GWF * 64 >= GWF * KSW * MT * 16, "X items of nkb <= GWF * KSW blocks");
   const int nitems = nkb * M * 16;
   uint4 xv[XI][2];
 #pragma unroll
@@ -567,9 +589,9 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   }
 }
 
-template <int D, int RG, int KSW, int M>
+template <int D, int RG, int KSW, int MT>
 static hipError_t launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
-                               const GemvBatch& b, int K) {
+                               const GemvBatch& b, int K, int M) {
   // Dynamic LDS beyond 64 KiB must be requested for the kernel, once per device: a
   // process-wide cache of the devices done (the first 64; beyond that it is requested on
   // every launch). A failed request is returned, and not cached.
@@ -579,27 +601,32 @@ static hipError_t launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint1
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
   if (!bit || !(done.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW, M>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_fused<D, RG, KSW, MT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMV_LDS_MAX);
     if (e != hipSuccess) return e;
     done.fetch_or(bit, std::memory_order_acq_rel);
   }
-  LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW, M>), grid, dim3(GWF * 64), shm, s, X, b, K);
+  LCVQ_LAUNCH(PROF_GEMV, (k_gemv_fused<D, RG, KSW, MT>), grid, dim3(GWF * 64), shm, s, X, b, K,
+              M);
   return hipGetLastError();
 }
 
-// M = 3, 4 take the fused path only for K up to 32 blocks, i.e. KSW <= 4.
+// The instances gemv_fused() can reach: M = 3, 4 with two row groups only for K up to 32
+// blocks (KSW <= 4); M = 5..12 with one row group and K up to 16 blocks (KSW = 2).
 template <int D, int RG, int KSW>
 static hipError_t launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
                                  const GemvBatch& b, int K) {
-  static_assert(GEMV_FUSED_M == 4, "fused path instantiated for one to four tokens");
-  if (M == 1) return launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K);
-  if (M == 2) return launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K);
-  if constexpr (KSW <= 4) {
-    if (M == 3) return launch_fused<D, RG, KSW, 3>(grid, shm, s, X, b, K);
-    return launch_fused<D, RG, KSW, 4>(grid, shm, s, X, b, K);
+  if (M == 1) return launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K, M);
+  if (M == 2) return launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K, M);
+  if constexpr (KSW <= 4 || RG == 1) {
+    if (M == 3) return launch_fused<D, RG, KSW, 3>(grid, shm, s, X, b, K, M);
+    if (M == 4) return launch_fused<D, RG, KSW, 4>(grid, shm, s, X, b, K, M);
   }
-  return hipErrorInvalidValue;       // not reached: gemv_fused() keeps M > 2 to KSW <= 4
+  if constexpr (RG == 1 && KSW <= 2) {
+    if (M <= 8) return launch_fused<D, RG, KSW, 8>(grid, shm, s, X, b, K, M);
+    if (M <= 12) return launch_fused<D, RG, KSW, 12>(grid, shm, s, X, b, K, M);
+  }
+  return hipErrorInvalidValue;       // not reached: gemv_fused() picks only the cases above
 }
 
 template <int D>
@@ -632,9 +659,7 @@ hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b
     b.wg0[i] = wgs;
     wgs += two ? (b.N[i] + 31) / 32 : b.N[i] / 16;
   }
-  const int nkb = K / GK;
-  const size_t base = (size_t)nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
-  const size_t shm = std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
+  const size_t shm = gemv_fused_lds(M, K, d, two);
   switch (d) {
     case 4: return launch_fused_d<4>(M, K, two, shm, s, X, b, wgs);
     case 8: return launch_fused_d<8>(M, K, two, shm, s, X, b, wgs);
@@ -648,7 +673,7 @@ hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A
   const int nkb = K / GK;
   // Two row groups per workgroup when N still gives a workgroup per CU.
   const bool two = N >= 2 * 16 * 256;
-  if (gemv_fused(M, K)) {
+  if (gemv_fused(M, K, N, d)) {
     GemvBatch b = {};
     b.count = 1;
     b.packed[0] = packed; b.A16[0] = A16; b.B16[0] = B16; b.Y[0] = Y; b.N[0] = N;

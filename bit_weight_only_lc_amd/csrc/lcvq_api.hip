@@ -470,7 +470,7 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
   const GemvWs w = gemv_ws(K);
   if (!workspace || workspace_bytes < w.total) return LCVQ_ERR_WORKSPACE;
   hipStream_t s = as_stream(stream);
-  if (gemv_fused_path((int)M, (int)K)) {
+  if (gemv_fused_path((int)M, (int)K, groups * 16, d)) {
     GemvBatch b = {};
     b.count = count;
     for (int i = 0; i < count; ++i) {

@@ -8,7 +8,7 @@ namespace lcvq {
 // Kernel ids of the profiling hook (lcvq_profile_next).
 enum { PROF_QUANTIZE = 1, PROF_FWD = 2, PROF_DX = 3, PROF_DW = 4, PROF_GEMV = 5, PROF_BWD_PREP = 6,
        PROF_GRAM = 7, PROF_PTQ_SWEEP = 8, PROF_READ_PROBE = 9,
-       PROF_MFMA_PROBE = 10, PROF_LAST = 10 };
+       PROF_MFMA_PROBE = 10, PROF_PACK = 11, PROF_UNPACK = 12, PROF_LAST = 12 };
 // True (once) if the calling thread armed timing for kernel `id`; returns the events.
 bool take_profile(int id, hipEvent_t* start, hipEvent_t* stop);
 
@@ -108,7 +108,7 @@ struct GemvBatch {
   int count;
 };
 // True when the fused single-launch path serves M tokens at this K.
-bool gemv_fused_path(int M, int K);
+bool gemv_fused_path(int M, int K, int64_t rows, int d);
 hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b,
                              hipStream_t s);
 

@@ -140,34 +140,72 @@ __global__ __launch_bounds__(256) void k_quantize(
 }
 
 // ------------------------------------------------------------------ pack / unpack
+// Code k = 4b + t of a row goes to bits [2t, 2t+1] of byte b. A dword of four one-byte
+// codes packs into one byte, and a packed byte unpacks into one dword:
+__device__ __forceinline__ uint32_t pack_dword(uint32_t w) {
+  const uint32_t x = w & 0x03030303u;              // codes in bits 0-1 of each byte
+  const uint32_t y = (x | (x >> 6)) & 0x000F000Fu; // bytes 0 and 2: two codes each
+  return (y | (y >> 12)) & 0xFFu;
+}
+__device__ __forceinline__ uint32_t unpack_byte(uint32_t b) {
+  const uint32_t y = (b | (b << 12)) & 0x000F000Fu;
+  return (y | (y << 6)) & 0x03030303u;
+}
+__device__ __forceinline__ uint32_t pack_group(const u32x4& q) {   // 16 codes -> 1 word
+  return pack_dword(q[0]) | (pack_dword(q[1]) << 8) | (pack_dword(q[2]) << 16) |
+         (pack_dword(q[3]) << 24);
+}
+__device__ __forceinline__ u32x4 unpack_group(uint32_t p) {       // 1 word -> 16 codes
+  return u32x4{unpack_byte(p & 0xFFu), unpack_byte((p >> 8) & 0xFFu),
+               unpack_byte((p >> 16) & 0xFFu), unpack_byte(p >> 24)};
+}
+
+// A group is 16 codes (16 bytes unpacked, one 4-byte word packed). Each wave takes
+// chunks of 256 consecutive groups: lane l handles groups 64 j + l, j = 0..3, with the
+// four loads issued together, so that every load and store instruction of the wave covers
+// one contiguous run (1 KiB of codes or 256 bytes of words) and each lane keeps four
+// loads in flight. Groups past the end read the last group and are not stored.
+constexpr int PACK_CHUNK = 256;
 __global__ __launch_bounds__(256) void k_pack2b(const uint8_t* __restrict__ z, int64_t groups,
                                                 uint32_t* __restrict__ packed) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
-    const uint4 q = reinterpret_cast<const uint4*>(z)[gi];
-    const uint32_t in[4] = {q.x, q.y, q.z, q.w};
-    uint32_t p = 0;
+  const int lane = threadIdx.x & 63;
+  const int64_t nchunks = (groups + PACK_CHUNK - 1) / PACK_CHUNK;
+  const u32x4* zi = reinterpret_cast<const u32x4*>(z);
+  for (int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); c < nchunks;
+       c += (int64_t)gridDim.x * 4) {
+    u32x4 q[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int j = 0; j < 4; ++j) {
+      const int64_t g = c * PACK_CHUNK + 64 * j + lane;
+      q[j] = __builtin_nontemporal_load(zi + (g < groups ? g : groups - 1));
+    }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) p |= ((in[b] >> (8 * t)) & 3u) << (2 * (4 * b + t));
-    packed[gi] = p;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t g = c * PACK_CHUNK + 64 * j + lane;
+      if (g < groups) packed[g] = pack_group(q[j]);
+    }
   }
 }
 
+// The inverse, with the same chunks: four 4-byte loads and four 16-byte stores per lane.
 __global__ __launch_bounds__(256) void k_unpack2b(const uint32_t* __restrict__ packed,
                                                   int64_t groups, uint8_t* __restrict__ z) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
-    const uint32_t p = packed[gi];
-    uint32_t o[4];
+  const int lane = threadIdx.x & 63;
+  const int64_t nchunks = (groups + PACK_CHUNK - 1) / PACK_CHUNK;
+  u32x4* zo = reinterpret_cast<u32x4*>(z);
+  for (int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); c < nchunks;
+       c += (int64_t)gridDim.x * 4) {
+    uint32_t p[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      o[b] = 0;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) o[b] |= ((p >> (2 * (4 * b + t))) & 3u) << (8 * t);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t g = c * PACK_CHUNK + 64 * j + lane;
+      p[j] = __builtin_nontemporal_load(packed + (g < groups ? g : groups - 1));
     }
-    reinterpret_cast<uint4*>(z)[gi] = make_uint4(o[0], o[1], o[2], o[3]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t g = c * PACK_CHUNK + 64 * j + lane;
+      if (g < groups) zo[g] = unpack_group(p[j]);
+    }
   }
 }
 
@@ -514,17 +552,18 @@ hipError_t launch_quantize(const float* wp, int64_t N, int64_t K, uint8_t* z, ui
   return hipGetLastError();
 }
 
+// pack / unpack: one workgroup of four waves per 4 chunks of 256 groups
 hipError_t launch_pack2b(const uint8_t* z, int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
   const int64_t groups = N * K / 16;
-  hipLaunchKernelGGL(k_pack2b, dim3(grid_for(groups)), dim3(256), 0, s, z, groups,
-                     reinterpret_cast<uint32_t*>(packed));
+  LCVQ_LAUNCH(PROF_PACK, k_pack2b, dim3(grid_for((groups + 3) / 4)), dim3(256), 0, s, z, groups,
+              reinterpret_cast<uint32_t*>(packed));
   return hipGetLastError();
 }
 
 hipError_t launch_unpack2b(const uint8_t* packed, int64_t N, int64_t K, uint8_t* z, hipStream_t s) {
   const int64_t groups = N * K / 16;
-  hipLaunchKernelGGL(k_unpack2b, dim3(grid_for(groups)), dim3(256), 0, s,
-                     reinterpret_cast<const uint32_t*>(packed), groups, z);
+  LCVQ_LAUNCH(PROF_UNPACK, k_unpack2b, dim3(grid_for((groups + 3) / 4)), dim3(256), 0, s,
+              reinterpret_cast<const uint32_t*>(packed), groups, z);
   return hipGetLastError();
 }
 

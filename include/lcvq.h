@@ -221,7 +221,10 @@ lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t 
  * own codes and its own A, B (LC-QAT summary, Methodology 1: A and B are shared within
  * one weight matrix). Every output equals what lcvq_gemv2b gives for that matrix, byte
  * for byte. With M <= 2 and K <= 16384, or M <= 4 and K <= 8192, all of them run in
- * one launch; otherwise one matrix after the other, on `stream`.
+ * one launch; likewise for up to 4096 rows in all with 3 <= M <= 12, where the one-launch
+ * kernel's bound on its activation work, M * (K / 256) * d <= 1792 (K <= 16384 for
+ * M <= 4, K <= 4096 beyond), holds; otherwise each matrix is computed as lcvq_gemv2b
+ * computes it, one after the other, on `stream`.
  *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 256
  *   mats    host array of `count` descriptors, 1 <= count <= 8; mats[i].N a multiple of
  *           16, the N summed over the matrices at most 2^26, each N * K <= 2^36; packed
@@ -329,7 +332,8 @@ lcvq_status_t lcvq_mfma_probe(int64_t iters, uint32_t* sink, void* stream);
  * it takes two launches, the X' prologue and the product, the events bracket both),
  * 6 backward prologue (r = dY 1 and the transposed codes, lcvq_linear_bwd), 7 Gram
  * product (lcvq_hessian), 8 PTQ integer step (lcvq_ptq_init; each call times the first),
- * 9 read probe (lcvq_read_probe), 10 MFMA probe (lcvq_mfma_probe).
+ * 9 read probe (lcvq_read_probe), 10 MFMA probe (lcvq_mfma_probe), 11 packer
+ * (lcvq_pack2b), 12 unpacker (lcvq_unpack2b).
  * Passing NULL events disarms. Returns LCVQ_ERR_SHAPE for an unknown kernel_id.
  */
 lcvq_status_t lcvq_profile_next(int kernel_id, void* start_event, void* stop_event);

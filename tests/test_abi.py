@@ -213,10 +213,10 @@ def test_workspace_sizes_grow_with_shape(L):
 
 
 def test_profile_hook_ids(L):
-    """The timing hook knows kernel ids 1..10; arming with NULL events disarms (no GPU call)."""
-    for kid in (0, 11, -1):
+    """The timing hook knows kernel ids 1..12; arming with NULL events disarms (no GPU call)."""
+    for kid in (0, 13, -1):
         assert L.lcvq_profile_next(kid, None, None) == 2          # LCVQ_ERR_SHAPE
-    for kid in range(1, 11):
+    for kid in range(1, 13):
         assert L.lcvq_profile_next(kid, None, None) == 0
 
 

@@ -88,6 +88,17 @@ def test_pack_unpack(P):
     P.lcvq_unpack2b(allb.cuda(), out)
     torch.cuda.synchronize()
     assert np.array_equal(host(out), O.unpack2b(allb.numpy(), 1024))
+    # group counts (N K / 16) that leave 1..3 groups past the last whole set of four, with
+    # bits above the code set in the inputs (ignored)
+    for (n, k) in ((3, 16), (5, 48), (1, 16), (7, 80), (4097, 4096)):
+        zb = torch.randint(0, 256, (n, k), generator=g, dtype=torch.uint8)
+        pk2 = torch.empty((n, k // 4), dtype=torch.uint8, device="cuda")
+        P.lcvq_pack2b(zb.cuda(), pk2)
+        back2 = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        P.lcvq_unpack2b(pk2, back2)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(pk2), O.pack2b(zb.numpy() & 3)), (n, k)
+        assert np.array_equal(host(back2), zb.numpy() & 3), (n, k)
 
 
 # ------------------------------------------------------------------ linear layer
@@ -212,6 +223,31 @@ def test_gemv(P, N, K, M):
     torch.cuda.synchronize()
     ref = O.gemv2b(host(X), host(pk), A.half().double().numpy(), B.half().double().numpy(), d)
     note(f"  {fmt(check(host(Y), ref, TOL, 'gemv'))}")
+
+
+@pytest.mark.parametrize("N,K,M,d", [(4096, 4096, 5, 8), (4096, 4096, 8, 8), (4096, 4096, 12, 8),
+                                     (4096, 4096, 12, 4), (1024, 4096, 11, 16), (272, 4096, 9, 8),
+                                     (4096, 16384, 4, 8), (256, 16384, 3, 16), (2048, 16384, 4, 4),
+                                     (4352, 4096, 12, 8), (256, 8192, 12, 8), (4096, 4096, 13, 8),
+                                     (4096, 4096, 7, 16)])
+def test_gemv_more_tokens(P, N, K, M, d):
+    """Token counts and K at the edges of the one-launch path's range: five to twelve
+    tokens with K up to 16 blocks of 256, three or four tokens with K up to 64 blocks, and
+    just past them (more than 256 row groups, K of 32 blocks at 12 tokens, 13 tokens),
+    which take the prologue + product path."""
+    note(f"gemv more tokens N={N} K={K} M={M} d={d}")
+    wp = SI.make_wp(N, K, seed=3400 + N + K, device="cuda")
+    A, B = SI.make_ab(d, seed=3400 + d + M)
+    X = SI.make_act(M, K, seed=3500 + M, device="cuda")
+    pk = torch.empty((N, K // 4), dtype=torch.uint8, device="cuda")
+    P.lcvq_quantize(wp, None, pk, None)
+    A16, B16 = A.half().cuda(), B.half().cuda()
+    Y = P.gemv2b(X, pk, A16, B16, d)
+    Ys = P.gemv2b(X, P.gemv2b_shuffle(pk), A16, B16, d, shuffled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Ys)
+    ref = O.gemv2b(host(X), host(pk), A.half().double().numpy(), B.half().double().numpy(), d)
+    note(f"  {fmt(check(host(Y), ref, TOL, 'gemv more tokens'))}")
 
 
 @pytest.mark.parametrize("d", [4, 16])
@@ -418,8 +454,8 @@ def test_gemv_shuffled_matches(P, N, K, M):
 
 
 @pytest.mark.parametrize("shapes,K", [([4096, 1024, 1024], 4096), ([14336, 14336], 4096),
-                                      ([8192, 272], 256), ([4096], 14336)])
-@pytest.mark.parametrize("M", [1, 2, 4])
+                                      ([8192, 272], 256), ([4096], 14336), ([1024, 1024], 4096)])
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 8])
 def test_gemv_batched(P, shapes, K, M):
     """Several matrices sharing X in one call: every output equals the single-matrix
     call's bytes and the oracle's product."""
