@@ -220,6 +220,11 @@ def time_layers(torch, P, L, mats, M, d, dev, seed, reps, warm_s):
     return out
 
 
+def section(name):
+    """One progress line per section on stderr (stdout carries only the JSON line)."""
+    print(f"bench: {name}", file=sys.stderr, flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -236,6 +241,7 @@ def main():
     torch.cuda.set_device(dev)
 
     # ---------------------------------------------------------------- training step
+    section("training step")
     c = SI.CONFIGS["c1_square_4096"]
     (N, K), M, d = c["mats"][0], c["M"], c["d"]
     inp = SI.make_layer(N, K, M, d, seed=1000, device=dev)
@@ -367,6 +373,7 @@ def main():
     roofline["quantize_prologue_gbs"] = round(q_bytes / (kern["quantize_prologue"] * 1e-3) / 1e9, 1)
 
     # ------------------------------------------- MLP chain and 8B-shaped layer steps
+    section("MLP chain and 8B-shaped layer steps")
     # The same fwd + bwd on the Llama-7B MLP (gate and up 11008 x 4096, down 4096 x 11008)
     # and on one layer of an 8B-shaped stack (q, k, v, o, gate, up, down) at 8192 tokens,
     # d = 8 (MLP) and d in {4, 8, 16} (layer); the 32-layer step is 32 times one layer
@@ -406,6 +413,7 @@ def main():
                 "shapes": r4}
 
     # ------------------------------------------------------------ PTQ initialisation
+    section("PTQ initialisation")
     # One 4096 x 4096 weight (W0 ~ 0.02 N(0, 1)) from 8192 calibration tokens (X ~ N(0, 1)
     # in bf16): the Gram product H = X^T X, then the damped factorisation and 4 alternations.
     ptq = None
@@ -458,6 +466,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- decode product
+    section("decode product")
     decode = None
     read_ceiling = {}
     if not args.no_decode:
@@ -555,6 +564,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ------------------------------------------------- decode step of an 8B-shaped stack
+    section("decode step of an 8B-shaped stack")
     # One token through all 7 projections of 32 layers (1.63 GiB of codes, far beyond the
     # last-level cache), as 224 single calls, as 128 calls that group the matrices sharing
     # an input (q, k, v and gate, up) into one launch each, and as the same 128 calls on
@@ -654,6 +664,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ------------------------------------------------ standalone quantizer and packer
+    section("standalone quantizer and packer")
     # lcvq_quantize (Wp -> packed codes and mask bits: 4 + 0.25 + 0.125 B per weight) and
     # lcvq_pack2b (one code per byte -> packed: 1 + 0.25 B per weight) on the 4096 x 4096 and
     # 14336 x 4096 weights, each call on another buffer of a pool of >= 512 MiB, timed with
@@ -698,6 +709,7 @@ def main():
                 "frac": round(pb / tp / 1e9 / PEAK_HBM_GBS, 4)}
 
     # ---------------------------------------------------------------- HBM copy ceiling
+    section("HBM copy ceiling")
     # A plain device-to-device copy of 1 GiB: the streaming ceiling measured beside the
     # decode product, and the kernel of known size that scales the HBM byte counters.
     copy_probe = None
@@ -721,6 +733,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ---------------------------------------------------------------- CPU oracle
+    section("CPU oracle")
     cpu = None
     if not args.no_cpu_baseline:
         # The plain C++ float64 oracle (loops, OpenMP over rows) on a bounded sample of the
