@@ -24,10 +24,14 @@ constexpr int GK = 256;   // k per block (4 MFMA of k = 64)
 constexpr int GWF = 8;    // waves per workgroup of the fused kernel
 constexpr size_t GEMV_LDS_MAX = 160 * 1024;
 
+// Blocks of 256 columns along K (a multiple of 64): the last one holds K - 256 (nkb - 1)
+// = 64, 128, 192 or 256 columns. Columns past K contribute nothing: their X' is zero.
+__host__ __device__ inline int gemv_blocks(int64_t K) { return (int)((K + GK - 1) / GK); }
+
 // Dynamic LDS of the fused kernel: the dense X' limbs (nkb * 32 * M * 16 bytes), the block
 // scales (nkb * 128) and A, B; at least the final reduction's area.
 inline size_t gemv_fused_lds(int M, int K, int d, bool two) {
-  const size_t nkb = K / GK;
+  const size_t nkb = gemv_blocks(K);
   const size_t base = nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
   return std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
 }
@@ -44,7 +48,7 @@ inline size_t gemv_fused_lds(int M, int K, int d, bool two) {
 // bound the fused launch took 0.56-0.91x the two launches; beyond it 1.0-1.28x.)
 constexpr int GEMV_FUSED_WORK = 1792;
 inline bool gemv_fused(int M, int K, int64_t rows, int d) {
-  const int nkb = K / GK;
+  const int nkb = gemv_blocks(K);
   if (M <= 2) return nkb <= 64;
   if (M <= 4 && nkb <= 32) return true;
   const bool two = rows >= 2 * 16 * 256;
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(256) void k_gemv_prologue(const uint16_t* __restric
   const int t = threadIdx.x;
   const int m = t >> 4, kc = t & 15;
   uint4 a = make_uint4(0, 0, 0, 0), b = a;
-  if (m < M) {
+  if (m < M && kb * GK + kc * 16 < K) {             // columns past K: X' = 0
     const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)m * K + kb * GK + kc * 16);
     a = src[0];
     b = src[1];
@@ -206,6 +210,15 @@ __device__ __forceinline__ CodeAddr code_addr(const uint8_t* packed, int shuffle
     c.kstride = 4;
   }
   return c;
+}
+
+// In a last block of fewer than 256 columns (canonical layout only; the decode layout needs
+// K % 256 == 0), a lane whose 64 columns lie past K reads the row's first 64 columns of
+// that block instead: a valid address, and its X' is zero. Returned in 16-byte units, to
+// be subtracted from the lane's address.
+__device__ __forceinline__ int code_tail_back(int kb, int nkb, int K, int lane) {
+  const int kq = lane >> 4;
+  return (kb == nkb - 1 && kb * GK + 64 * kq >= K) ? kq : 0;
 }
 
 // Canonical packed codes -> decode layout (see code_addr): one 1 KiB tile per wave.
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16 * RG;
   const int nl = lane & 15, kq = lane >> 4;
-  const int nkb = K / GK;
+  const int nkb = gemv_blocks(K);
   const CodeAddr ca = code_addr(packed, shuffled, n0, K, lane);
   const i32x4* xa = reinterpret_cast<const i32x4*>(xq) + lane;
   const f32x4* ri = reinterpret_cast<const f32x4*>(rowinfo) + 2 * kq;
@@ -327,7 +340,8 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
 #pragma unroll
       for (int g = 0; g < RG; ++g)
         cw[u][g] = (kb < nkb && n0 + 16 * g < N)
-                       ? __builtin_nontemporal_load(ca.base + g * ca.gstride + kb * ca.kstride)
+                       ? __builtin_nontemporal_load(ca.base + g * ca.gstride + kb * ca.kstride -
+                                                    code_tail_back(kb, nkb, K, lane))
                        : u32x4{0, 0, 0, 0};
     }
     GemvA a[2];
@@ -395,7 +409,7 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
   const int N = batch.N[mi];
   const int n0 = ((int)blockIdx.x - batch.wg0[mi]) * 16 * RG;
   const int nl = lane & 15, kq = lane >> 4;
-  const int nkb = K / GK;
+  const int nkb = gemv_blocks(K);
   const int XB = nkb * 32 * M * 16;                // dense X' bytes
   float2* ris = reinterpret_cast<float2*>(gsm + XB);              // [nkb][16]
   float* As = reinterpret_cast<float*>(gsm + XB + nkb * 128);     // [D][D], then B [D]
@@ -418,7 +432,8 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
     const int i = min(t + j * GWF * 64, nitems - 1);     // threads past the end: not used
     const int kc = i & 15, gm = i >> 4;
     const int m = gm % M, kb = gm / M;
-    const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)m * K + kb * GK + kc * 16);
+    const int col = kb * GK + kc * 16;                   // past K: read column 0, X' = 0
+    const uint4* src = reinterpret_cast<const uint4*>(X + (int64_t)m * K + (col < K ? col : 0));
     xv[j][0] = src[0];
     xv[j][1] = src[1];
   }
@@ -437,7 +452,8 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       const int gc = n0 + 16 * g < N ? g : 0;
-      cw[u][g] = __builtin_nontemporal_load(ca.base + gc * ca.gstride + kb * ca.kstride);
+      cw[u][g] = __builtin_nontemporal_load(ca.base + gc * ca.gstride + kb * ca.kstride -
+                                            code_tail_back(kb, nkb, K, lane));
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -468,7 +484,9 @@ __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restr
     const int m = gm % M, kb = gm / M;
     uint32_t hi[4], lo[4];
     float scale, bsum;
-    xprime_chunk<D>(xv[j][0], xv[j][1], Au, Bu, hi, lo, scale, bsum);
+    const bool in_k = kb * GK + kc * 16 < K;
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    xprime_chunk<D>(in_k ? xv[j][0] : z4, in_k ? xv[j][1] : z4, Au, Bu, hi, lo, scale, bsum);
     const int q = kc >> 2, s = kc & 3;
     *reinterpret_cast<uint4*>(gsm + (((kb * 8 + 2 * s) * 4 + q) * M + m) * 16) =
         make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -632,7 +650,7 @@ static hipError_t launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, co
 template <int D>
 static hipError_t launch_fused_d(int M, int K, bool two, size_t shm, hipStream_t s,
                                  const uint16_t* X, const GemvBatch& b, int wgs) {
-  const int pw = (K / GK + GWF - 1) / GWF;
+  const int pw = (gemv_blocks(K) + GWF - 1) / GWF;
   const dim3 grid(wgs);
 #define LCVQ_FUSED(RG, KSW) return launch_fused_m<D, RG, KSW>(M, grid, shm, s, X, b, K)
   if (two) {
@@ -670,7 +688,7 @@ hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b
 hipError_t launch_gemv(const uint16_t* X, int M, int N, int K, const uint16_t* A16,
                        const uint16_t* B16, int d, const uint8_t* packed, int shuffled,
                        uint16_t* Y, int8_t* xq, float* rowinfo, hipStream_t s) {
-  const int nkb = K / GK;
+  const int nkb = gemv_blocks(K);
   // Two row groups per workgroup when N still gives a workgroup per CU.
   const bool two = N >= 2 * 16 * 256;
   if (gemv_fused(M, K, N, d)) {

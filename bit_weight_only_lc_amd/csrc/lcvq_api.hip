@@ -55,9 +55,14 @@ inline bool layer_shape_ok(int64_t M, int64_t N, int64_t K) {
   return true;
 }
 
+// Decode products: K a multiple of 64 (the canonical packed layout); the decode layout of
+// lcvq_gemv2b_shuffle is made of whole 256-column blocks, so it also needs K % 256 == 0.
 inline bool decode_shape_ok(int64_t N, int64_t K) {
-  return N >= 16 && (N % 16) == 0 && K >= 256 && (K % 256) == 0 && N <= kMaxDecodeRows &&
+  return N >= 16 && (N % 16) == 0 && K >= 64 && (K % 64) == 0 && N <= kMaxDecodeRows &&
          K <= INT32_MAX && N * K <= kMaxDecodeWeights;
+}
+inline bool decode_layout_shape_ok(int64_t N, int64_t K) {
+  return decode_shape_ok(N, K) && (K % 256) == 0;
 }
 
 // Blocked R16 code words for `rows` operand rows and a contraction of length `kc`.
@@ -102,7 +107,7 @@ struct GemvWs {
   size_t xq, rowinfo, total;
 };
 constexpr GemvWs gemv_ws(int64_t K) {
-  const size_t nkb = (size_t)(K / 256);
+  const size_t nkb = (size_t)((K + 255) / 256);       // the last block may be partial
   GemvWs w{0, 0, 0};
   w.rowinfo = up(nkb * 4 * 2 * 1024);
   w.total = w.rowinfo + up(nkb * 16 * 8);
@@ -353,6 +358,7 @@ static lcvq_status_t gemv2b_impl(const void* X, int64_t M, int64_t N, int64_t K,
   if (!X || !packed || !A16 || !B16 || !Y) return LCVQ_ERR_NULL;
   if (!d_ok(d)) return LCVQ_ERR_D;
   if (M < 1 || M > 16 || !decode_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
+  if (shuffled && !decode_layout_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(packed) || !aligned16(A16) || !aligned16(B16) ||
       !aligned16(Y) || !aligned16(workspace))
     return LCVQ_ERR_ALIGN;
@@ -442,7 +448,7 @@ lcvq_status_t lcvq_mfma_probe(int64_t iters, uint32_t* sink, void* stream) {
 lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
                                   void* stream) {
   if (!packed || !codes) return LCVQ_ERR_NULL;
-  if (!decode_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
+  if (!decode_layout_shape_ok(N, K)) return LCVQ_ERR_SHAPE;
   if (!aligned16(packed) || !aligned16(codes)) return LCVQ_ERR_ALIGN;
   return from_hip(launch_gemv_shuffle(packed, N, K, codes, as_stream(stream)));
 }
@@ -460,6 +466,7 @@ lcvq_status_t lcvq_gemv2b_batched(const void* X, int64_t M, int64_t K, int d,
     if (!m.packed || !m.A16 || !m.B16 || !m.Y) return LCVQ_ERR_NULL;
     if (m.layout != 0 && m.layout != 1) return LCVQ_ERR_VALUE;
     if (!decode_shape_ok(m.N, K)) return LCVQ_ERR_SHAPE;
+    if (m.layout == 1 && !decode_layout_shape_ok(m.N, K)) return LCVQ_ERR_SHAPE;
     if (!aligned16(m.packed) || !aligned16(m.A16) || !aligned16(m.B16) || !aligned16(m.Y))
       return LCVQ_ERR_ALIGN;
     nmax = m.N > nmax ? m.N : nmax;

@@ -156,7 +156,7 @@ lcvq_status_t lcvq_linear_bwd_dge(const void* dY, const void* X, lcvq_dtype_t dt
  * Y = X What^T for a few tokens (decoupleQ, section 3.2: one linear transform turns the
  * integer part back into weights; LC-QAT summary, Methodology 3).
  *   X   bfloat16 [M, K], 1 <= M <= 16;  packed uint8 [N, K/4]
- *   N a multiple of 16, at most 2^26; K a multiple of 256; N * K <= 2^36
+ *   N a multiple of 16, at most 2^26; K a multiple of 64; N * K <= 2^36
  *   A16 float16 [d, d];  B16 float16 [d]
  *   Y   bfloat16 [M, N]                                          out
  *   workspace >= lcvq_gemv2b_workspace_size(M, N, K, d) bytes (0 for invalid shapes)
@@ -207,7 +207,8 @@ lcvq_status_t lcvq_gemv2b_shuffle(const uint8_t* packed, int64_t N, int64_t K, u
 
 /*
  * lcvq_gemv2b with the codes in the decode layout (lcvq_gemv2b_shuffle). Arguments,
- * errors and numerics as for lcvq_gemv2b; the output is byte for byte the same as
+ * errors and numerics as for lcvq_gemv2b, except that K must be a multiple of 256 (the
+ * layout is made of whole 256-column blocks); the output is byte for byte the same as
  * lcvq_gemv2b's on the canonical codes.
  */
 lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t K, int d,
@@ -225,7 +226,8 @@ lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t 
  * kernel's bound on its activation work, M * (K / 256) * d <= 1792 (K <= 16384 for
  * M <= 4, K <= 4096 beyond), holds; otherwise each matrix is computed as lcvq_gemv2b
  * computes it, one after the other, on `stream`.
- *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 256
+ *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 64 (of 256 if any matrix is
+ *           in the decode layout)
  *   mats    host array of `count` descriptors, 1 <= count <= 8; mats[i].N a multiple of
  *           16, the N summed over the matrices at most 2^26, each N * K <= 2^36; packed
  *           (N * K / 4 bytes: canonical [N, K/4] for layout 0, the decode layout of
@@ -233,8 +235,9 @@ lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t 
  *           output Y bfloat16 [M, N] are device pointers; outputs must not overlap
  *           anything
  *   workspace >= lcvq_gemv2b_workspace_size(M, largest N, K, d) bytes
- * Errors as for lcvq_gemv2b; LCVQ_ERR_SHAPE also for count outside 1..8, LCVQ_ERR_VALUE
- * for a layout other than 0 or 1.
+ * Errors as for lcvq_gemv2b; LCVQ_ERR_SHAPE also for count outside 1..8 and for a matrix
+ * in the decode layout with K not a multiple of 256, LCVQ_ERR_VALUE for a layout other
+ * than 0 or 1.
  */
 typedef struct {
   const uint8_t* packed;

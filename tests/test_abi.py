@@ -142,10 +142,16 @@ def test_gemv_errors(L):
     assert g(X=None) == 1
     assert g(M=17) == 2
     assert g(M=0) == 2
-    assert g(K=320) == 2
+    assert g(K=288) == 2                               # K % 64
+    assert g(K=32) == 2
+    assert g(K=0) == 2
     assert g(N=40) == 2
     assert g(d=5) == 3
     assert g(Y=MIS) == 5
+    # a partial last block of 256 columns: sized as the whole block
+    assert L.lcvq_gemv2b_workspace_size(1, 256, 320, 8) == \
+        L.lcvq_gemv2b_workspace_size(1, 256, 512, 8) > L.lcvq_gemv2b_workspace_size(1, 256, 256, 8)
+    assert L.lcvq_gemv2b_workspace_size(1, 256, 64, 8) == L.lcvq_gemv2b_workspace_size(1, 256, 256, 8)
     assert g(wsb=L.lcvq_gemv2b_workspace_size(1, 256, 256, 8) - 1) == 6
     need = L.lcvq_gemv2b_workspace_size(16, 4096, 14336, 8)
     assert need > L.lcvq_gemv2b_workspace_size(1, 4096, 4096, 8) > 0
@@ -171,6 +177,7 @@ def test_gemv_shuffle_errors(L):
                                       a["A"], a["B"], a["Y"], a["ws"], a["wsb"], None)
     assert s(codes=None) == 1
     assert s(M=17) == 2
+    assert s(K=320) == 2                               # the decode layout needs K % 256
     assert s(d=5) == 3
     assert s(codes=MIS) == 5
 
@@ -187,9 +194,12 @@ def test_gemv_batched_errors(L):
     assert g(count=0) == 2
     assert g(count=9) == 2
     assert g(M=17) == 2
-    assert g(K=320) == 2
+    assert g(K=288) == 2
     assert g(d=5) == 3
     assert g(wsb=ws - 1) == 6
+    mats[1].layout = 1                                # decode layout: K % 256
+    assert g(K=320, wsb=1 << 30) == 2
+    mats[1].layout = 0
     mats[1].N = 40
     assert g() == 2
     mats[1].N = 256
@@ -261,9 +271,10 @@ def test_gemv_noalloc_errors(L):
     assert g(Y=None) == 1
     assert g(M=17) == 2
     assert g(N=40) == 2
-    assert g(K=320) == 2
+    assert g(K=288) == 2
     assert g(d=5) == 3
     assert g(K=65536 + 256) == 9                     # LCVQ_ERR_SCRATCH
+    assert g(K=65536 + 64) == 9
     assert g(K=1 << 20, N=16) == 9
     assert L.lcvq_status_string(9) != b"unknown status"
 

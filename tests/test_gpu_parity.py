@@ -250,6 +250,32 @@ def test_gemv_more_tokens(P, N, K, M, d):
     note(f"  {fmt(check(host(Y), ref, TOL, 'gemv more tokens'))}")
 
 
+@pytest.mark.parametrize("N,K,M,d", [(256, 64, 1, 8), (512, 192, 12, 8), (4096, 4160, 1, 8),
+                                     (4096, 4160, 4, 8), (4096, 4160, 16, 8), (14336, 4288, 2, 8),
+                                     (1024, 14400, 3, 16), (272, 16320, 1, 4),
+                                     (4096, 16448, 1, 8), (2048, 320, 7, 16)])
+def test_gemv_partial_block(P, N, K, M, d):
+    """K a multiple of 64 but not of 256: the last 256-column block is partial, on the
+    one-launch path and on the prologue + product path (K < 256 included)."""
+    note(f"gemv partial block N={N} K={K} M={M} d={d}")
+    wp = SI.make_wp(N, K, seed=3600 + N + K, device="cuda")
+    A, B = SI.make_ab(d, seed=3600 + d + M)
+    X = SI.make_act(M, K, seed=3700 + M, device="cuda")
+    pk = torch.empty((N, K // 4), dtype=torch.uint8, device="cuda")
+    P.lcvq_quantize(wp, None, pk, None)
+    ws = torch.empty(P.lcvq_gemv2b_workspace_size(M, N, K, d), dtype=torch.uint8,
+                     device="cuda")
+    ys = []
+    for _ in range(2):                       # repeated calls through one workspace
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        P.lcvq_gemv2b(X, pk, A.half().cuda(), B.half().cuda(), d, Y, ws)
+        ys.append(Y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0], ys[1])
+    ref = O.gemv2b(host(X), host(pk), A.half().double().numpy(), B.half().double().numpy(), d)
+    note(f"  {fmt(check(host(ys[0]), ref, TOL, 'gemv partial block'))}")
+
+
 @pytest.mark.parametrize("d", [4, 16])
 @pytest.mark.parametrize("N,K", [(4096, 4096), (2048, 14336)])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 16])
@@ -454,7 +480,8 @@ def test_gemv_shuffled_matches(P, N, K, M):
 
 
 @pytest.mark.parametrize("shapes,K", [([4096, 1024, 1024], 4096), ([14336, 14336], 4096),
-                                      ([8192, 272], 256), ([4096], 14336), ([1024, 1024], 4096)])
+                                      ([8192, 272], 256), ([4096], 14336), ([1024, 1024], 4096),
+                                      ([4096, 1024, 1024], 4160)])
 @pytest.mark.parametrize("M", [1, 2, 4, 5, 8])
 def test_gemv_batched(P, shapes, K, M):
     """Several matrices sharing X in one call: every output equals the single-matrix
@@ -473,15 +500,17 @@ def test_gemv_batched(P, shapes, K, M):
         singles.append(P.gemv2b(X, pk, A16, B16, d))
         refs.append((pk, A.half().double().numpy(), B.half().double().numpy()))
     P.lcvq_gemv2b_batched(X, mats, d)
-    # the same call with every other matrix in the decode layout
+    # the same call with every other matrix in the decode layout (whole 256-column blocks)
     mixed = [(P.gemv2b_shuffle(pk), a16, b16, torch.empty_like(y), 1) if i % 2 else
              (pk, a16, b16, torch.empty_like(y), 0)
-             for i, (pk, a16, b16, y) in enumerate(mats)]
-    P.lcvq_gemv2b_batched(X, mixed, d)
+             for i, (pk, a16, b16, y) in enumerate(mats)] if K % 256 == 0 else None
+    if mixed is not None:
+        P.lcvq_gemv2b_batched(X, mixed, d)
     torch.cuda.synchronize()
-    for (pk, _, _, Y), mx, ys, (pkr, Ah, Bh) in zip(mats, mixed, singles, refs):
+    for i, ((pk, _, _, Y), ys, (pkr, Ah, Bh)) in enumerate(zip(mats, singles, refs)):
         assert torch.equal(Y, ys)
-        assert torch.equal(mx[3], ys)
+        if mixed is not None:
+            assert torch.equal(mixed[i][3], ys)
         check(host(Y), O.gemv2b(host(X), host(pkr), Ah, Bh, d), TOL, "gemv batched")
 
 

@@ -56,6 +56,7 @@ def _noalloc(P, X, pk, A16, B16, d, Y):
     ((4096, 14336, 16), (1024, 4096, 5)),     # prologue + product path, then a smaller one
     ((14336, 4096, 1), (272, 2048, 2)),       # one-launch path, then a smaller one
     ((4096, 65536, 16), (512, 8192, 3)),      # the largest K the scratch holds
+    ((4096, 4160, 16), (1024, 4288, 1)),      # a partial last block of 256 columns
 ])
 def test_noalloc_matches_workspace_call(P, d, first, second):
     outs = []
