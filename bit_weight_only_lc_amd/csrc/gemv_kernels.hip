@@ -38,23 +38,33 @@ inline size_t gemv_fused_lds(int M, int K, int d, bool two) {
 
 // The fused path (X' formed in LDS by every workgroup) repeats the M * K * d multiply-adds
 // of X' in every workgroup, under the code stream; the two-kernel path pays a second
-// launch and the X' round trip through memory instead. Fused: one or two tokens with K
-// up to 64 blocks; three or four with K up to 32 blocks (one or two row groups per
-// workgroup); and where each workgroup takes one row group, its LDS fits, the grid runs
-// in one round of one workgroup per CU (rows / 16 <= 256) and the X' work per workgroup,
-// M * (K / 256) * d, is at most 1792: three or four tokens with K up to 64 blocks, five
-// to twelve tokens with K up to 16 blocks. (Measured on 4096 x 4096, 1024 x 4096 and
-// 4096 x 14336 at d = 4, 8, 16, one build against the other on one GPU: within that
-// bound the fused launch took 0.56-0.91x the two launches; beyond it 1.0-1.28x.)
+// launch and the X' round trip through memory instead. Fused:
+//  * base range: one or two tokens with K up to 64 blocks; three or four with K up to 32
+//    blocks; one row group per workgroup, or two from 8192 rows on;
+//  * extended range, where the X' work per workgroup, M * (K / 256) * d, is at most 1792,
+//    the grid runs in one round of one workgroup per CU and the LDS fits: one row group
+//    per workgroup up to 4096 rows (three or four tokens with K up to 64 blocks, five to
+//    sixteen with K up to 16 blocks), two up to 8192 rows (five to sixteen tokens).
+// (Measured one build against the other on one GPU, shapes 4096 x 4096, 1024 x 4096,
+// 4096 x 2048, 8192 x 4096 and 4096 x 14336 at d = 4, 8, 16: within the bound the fused
+// launch took 0.56-0.91x the two launches, beyond it 1.0-1.28x.)
 constexpr int GEMV_FUSED_WORK = 1792;
+inline bool gemv_fused_base(int M, int nkb) {
+  return M <= 2 ? nkb <= 64 : (M <= 4 && nkb <= 32);
+}
 inline bool gemv_fused(int M, int K, int64_t rows, int d) {
   const int nkb = gemv_blocks(K);
-  if (M <= 2) return nkb <= 64;
-  if (M <= 4 && nkb <= 32) return true;
-  const bool two = rows >= 2 * 16 * 256;
-  if (two || rows / 16 > 256 || gemv_fused_lds(M, K, d, false) > GEMV_LDS_MAX) return false;
-  if (M > 12 || M * nkb * d > GEMV_FUSED_WORK) return false;
+  if (gemv_fused_base(M, nkb)) return true;
+  if (M > 16 || M * nkb * d > GEMV_FUSED_WORK) return false;
+  const bool two = rows > 16 * 256;
+  if (rows > (two ? 2 : 1) * 16 * 256 || (two && M <= 4)) return false;
+  if (gemv_fused_lds(M, K, d, two) > GEMV_LDS_MAX) return false;
   return M <= 4 ? nkb <= 64 : nkb <= 16;
+}
+// Two row groups per workgroup: from 8192 rows on in the base range, beyond 4096 rows in
+// the extended range (each keeps the grid to about a workgroup per CU).
+inline bool gemv_two_groups(int M, int K, int64_t rows) {
+  return gemv_fused_base(M, gemv_blocks(K)) ? rows >= 2 * 16 * 256 : rows > 16 * 256;
 }
 bool gemv_fused_path(int M, int K, int64_t rows, int d) { return gemv_fused(M, K, rows, d); }
 
@@ -387,8 +397,8 @@ __global__ __launch_bounds__(GW * 64) void k_gemv(const int8_t* __restrict__ xq,
 // and the X' round trip through memory.
 // One launch can serve up to GEMV_MAX_BATCH matrices that share X (and K), each with its
 // own codes, A, B and output: workgroups [wg0[i], wg0[i+1]) belong to matrix i.
-// MT is the token count, or for MT = 8 and 12 a bound on the run-time count Mrt (5..8,
-// 9..12), which then sets the LDS layout and the X' work.
+// MT is the token count, or for MT = 8, 12 and 16 a bound on the run-time count Mrt
+// (5..8, 9..12, 13..16), which then sets the LDS layout and the X' work.
 template <int D, int RG, int KSW, int MT>
 __global__ __launch_bounds__(GWF * 64) void k_gemv_fused(const uint16_t* __restrict__ X,
                                                          GemvBatch batch, int K, int Mrt) {
@@ -630,7 +640,7 @@ static hipError_t launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint1
 }
 
 // The instances gemv_fused() can reach: M = 3, 4 with two row groups only for K up to 32
-// blocks (KSW <= 4); M = 5..12 with one row group and K up to 16 blocks (KSW = 2).
+// blocks (KSW <= 4); M = 5..16 with K up to 16 blocks (KSW = 2).
 template <int D, int RG, int KSW>
 static hipError_t launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
                                  const GemvBatch& b, int K) {
@@ -640,9 +650,10 @@ static hipError_t launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, co
     if (M == 3) return launch_fused<D, RG, KSW, 3>(grid, shm, s, X, b, K, M);
     if (M == 4) return launch_fused<D, RG, KSW, 4>(grid, shm, s, X, b, K, M);
   }
-  if constexpr (RG == 1 && KSW <= 2) {
+  if constexpr (KSW <= 2) {     // the X' items a thread holds grow with the bound
     if (M <= 8) return launch_fused<D, RG, KSW, 8>(grid, shm, s, X, b, K, M);
     if (M <= 12) return launch_fused<D, RG, KSW, 12>(grid, shm, s, X, b, K, M);
+    if (M <= 16) return launch_fused<D, RG, KSW, 16>(grid, shm, s, X, b, K, M);
   }
   return hipErrorInvalidValue;       // not reached: gemv_fused() picks only the cases above
 }
@@ -670,8 +681,7 @@ hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b
                              hipStream_t s) {
   int64_t rows = 0;
   for (int i = 0; i < b.count; ++i) rows += b.N[i];
-  // Two row groups per workgroup when the rows still give a workgroup per CU.
-  const bool two = rows >= 2 * 16 * 256;
+  const bool two = gemv_two_groups(M, K, rows);
   int wgs = 0;
   for (int i = 0; i < b.count; ++i) {
     b.wg0[i] = wgs;

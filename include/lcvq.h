@@ -222,10 +222,10 @@ lcvq_status_t lcvq_gemv2b_shuffled(const void* X, int64_t M, int64_t N, int64_t 
  * own codes and its own A, B (LC-QAT summary, Methodology 1: A and B are shared within
  * one weight matrix). Every output equals what lcvq_gemv2b gives for that matrix, byte
  * for byte. With M <= 2 and K <= 16384, or M <= 4 and K <= 8192, all of them run in
- * one launch; likewise for up to 4096 rows in all with 3 <= M <= 12, where the one-launch
- * kernel's bound on its activation work, M * (K / 256) * d <= 1792 (K <= 16384 for
- * M <= 4, K <= 4096 beyond), holds; otherwise each matrix is computed as lcvq_gemv2b
- * computes it, one after the other, on `stream`.
+ * one launch; likewise for up to 8192 rows in all (4096 with M <= 4) with M >= 3, where
+ * the one-launch kernel's bound on its activation work, M * ceil(K / 256) * d <= 1792
+ * (K <= 16384 for M <= 4, K <= 4096 beyond), holds; otherwise each matrix is computed as
+ * lcvq_gemv2b computes it, one after the other, on `stream`.
  *   X       bfloat16 [M, K], 1 <= M <= 16, K a multiple of 64 (of 256 if any matrix is
  *           in the decode layout)
  *   mats    host array of `count` descriptors, 1 <= count <= 8; mats[i].N a multiple of

@@ -229,12 +229,15 @@ def test_gemv(P, N, K, M):
                                      (4096, 4096, 12, 4), (1024, 4096, 11, 16), (272, 4096, 9, 8),
                                      (4096, 16384, 4, 8), (256, 16384, 3, 16), (2048, 16384, 4, 4),
                                      (4352, 4096, 12, 8), (256, 8192, 12, 8), (4096, 4096, 13, 8),
-                                     (4096, 4096, 7, 16)])
+                                     (4096, 4096, 7, 16), (8192, 4096, 9, 8), (6144, 4096, 5, 8),
+                                     (4096, 2048, 16, 8), (4096, 4096, 16, 4), (8192, 4096, 7, 16),
+                                     (8208, 4096, 8, 8), (4096, 4096, 15, 8)])
 def test_gemv_more_tokens(P, N, K, M, d):
-    """Token counts and K at the edges of the one-launch path's range: five to twelve
-    tokens with K up to 16 blocks of 256, three or four tokens with K up to 64 blocks, and
-    just past them (more than 256 row groups, K of 32 blocks at 12 tokens, 13 tokens),
-    which take the prologue + product path."""
+    """Token counts and K at the edges of the one-launch path's range (five to sixteen
+    tokens with K up to 16 blocks of 256, three or four tokens with K up to 64 blocks, one
+    row group per workgroup up to 4096 rows and two up to 8192, within the bound on the
+    activation work), and just past them (more than 8192 rows, K of 32 blocks at 12
+    tokens, work past the bound), which take the prologue + product path."""
     note(f"gemv more tokens N={N} K={K} M={M} d={d}")
     wp = SI.make_wp(N, K, seed=3400 + N + K, device="cuda")
     A, B = SI.make_ab(d, seed=3400 + d + M)
