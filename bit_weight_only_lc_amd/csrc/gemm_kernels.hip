@@ -810,16 +810,20 @@ constexpr int TROWB = 512;                     // bytes per LDS row of a transpo
 constexpr int TTILEB = 64 * TROWB;             // 32 KiB
 __device__ __forceinline__ int tswz(int m) { return (m & 3) << 2; }
 
-__device__ __forceinline__ bf16x8 trans_frag(const uint8_t* tile, int colbase, int s, int lane) {
+// `buf` is the LDS array itself and `tile` the tile's byte offset in it: each read's
+// address is one offset from the array, so that the compiler can attribute the read to
+// that array (its alias scope is carried only along short chains of address arithmetic).
+__device__ __forceinline__ bf16x8 trans_frag(const uint8_t* buf, int tile, int colbase, int s,
+                                             int lane) {
   const int g = lane >> 4, t = lane & 15;
   const int col = colbase + 16 * (g & 1) + 4 * (t & 3);
   const int m = 16 * s + 8 * (g >> 1) + (t >> 2);
   const int m2 = m + 4;
-  const LCVQ_LDS uint8_t* base = (const LCVQ_LDS uint8_t*)tile;
-  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (LCVQ_LDS v4i16*)(base + m * TROWB + (((col >> 3) ^ tswz(m)) << 4) + ((col & 4) << 1)));
-  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (LCVQ_LDS v4i16*)(base + m2 * TROWB + (((col >> 3) ^ tswz(m2)) << 4) + ((col & 4) << 1)));
+  const LCVQ_LDS uint8_t* base = (const LCVQ_LDS uint8_t*)buf;
+  const int off_lo = tile + m * TROWB + (((col >> 3) ^ tswz(m)) << 4) + ((col & 4) << 1);
+  const int off_hi = tile + m2 * TROWB + (((col >> 3) ^ tswz(m2)) << 4) + ((col & 4) << 1);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(base + off_lo));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(base + off_hi));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
   const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
@@ -883,30 +887,37 @@ __device__ __forceinline__ DwLaneOffsets dw_lane_offsets(int N, int K, int p0, i
   }
   return o;
 }
+// Operand OPN (0: X, 1: dY) of one stage, so that a stage's loads can be issued in two
+// halves.
+template <int OPN>
+__device__ __forceinline__ void issue_dw_stage_rows_op(uint8_t* slot, const uint16_t* X,
+                                                       const uint16_t* dY, int M, int N, int K,
+                                                       int m0, const DwLaneOffsets& o, int wave,
+                                                       int lane) {
+  const uint16_t* mat = OPN == 0 ? X : dY;
+  const int ld = OPN == 0 ? K : N;
+  uint8_t* tile = slot + OPN * TTILEB;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int row = m0 + wave * 8 + i * 2;                   // uniform
+    uint32_t off = o.v[OPN][i & 1];
+    if (row + 1 >= M) {
+      // the second row of the pair (or both) lies past M: both halves read row
+      // min(row, M - 1), whose copy in a row past M is cleared afterwards
+      row = row < M ? row : M - 1;
+      off -= (uint32_t)((lane >> 5) * ld * 2);
+    }
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(mat + (int64_t)row * ld);
+    __builtin_amdgcn_global_load_lds(base + off,
+                                     (LCVQ_LDS void*)(tile + (wave * 8 + i * 2) * TROWB), 16, 0, 0);
+  }
+}
 __device__ __forceinline__ void issue_dw_stage_rows(uint8_t* slot, const uint16_t* X,
                                                     const uint16_t* dY, int M, int N, int K,
                                                     int m0, const DwLaneOffsets& o, int wave,
                                                     int lane) {
-#pragma unroll
-  for (int op = 0; op < 2; ++op) {
-    const uint16_t* mat = op == 0 ? X : dY;
-    const int ld = op == 0 ? K : N;
-    uint8_t* tile = slot + op * TTILEB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = m0 + wave * 8 + i * 2;                   // uniform
-      uint32_t off = o.v[op][i & 1];
-      if (row + 1 >= M) {
-        // the second row of the pair (or both) lies past M: both halves read row
-        // min(row, M - 1), whose copy in a row past M is cleared afterwards
-        row = row < M ? row : M - 1;
-        off -= (uint32_t)((lane >> 5) * ld * 2);
-      }
-      const uint8_t* base = reinterpret_cast<const uint8_t*>(mat + (int64_t)row * ld);
-      __builtin_amdgcn_global_load_lds(base + off,
-                                       (LCVQ_LDS void*)(tile + (wave * 8 + i * 2) * TROWB), 16, 0, 0);
-    }
-  }
+  issue_dw_stage_rows_op<0>(slot, X, dY, M, N, K, m0, o, wave, lane);
+  issue_dw_stage_rows_op<1>(slot, X, dY, M, N, K, m0, o, wave, lane);
 }
 // Wave w clears its own rows [8w, 8w + 8) of both tiles where m0 + row >= M; called after
 // its loads have landed and before the stage's barrier.
@@ -931,9 +942,53 @@ template <int WJ>
 __device__ __forceinline__ void dw_read(const uint8_t* slot, int s, int wp, int wq, int lane,
                                         DwFrags<WJ>& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = trans_frag(slot, wp * 128 + i * 32, s, lane);
+  for (int i = 0; i < 4; ++i) f.a[i] = trans_frag(slot, 0, wp * 128 + i * 32, s, lane);
 #pragma unroll
-  for (int j = 0; j < WJ; ++j) f.b[j] = trans_frag(slot + TTILEB, wq * 32 * WJ + j * 32, s, lane);
+  for (int j = 0; j < WJ; ++j) f.b[j] = trans_frag(slot, TTILEB, wq * 32 * WJ + j * 32, s, lane);
+}
+
+// The same fragments from per-lane byte offsets computed once (dw_frag_offsets): the
+// fragment of sub-step s starts 16 s rows = 8192 bytes further, and its second half
+// (rows m + 4, same swizzle) 2048 bytes further. Each read address is then the LDS array
+// plus one opaque offset plus a constant, a chain short enough that the compiler keeps
+// the read attributed to its array.
+struct DwOffsets {
+  int a[4], b[2];
+};
+__device__ __forceinline__ int dw_frag_off(int k, int lane) {   // column block 32 k, s = 0
+  const int g = lane >> 4, t = lane & 15;
+  const int col = 32 * k + 16 * (g & 1) + 4 * (t & 3);
+  const int m = 8 * (g >> 1) + (t >> 2);
+  return m * TROWB + (((col >> 3) ^ tswz(m)) << 4) + ((col & 4) << 1);
+}
+__device__ __forceinline__ DwOffsets dw_frag_offsets(int wp, int wq, int lane) {
+  DwOffsets o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o.a[i] = dw_frag_off(4 * wp + i, lane);
+    asm volatile("" : "+v"(o.a[i]));
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    o.b[j] = TTILEB + dw_frag_off(2 * wq + j, lane);
+    asm volatile("" : "+v"(o.b[j]));
+  }
+  return o;
+}
+__device__ __forceinline__ bf16x8 trans_frag_at(const uint8_t* buf, int off) {
+  const LCVQ_LDS uint8_t* base = (const LCVQ_LDS uint8_t*)buf;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(base + off));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LCVQ_LDS v4i16*)(base + off + 4 * TROWB));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ void dw_read_at(const uint8_t* buf, int s, const DwOffsets& o,
+                                           DwFrags<2>& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = trans_frag_at(buf, o.a[i] + s * 16 * TROWB);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f.b[j] = trans_frag_at(buf, o.b[j] + s * 16 * TROWB);
 }
 
 template <int WJ>
@@ -958,33 +1013,41 @@ __device__ __forceinline__ void dw_mfma(const DwFrags<WJ>& f, f32x16 acc[4][WJ])
 // v(z) fragments expanded from the tile's transposed code words (the dX product's code
 // layout). Each wave's sums run over all its blocks; the waves' sums are then added in a
 // fixed order into the tile's partial row `prow`.
-// dW LDS map: the double buffer (2 x 64 KiB) during the main loop, then per-wave
-// epilogue areas below 128 KiB; the tile's transposed code words (4 slabs of 256 rows k x
-// 16 bytes) and mask bits (256 columns n x 32 bytes) live above it from kernel start.
-constexpr int DW_CODES_OFF = 128 * 1024;
-constexpr int DW_MASK_OFF = DW_CODES_OFF + 4 * 4096;    // 144 KiB
-constexpr int DW_SMEM = DW_MASK_OFF + 256 * 32;         // 152 KiB
+// dW LDS map: two arrays. The main loop's double buffer is stage buffer 0 at the start of
+// the first array and stage buffer 1, the second array (64 KiB each); the tile's
+// transposed code words (4 slabs of 256 rows k x 16 bytes) and mask bits (256 columns n x
+// 32 bytes) follow buffer 0 in the first array from kernel start. The two buffers are
+// separate arrays so that the compiler can tell a direct load into one from a read of
+// the other: with one array it makes every LDS read wait for the direct loads issued
+// before it. The epilogue's per-wave areas then take waves 0-4 in buffer 0 and waves 5-7,
+// the waves' sums and A's copy in buffer 1.
+constexpr int DW_CODES_OFF = 64 * 1024;
+constexpr int DW_MASK_OFF = DW_CODES_OFF + 4 * 4096;    // 80 KiB
+constexpr int DW_SMEM0 = DW_MASK_OFF + 256 * 32;        // 88 KiB
+constexpr int DW_SMEM1 = 64 * 1024;
+constexpr int DW_WREG = 12 * 1024;                      // per-wave epilogue area
+constexpr int DW_WAVES_IN_B0 = 5;
+constexpr int DW_WSUM_OFF = (8 - DW_WAVES_IN_B0) * DW_WREG;   // in buffer 1
+constexpr int DW_A_OFF = 56 * 1024;                           // in buffer 1
 constexpr int GTROWB = 72;                 // bytes per row n of a staged bf16 half of G
 
 // ALDS: A is read from its copy in LDS (d = 16, and the second phase of a split launch).
-// CO, MO: LDS offsets of the tile's code words and mask bits.
-template <int D, int NW, int WJ, bool ALDS, int CO = DW_CODES_OFF, int MO = DW_MASK_OFF>
+// area: this wave's DW_WREG bytes of LDS (staging, then its reduction); wsum: the waves'
+// sums [NW][d*d + d]; codes_lds, mask_lds: the tile's code words and mask bits in LDS.
+template <int D, int NW, int WJ, bool ALDS>
 __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ], int p0, int q0, int wp, int wq,
-                            int lane, int wave, int prow, uint8_t* smem, const float* Alds) {
-  constexpr int WREG = 12 * 1024;              // per-wave LDS area: staging, then reduction
+                            int lane, int wave, int prow, uint8_t* area, float* wsum,
+                            const uint8_t* codes_lds, const uint8_t* mask_lds, const float* Alds) {
   constexpr int SBYTES = 32 * SROWT * 4;
   constexpr int GTB = 32 * GTROWB;
   constexpr int NO = D * D + D;
   constexpr int DBS = D == 16 ? 8 : 4;         // dB partial sums per lane
   constexpr int RRED = 17;                     // row of the wave reduction (16 + pad)
-  static_assert(SBYTES + 2 * GTB <= WREG && (64 * RRED + 16) * 4 <= WREG, "per-wave LDS area");
-  static_assert(NW * WREG + NW * NO * 4 <= (CO == DW_CODES_OFF ? 120 : 28) * 1024,
-                "per-wave areas and sums below A's copy");
-  uint8_t* area = smem + wave * WREG;
+  static_assert(SBYTES + 2 * GTB <= DW_WREG && (64 * RRED + 16) * 4 <= DW_WREG,
+                "per-wave LDS area");
   float* S = reinterpret_cast<float*>(area);
   uint8_t* GTh = area + SBYTES;
   uint8_t* GTl = GTh + GTB;
-  float* wsum = reinterpret_cast<float*>(smem + NW * WREG);      // [NW][NO]
   const int q = lane & 31, h = lane >> 5;
 
   // Mix operands. In the MFMA over accumulator registers 8t .. 8t+7, slot e of lane half h
@@ -1056,7 +1119,7 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
       o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(AMh[1], Gl1, o, 0, 0, 0);
       // mask bits of (n, kb .. kb+31): register r of o is row 8(r/4) + 4h + r%4
       const uint32_t mw =
-          *reinterpret_cast<const uint32_t*>(smem + MO + (n - q0) * 32 + ((kb - p0) >> 3)) >> (4 * h);
+          *reinterpret_cast<const uint32_t*>(mask_lds + (n - q0) * 32 + ((kb - p0) >> 3)) >> (4 * h);
       wave_sync();                    // the previous block's store and reads are done
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
@@ -1088,7 +1151,7 @@ __device__ __forceinline__ void epilogue_dw(const GemmArgs& a, f32x16 acc[4][WJ]
         const bf16x8 Ah = __builtin_bit_cast(bf16x8, v8i16{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]});
         const bf16x8 Al = __builtin_bit_cast(bf16x8, v8i16{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]});
         const int nl = nb - q0 + 16 * u;
-        const uint32_t w = codes_word(smem + CO + (nl >> 6) * 4096, kb - p0 + q, (nl >> 4) & 3);
+        const uint32_t w = codes_word(codes_lds + (nl >> 6) * 4096, kb - p0 + q, (nl >> 4) & 3);
         const bf16x8 bv = codes_expand(w, ek);
         P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Ah, bv, P, 0, 0, 0);
         P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(Al, bv, P, 0, 0, 0);
@@ -1188,7 +1251,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_dw(GemmArgs a) {
   static_assert(SPL == 0 || SPL == 1, "phase 2 of a split dW is k_gemm_dw_epi");
   constexpr int NW = 8, WGQ = 4, WJ = 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[DW_SMEM];   // 152 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[DW_SMEM0];   // buffer 0, codes, mask
+  __shared__ __attribute__((aligned(1024))) uint8_t smem1[DW_SMEM1];  // buffer 1
   int tp, tq, tile;
   // X and dY panels weigh the same: 4 x 8 tiles per XCD reads the fewest panels.
   int split = 0;
@@ -1204,6 +1268,8 @@ void k_gemm_dw(GemmArgs a) {
   int kt0 = 0, kt1 = (a.R + BK - 1) / BK;
   if constexpr (SPL == 1) split_range(kt1, split, a.splits, kt0, kt1);
   const DwLaneOffsets lo = dw_lane_offsets(a.N, a.K, p0, q0, lane);
+  static_assert(WJ == 2, "dw_frag_offsets holds two column fragments");
+  const DwOffsets fo = dw_frag_offsets(wp, wq, lane);
   if constexpr (SPL == 0)                            // for the epilogue
     issue_dw_codes(smem + DW_CODES_OFF, smem + DW_MASK_OFF, a.codes, a.mask, a.N, a.K, p0, q0,
                    wave, lane);
@@ -1222,49 +1288,67 @@ void k_gemm_dw(GemmArgs a) {
     issue_dw_stage(smem, Lp, Rp, a.M, a.N, a.K, kt0 * BK, p0, q0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // Every transposing LDS read of a stage is issued before the next stage's direct
-    // loads: the compiler makes an LDS read that follows a direct global->LDS load in
-    // program order wait for that load, which would serialize the two. Sub-steps 0-2 are
-    // read first, sub-step 3 into sub-step 0's registers once its MFMAs have issued, and
-    // the next stage's loads then run under the MFMAs of sub-steps 1-3.
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const uint8_t* slot = smem + ((kt - kt0) & 1) * 2 * TTILEB;
-      DwFrags<WJ> f0, f1, f2;
-      dw_read<WJ>(slot, 0, wp, wq, lane, f0);
-      dw_read<WJ>(slot, 1, wp, wq, lane, f1);
-      dw_read<WJ>(slot, 2, wp, wq, lane, f2);
+    // One stage: the current buffer's fragments are read up to two sub-steps ahead of
+    // their MFMAs, and the next stage's direct loads go into the other buffer (free since
+    // the last barrier) in two halves, X's rows under sub-step 0's MFMAs and dY's under
+    // sub-step 1's, so that they land under the rest of the stage without crowding its
+    // first reads. The buffers are fixed per call (the loop is unrolled by two), so the
+    // compiler sees that the reads of one buffer do not depend on the loads into the
+    // other. (Measured against the earlier order, all fragment reads of sub-steps 0-2
+    // before one batch of loads: c1 dW 115.5 -> 112.9 us, 896-tile 14336 x 4096 dW at 8192
+    // tokens 888 -> 832 us; issuing all loads at the start of the stage was slower.)
+    auto stage = [&](const uint8_t* cur, uint8_t* nxt, int kt) __attribute__((always_inline)) {
+      DwFrags<WJ> f0, f1;
+      dw_read_at(cur, 0, fo, f0);
+      dw_read_at(cur, 1, fo, f1);
       __builtin_amdgcn_sched_barrier(0);
       dw_mfma<WJ>(f0, acc);
       __builtin_amdgcn_sched_barrier(0);
-      dw_read<WJ>(slot, 3, wp, wq, lane, f0);
-      __builtin_amdgcn_sched_barrier(0);
-      uint8_t* next = smem + (((kt - kt0) & 1) ^ 1) * 2 * TTILEB;
       if (kt + 1 < kt1)
-        issue_dw_stage_rows(next, Lp, Rp, a.M, a.N, a.K, (kt + 1) * BK, lo, wave, lane);
+        issue_dw_stage_rows_op<0>(nxt, Lp, Rp, a.M, a.N, a.K, (kt + 1) * BK, lo, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      dw_read_at(cur, 2, fo, f0);
       __builtin_amdgcn_sched_barrier(0);
       dw_mfma<WJ>(f1, acc);
-      dw_mfma<WJ>(f2, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < kt1)
+        issue_dw_stage_rows_op<1>(nxt, Lp, Rp, a.M, a.N, a.K, (kt + 1) * BK, lo, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      dw_read_at(cur, 3, fo, f1);
+      __builtin_amdgcn_sched_barrier(0);
       dw_mfma<WJ>(f0, acc);
+      dw_mfma<WJ>(f1, acc);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(0);
       if (kt + 1 < kt1 && (kt + 1) * BK + wave * 8 + 8 > a.M)
-        zero_dw_rows(next, (kt + 1) * BK, a.M, wave, lane);
+        zero_dw_rows(nxt, (kt + 1) * BK, a.M, wave, lane);
       __syncthreads();
+    };
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      stage(smem, smem1, kt);
+      if (kt + 1 < kt1) stage(smem1, smem, kt + 1);
     }
   }
   if constexpr (SPL == 1) {
     split_store<4, WJ>(a, acc, tile, split, tid);
     return;
   }
-  // The buffers are free after the last barrier: per-wave areas of 12 KiB from 0, the
-  // per-wave sums after them, and for d = 16 a copy of A at 120 KiB.
-  float* Alds = reinterpret_cast<float*>(smem + 120 * 1024);
+  // The buffers are free after the last barrier: per-wave areas of 12 KiB (waves 0-4 in
+  // buffer 0, 5-7 in buffer 1), the waves' sums and for d = 16 a copy of A in buffer 1.
+  static_assert(DW_WAVES_IN_B0 * DW_WREG <= DW_CODES_OFF, "waves 0-4 below the code words");
+  static_assert(DW_WSUM_OFF + NW * (D * D + D) * 4 <= DW_A_OFF &&
+                DW_A_OFF + D * D * 4 <= DW_SMEM1, "sums and A in buffer 1");
+  float* Alds = reinterpret_cast<float*>(smem1 + DW_A_OFF);
   constexpr bool ALDS = D == 16;
   if (ALDS) {
     if (tid < D * D) Alds[tid] = a.A[tid];
     __syncthreads();
   }
-  epilogue_dw<D, NW, WJ, ALDS>(a, acc, p0, q0, wp, wq, lane, wave, tile, smem, Alds);
+  uint8_t* area = wave < DW_WAVES_IN_B0 ? smem + wave * DW_WREG
+                                        : smem1 + (wave - DW_WAVES_IN_B0) * DW_WREG;
+  epilogue_dw<D, NW, WJ, ALDS>(a, acc, p0, q0, wp, wq, lane, wave, tile, area,
+                               reinterpret_cast<float*>(smem1 + DW_WSUM_OFF),
+                               smem + DW_CODES_OFF, smem + DW_MASK_OFF, Alds);
 }
 
 // Phase 2 of a split dW launch, spread over DW_EPI_G workgroups per tile so that few-tile
@@ -1302,8 +1386,12 @@ __global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
   split_load<4, WJ>(a, acc, tile, v * 64 + lane, 512);
   __builtin_amdgcn_s_waitcnt(0);                          // the codes and mask in LDS
   __syncthreads();
-  epilogue_dw<D, DW_EPI_NW, WJ, true, EPI_CODES_OFF, EPI_MASK_OFF>(
-      a, acc, p0, q0, wp, wq, lane, lw, DW_EPI_G * tile + g, smem, Alds);
+  static_assert(DW_EPI_NW * DW_WREG + DW_EPI_NW * (D * D + D) * 4 <= EPI_A_OFF,
+                "per-wave areas and sums below A's copy");
+  epilogue_dw<D, DW_EPI_NW, WJ, true>(a, acc, p0, q0, wp, wq, lane, lw, DW_EPI_G * tile + g,
+                                      smem + lw * DW_WREG,
+                                      reinterpret_cast<float*>(smem + DW_EPI_NW * DW_WREG),
+                                      smem + EPI_CODES_OFF, smem + EPI_MASK_OFF, Alds);
 }
 
 // dA/dB partial rows the dW product of this shape writes (the reduction's input).
