@@ -94,6 +94,11 @@ struct GemmArgs {
   // epilogue. splits = 1: one launch, one workgroup per tile.
   int splits;
   float* split_ws;
+  // dW tail split (hyb_L > 0): tile t = x * hyb_per + i of XCD x (map_tile's order); the
+  // first hyb_F of each XCD's tiles run unsplit in one launch, the last hyb_L split their
+  // contraction in two (splits = 2) over a phase 1 and a phase 2 launch; their partial
+  // tiles are indexed x * hyb_L + (i - hyb_F).
+  int hyb_per, hyb_F, hyb_L;
   int bpt;                     // forward: tile rows along P, 256 or 128 (host side)
 };
 
@@ -103,6 +108,15 @@ __device__ __forceinline__ int lds_off(int row, int chunk) { return row * ROWB +
 // Tiles are spread so that consecutive workgroup ids land on different XCDs (the
 // dispatcher deals workgroups round-robin over the 8 XCDs) while each XCD works on a
 // compact group of GR tile-rows, which keeps its operand panels in its own L2.
+template <int GR>
+__device__ __forceinline__ void tile_coords(int t, int tilesP, int tilesQ, int& tp, int& tq) {
+  const int group = t / (GR * tilesQ);
+  const int within = t - group * GR * tilesQ;
+  int rows = tilesP - group * GR;
+  if (rows > GR) rows = GR;
+  tp = group * GR + within % rows;
+  tq = within / rows;
+}
 template <int GR>
 __device__ __forceinline__ bool map_tile(int b, int tilesP, int tilesQ, int ntiles, int& tp, int& tq, int& t) {
   const int per = (ntiles + 7) >> 3;
@@ -127,6 +141,22 @@ __device__ __forceinline__ bool map_split(int b, int tilesQ, int ntiles, int spl
   split = b / ntiles;
   tp = tile / tilesQ;
   tq = tile % tilesQ;
+  return true;
+}
+
+// dW tail split: workgroup b of a launch with `per_tile` workgroups per leftover tile ->
+// its XCD's leftover tile (as map_tile numbers the tiles, so that the tile's workgroups of
+// both phases share the XCD that the unsplit tiles of that range use), the index of its
+// partial tiles, and j = its slot among the tile's workgroups (split or epilogue group).
+__device__ __forceinline__ bool map_hybrid(const GemmArgs& a, int b, int per_tile, int& tp,
+                                           int& tq, int& tile, int& pidx, int& j) {
+  const int x = b & 7, w = b >> 3;
+  const int li = w % a.hyb_L;
+  j = w / a.hyb_L;
+  if (j >= per_tile) return false;
+  tile = x * a.hyb_per + a.hyb_F + li;
+  pidx = x * a.hyb_L + li;
+  tile_coords<4>(tile, a.tilesP, a.tilesQ, tp, tq);
   return true;
 }
 
@@ -1255,9 +1285,14 @@ void k_gemm_dw(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem1[DW_SMEM1];  // buffer 1
   int tp, tq, tile;
   // X and dY panels weigh the same: 4 x 8 tiles per XCD reads the fewest panels.
-  int split = 0;
+  int split = 0, pidx = 0;
   if constexpr (SPL == 1) {
-    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+    if (a.hyb_L) {
+      if (!map_hybrid(a, blockIdx.x, 2, tp, tq, tile, pidx, split)) return;
+    } else {
+      if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+      pidx = tile;
+    }
   } else if (!map_tile<4>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
     return;
   }
@@ -1330,7 +1365,7 @@ void k_gemm_dw(GemmArgs a) {
     }
   }
   if constexpr (SPL == 1) {
-    split_store<4, WJ>(a, acc, tile, split, tid);
+    split_store<4, WJ>(a, acc, pidx, split, tid);
     return;
   }
   // The buffers are free after the last barrier: per-wave areas of 12 KiB (waves 0-4 in
@@ -1357,7 +1392,8 @@ void k_gemm_dw(GemmArgs a) {
 // XCD, whose L2 holds the partials) and group g = b / ntiles, i.e. the tile's waves
 // v = DW_EPI_NW g .. + DW_EPI_NW - 1 of the 8-wave layout of phase 1. It adds their partial
 // accumulators in split order and runs their part of the straight-through epilogue; its
-// dA/dB sums go to partial row DW_EPI_G * tile + g. LDS: the waves' 12 KiB areas, their
+// dA/dB sums go to partial row DW_EPI_G * tile + g (tail split: see map_hybrid and prow
+// below). LDS: the waves' 12 KiB areas, their
 // sums, A, then the whole tile's codes and mask bits.
 constexpr int DW_EPI_NW = 2;
 constexpr int DW_EPI_G = 8 / DW_EPI_NW;
@@ -1369,9 +1405,20 @@ template <int D>
 __global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
   constexpr int WGQ = 4, WJ = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[EPI_SMEM];
-  const int tile = (int)blockIdx.x % a.ntiles, g = (int)blockIdx.x / a.ntiles;
-  if (g >= DW_EPI_G) return;
-  const int tp = tile / a.tilesQ, tq = tile % a.tilesQ;   // as map_split
+  int tile, g, tp, tq, pidx, prow;
+  if (a.hyb_L) {
+    if (!map_hybrid(a, blockIdx.x, DW_EPI_G, tp, tq, tile, pidx, g)) return;
+    // group 0 writes the tile's own partial row, groups 1-3 rows after the unsplit tiles'
+    prow = g == 0 ? tile : a.ntiles + (DW_EPI_G - 1) * pidx + g - 1;
+  } else {
+    tile = (int)blockIdx.x % a.ntiles;
+    g = (int)blockIdx.x / a.ntiles;
+    if (g >= DW_EPI_G) return;
+    tp = tile / a.tilesQ;                                // as map_split
+    tq = tile % a.tilesQ;
+    pidx = tile;
+    prow = DW_EPI_G * tile + g;
+  }
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int lw = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1383,21 +1430,46 @@ __global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
   float* Alds = reinterpret_cast<float*>(smem + EPI_A_OFF);
   for (int i = tid; i < D * D; i += DW_EPI_NW * 64) Alds[i] = a.A[i];
   f32x16 acc[4][WJ];
-  split_load<4, WJ>(a, acc, tile, v * 64 + lane, 512);
+  split_load<4, WJ>(a, acc, pidx, v * 64 + lane, 512);
   __builtin_amdgcn_s_waitcnt(0);                          // the codes and mask in LDS
   __syncthreads();
   static_assert(DW_EPI_NW * DW_WREG + DW_EPI_NW * (D * D + D) * 4 <= EPI_A_OFF,
                 "per-wave areas and sums below A's copy");
-  epilogue_dw<D, DW_EPI_NW, WJ, true>(a, acc, p0, q0, wp, wq, lane, lw, DW_EPI_G * tile + g,
+  epilogue_dw<D, DW_EPI_NW, WJ, true>(a, acc, p0, q0, wp, wq, lane, lw, prow,
                                       smem + lw * DW_WREG,
                                       reinterpret_cast<float*>(smem + DW_EPI_NW * DW_WREG),
                                       smem + EPI_CODES_OFF, smem + EPI_MASK_OFF, Alds);
 }
 
+// dW tail split: where the 256 x 256 tiles fill whole rounds of the 256 CUs plus a last
+// round at most half full (and the count is a multiple of the 8 XCDs), the tiles of the
+// full rounds run unsplit and each leftover tile splits its contraction in two, so that
+// the leftover work takes half a round instead of a whole one. Per XCD: hyb_per tiles,
+// the first hyb_F unsplit, the last hyb_L split. Needs at least 16 contraction stages.
+static bool dw_hybrid(int64_t M, int64_t N, int64_t K, int& per, int& F, int& L) {
+  const int64_t nt = gemm_tiles(K, N), r = nt % 256;
+  if (nt <= 256 || (nt % 8) || r == 0 || r > 128 || (M + BK - 1) / BK < 16) return false;
+  per = (int)(nt / 8);
+  L = (int)(r / 8);
+  F = per - L;
+  return true;
+}
+
 // dA/dB partial rows the dW product of this shape writes (the reduction's input).
 int dw_partial_rows(int64_t M, int64_t N, int64_t K) {
   const int nt = gemm_tiles(K, N);
-  return gemm_splits(K, N, M) > 1 ? nt * DW_EPI_G : nt;
+  int per, F, L;
+  if (gemm_splits(K, N, M) > 1) return nt * DW_EPI_G;
+  if (dw_hybrid(M, N, K, per, F, L)) return nt + (DW_EPI_G - 1) * 8 * L;
+  return nt;
+}
+
+// Bytes of float32 partial tiles the dW product needs (0: none).
+size_t dw_split_bytes(int64_t M, int64_t N, int64_t K) {
+  int per, F, L;
+  if (gemm_splits(K, N, M) > 1) return gemm_split_bytes(K, N, M);
+  if (dw_hybrid(M, N, K, per, F, L)) return (size_t)8 * L * 2 * BT * BT * 4;
+  return 0;
 }
 
 // ---- Gram matrix H = X^T X of calibration activations --------------------------------
@@ -1572,6 +1644,20 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   if constexpr (OP == OP_DX) {
     return launch_op1<OP, 0>(a, d, ((a.ntiles + 7) / 8) * 8, s);
   } else {
+    if constexpr (OP == OP_DW) {
+      if (a.hyb_L) {
+        // tail split: the full rounds unsplit, then the leftover tiles' two halves and
+        // their phase 2; the timing hook, when armed, brackets the three launches
+        hipEvent_t e0, e1;
+        const bool timed = take_profile(PROF_DW, &e0, &e1);
+        if (timed) (void)hipEventRecord(e0, s);
+        hipError_t e = launch_op1<OP, 0>(a, d, 8 * a.hyb_F, s);
+        if (e == hipSuccess) e = launch_op1<OP, 1>(a, d, 8 * a.hyb_L * 2, s);
+        if (e == hipSuccess) e = launch_op1<OP, 2>(a, d, 8 * a.hyb_L * DW_EPI_G, s);
+        if (timed) (void)hipEventRecord(e1, s);
+        return e;
+      }
+    }
     if (a.splits <= 1) return launch_op1<OP, 0>(a, d, ((a.ntiles + 7) / 8) * 8, s);
     // Split launch: the timing hook, when armed for this product, brackets both phases
     // with events on the stream.
@@ -1736,6 +1822,10 @@ hipError_t launch_gemm_dw(const uint16_t* x, const uint16_t* x_lo, const uint16_
                           float dge_alpha, bool reduce, void* split_ws, hipStream_t s) {
   GemmArgs a = {};
   set_splits(a, K, N, M, split_ws);
+  if (a.splits == 1 && split_ws && dw_hybrid(M, N, K, a.hyb_per, a.hyb_F, a.hyb_L)) {
+    a.splits = 2;
+    a.split_ws = static_cast<float*>(split_ws);
+  }
   a.P = K; a.Q = N; a.R = M;
   a.Lmat[0] = x; a.Rmat[0] = dy;
   a.npass = 1;

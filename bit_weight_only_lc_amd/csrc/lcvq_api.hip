@@ -99,7 +99,7 @@ inline BwdWs bwd_ws(int64_t M, int64_t N, int64_t K, int d, bool f32) {
   w.x_hi = w.dy_lo + dyb;
   w.x_lo = w.x_hi + xb;
   w.split = w.x_lo + xb;
-  w.total = w.split + up(gemm_split_bytes(K, N, M));   // dW's split partials, few-tile shapes
+  w.total = w.split + up(dw_split_bytes(M, N, K));   // dW's split partials
   return w;
 }
 
@@ -304,7 +304,7 @@ lcvq_status_t linear_bwd_impl(const void* dY, const void* X, lcvq_dtype_t dt, in
   const uint16_t* xb = f32 ? x_hi : static_cast<const uint16_t*>(X);
   // dW first; with dX wanted, the dX product then also reduces dW's dA/dB partials
   // (saving the reduction's own launch), otherwise a small kernel does.
-  void* split = gemm_split_bytes(K, N, M) ? static_cast<void*>(ws + w.split) : nullptr;
+  void* split = dw_split_bytes(M, N, K) ? static_cast<void*>(ws + w.split) : nullptr;
   e = launch_gemm_dw(xb, x_lo, dyb, dy_lo, r16t, mask, A, (int)M, (int)N, (int)K, d, dWp,
                      partials, dA, dB, Wp, alpha, !dX, split, s);
   if (e != hipSuccess) return LCVQ_ERR_HIP;

@@ -69,6 +69,9 @@ size_t gemm_fwd_split_bytes(int64_t M, int64_t N, int64_t K);
 // Rows of dA/dB partials ([rows][d*d + d] floats) the dW product writes for M tokens and a
 // weight [N, K]: one per tile, or DW_EPI_G per tile when its contraction is split.
 int dw_partial_rows(int64_t M, int64_t N, int64_t K);
+// Bytes of float32 partial tiles the dW product of this shape needs (few-tile split or the
+// tail split of its last partial round; 0: none).
+size_t dw_split_bytes(int64_t M, int64_t N, int64_t K);
 // Products. `*_lo` operands are NULL for bf16 activations; for float32 activations
 // they hold the low bf16 half of each value and add the cross terms in extra passes.
 hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint32_t* r16,

@@ -328,9 +328,9 @@ lcvq_status_t lcvq_mfma_probe(int64_t iters, uint32_t* sink, void* stream);
  * Profiling hook (changes no result). Arms a one-shot timing of the next launch of one
  * kernel by calls made from this host thread: the kernel is launched with
  * hipExtLaunchKernel between `start_event` and `stop_event` (hipEvent_t handles created
- * by the caller with timing enabled); a product split into two launches (few-tile forward
- * and dW, the decode product's two-launch path) gets the events recorded on the stream
- * around both. kernel_id: 1 quantizer, 2 forward product,
+ * by the caller with timing enabled); a product split into several launches (few-tile
+ * forward and dW, a dW whose last round of tiles is split, the decode product's two-launch
+ * path) gets the events recorded on the stream around all of them. kernel_id: 1 quantizer, 2 forward product,
  * 3 dX product, 4 dW product (with the straight-through epilogue), 5 decode product (where
  * it takes two launches, the X' prologue and the product, the events bracket both),
  * 6 backward prologue (r = dY 1 and the transposed codes, lcvq_linear_bwd), 7 Gram

@@ -561,6 +561,43 @@ def test_split_contraction_shapes(P, M, N, K, d, xdt):
     check_layer(P, inp, d, f"split M={M} N={N} K={K} d={d} {xdt}")
 
 
+# dW tail split: 288 and 272 tiles of 256 x 256 (one full round of the 256 CUs plus 32 or
+# 16 tiles): the full round runs unsplit, the leftover tiles split their contraction in
+# two, and a second launch adds the halves before the epilogue.
+TAIL_SHAPES = [(1000, 4608, 4096, 8, "bf16"),     # 288 dW tiles, ragged M
+               (1100, 4096, 4160, 16, "f32")]     # 272 dW tiles, ragged M and K, float32
+
+
+@pytest.mark.parametrize("M,N,K,d,xdt", TAIL_SHAPES)
+def test_dw_tail_split_shapes(P, M, N, K, d, xdt):
+    inp = SI.make_layer(N, K, M, d, seed=M + 5 * N + K, x_dtype=xdt, lo=-2.0, hi=5.0)
+    check_layer(P, inp, d, f"tail split M={M} N={N} K={K} d={d} {xdt}")
+
+
+def test_dw_tail_split_dge_no_dx_determinism(P):
+    """The tail split under the DGE estimator and without dX (the dA/dB partial rows then
+    reduced by their own launch): repeated calls give identical bytes, and match the
+    oracle."""
+    M, N, K, d = 1000, 4608, 4096, 8
+    inp = SI.make_layer(N, K, M, d, seed=4343, lo=-2.0, hi=5.0)
+    X, Wp, A, B, dY = (inp[k].cuda() for k in ("X", "Wp", "A", "B", "dY"))
+    f1 = P.linear_fwd(X, Wp, A, B, d)
+    g1 = P.linear_bwd(dY, X, f1["packed"], f1["mask"], A, B, d, want_dx=False, dge_wp=Wp,
+                      dge_alpha=5.0)
+    g2 = P.linear_bwd(dY, X, f1["packed"], f1["mask"], A, B, d, want_dx=False, dge_wp=Wp,
+                      dge_alpha=5.0)
+    torch.cuda.synchronize()
+    for k in ("dWp", "dA", "dB"):
+        assert torch.equal(g1[k], g2[k]), k
+    wp = inp["Wp"].numpy()
+    z, m = O.quantize(wp)
+    ob = O.linear_bwd(host(inp["dY"]), host(inp["X"]), z, m, inp["A"].double().numpy(),
+                      inp["B"].double().numpy(), d, wp=wp, dge_alpha=5.0)
+    note(f"tail split dge: dWp {fmt(check(host(g1['dWp']), ob['dWp'], TOL, 'tail dge dWp'))}")
+    note(f"  dA {fmt(check(host(g1['dA']), ob['dA'], TOL, 'tail dge dA'))}")
+    note(f"  dB {fmt(check(host(g1['dB']), ob['dB'], TOL, 'tail dge dB'))}")
+
+
 def test_split_contraction_dge_and_determinism(P):
     M, N, K, d = 1100, 320, 2112, 8
     inp = SI.make_layer(N, K, M, d, seed=4242, lo=-2.0, hi=5.0)
