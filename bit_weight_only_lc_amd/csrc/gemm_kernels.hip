@@ -94,10 +94,10 @@ struct GemmArgs {
   // epilogue. splits = 1: one launch, one workgroup per tile.
   int splits;
   float* split_ws;
-  // dW tail split (hyb_L > 0): tile t = x * hyb_per + i of XCD x (map_tile's order); the
-  // first hyb_F of each XCD's tiles run unsplit in one launch, the last hyb_L split their
-  // contraction in two (splits = 2) over a phase 1 and a phase 2 launch; their partial
-  // tiles are indexed x * hyb_L + (i - hyb_F).
+  // Tail split (forward and dW, hyb_L > 0): tile t = x * hyb_per + i of XCD x (map_tile's
+  // order); the first hyb_F of each XCD's tiles run unsplit in one launch, the last hyb_L
+  // split their contraction in two (splits = 2) over a phase 1 and a phase 2 launch; their
+  // partial tiles are indexed x * hyb_L + (i - hyb_F).
   int hyb_per, hyb_F, hyb_L;
   int bpt;                     // forward: tile rows along P, 256 or 128 (host side)
 };
@@ -144,10 +144,12 @@ __device__ __forceinline__ bool map_split(int b, int tilesQ, int ntiles, int spl
   return true;
 }
 
-// dW tail split: workgroup b of a launch with `per_tile` workgroups per leftover tile ->
-// its XCD's leftover tile (as map_tile numbers the tiles, so that the tile's workgroups of
-// both phases share the XCD that the unsplit tiles of that range use), the index of its
-// partial tiles, and j = its slot among the tile's workgroups (split or epilogue group).
+// Tail split: workgroup b of a launch with `per_tile` workgroups per leftover tile -> its
+// XCD's leftover tile (numbered as map_tile<GR> numbers the tiles, so that the tile's
+// workgroups of both phases share the XCD that the unsplit tiles of that range use), the
+// index of its partial tiles, and j = its slot among the tile's workgroups (split or
+// epilogue group).
+template <int GR>
 __device__ __forceinline__ bool map_hybrid(const GemmArgs& a, int b, int per_tile, int& tp,
                                            int& tq, int& tile, int& pidx, int& j) {
   const int x = b & 7, w = b >> 3;
@@ -156,7 +158,7 @@ __device__ __forceinline__ bool map_hybrid(const GemmArgs& a, int b, int per_til
   if (j >= per_tile) return false;
   tile = x * a.hyb_per + a.hyb_F + li;
   pidx = x * a.hyb_L + li;
-  tile_coords<4>(tile, a.tilesP, a.tilesQ, tp, tq);
+  tile_coords<GR>(tile, a.tilesP, a.tilesQ, tp, tq);
   return true;
 }
 
@@ -689,9 +691,14 @@ void k_gemm_ring(GemmArgs a) {
   // (256 KiB), so each XCD takes few tiles along the bf16 operand: forward tile-rows
   // are rows of X', dX tile-columns are rows of dY.
   constexpr int GR = OP == OP_FWD ? 2 : 16;
-  int split = 0;
+  int split = 0, pidx = 0;
   if constexpr (SPL == 1) {
-    if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+    if (a.hyb_L) {
+      if (!map_hybrid<GR>(a, blockIdx.x, 2, tp, tq, tile, pidx, split)) return;
+    } else {
+      if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
+      pidx = tile;
+    }
   } else if (!map_tile<GR>(blockIdx.x, a.tilesP, a.tilesQ, a.ntiles, tp, tq, tile)) {
     return;
   }
@@ -760,7 +767,7 @@ void k_gemm_ring(GemmArgs a) {
     __syncthreads();
   }
   if constexpr (SPL == 1) {
-    split_store<WI, WJ>(a, acc, tile, split, tid);
+    split_store<WI, WJ>(a, acc, pidx, split, tid);
     return;
   }
 
@@ -812,16 +819,24 @@ __global__ __launch_bounds__(FWD_EPI_NW * 64) void k_gemm_fwd_epi(GemmArgs a) {
   using T = Tiling<OP_FWD, 8>;
   constexpr int WI = T::WI, WJ = T::WJ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[FWD_EPI_NW * 32 * (32 * WJ + 4) * 4];
-  const int tile = (int)blockIdx.x % a.ntiles, g = (int)blockIdx.x / a.ntiles;
-  if (g >= FWD_EPI_G) return;
-  const int tp = tile / a.tilesQ, tq = tile % a.tilesQ;   // as map_split
+  int tile, g, tp, tq, pidx;
+  if (a.hyb_L) {
+    if (!map_hybrid<2>(a, blockIdx.x, FWD_EPI_G, tp, tq, tile, pidx, g)) return;
+  } else {
+    tile = (int)blockIdx.x % a.ntiles;
+    g = (int)blockIdx.x / a.ntiles;
+    if (g >= FWD_EPI_G) return;
+    tp = tile / a.tilesQ;                                // as map_split
+    tq = tile % a.tilesQ;
+    pidx = tile;
+  }
   const int p0 = tp * BT, q0 = tq * BT;
   const int tid = threadIdx.x, lane = tid & 63;
   const int lw = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int v = FWD_EPI_NW * g + lw;
   const int wp = v / T::WGQ, wq = v % T::WGQ;
   f32x16 acc[WI][WJ];
-  split_load<WI, WJ>(a, acc, tile, v * 64 + lane, 512);
+  split_load<WI, WJ>(a, acc, pidx, v * 64 + lane, 512);
   epilogue_fwd<FWD_EPI_NW, WI, WJ>(a, acc, p0, q0, wp, wq, lane, lw, smem);
 }
 
@@ -1288,7 +1303,7 @@ void k_gemm_dw(GemmArgs a) {
   int split = 0, pidx = 0;
   if constexpr (SPL == 1) {
     if (a.hyb_L) {
-      if (!map_hybrid(a, blockIdx.x, 2, tp, tq, tile, pidx, split)) return;
+      if (!map_hybrid<4>(a, blockIdx.x, 2, tp, tq, tile, pidx, split)) return;
     } else {
       if (!map_split(blockIdx.x, a.tilesQ, a.ntiles, a.splits, tp, tq, tile, split)) return;
       pidx = tile;
@@ -1407,7 +1422,7 @@ __global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[EPI_SMEM];
   int tile, g, tp, tq, pidx, prow;
   if (a.hyb_L) {
-    if (!map_hybrid(a, blockIdx.x, DW_EPI_G, tp, tq, tile, pidx, g)) return;
+    if (!map_hybrid<4>(a, blockIdx.x, DW_EPI_G, tp, tq, tile, pidx, g)) return;
     // group 0 writes the tile's own partial row, groups 1-3 rows after the unsplit tiles'
     prow = g == 0 ? tile : a.ntiles + (DW_EPI_G - 1) * pidx + g - 1;
   } else {
@@ -1446,13 +1461,17 @@ __global__ __launch_bounds__(DW_EPI_NW * 64) void k_gemm_dw_epi(GemmArgs a) {
 // full rounds run unsplit and each leftover tile splits its contraction in two, so that
 // the leftover work takes half a round instead of a whole one. Per XCD: hyb_per tiles,
 // the first hyb_F unsplit, the last hyb_L split. Needs at least 16 contraction stages.
-static bool dw_hybrid(int64_t M, int64_t N, int64_t K, int& per, int& F, int& L) {
-  const int64_t nt = gemm_tiles(K, N), r = nt % 256;
-  if (nt <= 256 || (nt % 8) || r == 0 || r > 128 || (M + BK - 1) / BK < 16) return false;
+// (The forward takes the same rule for its 256 x 256 tiles.)
+static bool tail_split(int64_t nt, int64_t R, int& per, int& F, int& L) {
+  const int64_t r = nt % 256;
+  if (nt <= 256 || (nt % 8) || r == 0 || r > 128 || (R + BK - 1) / BK < 16) return false;
   per = (int)(nt / 8);
   L = (int)(r / 8);
   F = per - L;
   return true;
+}
+static bool dw_hybrid(int64_t M, int64_t N, int64_t K, int& per, int& F, int& L) {
+  return tail_split(gemm_tiles(K, N), M, per, F, L);
 }
 
 // dA/dB partial rows the dW product of this shape writes (the reduction's input).
@@ -1615,8 +1634,17 @@ bool gemm_fwd_half_tiles(int64_t M, int64_t N) {
   return ((M + BT - 1) / BT) * tq <= 128 && ((M + 127) / 128) * tq > 128;
 }
 
+// The forward's 256 x 256 tiles: the few-tile split, or the tail split of a last round
+// at most half full.
+static bool fwd_hybrid(int64_t M, int64_t N, int64_t K, int& per, int& F, int& L) {
+  return gemm_splits(M, N, K) == 1 && tail_split(gemm_tiles(M, N), K, per, F, L);
+}
+
 size_t gemm_fwd_split_bytes(int64_t M, int64_t N, int64_t K) {
-  return gemm_fwd_half_tiles(M, N) ? 0 : gemm_split_bytes(M, N, K);
+  if (gemm_fwd_half_tiles(M, N)) return 0;
+  int per, F, L;
+  if (fwd_hybrid(M, N, K, per, F, L)) return (size_t)8 * L * 2 * BT * BT * 4;
+  return gemm_split_bytes(M, N, K);
 }
 
 template <int OP, int SPL>
@@ -1644,19 +1672,19 @@ static hipError_t launch_op(GemmArgs& a, int d, hipStream_t s) {
   if constexpr (OP == OP_DX) {
     return launch_op1<OP, 0>(a, d, ((a.ntiles + 7) / 8) * 8, s);
   } else {
-    if constexpr (OP == OP_DW) {
-      if (a.hyb_L) {
-        // tail split: the full rounds unsplit, then the leftover tiles' two halves and
-        // their phase 2; the timing hook, when armed, brackets the three launches
-        hipEvent_t e0, e1;
-        const bool timed = take_profile(PROF_DW, &e0, &e1);
-        if (timed) (void)hipEventRecord(e0, s);
-        hipError_t e = launch_op1<OP, 0>(a, d, 8 * a.hyb_F, s);
-        if (e == hipSuccess) e = launch_op1<OP, 1>(a, d, 8 * a.hyb_L * 2, s);
-        if (e == hipSuccess) e = launch_op1<OP, 2>(a, d, 8 * a.hyb_L * DW_EPI_G, s);
-        if (timed) (void)hipEventRecord(e1, s);
-        return e;
-      }
+    if (a.hyb_L) {
+      // tail split: the full rounds unsplit, then the leftover tiles' two halves and
+      // their phase 2; the timing hook, when armed, brackets the three launches
+      constexpr int id = OP == OP_FWD ? PROF_FWD : PROF_DW;
+      hipEvent_t e0, e1;
+      const bool timed = take_profile(id, &e0, &e1);
+      if (timed) (void)hipEventRecord(e0, s);
+      hipError_t e = launch_op1<OP, 0>(a, d, 8 * a.hyb_F, s);
+      if (e == hipSuccess) e = launch_op1<OP, 1>(a, d, 8 * a.hyb_L * 2, s);
+      if (e == hipSuccess)
+        e = launch_op1<OP, 2>(a, d, 8 * a.hyb_L * (OP == OP_DW ? DW_EPI_G : FWD_EPI_G), s);
+      if (timed) (void)hipEventRecord(e1, s);
+      return e;
     }
     if (a.splits <= 1) return launch_op1<OP, 0>(a, d, ((a.ntiles + 7) / 8) * 8, s);
     // Split launch: the timing hook, when armed for this product, brackets both phases
@@ -1784,6 +1812,10 @@ hipError_t launch_gemm_fwd(const uint16_t* xs, const uint16_t* xs_lo, const uint
   a.bpt = gemm_fwd_half_tiles(M, N) ? 128 : 256;
   if (a.bpt == 256) set_splits(a, M, N, K, split_ws);
   else a.splits = 1;
+  if (a.bpt == 256 && a.splits == 1 && split_ws && fwd_hybrid(M, N, K, a.hyb_per, a.hyb_F, a.hyb_L)) {
+    a.splits = 2;
+    a.split_ws = static_cast<float*>(split_ws);
+  }
   a.P = M; a.Q = N; a.R = K;
   a.Lmat[0] = xs; a.Lmat[1] = xs_lo;
   a.npass = xs_lo ? 2 : 1;

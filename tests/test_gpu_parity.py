@@ -561,11 +561,13 @@ def test_split_contraction_shapes(P, M, N, K, d, xdt):
     check_layer(P, inp, d, f"split M={M} N={N} K={K} d={d} {xdt}")
 
 
-# dW tail split: 288 and 272 tiles of 256 x 256 (one full round of the 256 CUs plus 32 or
-# 16 tiles): the full round runs unsplit, the leftover tiles split their contraction in
-# two, and a second launch adds the halves before the epilogue.
+# Tail split (dW, and the forward's 256 x 256 tiles): 288 and 272 tiles (one full round of
+# the 256 CUs plus 32 or 16 tiles): the full round runs unsplit, the leftover tiles split
+# their contraction in two, and a second launch adds the halves before the epilogue.
 TAIL_SHAPES = [(1000, 4608, 4096, 8, "bf16"),     # 288 dW tiles, ragged M
-               (1100, 4096, 4160, 16, "f32")]     # 272 dW tiles, ragged M and K, float32
+               (1100, 4096, 4160, 16, "f32"),     # 272 dW tiles, ragged M and K, float32
+               (4352, 4096, 1024, 8, "bf16"),     # 272 forward tiles
+               (4400, 4096, 1088, 4, "f32")]      # 288 forward tiles, ragged M and K
 
 
 @pytest.mark.parametrize("M,N,K,d,xdt", TAIL_SHAPES)
