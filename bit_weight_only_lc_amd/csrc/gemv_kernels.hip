@@ -30,10 +30,10 @@ __host__ __device__ inline int gemv_blocks(int64_t K) { return (int)((K + GK - 1
 
 // Dynamic LDS of the fused kernel: the dense X' limbs (nkb * 32 * M * 16 bytes), the block
 // scales (nkb * 128) and A, B; at least the final reduction's area.
-inline size_t gemv_fused_lds(int M, int K, int d, bool two) {
+inline size_t gemv_fused_lds(int M, int K, int d, int rg) {
   const size_t nkb = gemv_blocks(K);
   const size_t base = nkb * (32 * M + 8) * 16 + (size_t)(d * d + d) * 4;
-  return std::max<size_t>(base, (size_t)GWF * (two ? 2 : 1) * 64 * 16);
+  return std::max<size_t>(base, (size_t)GWF * rg * 64 * 16);
 }
 
 // The fused path (X' formed in LDS by every workgroup) repeats the M * K * d multiply-adds
@@ -58,13 +58,18 @@ inline bool gemv_fused(int M, int K, int64_t rows, int d) {
   if (M > 16 || M * nkb * d > GEMV_FUSED_WORK) return false;
   const bool two = rows > 16 * 256;
   if (rows > (two ? 2 : 1) * 16 * 256 || (two && M <= 4)) return false;
-  if (gemv_fused_lds(M, K, d, two) > GEMV_LDS_MAX) return false;
+  if (gemv_fused_lds(M, K, d, two ? 2 : 1) > GEMV_LDS_MAX) return false;
   return M <= 4 ? nkb <= 64 : nkb <= 16;
 }
-// Two row groups per workgroup: from 8192 rows on in the base range, beyond 4096 rows in
-// the extended range (each keeps the grid to about a workgroup per CU).
-inline bool gemv_two_groups(int M, int K, int64_t rows) {
-  return gemv_fused_base(M, gemv_blocks(K)) ? rows >= 2 * 16 * 256 : rows > 16 * 256;
+// Row groups of 16 per workgroup: in the base range two from 8192 rows on, and four from
+// 16384 rows on for one or two tokens with K up to 16 blocks (the 28672 rows of a batched
+// gate + up call then take 448 workgroups, which are resident at once, instead of 896);
+// in the extended range two beyond 4096 rows. Each keeps the grid to about one round.
+inline int gemv_row_groups(int M, int K, int64_t rows) {
+  const int nkb = gemv_blocks(K);
+  if (!gemv_fused_base(M, nkb)) return rows > 16 * 256 ? 2 : 1;
+  if (rows >= 4 * 16 * 256 && M <= 2 && nkb <= 16) return 4;
+  return rows >= 2 * 16 * 256 ? 2 : 1;
 }
 bool gemv_fused_path(int M, int K, int64_t rows, int d) { return gemv_fused(M, K, rows, d); }
 
@@ -640,17 +645,18 @@ static hipError_t launch_fused(dim3 grid, size_t shm, hipStream_t s, const uint1
 }
 
 // The instances gemv_fused() can reach: M = 3, 4 with two row groups only for K up to 32
-// blocks (KSW <= 4); M = 5..16 with K up to 16 blocks (KSW = 2).
+// blocks (KSW <= 4); M = 5..16 with K up to 16 blocks (KSW = 2); four row groups only for
+// M = 1, 2 and K up to 16 blocks.
 template <int D, int RG, int KSW>
 static hipError_t launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, const uint16_t* X,
                                  const GemvBatch& b, int K) {
   if (M == 1) return launch_fused<D, RG, KSW, 1>(grid, shm, s, X, b, K, M);
   if (M == 2) return launch_fused<D, RG, KSW, 2>(grid, shm, s, X, b, K, M);
-  if constexpr (KSW <= 4 || RG == 1) {
+  if constexpr (RG <= 2 && (KSW <= 4 || RG == 1)) {
     if (M == 3) return launch_fused<D, RG, KSW, 3>(grid, shm, s, X, b, K, M);
     if (M == 4) return launch_fused<D, RG, KSW, 4>(grid, shm, s, X, b, K, M);
   }
-  if constexpr (KSW <= 2) {     // the X' items a thread holds grow with the bound
+  if constexpr (RG <= 2 && KSW <= 2) {     // the X' items a thread holds grow with the bound
     if (M <= 8) return launch_fused<D, RG, KSW, 8>(grid, shm, s, X, b, K, M);
     if (M <= 12) return launch_fused<D, RG, KSW, 12>(grid, shm, s, X, b, K, M);
     if (M <= 16) return launch_fused<D, RG, KSW, 16>(grid, shm, s, X, b, K, M);
@@ -659,12 +665,14 @@ static hipError_t launch_fused_m(int M, dim3 grid, size_t shm, hipStream_t s, co
 }
 
 template <int D>
-static hipError_t launch_fused_d(int M, int K, bool two, size_t shm, hipStream_t s,
+static hipError_t launch_fused_d(int M, int K, int rg, size_t shm, hipStream_t s,
                                  const uint16_t* X, const GemvBatch& b, int wgs) {
   const int pw = (gemv_blocks(K) + GWF - 1) / GWF;
   const dim3 grid(wgs);
 #define LCVQ_FUSED(RG, KSW) return launch_fused_m<D, RG, KSW>(M, grid, shm, s, X, b, K)
-  if (two) {
+  if (rg == 4) {
+    LCVQ_FUSED(4, 2);               // gemv_row_groups() keeps four groups to K <= 4096
+  } else if (rg == 2) {
     if (pw <= 2) LCVQ_FUSED(2, 2);
     else if (pw <= 4) LCVQ_FUSED(2, 4);
     else LCVQ_FUSED(2, 8);
@@ -681,17 +689,17 @@ hipError_t launch_gemv_fused(const uint16_t* X, int M, int K, int d, GemvBatch b
                              hipStream_t s) {
   int64_t rows = 0;
   for (int i = 0; i < b.count; ++i) rows += b.N[i];
-  const bool two = gemv_two_groups(M, K, rows);
+  const int rg = gemv_row_groups(M, K, rows);
   int wgs = 0;
   for (int i = 0; i < b.count; ++i) {
     b.wg0[i] = wgs;
-    wgs += two ? (b.N[i] + 31) / 32 : b.N[i] / 16;
+    wgs += (b.N[i] + 16 * rg - 1) / (16 * rg);
   }
-  const size_t shm = gemv_fused_lds(M, K, d, two);
+  const size_t shm = gemv_fused_lds(M, K, d, rg);
   switch (d) {
-    case 4: return launch_fused_d<4>(M, K, two, shm, s, X, b, wgs);
-    case 8: return launch_fused_d<8>(M, K, two, shm, s, X, b, wgs);
-    default: return launch_fused_d<16>(M, K, two, shm, s, X, b, wgs);
+    case 4: return launch_fused_d<4>(M, K, rg, shm, s, X, b, wgs);
+    case 8: return launch_fused_d<8>(M, K, rg, shm, s, X, b, wgs);
+    default: return launch_fused_d<16>(M, K, rg, shm, s, X, b, wgs);
   }
 }
 
